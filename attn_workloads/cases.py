@@ -1,0 +1,75 @@
+"""The measured workloads and the small parity fixtures, by name.
+
+Shapes follow the pages' workloads: Gemma-4 global layers at head_dim 512,
+32 query heads over 4 KV heads for the 31B model (pegainfer issue 1051,
+"Description"; A custom attention kernel for Gemma 4 on the RTX PRO 6000,
+"The kernel in three steps") and one KV head for the 12B model (Flash-Decoding
+for MQA in CUDA, "One KV head breaks the textbook"), 64-token pages and 8 query
+heads over 4 KV heads for decode (vLLM flash-attention PR 199, "Performance").
+No public dataset is involved: every tensor is a seeded synthetic draw.
+"""
+from __future__ import annotations
+
+from typing import Callable, Dict
+
+from .gen import PagedCase, build_case, decode_lengths
+
+
+def tiny_prefill_mqa(device="cpu", seed=1) -> PagedCase:
+    """256 query rows causal over the same 256 keys, 8 q heads over 1 KV head, fp32 out."""
+    return build_case("tiny_prefill_mqa_256", seqs=[(256, 0, 256)], hq=8, hkv=1,
+                      seed=seed, out_dtype="fp32", device=device)
+
+
+def chunk_prefill_2k(device="cpu", seed=2) -> PagedCase:
+    """2048 rows causal over 2048 keys, 32 q heads over 4 KV heads, bf16 out."""
+    return build_case("chunk_prefill_2048", seqs=[(2048, 0, 2048)], hq=32, hkv=4,
+                      seed=seed, out_dtype="bf16", device=device)
+
+
+def chunk_prefill_8k_at_8k(device="cpu", seed=3) -> PagedCase:
+    """One 8192-row chunk at positions 8192..16383 over 16384 keys, 32/4 heads, bf16 out.
+
+    Hostile padding: 64 NaN q rows past the chunk, three spare NaN pages, a
+    NaN page behind the table's padding column.
+    """
+    return build_case("chunk_prefill_8192_at_8192", seqs=[(8192, 8192, 16384)], hq=32, hkv=4,
+                      seed=seed, out_dtype="bf16", device=device, q_pad_rows=64,
+                      extra_pages=3, table_pad=2)
+
+
+def long_mqa_32k(device="cpu", seed=4, q_zero=False, v_one=False) -> PagedCase:
+    """A 32768-token prompt as eight 4096-row causal chunks against the growing cache.
+
+    16 q heads over 1 KV head; every (row, head) of Q, K and V carries its own
+    factor U[0.5, 2]; fp32 out.  The whole 32768-key cache is resident from
+    the start, so keys past a chunk's kv_len are finite data that must stay
+    unread.  The q=0, V=1 variant must give exactly 1 everywhere.
+    """
+    chunks = [[(4096, 4096 * c, 4096 * (c + 1))] for c in range(8)]
+    name = "long_mqa_32k_8x4096" + ("_q0_v1" if (q_zero or v_one) else "")
+    return build_case(name, seqs=None, chunks=chunks, hq=16, hkv=1, seed=seed,
+                      out_dtype="fp32", device=device, row_scale=(0.5, 2.0),
+                      q_zero=q_zero, v_one=v_one)
+
+
+def decode_b64(device="cpu", seed=5, kv_dtype="bf16", batch=64, lo=4096, hi=28672) -> PagedCase:
+    """Batch-64 single-token decode, 8 q heads over 4 KV heads, lengths U{4096..28672}.
+
+    The FP8 variant stores the same bf16 values as E4M3 bytes with per-tensor
+    k_scale and v_scale.
+    """
+    lens = decode_lengths(batch, lo, hi, seed)
+    seqs = [(1, L - 1, L) for L in lens]
+    name = f"decode_b{batch}_splitk" + ("_fp8" if kv_dtype != "bf16" else "")
+    return build_case(name, seqs=seqs, hq=8, hkv=4, seed=seed, out_dtype="bf16",
+                      device=device, kv_dtype=kv_dtype)
+
+
+WORKLOADS: Dict[str, Callable[..., PagedCase]] = {
+    "tiny_prefill_mqa_256": tiny_prefill_mqa,
+    "chunk_prefill_2048": chunk_prefill_2k,
+    "chunk_prefill_8192_at_8192": chunk_prefill_8k_at_8k,
+    "long_mqa_32k_8x4096": long_mqa_32k,
+    "decode_b64_splitk": decode_b64,
+}
