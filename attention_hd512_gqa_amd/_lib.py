@@ -1,0 +1,134 @@
+"""ctypes binding of libattn_hd512.so: argument marshalling only.
+
+Every step of the attention runs in the library's HIP kernels; this module
+checks tensor dtypes, devices and contiguity, then passes raw device
+pointers, sizes and the current HIP stream.  Torch only owns the memory.
+If the library is not built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_hd512.so")
+
+ATTN_BF16, ATTN_FP32, ATTN_FP8_E4M3 = 0, 1, 2
+_DTYPE_CODES = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_FP32}
+_KV_CODES = {"bf16": ATTN_BF16, "fp8_e4m3": ATTN_FP8_E4M3}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise AttnError(f"{LIB_PATH} is missing: build it with "
+                            "`python -m attention_hd512_gqa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.attn_prefill_hd512.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P]
+        L.attn_prefill_hd512.restype = I
+        L.attn_decode_splitk_workspace_size.argtypes = [I, I, I, I, I]
+        L.attn_decode_splitk_workspace_size.restype = SZ
+        L.attn_decode_splitk.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, F,
+                                         P, SZ, P, I, P]
+        L.attn_decode_splitk.restype = I
+        L.attn_hbm_read_probe.argtypes = [P, SZ, P, P]
+        L.attn_hbm_read_probe.restype = I
+        L.attn_hbm_probe_sink_words.argtypes = [SZ]
+        L.attn_hbm_probe_sink_words.restype = SZ
+        L.attn_status_string.argtypes = [I]
+        L.attn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().attn_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise AttnError(f"{what}: {status_string(code)} (status {code})")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise AttnError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise AttnError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise AttnError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out, *,
+            total_q: int, max_q_len: int, softmax_scale: float, stream=None) -> None:
+    """Chunked causal prefill (attn_prefill_hd512).  Sizes are host ints: no sync."""
+    num_pages, hkv, page, d = k_pages.shape
+    hq = q.shape[1]
+    batch = kv_lens.shape[0]
+    code = lib().attn_prefill_hd512(
+        _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.bfloat16),
+        _dev(v_pages, "v_pages", torch.bfloat16), _dev(page_table, "page_table", torch.int32),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(q_start, "q_start", torch.int32),
+        _dev(kv_lens, "kv_lens", torch.int32), int(batch), int(total_q), int(max_q_len),
+        int(hq), int(hkv), int(d), int(page), int(num_pages), int(page_table.shape[1]),
+        float(softmax_scale), _dev(out, "out", (torch.bfloat16, torch.float32)),
+        _DTYPE_CODES[out.dtype], _stream(stream))
+    _check(code, "attn_prefill_hd512")
+
+
+def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_kv_len: int,
+                          keys_per_split: int = 0) -> int:
+    return int(lib().attn_decode_splitk_workspace_size(int(batch), int(num_q_heads),
+                                                       int(num_kv_heads), int(max_kv_len),
+                                                       int(keys_per_split)))
+
+
+def decode(q, k_pages, v_pages, page_table, kv_lens, out, workspace, *, max_kv_len: int,
+           softmax_scale: float, kv_dtype: str = "bf16", k_scale: float = 1.0,
+           v_scale: float = 1.0, keys_per_split: int = 0, stream=None) -> None:
+    """Split-K decode (attn_decode_splitk): split kernel then merge kernel."""
+    num_pages, hkv, page, d = k_pages.shape
+    batch, hq = q.shape[0], q.shape[1]
+    kvt = torch.bfloat16 if kv_dtype == "bf16" else torch.uint8
+    code = lib().attn_decode_splitk(
+        _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt), _dev(v_pages, "v_pages", kvt),
+        _KV_CODES[kv_dtype], float(k_scale), float(v_scale),
+        _dev(page_table, "page_table", torch.int32), _dev(kv_lens, "kv_lens", torch.int32),
+        int(batch), int(hq), int(hkv), int(d), int(page), int(num_pages),
+        int(page_table.shape[1]), int(max_kv_len), int(keys_per_split), float(softmax_scale),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
+        _stream(stream))
+    _check(code, "attn_decode_splitk")
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Stream `buf` once (measurement helper for the HBM read roofline)."""
+    nbytes = buf.numel() * buf.element_size()
+    code = lib().attn_hbm_read_probe(_dev(buf, "buf"), nbytes, _dev(sink, "sink"), _stream(stream))
+    _check(code, "attn_hbm_read_probe")
+
+
+def hbm_probe_sink_words(nbytes: int) -> int:
+    return int(lib().attn_hbm_probe_sink_words(int(nbytes)))

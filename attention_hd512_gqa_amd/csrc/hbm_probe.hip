@@ -1,0 +1,48 @@
+// Same-process HBM read roofline: stream a buffer once with 16-byte loads.
+// The buffer should be well beyond the 256 MB Infinity Cache so the rate is
+// the HBM rate.  Each workgroup folds what it read into one word of `sink`
+// so the loads cannot be dropped.
+#include "device_common.h"
+#include "attn_host.h"
+
+namespace attn {
+namespace {
+
+constexpr int kProbeThreads = 256;
+constexpr int kProbeUnroll = 8;          // 16-byte loads in flight per thread
+constexpr size_t kBytesPerWg = (size_t)kProbeThreads * 16 * kProbeUnroll;
+
+__global__ __launch_bounds__(kProbeThreads) void hbm_read_kernel(const u32x4* buf, size_t n16,
+                                                                 uint32_t* sink) {
+    u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+    const size_t base = (size_t)blockIdx.x * kProbeThreads * kProbeUnroll + threadIdx.x;
+    u32x4 v[kProbeUnroll];
+#pragma unroll
+    for (int i = 0; i < kProbeUnroll; ++i) {
+        const size_t idx = base + (size_t)i * kProbeThreads;
+        v[i] = idx < n16 ? __builtin_nontemporal_load(buf + idx) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kProbeUnroll; ++i) acc ^= v[i];
+    uint32_t w = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    for (int off = 32; off > 0; off >>= 1) w ^= __shfl_xor(w, off);
+    if (threadIdx.x == 0) sink[blockIdx.x] = w;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" size_t attn_hbm_probe_sink_words(size_t bytes) {
+    return (bytes + attn::kBytesPerWg - 1) / attn::kBytesPerWg;
+}
+
+extern "C" int attn_hbm_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream) {
+    using namespace attn;
+    if (!buf || !sink) return ATTN_ERR_NULL;
+    if (bytes == 0 || bytes % 16) return ATTN_ERR_SHAPE;
+    const size_t grid = attn_hbm_probe_sink_words(bytes);
+    if (grid > 0x7fffffffULL) return ATTN_ERR_SHAPE;
+    hipLaunchKernelGGL(hbm_read_kernel, dim3((unsigned)grid), dim3(kProbeThreads), 0, stream,
+                       (const u32x4*)buf, bytes / 16, (uint32_t*)sink);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}

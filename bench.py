@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the hd512 paged GQA attention path on one MI355X.
+
+Headline (one JSON line on stdout): causal prefill TFLOP/s of one 8192-row
+chunk at positions 8192..16383 over 16384 paged keys, 32 query heads over 4
+KV heads, head_dim 512, bf16 in and out -- the shape the pegainfer issue 1051
+("Description") measures -- with its fraction of a bf16 GEMM measured in the
+same process and of the chip's dense bf16 MFMA peak.  One step is one prefill
+launch; inputs are resident in HBM before the timed region.
+
+Also reported: split-K decode (batch 64, 8 query heads over 4 KV heads,
+lengths U{4096..28672}, bf16 and FP8-E4M3 pools) in us per call and GB/s of
+live KV bytes against an HBM read probe taken in the same process; the other
+prefill workloads; and the CPU oracle timed on a bounded sample of the
+headline workload (a baseline, not a target).
+
+FLOP convention: 4 * head_dim per visible (query, key) pair and head.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (no sparsity)
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the other prefill workloads")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target wall time of the CPU-oracle sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: this library has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_hd512_gqa_amd as A
+    import attn_workloads as W
+
+    A.lib()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n, warmup):
+        """Mean ms per call of fn over n calls after warmup, events on the launch stream."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # ---- same-process bf16 GEMM roofline ---------------------------------
+    def gemm_rate():
+        best = 0.0
+        for n in (8192, 16384):
+            a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+            b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+            ms = timed(lambda: torch.matmul(a, b), 10 if n == 8192 else 4, 3)
+            best = max(best, 2.0 * n ** 3 / (ms * 1e-3) / 1e12)
+            del a, b
+        torch.cuda.empty_cache()
+        return best
+
+    gemm_before = gemm_rate()
+    log(f"bf16 GEMM roofline (torch.matmul, before): {gemm_before:.1f} TFLOP/s")
+
+    # ---- same-process HBM read probe --------------------------------------
+    hbm_bytes = 8 << 30
+    buf = torch.empty(hbm_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(A.hbm_probe_sink_words(hbm_bytes), dtype=torch.int32, device="cuda")
+    ms = timed(lambda: A.hbm_read_probe(buf, sink), 10, 3)
+    hbm_read = hbm_bytes / (ms * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    log(f"HBM read probe over 8 GiB: {hbm_read:.0f} GB/s")
+
+    # ---- headline: prefill of one 8192-row chunk at 8192..16383 ------------
+    case = W.chunk_prefill_8k_at_8k(device="cuda")
+    lc = case.launches[0]
+    out = torch.empty((lc.total_q, case.num_q_heads, W.HEAD_DIM), dtype=torch.bfloat16,
+                      device="cuda")
+    flops = W.prefill_flops(lc.q_lens, lc.q_starts, lc.kv_lens, case.num_q_heads)
+
+    def prefill_step(c=case, l=lc, o=out):
+        A.prefill(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q, l.q_start, l.kv_len, o,
+                  total_q=l.total_q, max_q_len=l.max_q_len, softmax_scale=c.softmax_scale,
+                  stream=stream)
+
+    for _ in range(args.warmup):
+        prefill_step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        prefill_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    log(f"prefill chunk 8192@8192: {ms_step:.3f} ms/launch, {tflops:.1f} TFLOP/s")
+    assert torch.isfinite(out.float()).all()
+
+    extra = {}
+    if not args.no_extra:
+        c2 = W.chunk_prefill_2k(device="cuda")
+        l2 = c2.launches[0]
+        o2 = torch.empty((l2.total_q, c2.num_q_heads, W.HEAD_DIM), dtype=torch.bfloat16,
+                         device="cuda")
+        ms2 = timed(lambda: prefill_step(c2, l2, o2), 20, 5)
+        f2 = W.prefill_flops(l2.q_lens, l2.q_starts, l2.kv_lens, c2.num_q_heads)
+        extra["chunk_prefill_2048"] = {"ms_per_launch": ms2, "tflops": f2 / (ms2 * 1e-3) / 1e12}
+        del c2, o2
+        c4 = W.long_mqa_32k(device="cuda")
+        o4 = torch.empty((4096, c4.num_q_heads, W.HEAD_DIM), dtype=torch.float32, device="cuda")
+
+        def long_prompt():
+            for l4 in c4.launches:
+                prefill_step(c4, l4, o4)
+        ms4 = timed(long_prompt, 3, 1)
+        f4 = sum(W.prefill_flops(l.q_lens, l.q_starts, l.kv_lens, c4.num_q_heads)
+                 for l in c4.launches)
+        extra["long_mqa_32k_8x4096"] = {"ms_per_prompt": ms4, "tflops": f4 / (ms4 * 1e-3) / 1e12}
+        del c4, o4
+        torch.cuda.empty_cache()
+        log(f"other prefill workloads: {json.dumps(extra)}")
+
+    # ---- split-K decode ------------------------------------------------------
+    decode = {}
+    if not args.no_decode:
+        for kv_dtype in ("bf16", "fp8_e4m3"):
+            dc = W.decode_b64(device="cuda", kv_dtype=kv_dtype)
+            dl = dc.launches[0]
+            dout = torch.empty((dl.batch, dc.num_q_heads, W.HEAD_DIM), dtype=torch.bfloat16,
+                               device="cuda")
+            ws = torch.empty(A.decode_workspace_size(dl.batch, dc.num_q_heads, dc.num_kv_heads,
+                                                     dl.max_kv_len) // 4,
+                             dtype=torch.float32, device="cuda")
+            qd = dl.q[:dl.batch].contiguous()
+
+            def decode_call():
+                A.decode(qd, dc.k_pool, dc.v_pool, dc.page_table, dl.kv_len, dout, ws,
+                         max_kv_len=dl.max_kv_len, softmax_scale=dc.softmax_scale,
+                         kv_dtype=dc.kv_dtype, k_scale=dc.k_scale, v_scale=dc.v_scale,
+                         stream=stream)
+            # median of 7 windows of 20 calls after warmup (windowed timing)
+            for _ in range(10):
+                decode_call()
+            wins = sorted(timed(decode_call, 20, 0) for _ in range(7))
+            us = wins[3] * 1e3
+            nbytes = W.decode_kv_bytes(dl.kv_lens, dc.num_kv_heads, W.HEAD_DIM,
+                                       1 if kv_dtype == "fp8_e4m3" else 2)
+            gbps = nbytes / (us * 1e-6) / 1e9
+            decode[kv_dtype] = {
+                "workload": dc.name, "us_per_call": us, "us_min": wins[0] * 1e3,
+                "us_max": wins[-1] * 1e3, "kv_bytes": nbytes, "GB_per_s": gbps,
+                "frac_of_hbm_probe": gbps / hbm_read, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS,
+                "kernels": "split + merge, one stream"}
+            log(f"decode {kv_dtype}: {us:.1f} us/call, {gbps:.0f} GB/s "
+                f"({100 * gbps / hbm_read:.1f}% of probe)")
+            del dc, dout, ws, qd
+            torch.cuda.empty_cache()
+
+    gemm_after = gemm_rate()
+    log(f"bf16 GEMM roofline (after): {gemm_after:.1f} TFLOP/s")
+    gemm = max(gemm_before, gemm_after)
+
+    # ---- CPU oracle on a bounded sample of the headline workload ------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        host = case.to("cpu")
+        cores = len(os.sched_getaffinity(0))
+        hq = case.num_q_heads
+
+        def run_tokens(tokens):
+            rows = (np.asarray(tokens)[:, None] * hq + np.arange(hq)[None, :]).reshape(-1)
+            t0 = time.perf_counter()
+            oracle.attend_rows(host, rows, threads=cores)
+            wall = time.perf_counter() - t0
+            pairs = sum(min(lc.q_starts[0] + t + 1, lc.kv_lens[0]) for t in tokens) * hq
+            return wall, pairs * 4 * W.HEAD_DIM
+
+        probe_tokens = [lc.total_q - 1 - 64 * i for i in range(4)]
+        wall, f = run_tokens(probe_tokens)
+        rate = f / wall
+        n_tok = max(4, min(lc.total_q, int(args.cpu_seconds * rate / (f / len(probe_tokens)))))
+        tokens = sorted(set(np.linspace(0, lc.total_q - 1, n_tok).astype(int).tolist()))
+        wall, f = run_tokens(tokens)
+        cpu = {"value": f / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": f"{len(tokens)} query rows spread over the 8192-row chunk, all "
+                         f"{hq} heads ({f / 1e9:.1f} GFLOP algorithmic, {wall:.1f} s wall, "
+                         f"fp32 C oracle, {cores} threads)"}
+        log(f"CPU oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cores} threads")
+
+    result = {
+        "metric": "hd512 causal prefill TFLOP/s + % of same-process bf16 MFMA GEMM peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled 64-token page table)",
+        "config": {"workload": case.name, "q_rows": lc.total_q, "q_start": lc.q_starts[0],
+                   "kv_len": lc.kv_lens[0], "q_heads": case.num_q_heads,
+                   "kv_heads": case.num_kv_heads, "head_dim": W.HEAD_DIM,
+                   "page_size": W.PAGE_SIZE, "out_dtype": "bf16", "flop_per_launch": flops},
+        "gemm_roofline": {"tflops": gemm, "before": gemm_before, "after": gemm_after,
+                          "frac": tflops / gemm, "how": "torch.matmul bf16 8192^3 and 16384^3, best"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "prefill_hd512_kernel"},
+        "hbm": {"read_probe_GB_per_s": hbm_read, "probe_bytes": hbm_bytes},
+        "decode": decode,
+        "prefill_other": extra,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * attn_hd512 -- head-dim-512 causal GQA/MQA attention over a paged KV cache
+ * for AMD MI355X (gfx950).  C ABI of libattn_hd512.so.
+ *
+ * Two operations, both FlashAttention forwards whose online softmax never
+ * writes the [query x attended key] score matrix to device memory (Writing a
+ * FlashAttention Prefill Kernel for Gemma 4, intro and "The starting point"):
+ *   - attn_prefill_hd512: chunked causal prefill, one call per chunk; a chunk
+ *     attends to every key before it in the cache (pegainfer issue 1051,
+ *     "Description");
+ *   - attn_decode_splitk: Flash-Decoding for one query token per sequence:
+ *     the key range is split across workgroups, each writes an unnormalised
+ *     (O, m, l) partial, and a merge kernel combines them (Flash-Decoding for
+ *     MQA in CUDA, "One KV head breaks the textbook").
+ *
+ * Common conventions
+ *   Pointers are device pointers unless stated otherwise; the caller owns and
+ *   frees every buffer.  Calls only enqueue work on `stream` and never
+ *   synchronise; the library allocates nothing and keeps no per-call state.
+ *   Shapes, counts and pointers are checked on the host before any launch;
+ *   a failed check returns a non-zero attn_status_t and launches nothing.
+ *   Device-resident data (page ids, lengths, offsets) is NOT validated,
+ *   because that would need a device synchronisation (vLLM flash-attention
+ *   PR 199, review finding F2 makes the same choice); it is clamped inside
+ *   the kernels so that bad values cannot read outside the buffers, but the
+ *   results are then undefined.
+ *
+ *   head_dim must be 512 and page_size 64.  num_q_heads must be a multiple
+ *   of num_kv_heads, with group g = num_q_heads / num_kv_heads <= 128; query
+ *   head h uses KV head h / g (consecutive grouping, so that [B, 1, Hq*D] and
+ *   [B*Hkv, g, D] are one layout: Flash-Decoding for MQA in CUDA, "One KV head
+ *   breaks the textbook").
+ *
+ *   Page pools: [num_pages][num_kv_heads][64][512], row-major.  One (page, KV
+ *   head) is one contiguous 64-key tile, the pool being paged at the key-tile
+ *   size (pegainfer issue 1051, "Proposed Plan").  Logical key j of sequence b
+ *   is slot j % 64 of page page_table[b * max_pages_per_seq + j / 64].  Only
+ *   keys j < kv_lens[b] are ever read: page slots and table entries past the
+ *   live band may hold anything, NaN included, without affecting results
+ *   (pegainfer issue 1051, "Acceptance Criteria"; Flash-Decoding for MQA in
+ *   CUDA, "The test that catches what parity misses").
+ */
+#ifndef ATTN_HD512_H
+#define ATTN_HD512_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_BF16 = 0,      /* bfloat16 */
+    ATTN_FP32 = 1,      /* IEEE binary32 */
+    ATTN_FP8_E4M3 = 2   /* OCP 8-bit E4M3FN (no infinities, max 448) */
+} attn_dtype_t;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = 2,        /* a count or size is out of range or inconsistent */
+    ATTN_ERR_UNSUPPORTED = 3,  /* valid request outside the supported set (dtype, head_dim, ...) */
+    ATTN_ERR_WORKSPACE = 4,    /* decode workspace missing or too small */
+    ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} attn_status_t;
+
+/*
+ * Chunked causal prefill.
+ *
+ *   q            bf16 [total_q][num_q_heads][512]; rows cu_seqlens_q[b] ..
+ *                cu_seqlens_q[b+1]-1 are sequence b's query rows, in order.
+ *   k_pages,
+ *   v_pages      bf16 page pools (layout above).
+ *   page_table   int32 [batch][max_pages_per_seq].
+ *   cu_seqlens_q int32 [batch + 1], cu_seqlens_q[0] = 0, non-decreasing,
+ *                cu_seqlens_q[batch] = total_q.
+ *   q_start_pos  int32 [batch]: absolute position of sequence b's first
+ *                query row (the chunk offset).
+ *   kv_lens      int32 [batch]: keys in the cache for sequence b, this chunk
+ *                included.  Precondition: q_start_pos[b] + q_len_b <= kv_lens[b]
+ *                <= 64 * max_pages_per_seq.
+ *   out          [total_q][num_q_heads][512] of out_dtype (ATTN_BF16, rounded
+ *                to nearest even, or ATTN_FP32).  Only rows < total_q are
+ *                written.
+ *
+ * Query row i of sequence b sits at position p = q_start_pos[b] + i and sees
+ * keys j <= p (bottom-right causal alignment).  Its output is
+ * softmax(scale * q K^T) V over those keys, computed with fp32 statistics and
+ * accumulators from bf16 products.  max_q_len is an upper bound of the
+ * per-sequence query counts and sets the grid; sequences with q_len = 0 are
+ * allowed and write nothing.
+ */
+int attn_prefill_hd512(const void* q, const void* k_pages, const void* v_pages,
+                       const int32_t* page_table, const int32_t* cu_seqlens_q,
+                       const int32_t* q_start_pos, const int32_t* kv_lens, int batch,
+                       int total_q, int max_q_len, int num_q_heads, int num_kv_heads,
+                       int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                       float softmax_scale, void* out, int out_dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace attn_decode_splitk needs for these sizes
+ * (fp32 partial outputs plus (m, l) per split, query head and sequence).
+ * keys_per_split = 0 selects the library default.  Returns 0 for invalid sizes.
+ */
+size_t attn_decode_splitk_workspace_size(int batch, int num_q_heads, int num_kv_heads,
+                                         int max_kv_len, int keys_per_split);
+
+/*
+ * Split-K decode: one query token per sequence at position kv_lens[b] - 1.
+ *
+ *   q            bf16 [batch][num_q_heads][512].
+ *   k_pages,
+ *   v_pages      page pools of kv_dtype: ATTN_BF16, or ATTN_FP8_E4M3 bytes
+ *                whose real values are byte * k_scale (keys) and
+ *                byte * v_scale (values), per-tensor fp32 scales.  FP8 values
+ *                are widened exactly to bf16 inside the kernel and every
+ *                product is accumulated in fp32 per key block (vLLM
+ *                flash-attention PR 199, commit 3 of the first review).
+ *   page_table, kv_lens   as for prefill; 1 <= kv_lens[b] <= max_kv_len.
+ *   keys_per_split        keys per partial, a positive multiple of 64, or 0
+ *                for the library default.
+ *   workspace    device buffer of at least
+ *                attn_decode_splitk_workspace_size(...) bytes; contents on
+ *                entry are ignored; it must not be shared by concurrent calls.
+ *   out          [batch][num_q_heads][512] of out_dtype (ATTN_BF16 or ATTN_FP32).
+ *
+ * Two kernels run back to back on `stream`: the split kernel writes one
+ * partial per (sequence, KV head, split) for every query head of the group,
+ * and the merge kernel combines them.  A split past a sequence's kv_len is
+ * empty (m = -inf, l = 0) and contributes nothing.
+ */
+int attn_decode_splitk(const void* q, const void* k_pages, const void* v_pages, int kv_dtype,
+                       float k_scale, float v_scale, const int32_t* page_table,
+                       const int32_t* kv_lens, int batch, int num_q_heads, int num_kv_heads,
+                       int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                       int max_kv_len, int keys_per_split, float softmax_scale,
+                       void* workspace, size_t workspace_bytes, void* out, int out_dtype,
+                       hipStream_t stream);
+
+/*
+ * Measurement helper: streams `bytes` (a multiple of 16) of device memory
+ * once with 16-byte loads and writes one word per workgroup to `sink`
+ * (at least attn_hbm_probe_sink_words(bytes) uint32 values).  Used to take
+ * the same-process HBM read roofline that decode is reported against.
+ */
+int attn_hbm_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream);
+size_t attn_hbm_probe_sink_words(size_t bytes);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_HD512_H */

@@ -1,0 +1,114 @@
+"""C ABI checks that need no GPU: exported symbols and host-side validation.
+
+Every call below carries at least one argument that the host checks reject,
+so no kernel is ever launched (the pointers are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_hd512.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import attention_hd512_gqa_amd as A
+    if not os.path.exists(A.LIB_PATH):
+        from attention_hd512_gqa_amd import build
+        build.build()
+    return A.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("attn_prefill_hd512", "attn_decode_splitk", "attn_decode_splitk_workspace_size",
+              "attn_status_string", "attn_hbm_read_probe", "attn_hbm_probe_sink_words"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} is declared in the header but not exported"
+
+
+def test_status_strings(L):
+    for code in range(6):
+        assert L.attn_status_string(code)
+    assert L.attn_status_string(99) == b"unknown status"
+
+
+FAKE = 0x1000  # never dereferenced: each call fails validation first
+
+
+def prefill(L, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, pt=FAKE, cu=FAKE, qs=FAKE, kl=FAKE, batch=1, total_q=4,
+             max_q_len=4, hq=8, hkv=1, d=512, page=64, num_pages=4, max_pages=4, scale=0.04,
+             out=FAKE, out_dtype=1, stream=None)
+    a.update(over)
+    return L.attn_prefill_hd512(a["q"], a["k"], a["v"], a["pt"], a["cu"], a["qs"], a["kl"],
+                                a["batch"], a["total_q"], a["max_q_len"], a["hq"], a["hkv"],
+                                a["d"], a["page"], a["num_pages"], a["max_pages"], a["scale"],
+                                a["out"], a["out_dtype"], a["stream"])
+
+
+def test_prefill_validation(L):
+    assert prefill(L, q=None) == 1
+    assert prefill(L, out=None) == 1
+    assert prefill(L, batch=0) == 2
+    assert prefill(L, hq=6, hkv=4) == 2
+    assert prefill(L, d=256) == 3
+    assert prefill(L, page=16) == 3
+    assert prefill(L, out_dtype=2) == 3
+    assert prefill(L, hq=256, hkv=1) == 3
+    assert prefill(L, scale=float("nan")) == 2
+    assert prefill(L, max_q_len=5) == 2          # larger than total_q
+    assert prefill(L, total_q=0, max_q_len=0) == 0  # empty call: nothing to launch
+
+
+def decode(L, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kvd=0, ks=1.0, vs=1.0, pt=FAKE, kl=FAKE, batch=2, hq=8,
+             hkv=4, d=512, page=64, num_pages=8, max_pages=4, max_kv=256, kps=0, scale=0.04,
+             ws=FAKE, ws_bytes=1 << 30, out=FAKE, out_dtype=0, stream=None)
+    a.update(over)
+    return L.attn_decode_splitk(a["q"], a["k"], a["v"], a["kvd"], a["ks"], a["vs"], a["pt"],
+                                a["kl"], a["batch"], a["hq"], a["hkv"], a["d"], a["page"],
+                                a["num_pages"], a["max_pages"], a["max_kv"], a["kps"],
+                                a["scale"], a["ws"], a["ws_bytes"], a["out"], a["out_dtype"],
+                                a["stream"])
+
+
+def test_decode_validation(L):
+    assert decode(L, v=None) == 1
+    assert decode(L, kps=100) == 2                 # not a multiple of 64
+    assert decode(L, max_kv=257) == 2              # beyond max_pages * 64
+    assert decode(L, hq=6) == 2
+    assert decode(L, d=128) == 3
+    assert decode(L, hq=64, hkv=2) == 3            # group of 32 > 16
+    assert decode(L, kvd=1) == 3                   # fp32 pool
+    assert decode(L, out_dtype=2) == 3
+    assert decode(L, kvd=2, ks=0.0) == 2           # FP8 needs positive scales
+    assert decode(L, ws=None) == 4
+    assert decode(L, ws_bytes=16) == 4
+
+
+def test_workspace_size(L):
+    n = L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 1024)
+    assert n == 64 * 8 * 28 * (512 + 2) * 4
+    assert L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 100) == 0
+    assert L.attn_decode_splitk_workspace_size(0, 8, 4, 28672, 0) == 0
+    assert L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 0) > 0
+
+
+def test_probe_validation(L):
+    assert L.attn_hbm_read_probe(None, 1024, FAKE, None) == 1
+    assert L.attn_hbm_read_probe(FAKE, 1000, FAKE, None) == 2
+    assert L.attn_hbm_probe_sink_words(1 << 20) >= 1

@@ -1,0 +1,117 @@
+"""GPU parity of attn_prefill_hd512 against the CPU oracle (through the C ABI).
+
+Small shapes are compared element by element on every output; the measured
+workloads at full size are compared on sampled query rows (all heads of each
+sampled row, the first and last rows of the chunk included) and through
+properties that hold at any size (q = 0 with V = 1 gives exactly 1).  Every
+case also checks that padding rows of the output stay untouched and that
+NaN-poisoned page slots, spare pages and table padding never leak in.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_workloads as W
+import oracle
+from _gpu_helpers import (check_parity, library, run_prefill, sample_rows, sentinel_intact)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    return library()
+
+
+def _full_check(A, case, out_dtype=None, pad_rows=5, li=0):
+    out = run_prefill(A, case, li=li, out_dtype=out_dtype, pad_rows=pad_rows)
+    lc = case.launches[li]
+    ref = oracle.attend_all(case.to("cpu"), launch_idx=li)
+    assert sentinel_intact(out[lc.total_q:]), "rows past total_q were written"
+    return check_parity(out[:lc.total_q], ref, f"{case.name}[{li}] out={out.dtype}")
+
+
+SMALL = [
+    # (seqs (q_len, q_start, kv_len), hq, hkv)
+    ([(1, 0, 1)], 8, 1),                          # one row, one key
+    ([(37, 0, 37)], 8, 1),                        # ragged tile, partial page
+    ([(100, 28, 128)], 4, 4),                     # MHA (g = 1), offset chunk
+    ([(64, 64, 200)], 16, 8),                     # g = 2, keys past the chunk's end masked
+    ([(19, 5, 24), (70, 130, 200), (1, 63, 64)], 12, 4),  # g = 3 (rows left unused), batch 3
+    ([(130, 0, 130), (7, 300, 307)], 16, 1),      # g = 16 (8 tokens per workgroup)
+    ([(129, 2000, 2129)], 32, 4),                 # g = 8, long prefix, one-row tail tile
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: f"{s[0]}-{s[1]}x{s[2]}")
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_small_shapes(A, shape, out_dtype):
+    seqs, hq, hkv = shape
+    case = W.build_case("small", seqs=seqs, hq=hq, hkv=hkv, seed=17, out_dtype=out_dtype,
+                        device="cuda", q_pad_rows=3, extra_pages=2, table_pad=2)
+    _full_check(A, case)
+
+
+def test_tiny_prefill_mqa_256(A):
+    case = W.tiny_prefill_mqa(device="cuda")
+    _full_check(A, case)
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp32"])
+def test_chunk_prefill_2048(A, out_dtype):
+    case = W.chunk_prefill_2k(device="cuda")
+    _full_check(A, case, out_dtype=out_dtype)
+
+
+def test_chunk_prefill_8192_at_8192_sampled(A):
+    case = W.chunk_prefill_8k_at_8k(device="cuda")
+    lc = case.launches[0]
+    out = run_prefill(A, case, pad_rows=64)
+    assert sentinel_intact(out[lc.total_q:])
+    g = np.random.default_rng(3)
+    tokens = list(range(0, 16)) + list(range(lc.total_q - 16, lc.total_q)) + \
+        g.integers(0, lc.total_q, 32).tolist()
+    rows, toks = sample_rows(lc, case.num_q_heads, tokens)
+    ref = oracle.attend_rows(case.to("cpu"), rows).reshape(len(toks), case.num_q_heads, -1)
+    check_parity(out[torch.as_tensor(toks, device="cuda")], ref, "chunk_8192_at_8192 sampled")
+
+
+def test_long_mqa_32k_chunks_sampled(A):
+    case = W.long_mqa_32k(device="cuda")
+    host = case.to("cpu")
+    g = np.random.default_rng(4)
+    for li, lc in enumerate(case.launches):
+        out = run_prefill(A, case, li=li, pad_rows=3)
+        assert sentinel_intact(out[lc.total_q:])
+        tokens = [0, 1, 2, lc.total_q - 1] + g.integers(0, lc.total_q, 12).tolist()
+        rows, toks = sample_rows(lc, case.num_q_heads, tokens)
+        ref = oracle.attend_rows(host, rows, launch_idx=li).reshape(len(toks), case.num_q_heads, -1)
+        check_parity(out[torch.as_tensor(toks, device="cuda")], ref, f"long_mqa chunk {li}")
+
+
+def test_long_mqa_32k_q0_v1_is_exactly_one(A):
+    case = W.long_mqa_32k(device="cuda", q_zero=True, v_one=True)
+    for li, lc in enumerate(case.launches):
+        out = run_prefill(A, case, li=li)
+        assert bool((out[:lc.total_q] == 1.0).all()), f"chunk {li}: output differs from 1"
+
+
+def test_deterministic_bitwise(A):
+    case = W.chunk_prefill_2k(device="cuda")
+    a = run_prefill(A, case)
+    b = run_prefill(A, case)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_empty_launch_and_bad_arguments(A):
+    case = W.tiny_prefill_mqa(device="cuda")
+    lc = case.launches[0]
+    out = torch.zeros((lc.total_q, 8, 512), dtype=torch.float32, device="cuda")
+    with pytest.raises(A.AttnError):
+        A.prefill(lc.q, case.k_pool, case.v_pool, case.page_table, lc.cu_seqlens_q, lc.q_start,
+                  lc.kv_len, out, total_q=lc.total_q, max_q_len=lc.total_q + 1,
+                  softmax_scale=case.softmax_scale)
+    A.prefill(lc.q, case.k_pool, case.v_pool, case.page_table, lc.cu_seqlens_q, lc.q_start,
+              lc.kv_len, out, total_q=0, max_q_len=0, softmax_scale=case.softmax_scale)
+    torch.cuda.synchronize()
+    assert not out.any()
