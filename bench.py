@@ -39,11 +39,12 @@ def log(msg: str) -> None:
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other prefill workloads")
+    p.add_argument("--no-gemm", action="store_true", help="skip the same-process GEMM roofline")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target wall time of the CPU-oracle sample")
     return p.parse_args()
@@ -93,7 +94,7 @@ def main():
         torch.cuda.empty_cache()
         return best
 
-    gemm_before = gemm_rate()
+    gemm_before = 0.0 if args.no_gemm else gemm_rate()
     log(f"bf16 GEMM roofline (torch.matmul, before): {gemm_before:.1f} TFLOP/s")
 
     # ---- same-process HBM read probe --------------------------------------
@@ -193,7 +194,7 @@ def main():
             del dc, dout, ws, qd
             torch.cuda.empty_cache()
 
-    gemm_after = gemm_rate()
+    gemm_after = 0.0 if args.no_gemm else gemm_rate()
     log(f"bf16 GEMM roofline (after): {gemm_after:.1f} TFLOP/s")
     gemm = max(gemm_before, gemm_after)
 
@@ -243,7 +244,8 @@ def main():
                    "kv_heads": case.num_kv_heads, "head_dim": W.HEAD_DIM,
                    "page_size": W.PAGE_SIZE, "out_dtype": "bf16", "flop_per_launch": flops},
         "gemm_roofline": {"tflops": gemm, "before": gemm_before, "after": gemm_after,
-                          "frac": tflops / gemm, "how": "torch.matmul bf16 8192^3 and 16384^3, best"},
+                          "frac": (tflops / gemm) if gemm else None,
+                          "how": "torch.matmul bf16 8192^3 and 16384^3, best"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
                      "kernel": "prefill_hd512_kernel"},
