@@ -62,12 +62,7 @@ __device__ __forceinline__ const char* page_tile(const char* pool, const int* pt
 // bf16 pool: 16 rows per wave, global -> LDS, rows past `valid` arrive as zeros.
 __device__ __forceinline__ void issue_tile_bf16(const char* src, int valid, ATTN_LDS char* buf,
                                                 int wave, int lane16) {
-    const u32x4 rsrc = buffer_rsrc(src, (uint32_t)valid * kRowBytes);
-#pragma unroll
-    for (int i = 0; i < kRowsPerWaveLoad; ++i) {
-        const int r = wave * kRowsPerWaveLoad + i;
-        row_to_lds(rsrc, buf + r * kRowBytes, lane16 ^ (swz(i) << 4), r * kRowBytes);
-    }
+    rows16_to_lds(buffer_rsrc(src, (uint32_t)valid * kRowBytes), buf, wave, lane16);
 }
 
 // FP8 pool: a 64-key tile is 64 rows of 512 bytes.  Each wave loads 16 rows,

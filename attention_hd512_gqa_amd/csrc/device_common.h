@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -26,7 +28,7 @@ constexpr int kTileBytes = kPage * kRowBytes;  // 64 KB
 // operand reads) and 4 consecutive rows x 4 consecutive chunks (the
 // transposed V operand reads).  swz is a bijection on r mod 16; its bits
 // 1..2 separate the 4 rows of an aligned quad and so do its bits 2..3.
-__device__ __forceinline__ int swz(int r) {
+__host__ __device__ constexpr int swz(int r) {
     return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | ((r & 1) << 2) |
            ((((r >> 1) ^ (r >> 3)) & 1) << 3);
 }
@@ -43,25 +45,62 @@ __device__ __forceinline__ void wait_vmcnt() {
 // 32-bit data format).  Loads at offsets >= bytes return zeros.
 __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
     const uint64_t a = (uint64_t)base;
-    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+    // the words are wave-uniform; readfirstlane keeps them in SGPRs
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
 }
 
-// One wave moves one 1 KB row of a tile straight into LDS (16 bytes per lane,
-// no VGPR staging): lane i's 16 bytes, read at byte row_off + lane_off of the
-// resource, land at lds_row + 16 i.  With lane_off = (16 i) ^ (swz(row) << 4)
-// the row is stored swizzled.  Bytes past the resource's extent arrive as
+// One wave moves one 1 KB tile row straight into LDS (16 bytes per lane, no
+// VGPR staging).  The row lies REL bytes past byte `soff` of the resource and
+// past LDS byte `lds_base`.  Lane i's 16 bytes land at LDS row start + 16 i,
+// so lane i fetches the logical chunk the swizzle stores at chunk i: lane
+// offset lane_off ^ SWZ, with lane_off = 16 i (possibly pre-XORed with a
+// wave-dependent part of the row's swizzle) and SWZ the row's remaining
+// swizzle bits, shifted to bytes.  Bytes past the resource's extent arrive as
 // zeros, which is how keys past the cache length are zero-filled.
 //
 // Issued from asm so that the compiler does not track it: its LDS-DMA
 // bookkeeping would otherwise wait for every outstanding tile load before
-// any LDS read.  The caller orders it with wait_vmcnt and lds_barrier.
-__device__ __forceinline__ void row_to_lds(u32x4 rsrc, const ATTN_LDS char* lds_row,
-                                           int lane_off, int row_off) {
-    const uint32_t lds = (uint32_t)(uintptr_t)lds_row;
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds), "v"(lane_off), "s"(rsrc), "s"(row_off)
-                 : "memory", "m0");
+// any LDS read.  Callers order it with wait_vmcnt and lds_barrier.  M0 carries
+// the LDS address (one wait state after the SALU write); none of the kernels
+// built with these helpers use M0 for anything else.
+template <int SWZ, int REL>
+__device__ __forceinline__ void dma_row(u32x4 rsrc, uint32_t lds_base, uint32_t soff,
+                                        int lane_off) {
+    int voff;
+    asm volatile(
+        "v_xor_b32 %0, %1, %2\n\t"
+        "v_or_b32 %0, %3, %0\n\t"
+        "s_add_u32 m0, %4, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %5, %6 offen lds"
+        : "=&v"(voff)
+        : "i"(SWZ), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>{}) for i = 0 .. N-1, so
+// that the index can feed template arguments and asm immediates.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// A wave's 16 rows of one tile, rows 16 wave .. 16 wave + 15 (row 16 wave + i
+// has swizzle swz(i)).
+__device__ __forceinline__ void rows16_to_lds(u32x4 rsrc, const ATTN_LDS char* buf, int wave,
+                                              int lane16) {
+    const uint32_t off = (uint32_t)wave * 16 * kRowBytes;
+    const uint32_t base = (uint32_t)(uintptr_t)buf + off;
+    static_for<16>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        dma_row<(swz(i) << 4), i * kRowBytes>(rsrc, base, off, lane16);
+    });
 }
 
 // Workgroup barrier for LDS hand-offs: this wave's LDS operations complete,
@@ -91,35 +130,10 @@ __device__ __forceinline__ void mfma32x32x16_vgpr_first(f32x16& acc, bf16x8 a, b
 }
 
 // Wait states covering an XDL MFMA write -> VALU/VMEM/DS read of its result
-// (at most 16 passes + a few on gfx950; 3 x 8 = 24 here), tied to the two
-// accumulators so that no reader can be scheduled above it.
-__device__ __forceinline__ void mfma_vgpr_drain(f32x16& a0, f32x16& a1) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
-}
-
-// acc *= alpha for an accumulator tile that lives in AGPRs, in place (VALU
-// instructions cannot address AGPRs; each element goes through one VGPR).
-__device__ __forceinline__ void agpr_scale(f32x16& acc, float alpha) {
-    float e0 = acc[0], e1 = acc[1], e2 = acc[2], e3 = acc[3], e4 = acc[4], e5 = acc[5],
-          e6 = acc[6], e7 = acc[7], e8 = acc[8], e9 = acc[9], e10 = acc[10], e11 = acc[11],
-          e12 = acc[12], e13 = acc[13], e14 = acc[14], e15 = acc[15];
-    float t0, t1;
-#define ATTN_SC2(A, B)                                  \
-    "v_accvgpr_read_b32 %16, " A "\n\t"                 \
-    "v_accvgpr_read_b32 %17, " B "\n\t"                 \
-    "v_mul_f32 %16, %16, %18\n\t"                       \
-    "v_mul_f32 %17, %17, %18\n\t"                       \
-    "v_accvgpr_write_b32 " A ", %16\n\t"                \
-    "v_accvgpr_write_b32 " B ", %17\n\t"
-    asm volatile(ATTN_SC2("%0", "%1") ATTN_SC2("%2", "%3") ATTN_SC2("%4", "%5")
-                 ATTN_SC2("%6", "%7") ATTN_SC2("%8", "%9") ATTN_SC2("%10", "%11")
-                 ATTN_SC2("%12", "%13") ATTN_SC2("%14", "%15") "s_nop 1"
-                 : "+a"(e0), "+a"(e1), "+a"(e2), "+a"(e3), "+a"(e4), "+a"(e5), "+a"(e6),
-                   "+a"(e7), "+a"(e8), "+a"(e9), "+a"(e10), "+a"(e11), "+a"(e12), "+a"(e13),
-                   "+a"(e14), "+a"(e15), "=&v"(t0), "=&v"(t1)
-                 : "v"(alpha));
-#undef ATTN_SC2
-    acc = f32x16{e0, e1, e2, e3, e4, e5, e6, e7, e8, e9, e10, e11, e12, e13, e14, e15};
+// (at most 16 passes + a few on gfx950; 3 x 8 = 24 here), tied to the
+// accumulator so that no reader can be scheduled above it.
+__device__ __forceinline__ void mfma_vgpr_drain(f32x16& a0) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0));
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -1,6 +1,6 @@
 // Chunked causal GQA/MQA prefill at head_dim 512 over a paged bf16 KV cache,
-// for gfx950 (MI355X).  One FlashAttention-style pass per workgroup: the score
-// tile lives in registers only, with an online softmax in fp32 (Writing a
+// for gfx950 (MI355X).  One FlashAttention-style pass per workgroup: scores
+// live in registers only, with an online softmax in fp32 (Writing a
 // FlashAttention Prefill Kernel for Gemma 4, "Head dim 512 breaks the
 // textbook" and "The bug that passed every test").
 //
@@ -16,21 +16,27 @@
 //
 // Per 64-key tile (= one page of one KV head):
 //   K and V arrive in two separate 64 KB LDS buffers (no time-sharing of one
-//   buffer; pegainfer issue 1051, "Description") by direct global->LDS loads,
+//   buffer; pegainfer issue 1051, "Description") by direct buffer->LDS loads,
 //   one coalesced 1 KB key row per wave instruction, XOR-swizzled per 16 bytes;
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (fp32 accumulators), so that each
-//   lane holds one query row's scores and softmax statistics;
+//   lane holds one query row's scores;
 //   masked keys get -inf (only tiles that cross a row's causal limit or the
 //   cache length are masked; tiles past the last row's limit are never loaded);
 //   softmax statistics in fp32 with exp2, per 64-key tile (Flash-Decoding for
 //   MQA in CUDA, "One KV head breaks the textbook": statistics per tile, not
-//   per key), against a per-row reference maximum (see the loop below for why
-//   O is never rescaled in place);
+//   per key), against a per-row reference maximum (see below);
 //   P goes to bf16 and O^T += V^T P^T on the same MFMA, V^T read with the
 //   gfx950 transposing LDS load.  O accumulates in fp32 across the whole key
 //   range (vLLM flash-attention PR 199, commit 3 of the first review).
-// K(j+1) streams in while softmax and P.V of tile j run; V(j+1) while Q.K^T of
-// tile j+1 runs.
+//
+// Within a wave the tile is processed as two 32-key blocks whose chains
+// overlap: Q.K^T of block 1 issues on the matrix core while the VALU runs the
+// softmax of block 0, and P.V of block 0 while the softmax of block 1 runs.
+// The four phases (Q.K^T and P.V of each block) each free one 32-key half of
+// the K or V buffer; after the phase's barrier that half is refilled for the
+// tile that needs it two phases later, with the wave's 8 row loads spread one
+// per four MFMAs over the next phase (a burst of 1 KB buffer->LDS loads would
+// stall the wave's instruction issue and starve the matrix core).
 #include "device_common.h"
 #include "attn_host.h"
 
@@ -42,9 +48,17 @@ constexpr int kRowsPerWg = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWaveLoad = kPage / kWaves;  // tile rows each wave moves
-// Largest allowed excess (log2 units) of a row's running maximum over its
-// reference maximum: p <= 2^24, l <= 2^24 * keys, all well inside fp32/bf16.
-constexpr float kRescaleMargin = 24.f;
+// Largest allowed excess (log2 units) of a row's scores over its reference
+// maximum: p <= 2^32 and l <= 2^32 * keys stay far inside fp32 and bf16.
+constexpr float kRescaleMargin = 32.f;
+constexpr int kPrefetch = 4;  // LDS operand reads in flight ahead of their MFMA
+// Page ids of the first kPagesInLds tiles are staged in LDS at the start of
+// the workgroup (reading them from the scalar cache inside the loop stalls
+// the wave: scalar loads share the LDS wait counter and return out of order).
+constexpr int kPagesInLds = 4096;
+// Restarts per workgroup are capped so that non-finite inputs (a caller error)
+// cannot loop forever; each genuine restart raises a row's reference by > 32.
+constexpr int kMaxRestarts = 8;
 
 struct PrefillArgs {
     const __bf16* q;
@@ -61,64 +75,176 @@ struct PrefillArgs {
     float scale_log2;   // softmax_scale * log2(e)
 };
 
-// Queue the 64 rows of one (page, KV head) tile into an LDS tile buffer.  Each
-// wave moves 16 rows with exactly 16 vector-memory operations, which the
-// callers' vmcnt arithmetic relies on.  The resource covers only the `valid`
-// rows, so rows of keys past the cache length (whose slots may hold anything)
-// arrive as zeros.
-__device__ __forceinline__ void issue_tile(const char* pool, const int* ptab, int kt,
-                                           int num_pages, int hkv, int kvh, int valid,
-                                           ATTN_LDS char* buf, int wave, int lane16) {
-    int page = load_uniform(ptab, kt);
+// Refill of one 32-key half (rows 32 half .. 32 half + 31) of a K or V tile
+// buffer from one (page, KV head) tile: each wave moves rows
+// 32 half + 8 wave + j, j = 0..7, one buffer->LDS load per row.  The resource
+// covers only the tile's `valid` rows, so rows of keys past the cache length
+// (whose slots may hold anything) arrive as zeros.  Row 32 half + 8 wave + j
+// has swizzle swz(j) ^ 8 (wave & 1), the second term folded into lane_off.
+struct HalfDma {
+    u32x4 rsrc;
+    uint32_t lds_base;  // LDS address of this wave's first row
+    uint32_t soff;      // byte offset of this wave's first row in the tile
+    bool on;            // wave-uniform: this refill exists
+};
+
+__device__ __forceinline__ HalfDma half_dma(const char* pool, int page, int num_pages, int hkv,
+                                            int kvh, int valid, const ATTN_LDS char* buf,
+                                            int half, int wave, bool on) {
     page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
     const char* src = pool + ((size_t)page * hkv + kvh) * (size_t)kTileBytes;
-    const u32x4 rsrc = buffer_rsrc(src, (uint32_t)valid * kRowBytes);
+    HalfDma d;
+    d.rsrc = buffer_rsrc(src, (uint32_t)(valid > 0 ? valid : 0) * kRowBytes);
+    d.soff = (uint32_t)__builtin_amdgcn_readfirstlane((32 * half + 8 * wave) * kRowBytes);
+    d.lds_base = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(uintptr_t)buf + d.soff));
+    d.on = on;
+    return d;
+}
+
+template <int J>
+__device__ __forceinline__ void half_dma_row(const HalfDma& d, int lane_off) {
+    dma_row<(swz(J) << 4), J * kRowBytes>(d.rsrc, d.lds_base, d.soff, lane_off);
+}
+
+__device__ __forceinline__ void half_dma_all(const HalfDma& d, int lane_off) {
+    static_for<8>([&](auto J) { half_dma_row<decltype(J)::value>(d, lane_off); });
+}
+
+// Per-lane state of the softmax of one 32-key block.  Scores arrive already
+// masked (masked keys -inf) in raw units: x = s * scale_log2.
+struct SoftmaxCtx {
+    float scale_log2;
+    float neg_m_ref;  // -m_ref
+};
+
+// One softmax element: p = 2^(s * scale - m_ref) (0 for masked keys).  Tracks
+// the lane's running maximum of the raw scores (the scale is positive, so the
+// scaled maximum is mx * scale) and its sum; packs p into the P^T operand.
+// The empty asms pin the element to the MFMA step it is issued with (inputs
+// taken and running values produced inside the step): without them, IR
+// passes gather the softmax arithmetic into one cluster after the MFMA chain
+// and the matrix core idles while it runs.
+__device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float s, int i, float& mx,
+                                             float& psum, bf16x8& pf) {
+    asm volatile("" : "+v"(s));
+    mx = fmaxf(mx, s);
+    const float p = fast_exp2(__builtin_fmaf(s, c.scale_log2, c.neg_m_ref));
+    psum += p;
+    pf[i & 7] = (__bf16)p;
+    asm volatile("" : "+v"(mx), "+v"(psum));
+}
+
+// Masks one block's raw scores in place: element i is key
+// key_base + 8(i/4) + (i%4) (key_base includes 4h); keys >= n_row get -inf.
+__device__ __forceinline__ void mask_block(f32x16& s, int key_base, int n_row) {
 #pragma unroll
-    for (int i = 0; i < kRowsPerWaveLoad; ++i) {
-        const int r = wave * kRowsPerWaveLoad + i;   // r % 16 == i, so swz(r) == swz(i)
-        row_to_lds(rsrc, buf + r * kRowBytes, lane16 ^ (swz(i) << 4), r * kRowBytes);
+    for (int i = 0; i < 16; ++i) {
+        const int key = key_base + 8 * (i >> 2) + (i & 3);
+        s[i] = key < n_row ? s[i] : -__builtin_inff();
     }
 }
 
-template <bool FIRST>
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[16], const bf16x8 (&pf)[4],
-                                        const ATTN_LDS char* sV, int lane) {
-    const int h = lane >> 5;
-    const int grp = lane & 15;
-    const int dsub = (lane >> 4) & 1;
-    const int krow = 4 * h + (grp >> 2);               // + 16 c (+ 8)
-    // 32-dim block db covers chunks 4 db .. 4 db + 3; this lane reads chunk
-    // 4 db + cb at byte `within`.  The swizzle permutes chunks within aligned
-    // groups of 16, so with db = 4 u + w the offset is voff[w] + 256 u.
-    const int cb = 2 * dsub + ((grp & 3) >> 1);
-    const int within = 8 * (grp & 1);
+// V^T operand reader for the P.V MFMAs: step = 16 c + db reads keys
+// 16c + 8(j/4) + 4h + (j%4) (j = operand slot) of output-dim block db.
+struct VReader {
     int voffA[4], voffB[4];
+    __device__ __forceinline__ explicit VReader(int lane) {
+        const int h = lane >> 5;
+        const int grp = lane & 15;
+        const int dsub = (lane >> 4) & 1;
+        const int krow = 4 * h + (grp >> 2);              // + 16 c (+ 8)
+        // 32-dim block db covers chunks 4 db .. 4 db + 3; this lane reads chunk
+        // 4 db + cb at byte `within`.  The swizzle permutes chunks within
+        // aligned groups of 16, so with db = 4 u + w the offset is voff[w] + 256 u.
+        const int cb = 2 * dsub + ((grp & 3) >> 1);
+        const int within = 8 * (grp & 1);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        voffA[w] = krow * kRowBytes + (((4 * w + cb) ^ swz(krow)) << 4) + within;
-        voffB[w] = (krow + 8) * kRowBytes + (((4 * w + cb) ^ swz(krow + 8)) << 4) + within;
+        for (int w = 0; w < 4; ++w) {
+            voffA[w] = krow * kRowBytes + (((4 * w + cb) ^ swz(krow)) << 4) + within;
+            voffB[w] = (krow + 8) * kRowBytes + (((4 * w + cb) ^ swz(krow + 8)) << 4) + within;
+        }
     }
-    auto vread = [&](int step) -> bf16x8 {
+    __device__ __forceinline__ bf16x8 read(const ATTN_LDS char* sV, int step) const {
         const int c = step >> 4, db = step & 15;
         const int rel = 16 * c * kRowBytes + 256 * (db >> 2);  // swz(16c + k) == swz(k)
         const bf16x4 va = lds_read_tr16(sV + voffA[db & 3] + rel);
         const bf16x4 vb = lds_read_tr16(sV + voffB[db & 3] + rel);
         return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+// Q.K^T of one 32-key block kb: 32 MFMAs (VGPR accumulator) over the 32
+// k-steps of head_dim.  When OVERLAP, one softmax element of the previous
+// block's scores `sp` is computed after every other MFMA; the half-tile
+// refill `dma` issues one row load after every fourth MFMA.
+template <bool OVERLAP>
+__device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[32],
+                                         const ATTN_LDS char* sK, const int (&koff)[8],
+                                         const f32x16& sp, const SoftmaxCtx& c, float& mx,
+                                         float& psum, bf16x8& pf0, bf16x8& pf1,
+                                         const HalfDma& dma, int lane_off) {
+    // step ks reads chunk 2 ks + h of key row 32 kb + n; with ks = 8 u + v the
+    // byte offset is koff[v] + 256 u + 32 KiB kb.
+    auto kread = [&](int ks) -> bf16x8 {
+        return *(const ATTN_LDS bf16x8*)(sK + koff[ks & 7] + 256 * (ks >> 3) +
+                                          kb * 32 * kRowBytes);
     };
-    constexpr int kPrefetch = 4;
+    bf16x8 kbuf[kPrefetch];
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) kbuf[j] = kread(j);
+    static_for<32>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        const bf16x8 cur = kbuf[ks % kPrefetch];
+        if (ks + kPrefetch < 32) kbuf[ks % kPrefetch] = kread(ks + kPrefetch);
+        if constexpr (ks == 0)
+            mfma32x32x16_vgpr_first(s, cur, qf[0]);
+        else
+            mfma32x32x16_vgpr(s, cur, qf[ks]);
+        if constexpr (ks % 4 == 0) {
+            if (dma.on) half_dma_row<ks / 4>(dma, lane_off);
+        }
+        if constexpr (OVERLAP && (ks & 1)) {
+            constexpr int i = ks >> 1;
+            softmax_elem(c, sp[i], i, mx, psum, i < 8 ? pf0 : pf1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// P.V of one 32-key block (k-steps c = 2 kb, 2 kb + 1, all 16 dim blocks).
+// FIRST: the tile's first k-step starts O from zero (inline c = 0), so O is
+// only ever written by MFMAs.  When OVERLAP, one softmax element of the next
+// block's scores `sn` is computed after every other MFMA; the half-tile
+// refill `dma` issues one row load after every fourth MFMA.
+template <bool FIRST, bool OVERLAP>
+__device__ __forceinline__ void pv_block(f32x16 (&o)[16], int kb, const bf16x8& p0,
+                                         const bf16x8& p1, const ATTN_LDS char* sV,
+                                         const VReader& vr, const f32x16& sn,
+                                         const SoftmaxCtx& c, float& mx, float& psum,
+                                         bf16x8& pn0, bf16x8& pn1, const HalfDma& dma,
+                                         int lane_off) {
+    const int base = 32 * kb;   // steps 32 kb .. 32 kb + 31 of the tile
     bf16x8 vbuf[kPrefetch];
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) vbuf[j] = vread(j);
-#pragma unroll
-    for (int step = 0; step < 64; ++step) {
-        const bf16x8 cur = vbuf[step % kPrefetch];
-        if (step + kPrefetch < 64) vbuf[step % kPrefetch] = vread(step + kPrefetch);
-        if (FIRST && step < 16)
-            o[step] = mfma32x32x16(cur, pf[0], f32x16{});
+    for (int j = 0; j < kPrefetch; ++j) vbuf[j] = vr.read(sV, base + j);
+    static_for<32>([&](auto ST) {
+        constexpr int st = decltype(ST)::value;
+        const bf16x8 cur = vbuf[st % kPrefetch];
+        if (st + kPrefetch < 32) vbuf[st % kPrefetch] = vr.read(sV, base + st + kPrefetch);
+        constexpr int db = st & 15;
+        if constexpr (FIRST && st < 16)
+            o[db] = mfma32x32x16(cur, p0, f32x16{});
         else
-            o[step & 15] = mfma32x32x16(cur, pf[step >> 4], o[step & 15]);
+            o[db] = mfma32x32x16(cur, st < 16 ? p0 : p1, o[db]);
+        if constexpr (st % 4 == 0) {
+            if (dma.on) half_dma_row<st / 4>(dma, lane_off);
+        }
+        if constexpr (OVERLAP && (st & 1)) {
+            constexpr int i = st >> 1;
+            softmax_elem(c, sn[i], i, mx, psum, i < 8 ? pn0 : pn1);
+        }
         __builtin_amdgcn_sched_barrier(0);
-    }
+    });
 }
 
 template <bool OUT_FP32>
@@ -126,6 +252,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void prefill_hd512_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes];
     __shared__ int sFlag[kWaves];
+    __shared__ int sPage[kPagesInLds];
     ATTN_LDS char* sK = (ATTN_LDS char*)smem;
     ATTN_LDS char* sV = sK + kTileBytes;
 
@@ -152,7 +279,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
     const int t_last = min(t0 + a.tok_per_wg, q_len) - 1;
     int L = a.kv_lens[b];
     L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
-    const int qs = a.q_start[b];
+    const int qs = max(a.q_start[b], 0);   // every row then sees key 0
     const int n_max = min(qs + t_last + 1, L);   // keys the last row sees
     const int n_min = min(qs + t0 + 1, L);       // keys the first row sees
     const int ntiles = n_max > 0 ? (n_max + kPage - 1) / kPage : 0;
@@ -179,12 +306,16 @@ void prefill_hd512_kernel(PrefillArgs a) {
             qf[ks] = valid ? v : bf16x8{};
         }
     }
+    int koff[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) koff[v] = n * kRowBytes + (((2 * v + h) ^ swz(n)) << 4);
+    const VReader vr(lane);
 
     f32x16 o[16];  // written first by tile 0's P.V
     // Online softmax with a fixed per-row reference maximum: p = 2^(x - m_ref)
-    // where m_ref is the row's maximum over the first tile.  O and l carry the
-    // same factor 2^(m_true - m_ref), which cancels in O / l.  A row whose
-    // maximum climbs more than kRescaleMargin above m_ref would push p past
+    // where m_ref is the row's maximum over its first 32 keys.  O and l carry
+    // the same factor 2^(m_true - m_ref), which cancels in O / l.  A row whose
+    // scores climb more than kRescaleMargin above m_ref would push p past
     // 2^kRescaleMargin, so the workgroup then restarts its key loop with every
     // row's reference raised to the maximum seen so far: the rescale of O is
     // replaced by a recompute that typical inputs never trigger.  This keeps
@@ -193,122 +324,116 @@ void prefill_hd512_kernel(PrefillArgs a) {
     float m_ref = -__builtin_inff();
     float m_seen = -__builtin_inff();
     float l_run = 0.f;
+    int restarts = 0;
 
     const int* ptab = a.page_table + (size_t)b * a.max_pages;
     const int lane16 = lane * 16;
-    int koff[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) koff[v] = n * kRowBytes + (((2 * v + h) ^ swz(n)) << 4);
-    if (ntiles > 0) {
-        const int v0 = min(L, kPage);
-        issue_tile(a.k_pages, ptab, 0, a.num_pages, a.hkv, kvh, v0, sK, wave, lane16);
-        issue_tile(a.v_pages, ptab, 0, a.num_pages, a.hkv, kvh, v0, sV, wave, lane16);
-    }
+    const int lane_off = lane16 ^ ((wave & 1) << 7);
+    const int staged = min(ntiles, kPagesInLds);
+    for (int i = threadIdx.x; i < staged; i += kThreads) sPage[i] = ptab[i];
+    __syncthreads();
+    auto page_of = [&](int tile) -> int {
+        return tile < kPagesInLds ? __builtin_amdgcn_readfirstlane(sPage[tile])
+                                  : load_uniform(ptab, tile);
+    };
+    auto flags_set = [&]() -> bool { return (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0; };
 
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const bool more = kt + 1 < ntiles;
-        const int key0 = kt * kPage;
-        // K(kt) has landed when only V(kt)'s 16 loads may still be in flight
-        wait_vmcnt<kRowsPerWaveLoad>();
-        lds_barrier();
-
-        // ---- S^T[key][row] = K Q^T for the tile's two 32-key blocks.  The K
-        // operand of step j is read kPrefetch steps ahead of its MFMA; the
-        // scheduling fences keep the compiler from hoisting more reads than that.
-        f32x16 s[2];
-        {
-            // step = 32 kb + ks reads chunk 2 ks + h of key row 32 kb + n; the
-            // swizzle permutes chunks within aligned groups of 16, so with
-            // ks = 8 u + v the byte offset is koff[v] + 256 u + 32 KiB kb.
-            auto kread = [&](int step) -> bf16x8 {
-                const int kb = step >> 5, ks = step & 31;
-                return *(const ATTN_LDS bf16x8*)(sK + koff[ks & 7] + 256 * (ks >> 3) +
-                                                  kb * 32 * kRowBytes);
-            };
-            constexpr int kPrefetch = 4;
-            bf16x8 kbuf[kPrefetch];
-#pragma unroll
-            for (int j = 0; j < kPrefetch; ++j) kbuf[j] = kread(j);
-#pragma unroll
-            for (int step = 0; step < 64; ++step) {
-                const bf16x8 cur = kbuf[step % kPrefetch];
-                if (step + kPrefetch < 64) kbuf[step % kPrefetch] = kread(step + kPrefetch);
-                if ((step & 31) == 0)
-                    mfma32x32x16_vgpr_first(s[step >> 5], cur, qf[0]);
-                else
-                    mfma32x32x16_vgpr(s[step >> 5], cur, qf[step & 31]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            mfma_vgpr_drain(s[0], s[1]);
-        }
-
-        // ---- scores in log2 units, masked; accumulator element i of block kb
-        // holds key kb*32 + 8(i/4) + 4h + (i%4) of this tile for this lane's row.
-        const bool mask = key0 + kPage > n_min;
-        float mt = -__builtin_inff();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v = s[kb][i] * a.scale_log2;
-                if (mask) {
-                    const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                    v = key < n_row ? v : -__builtin_inff();
-                }
-                s[kb][i] = v;
-                mt = fmaxf(mt, v);
-            }
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        m_seen = fmaxf(m_seen, mt);
-        if (kt == 0) m_ref = mt;   // every row sees key 0, so this is finite
-        if (lane == 0) sFlag[wave] = __any(mt > m_ref + kRescaleMargin) ? 1 : 0;
-        lds_barrier();  // every wave is done with sK; restart flags visible
-        if (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) {
-            // drain this wave's V(kt) loads before sV is refilled from key 0
-            wait_vmcnt<0>();
-            lds_barrier();
-            m_ref = m_seen;
-            l_run = 0.f;   // O restarts too: tile 0's P.V overwrites it
+    // Vector-memory accounting: every wave issues its half-tile refills in the
+    // order V1(j) [during QK0(j)], K0(j+1) [QK1(j)], K1(j+1) [PV0(j)],
+    // V0(j+1) [PV1(j)], 8 loads each; before each phase the half it reads was
+    // issued two refills (16 loads) before the newest, except where the tile
+    // has no successor and those later refills do not exist.
+    for (;;) {   // one pass over the key range; a restart begins a new pass
+        if (ntiles > 0) {
+            const int page0 = page_of(0);
             const int v0 = min(L, kPage);
-            issue_tile(a.k_pages, ptab, 0, a.num_pages, a.hkv, kvh, v0, sK, wave, lane16);
-            issue_tile(a.v_pages, ptab, 0, a.num_pages, a.hkv, kvh, v0, sV, wave, lane16);
-            kt = -1;
-            continue;
+            half_dma_all(half_dma(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 0, wave, true), lane_off);
+            half_dma_all(half_dma(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 1, wave, true), lane_off);
+            half_dma_all(half_dma(a.v_pages, page0, a.num_pages, a.hkv, kvh, v0, sV, 0, wave, true), lane_off);
         }
-        if (more) {
-            const int vn = min(L - (key0 + kPage), kPage);
-            issue_tile(a.k_pages, ptab, kt + 1, a.num_pages, a.hkv, kvh, vn, sK, wave, lane16);
-        }
+        bool restart = false;
+        for (int kt = 0; kt < ntiles; ++kt) {
+            const bool more = kt + 1 < ntiles;
+            const int key0 = kt * kPage;
+            const int valid = min(L - key0, kPage);
+            const int valid_n = more ? min(L - key0 - kPage, kPage) : 0;
+            const int page = page_of(kt);
+            const int page_n = more ? page_of(kt + 1) : page;
+            const bool mask = key0 + kPage > n_min;   // the tile crosses a row's causal limit
+            SoftmaxCtx c0{a.scale_log2, -m_ref};
+            float mx = -__builtin_inff();   // raw-score maximum of the tile
+            float psum = 0.f;
+            bf16x8 pf[4];
+            f32x16 s0, s1;
 
-        // ---- P = 2^(x - m_ref) in bf16 for the P.V MFMA; l in fp32
-        float psum = 0.f;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float p = fast_exp2(s[c >> 1][8 * (c & 1) + j] - m_ref);
-                psum += p;
-                pf[c][j] = (__bf16)p;
+            // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill
+            wait_vmcnt<16>();
+            lds_barrier();
+            if (kt > 0 && restarts < kMaxRestarts && flags_set()) {
+                restart = true;   // a row of tile kt-1 overshot its reference
+                break;
             }
-        }
-        l_run += psum;
+            qk_block<false>(s0, 0, qf, sK, koff, s0, c0, mx, psum, pf[0], pf[1],
+                            half_dma(a.v_pages, page, a.num_pages, a.hkv, kvh, valid, sV, 1, wave, true),
+                            lane_off);
+            mfma_vgpr_drain(s0);
+            if (mask) mask_block(s0, key0 + 4 * h, n_row);
+            if (kt == 0) {
+                // reference maximum: the row's maximum over keys 0..31 (key 0 is
+                // visible to every row, so it is finite)
+                float m0 = -__builtin_inff();
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
+                m0 = fmaxf(m0, __shfl_xor(m0, 32)) * a.scale_log2;
+                m_ref = m0;
+                c0.neg_m_ref = -m0;
+            }
 
-        // V(kt) has landed when only K(kt+1)'s loads may still be in flight
-        if (more) wait_vmcnt<kRowsPerWaveLoad>(); else wait_vmcnt<0>();
+            // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill
+            wait_vmcnt<16>();
+            lds_barrier();
+            qk_block<true>(s1, 1, qf, sK, koff, s0, c0, mx, psum, pf[0], pf[1],
+                           half_dma(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 0, wave, more),
+                           lane_off);
+            mfma_vgpr_drain(s1);
+            if (mask) mask_block(s1, key0 + 32 + 4 * h, n_row);
+
+            // ---- PV0 with block 1's softmax; K rows 32..63 of tile kt+1 refill
+            if (more) wait_vmcnt<16>(); else wait_vmcnt<8>();
+            lds_barrier();
+            const SoftmaxCtx& c1 = c0;
+            const HalfDma dk1 = half_dma(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 1, wave, more);
+            if (kt == 0)
+                pv_block<true, true>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off);
+            else
+                pv_block<false, true>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off);
+
+            // ---- PV1; V rows 0..31 of tile kt+1 refill
+            if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
+            lds_barrier();
+            pv_block<false, false>(o, 1, pf[2], pf[3], sV, vr, s1, c1, mx, psum, pf[2], pf[3],
+                                   half_dma(a.v_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sV, 0, wave, more),
+                                   lane_off);
+            l_run += psum;
+            mx *= a.scale_log2;
+            m_seen = fmaxf(m_seen, mx);
+            // restart flag of this tile: any row whose scores exceeded
+            // m_ref + margin (non-finite sums included); read after the next barrier
+            if (lane == 0)
+                sFlag[wave] = __any(!(mx <= m_ref + kRescaleMargin) || !(psum == psum)) ? 1 : 0;
+        }
+        if (!restart && ntiles > 0) {
+            lds_barrier();   // the last tile's flags are visible
+            restart = restarts < kMaxRestarts && flags_set();
+        }
+        if (!restart) break;
+        // start over with every row's reference raised to its maximum so far
+        ++restarts;
+        wait_vmcnt<0>();     // refills still landing in sK / sV
         lds_barrier();
-
-        // ---- O^T[d][row] += V^T P^T (tile 0 of a pass starts O from zero).
-        if (kt == 0)
-            pv_tile<true>(o, pf, sV, lane);
-        else
-            pv_tile<false>(o, pf, sV, lane);
-        lds_barrier();  // every wave is done with sV
-        if (more) {
-            const int vn = min(L - (key0 + kPage), kPage);
-            issue_tile(a.v_pages, ptab, kt + 1, a.num_pages, a.hkv, kvh, vn, sV, wave, lane16);
-        }
+        m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));
+        m_seen = m_ref;
+        l_run = 0.f;         // O restarts too: tile 0's P.V overwrites it
     }
 
     // ---- epilogue: lane holds d = 32 db + 8 (i/4) + 4 h + (i%4) of its row.
