@@ -3,26 +3,38 @@
 //
 // A single KV head per sequence would give one workgroup per (sequence, KV
 // head) and leave most CUs idle, so the key range is cut into splits of
-// `keys_per_split` keys, each handled by one workgroup that writes an
-// unnormalised partial (O, m, l) for every query head of the group; a merge
+// `keys_per_split` keys, each handled by one workgroup that writes
+// unnormalised partials (O, m, l) for the query heads of the group; a merge
 // kernel then combines the partials with the online-softmax rule (Flash-
 // Decoding for MQA in CUDA, "One KV head breaks the textbook").  Only the live
-// band [0, kv_len) is read (same page, "The starting point").
+// band [0, kv_len) is read (same page, "The starting point").  Every KV byte
+// is read once per call, with the non-temporal cache policy.
 //
-// Split workgroup (4 waves), per 64-key tile (= one page of one KV head):
-//   K and V land in separate 64 KB LDS buffers, swizzled as in prefill.  The
-//   bf16 pool goes global -> LDS directly; an FP8-E4M3 pool is loaded to
-//   registers, widened exactly to bf16 and written to the same layout (vLLM
-//   flash-attention PR 199, "Summary": FP8 KV with 16-bit MMA), with k_scale
-//   folded into the softmax scale and v_scale into the partial output.
-//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16: the g query heads of the group
-//   are the (zero-padded) 16 columns, wave w takes keys 16w .. 16w+15.  Scores
-//   meet in a 4 KB LDS buffer; every wave then runs the softmax for all 64
-//   keys (identical in each wave) and O^T += V^T P^T for its own 128 of the
-//   512 output dims, in fp32 per key block (vLLM flash-attention PR 199,
-//   commit 3 of the first review).
+// The g query heads of a group are the (zero-padded) 16 columns of
+// v_mfma_f32_16x16x32_bf16 products: S^T = K Q^T and O^T += V^T P^T, O in fp32
+// per key block (vLLM flash-attention PR 199, commit 3 of the first review).
 // Decode moves ~2 bytes per flop: HBM bandwidth, not the MFMA rate, bounds
-// it; the padded MFMA rows cost issue slots that are free at that ratio.
+// it, and the padded MFMA columns cost issue slots that are free at that
+// ratio.
+//
+// bf16 pool, one 64-key tile (= one page of one KV head) at a time per
+// workgroup of 4 waves: K and V tiles are DMA'd to separate 64 KB LDS
+// buffers (swizzled rows); wave w computes the scores of keys 16 w .. 16 w +
+// 15, the scores meet in a small LDS buffer, every wave runs the softmax of
+// all 64 keys and accumulates its own 128 of the 512 output dims.
+//
+// FP8-E4M3 pool: the four waves of a workgroup work independently, each on
+// its own 32-key half pages (wave w takes half pages w, w + 4, ... of the
+// split) and each writing its own partial, so the loop has no workgroup
+// barrier.  K goes from HBM straight into the MFMA operand registers; V is
+// staged through registers into a per-wave LDS buffer as raw E4M3 bytes and
+// read back transposed (ds_read_b64_tr_b8).  Both are widened exactly to
+// bf16 (every E4M3 value is a bf16 value) just before their MFMA, k_scale is
+// folded into the softmax scale and v_scale into the partial (vLLM
+// flash-attention PR 199, "Summary": FP8 KV with 16-bit MMA).  Each wave
+// keeps a reference maximum and rescales O only when a score exceeds it by
+// more than kRefMargin (log2 units), so the 128-register O accumulator is
+// rarely touched by the softmax.
 #include "device_common.h"
 #include "attn_host.h"
 
@@ -33,9 +45,17 @@ namespace {
 constexpr int kDecRows = 16;        // query heads of one group, zero-padded
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kRowsPerWaveLoad = kPage / kDecWaves;
 constexpr int kSxStride = 272;      // bytes per score-exchange row (256 + 16 pad)
 constexpr int kDefaultTargetWgs = 4096;
+constexpr int kNonTemporal = 2;     // buffer-load cache policy: nt (read-once stream)
+#ifndef FP8_WAVES
+#define FP8_WAVES 1
+#endif
+constexpr int kFp8Waves = FP8_WAVES; // waves per FP8 split workgroup, one partial each
+constexpr int kMaxSub = 4;          // partials per split workgroup (FP8: one per wave)
+constexpr int kHalfKeys = 32;       // FP8: keys per wave step
+constexpr int kHalfBytes = kHalfKeys * kHeadDim;   // FP8 rows are 512 bytes
+constexpr float kRefMargin = 10.f;  // FP8: allowed excess of a score over the reference max
 
 struct DecodeArgs {
     const __bf16* q;
@@ -43,128 +63,137 @@ struct DecodeArgs {
     const char* v_pages;
     const int* page_table;
     const int* kv_lens;
-    float* part_o;      // [batch][hkv][max_splits][g][512]
-    float* part_ml;     // [batch][hkv][max_splits][g][2]  (m in log2 units, l)
+    float* part_o;      // [batch][hkv][max_splits][sub][g][512]
+    float* part_ml;     // [batch][hkv][max_splits][sub][g][2]  (m in log2 units, l)
     int batch, hq, hkv, g, max_pages, num_pages;
-    int max_splits, tiles_per_split;
+    int max_splits, tiles_per_split, sub;
     float scale_log2;   // softmax_scale * log2(e) * k_scale
     float v_scale;
 };
 
-__device__ __forceinline__ const char* page_tile(const char* pool, const int* ptab, int tile,
-                                                 int num_pages, int hkv, int kvh,
-                                                 int tile_bytes) {
-    int page = load_uniform(ptab, tile);
-    page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
-    return pool + ((size_t)page * hkv + kvh) * (size_t)tile_bytes;
-}
-
-// bf16 pool: 16 rows per wave, global -> LDS, rows past `valid` arrive as zeros.
-__device__ __forceinline__ void issue_tile_bf16(const char* src, int valid, ATTN_LDS char* buf,
-                                                int wave, int lane16) {
-    rows16_to_lds(buffer_rsrc(src, (uint32_t)valid * kRowBytes), buf, wave, lane16);
-}
-
-// FP8 pool: a 64-key tile is 64 rows of 512 bytes.  Each wave loads 16 rows,
-// two per instruction (lanes 0-31 row r, lanes 32-63 row r+1, 16 bytes each);
-// rows past `valid` arrive as zeros.
-struct Fp8Stage {
-    u32x4 k[8];
-    u32x4 v[8];
+// The key range of one split workgroup and where its tiles live.
+struct SplitPlan {
+    int b, kvh, split;
+    int k_begin, k_end, ntiles;
+    const int* ptab;    // this sequence's row of the page table
 };
 
-__device__ __forceinline__ void load_fp8(u32x4 (&dst)[8], const char* src, int valid, int wave,
-                                         int lane) {
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, valid * 512, 0x00020000);
-    const int voff = (lane >> 5) * 512 + (lane & 31) * 16;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = wave * kRowsPerWaveLoad + 2 * i;
-        dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, r * 512, 0));
-    }
+// Split-major launch order: consecutive workgroups take the same split index
+// of different (sequence, KV head) pairs.  Workgroups are dealt round-robin
+// to the 8 XCDs, so each XCD gets the same mix of split indices (a split
+// index fixed per XCD would give some XCDs mostly empty late splits), and the
+// late, often empty splits come last.
+__device__ __forceinline__ bool plan_split(const DecodeArgs& a, SplitPlan& p) {
+    const int pairs = a.batch * a.hkv;
+    p.split = blockIdx.x / pairs;
+    const int rest = blockIdx.x - p.split * pairs;
+    p.kvh = rest % a.hkv;
+    p.b = rest / a.hkv;
+    int L = __builtin_amdgcn_readfirstlane(a.kv_lens[p.b]);   // wave-uniform
+    L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
+    p.k_begin = p.split * a.tiles_per_split * kPage;
+    if (p.k_begin >= L) return false;  // empty split: the merge never reads it
+    p.k_end = min(p.k_begin + a.tiles_per_split * kPage, L);
+    p.ntiles = (p.k_end - p.k_begin + kPage - 1) / kPage;
+    p.ptab = a.page_table + (size_t)p.b * a.max_pages;
+    return true;
 }
 
-// Widen 16 E4M3 values (exact in bf16) and store them as two swizzled chunks.
-__device__ __forceinline__ void store_fp8_as_bf16(const u32x4 (&src)[8], ATTN_LDS char* buf,
-                                                  int wave, int lane) {
+// Physical page of split tile t (clamped to the split's tiles, then to the
+// pool).
+__device__ __forceinline__ int split_page(const DecodeArgs& a, const SplitPlan& p, int t) {
+    const int tile = p.k_begin / kPage + min(max(t, 0), p.ntiles - 1);
+    const int page = load_uniform(p.ptab, tile);
+    return page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+}
+__device__ __forceinline__ const char* tile_base(const char* pool, const DecodeArgs& a, int page,
+                                                 int kvh, int tile_bytes) {
+    return pool + ((size_t)page * a.hkv + kvh) * (size_t)tile_bytes;
+}
+
+// Buffer resource over `bytes` bytes at `base`; both wave-uniform, kept in
+// SGPRs by readfirstlane.  Loads at offsets >= bytes return zeros and touch
+// no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0,
+                                                                          kNonTemporal));
+}
+
+// Unnormalised partial of head n: O^T element i of block db is dim
+// 16 db + 4 kq + i (db over NB blocks, starting at dim d0); l sums over the
+// four k-groups.
+template <int NB>
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, size_t slot, int n, int kq,
+                                              int d0, const f32x4 (&o)[NB], float m, float l) {
+    float l_row = l + __shfl_xor(l, 16);
+    l_row += __shfl_xor(l_row, 32);
+    if (n < a.g) {
+        float* dst = a.part_o + slot * kHeadDim + d0 + 4 * kq;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = wave * kRowsPerWaveLoad + 2 * i + (lane >> 5);
-        const int c0 = 2 * (lane & 31);  // logical 16-byte chunks c0, c0 + 1 of row r
-        bf16x8 lo, hi;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t word = src[i][w];
-            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-            bf16x8& dstv = w < 2 ? lo : hi;
-            const int base = (w & 1) * 4;
-            dstv[base + 0] = (__bf16)f01[0];
-            dstv[base + 1] = (__bf16)f01[1];
-            dstv[base + 2] = (__bf16)f23[0];
-            dstv[base + 3] = (__bf16)f23[1];
+        for (int db = 0; db < NB; ++db) *(f32x4*)(dst + 16 * db) = o[db] * a.v_scale;
+        if (kq == 0 && d0 == 0) {
+            a.part_ml[2 * slot] = m;
+            a.part_ml[2 * slot + 1] = l_row;
         }
-        const int sw = swz(r);
-        *(ATTN_LDS bf16x8*)(buf + r * kRowBytes + ((c0 ^ sw) << 4)) = lo;
-        *(ATTN_LDS bf16x8*)(buf + r * kRowBytes + (((c0 + 1) ^ sw) << 4)) = hi;
     }
 }
 
-template <bool FP8>
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_split_kernel(DecodeArgs a) {
+// ============================== bf16 pool ==================================
+
+// 16 rows per wave, global -> LDS, rows past `valid` arrive as zeros.
+__device__ __forceinline__ void issue_tile_bf16(const char* src, int valid, ATTN_LDS char* buf,
+                                                int wave, int lane16) {
+    rows16_to_lds<true>(buffer_rsrc(src, (uint32_t)valid * kRowBytes), buf, wave, lane16);
+}
+
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_split_bf16_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes + kDecRows * kSxStride];
+    SplitPlan p;
+    if (!plan_split(a, p)) return;
     ATTN_LDS char* sK = (ATTN_LDS char*)smem;
     ATTN_LDS char* sV = sK + kTileBytes;
     ATTN_LDS char* sX = sV + kTileBytes;
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int split = blockIdx.x % a.max_splits;
-    const int rest = blockIdx.x / a.max_splits;
-    const int kvh = rest % a.hkv;
-    const int b = rest / a.hkv;
-
-    int L = a.kv_lens[b];
-    L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
-    const int tile0 = split * a.tiles_per_split;
-    const int k_begin = tile0 * kPage;
-    if (k_begin >= L) return;  // empty split: the merge never reads it
-    const int k_end = min(k_begin + a.tiles_per_split * kPage, L);
-    const int ntiles = (k_end - k_begin + kPage - 1) / kPage;
-
-    // lane roles: n = query head of the group (MFMA column), kq = k-group
-    const int n = lane & 15;
-    const int kq = lane >> 4;
-    const bool row_ok = n < a.g;
+    const int n = lane & 15;   // query head of the group (MFMA column)
+    const int kq = lane >> 4;  // k-group
+    const int lane16 = lane * 16;
 
     // Q^T operand, k-step ks covers dims 32 ks .. 32 ks + 31; lane holds 32 ks + 8 kq .. + 7
     bf16x8 qf[16];
     {
-        const bf16x8* qp = (const bf16x8*)(a.q + ((size_t)b * a.hq + kvh * a.g +
-                                                  (row_ok ? n : 0)) * kHeadDim) + kq;
+        const bf16x8* qp = (const bf16x8*)(a.q + ((size_t)p.b * a.hq + p.kvh * a.g +
+                                                  (n < a.g ? n : 0)) * kHeadDim) + kq;
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
             const bf16x8 v = qp[4 * ks];
-            qf[ks] = row_ok ? v : bf16x8{};
+            qf[ks] = n < a.g ? v : bf16x8{};
         }
     }
-    // K operand offsets: row 16 wave + n, chunk 4 ks + kq; with ks = 4 u + v the
-    // byte offset is koff[v] + 256 u.
+    // K operand: row 16 wave + n, chunk 4 ks + kq; with ks = 4 u + v the byte
+    // offset is koff[v] + 256 u.
     int koff[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
         koff[v] = (16 * wave + n) * kRowBytes + (((4 * v + kq) ^ swz(n)) << 4);
-    // V^T operand (transposing reads): key row 32 c + 8 kq + (n >> 2) (+4 for the
-    // second read), dims 128 wave + 16 db + 4 (n & 3), i.e. logical chunk
+    // V^T operand (transposing reads): key row 32 c + 8 kq + (n >> 2) (+4 for
+    // the second read), dims 128 wave + 16 db + 4 (n & 3), i.e. logical chunk
     // 16 wave + 2 db + (n & 3) / 2 at byte 8 (n & 1).  Rows of different c
     // share the swizzle (32 c is a multiple of 16).
     int vrow[2], vsw[2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        vrow[half] = (8 * kq + (n >> 2) + 4 * half) * kRowBytes + 8 * (n & 1);
-        vsw[half] = swz(8 * kq + (n >> 2) + 4 * half);
+    for (int h = 0; h < 2; ++h) {
+        vrow[h] = (8 * kq + (n >> 2) + 4 * h) * kRowBytes + 8 * (n & 1);
+        vsw[h] = swz(8 * kq + (n >> 2) + 4 * h);
     }
     const int vchunk0 = 16 * wave + ((n & 3) >> 1);
     f32x4 o[8];
@@ -173,45 +202,20 @@ void decode_split_kernel(DecodeArgs a) {
     float m_run = -__builtin_inff();
     float l_run = 0.f;
 
-    const int* ptab = a.page_table + (size_t)b * a.max_pages;
-    const int lane16 = lane * 16;
-    const int tile_bytes = FP8 ? kTileBytes / 2 : kTileBytes;
-    Fp8Stage st;
-    if constexpr (FP8) {
-        const int valid0 = min(L - k_begin, kPage);
-        load_fp8(st.k, page_tile(a.k_pages, ptab, tile0, a.num_pages, a.hkv, kvh, tile_bytes),
-                 valid0, wave, lane);
-        load_fp8(st.v, page_tile(a.v_pages, ptab, tile0, a.num_pages, a.hkv, kvh, tile_bytes),
-                 valid0, wave, lane);
-    } else {
-        const int valid0 = min(L - k_begin, kPage);
-        issue_tile_bf16(page_tile(a.k_pages, ptab, tile0, a.num_pages, a.hkv, kvh, tile_bytes),
-                        valid0, sK, wave, lane16);
-        issue_tile_bf16(page_tile(a.v_pages, ptab, tile0, a.num_pages, a.hkv, kvh, tile_bytes),
-                        valid0, sV, wave, lane16);
+    auto valid_of = [&](int t) { return min(p.k_end - (p.k_begin + t * kPage), kPage); };
+    {
+        const int pg = split_page(a, p, 0);
+        issue_tile_bf16(tile_base(a.k_pages, a, pg, p.kvh, kTileBytes), valid_of(0), sK, wave, lane16);
+        issue_tile_bf16(tile_base(a.v_pages, a, pg, p.kvh, kTileBytes), valid_of(0), sV, wave, lane16);
     }
+    for (int t = 0; t < p.ntiles; ++t) {
+        const int key0 = p.k_begin + t * kPage;
+        const bool more = t + 1 < p.ntiles;
+        const int pg_next = split_page(a, p, t + 1);   // arrives by the next barrier
+        wait_vmcnt<kPage / kDecWaves>();   // K(t) in; V(t) may still be in flight
+        lds_barrier();
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int key0 = k_begin + t * kPage;
-        const bool more = t + 1 < ntiles;
-        if constexpr (FP8) {
-            // the previous tile's readers passed the barrier at the loop end
-            store_fp8_as_bf16(st.k, sK, wave, lane);
-            store_fp8_as_bf16(st.v, sV, wave, lane);
-            if (more) {
-                const int vn = min(L - (key0 + kPage), kPage);
-                load_fp8(st.k, page_tile(a.k_pages, ptab, tile0 + t + 1, a.num_pages, a.hkv, kvh,
-                                         tile_bytes), vn, wave, lane);
-                load_fp8(st.v, page_tile(a.v_pages, ptab, tile0 + t + 1, a.num_pages, a.hkv, kvh,
-                                         tile_bytes), vn, wave, lane);
-            }
-            lds_barrier();
-        } else {
-            wait_vmcnt<kRowsPerWaveLoad>();   // K(t) in; V(t) may still be in flight
-            lds_barrier();
-        }
-
-        // ---- S^T[16 keys of this wave][16 heads] over 512 dims
+        // S^T[16 keys of this wave][16 heads] over 512 dims
         f32x4 s = f32x4{};
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
@@ -221,15 +225,11 @@ void decode_split_kernel(DecodeArgs a) {
         // accumulator element i is key 16 wave + 4 kq + i of head n
         *(ATTN_LDS f32x4*)(sX + n * kSxStride + (16 * wave + 4 * kq) * 4) = s;
         lds_barrier();  // scores visible; every wave is done with sK
-        if constexpr (!FP8) {
-            if (more) {
-                const int vn = min(L - (key0 + kPage), kPage);
-                issue_tile_bf16(page_tile(a.k_pages, ptab, tile0 + t + 1, a.num_pages, a.hkv,
-                                          kvh, tile_bytes), vn, sK, wave, lane16);
-            }
-        }
+        if (more)
+            issue_tile_bf16(tile_base(a.k_pages, a, pg_next, p.kvh, kTileBytes), valid_of(t + 1),
+                            sK, wave, lane16);
 
-        // ---- online softmax over the tile; this lane takes keys 32 c + 8 kq + j
+        // online softmax over the tile; this lane takes keys 32 c + 8 kq + j
         float x[2][8];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -244,7 +244,7 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int key = key0 + 32 * c + 8 * kq + j;
-                const float v = key < k_end ? x[c][j] * a.scale_log2 : -__builtin_inff();
+                const float v = key < p.k_end ? x[c][j] * a.scale_log2 : -__builtin_inff();
                 x[c][j] = v;
                 mt = fmaxf(mt, v);
             }
@@ -259,9 +259,9 @@ void decode_split_kernel(DecodeArgs a) {
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float p = fast_exp2(x[c][j] - m_new);
-                psum += p;
-                pf[c][j] = (__bf16)p;
+                const float pv = fast_exp2(x[c][j] - m_new);
+                psum += pv;
+                pf[c][j] = (__bf16)pv;
             }
         }
         l_run = l_run * alpha + psum;
@@ -269,12 +269,10 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db] *= alpha;
 
-        if constexpr (!FP8) {
-            if (more) wait_vmcnt<kRowsPerWaveLoad>(); else wait_vmcnt<0>();
-            lds_barrier();  // V(t) visible
-        }
+        if (more) wait_vmcnt<kPage / kDecWaves>(); else wait_vmcnt<0>();
+        lds_barrier();  // V(t) visible
 
-        // ---- O^T[128 dims of this wave][16 heads] += V^T P^T
+        // O^T[128 dims of this wave][16 heads] += V^T P^T
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -288,33 +286,204 @@ void decode_split_kernel(DecodeArgs a) {
             }
         }
         lds_barrier();  // every wave is done with sV and sX
-        if constexpr (!FP8) {
-            if (more) {
-                const int vn = min(L - (key0 + kPage), kPage);
-                issue_tile_bf16(page_tile(a.v_pages, ptab, tile0 + t + 1, a.num_pages, a.hkv,
-                                          kvh, tile_bytes), vn, sV, wave, lane16);
-            }
-        }
+        if (more)
+            issue_tile_bf16(tile_base(a.v_pages, a, pg_next, p.kvh, kTileBytes), valid_of(t + 1),
+                            sV, wave, lane16);
     }
+    const size_t slot = (((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub * a.g + n;
+    write_partial<8>(a, slot, n, kq, 128 * wave, o, m_run, l_run);
+}
 
-    // ---- partial: O^T accumulator element i of block db is dim
-    // 128 wave + 16 db + 4 kq + i of head n.  l sums over the four k-groups.
-    float l_row = l_run + __shfl_xor(l_run, 16);
-    l_row += __shfl_xor(l_row, 32);
-    if (row_ok) {
-        const size_t slot = (((size_t)b * a.hkv + kvh) * a.max_splits + split) * a.g + n;
-        float* dst = a.part_o + slot * kHeadDim + 128 * wave + 4 * kq;
+// ============================== FP8 pool ===================================
+
+// LDS layout of a wave's V half page: row r (a key) is 512 bytes, its 16-byte
+// chunk c sits at chunk c ^ swz8(r).  swz8 separates the rows of each
+// transposed read (rows 4 kq .. 4 kq + 3 and 16 + 4 kq .. 16 + 4 kq + 3) and
+// of each half of a wave.
+__host__ __device__ constexpr int swz8(int r) { return (r & 15) ^ (((r >> 4) & 1) << 2); }
+
+// V half page (32 rows of 512 E4M3 bytes) -> this wave's LDS buffer by DMA, 2
+// rows per instruction: lane l lands at LDS byte 16 l of rows 2 i, 2 i + 1,
+// i.e. row 2 i + l / 32 at chunk position l % 32, and so fetches logical
+// chunk (l % 32) ^ swz8(row).  Rows past `rows` arrive as zeros.
+__device__ __forceinline__ void dma_v_half(const char* src, int rows, ATTN_LDS char* buf,
+                                           int lane) {
+    const u32x4 rsrc = buffer_rsrc(src, (uint32_t)rows * kHeadDim);
+    const uint32_t lds = (uint32_t)(uintptr_t)buf;
+    const int hl = lane >> 5;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * a.v_scale;
-        if (wave == 0 && kq == 0) {
-            a.part_ml[2 * slot] = m_run;
-            a.part_ml[2 * slot + 1] = l_row;
-        }
+    for (int i = 0; i < kHalfKeys / 2; ++i) {
+        const int r = 2 * i + hl;
+        const int voff = r * kHeadDim + (((lane & 31) ^ swz8(r)) << 4);
+        asm volatile(
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %0, %2, 0 offen nt lds"
+            :
+            : "v"(voff), "s"(lds + 2 * i * kHeadDim), "s"(rsrc)
+            : "memory", "m0");
     }
 }
 
+// K half page straight into MFMA A-operand registers: key group gm (keys
+// 16 gm .. 16 gm + 15), load i: key 16 gm + n, bytes 64 i + 16 kq .. + 15,
+// i.e. the lane's operands of k-steps 2 i and 2 i + 1 (8 dims each).
+struct KHalf {
+    u32x4 r[16];
+};
+
+__device__ __forceinline__ void load_k_half(KHalf& k, const char* src, int rows, int n, int kq) {
+    const __amdgpu_buffer_rsrc_t rsrc = uniform_rsrc(src, rows * kHeadDim);
+    const int ko = n * kHeadDim + 16 * kq;
+#pragma unroll
+    for (int gm = 0; gm < 2; ++gm)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) k.r[8 * gm + i] = load16(rsrc, ko + gm * 16 * kHeadDim + 64 * i);
+}
+
+__device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
+    const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+// Per wave step (half page u of this wave, V buffer c % 2):
+//   QK(u) from the K registers (their loads, and V(u)'s DMA issued before
+//   them, are waited for here), then V(u + 4) DMA -> the other buffer (its
+//   last readers, PV two steps back, are complete) and K(u + 4) -> the K
+//   registers, then softmax and PV(u).  Past the split's end the loads are
+//   zero-length.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_split_fp8_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[NW * 2 * kHalfBytes];
+    SplitPlan p;
+    if (!plan_split(a, p)) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;   // query head of the group (MFMA column)
+    const int kq = lane >> 4;  // k-group
+    ATTN_LDS char* sv0 = (ATTN_LDS char*)smem + wave * 2 * kHalfBytes;
+
+    // Q^T operand of k-step ks: dims 64 (ks / 2) + 16 kq + 8 (ks % 2) .. + 7,
+    // the order in which the K loads deliver them
+    bf16x8 qf[16];
+    {
+        const __bf16* qrow = a.q + ((size_t)p.b * a.hq + p.kvh * a.g + (n < a.g ? n : 0)) * kHeadDim;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const bf16x8 v = *(const bf16x8*)(qrow + 64 * (ks >> 1) + 16 * kq + 8 * (ks & 1));
+            qf[ks] = n < a.g ? v : bf16x8{};
+        }
+    }
+    // V^T operand, read transposed: within each 16-lane group kq, lane
+    // 2 j + h addresses key row r_j = (j < 4 ? 4 kq + j : 16 + 4 kq + j - 4) at
+    // byte 16 db + 8 h, and lane i receives dim 16 db + i of rows r_0 .. r_7:
+    // the same keys, in the same order, as this lane's P^T operand (the QK
+    // accumulators of key groups 0 and 1).
+    const int tj = n >> 1;
+    const int vr = tj < 4 ? 4 * kq + tj : 16 + 4 * kq + tj - 4;
+    const int vrow = vr * kHeadDim + 8 * (n & 1);
+    const int vsw = swz8(vr);
+
+    f32x4 o[32];
+#pragma unroll
+    for (int db = 0; db < 32; ++db) o[db] = f32x4{};
+    float m_ref = -__builtin_inff();
+    float l_run = 0.f;
+
+    const int nhalf = (p.k_end - p.k_begin + kHalfKeys - 1) / kHalfKeys;
+    const int count = nhalf > wave ? (nhalf - wave + NW - 1) / NW : 0;
+    KHalf kr;
+    auto issue = [&](int u, ATTN_LDS char* vbuf) {
+        int rows = p.k_end - (p.k_begin + u * kHalfKeys);
+        rows = rows < 0 ? 0 : (rows > kHalfKeys ? kHalfKeys : rows);
+        const int pg = split_page(a, p, u >> 1);
+        const int off = (u & 1) * kHalfBytes;
+        dma_v_half(tile_base(a.v_pages, a, pg, p.kvh, kTileBytes / 2) + off, rows, vbuf, lane);
+        load_k_half(kr, tile_base(a.k_pages, a, pg, p.kvh, kTileBytes / 2) + off, rows, n, kq);
+    };
+    issue(wave, sv0);
+    for (int c = 0; c < count; ++c) {
+        const int u = wave + NW * c;
+        const int key0 = p.k_begin + u * kHalfKeys;
+        ATTN_LDS char* sv = sv0 + (c & 1) * kHalfBytes;
+        // S^T[32 keys][16 heads]: key group gm = keys 16 gm .. 16 gm + 15
+        f32x4 s[2];
+#pragma unroll
+        for (int gm = 0; gm < 2; ++gm) {
+            f32x4 s0 = f32x4{}, s1 = f32x4{};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 w = kr.r[8 * gm + i];
+                s0 = mfma16x16x32(widen8(w[0], w[1]), qf[2 * i], s0);
+                s1 = mfma16x16x32(widen8(w[2], w[3]), qf[2 * i + 1], s1);
+            }
+            s[gm] = s0 + s1;   // element i: key 16 gm + 4 kq + i of head n
+        }
+        wait_vmcnt<0>();   // V(u) landed too (its DMA was issued before K(u))
+        // refill for this wave's next half page; the K registers are reused
+        // in place, so keep the loads below QK
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        issue(u + NW, sv0 + ((c + 1) & 1) * kHalfBytes);
+
+        // softmax against the reference maximum
+        float x[8];
+        float mt = -__builtin_inff();
+#pragma unroll
+        for (int gm = 0; gm < 2; ++gm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = key0 + 16 * gm + 4 * kq + i;
+                const float v = key < p.k_end ? s[gm][i] * a.scale_log2 : -__builtin_inff();
+                x[4 * gm + i] = v;
+                mt = fmaxf(mt, v);
+            }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        // every half page has a live key, so mt is finite; the first one
+        // always moves the reference (alpha = 0 on the zero O)
+        const bool up = mt > m_ref + kRefMargin;
+        if (__builtin_amdgcn_ballot_w64(up)) {
+            const float m_new = up ? mt : m_ref;
+            const float alpha = up ? fast_exp2(m_ref - m_new) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < 32; ++db) o[db] *= alpha;
+            m_ref = m_new;
+        }
+        bf16x8 pf;
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float pv = fast_exp2(x[j] - m_ref);
+            psum += pv;
+            pf[j] = (__bf16)pv;
+        }
+        l_run += psum;
+
+        // O^T[512 dims][16 heads] += V^T P^T over the 32 keys
+#pragma unroll
+        for (int db = 0; db < 32; ++db) {
+            const v2i32 t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (ATTN_LDS v2i32*)(sv + vrow + ((db ^ vsw) << 4)));
+            o[db] = mfma16x16x32(widen8((uint32_t)t8[0], (uint32_t)t8[1]), pf, o[db]);
+            // bound the operands in flight
+            if ((db & 7) == 7 && db < 31) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmcnt<0>();   // the last (zero-length) loads
+    const size_t slot =
+        ((((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub + wave) * a.g + n;
+    write_partial<32>(a, slot, n, kq, 0, o, m_ref, l_run);
+}
+
 // One workgroup per (sequence, query head): combine the sequence's partials,
-// mu = max m_i, o = sum 2^(m_i - mu) O_i / sum 2^(m_i - mu) l_i.
+// mu = max m_i, o = sum 2^(m_i - mu) O_i / sum 2^(m_i - mu) l_i.  A partial
+// that saw no key (m = -inf, l = 0, O = 0) adds nothing.
 template <bool OUT_FP32>
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, void* out) {
     const int b = blockIdx.x / a.hq;
@@ -325,8 +494,8 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, void* o
     L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
     const int split_keys = a.tiles_per_split * kPage;
     int ns = (L + split_keys - 1) / split_keys;
-    ns = ns > a.max_splits ? a.max_splits : ns;
-    const size_t slot0 = (((size_t)b * a.hkv + kvh) * a.max_splits) * a.g + r;
+    ns = (ns > a.max_splits ? a.max_splits : ns) * a.sub;   // every non-empty split wrote a.sub
+    const size_t slot0 = (((size_t)b * a.hkv + kvh) * a.max_splits) * a.sub * a.g + r;
     float mu = -__builtin_inff();
     for (int i = 0; i < ns; ++i) mu = fmaxf(mu, a.part_ml[2 * (slot0 + (size_t)i * a.g)]);
     f32x4 acc = f32x4{};
@@ -370,7 +539,7 @@ extern "C" size_t attn_decode_splitk_workspace_size(int batch, int num_q_heads, 
     const int kps = keys_per_split ? keys_per_split
                                    : default_keys_per_split(batch, num_kv_heads, max_kv_len);
     const size_t splits = (size_t)(max_kv_len + kps - 1) / kps;
-    const size_t slots = (size_t)batch * num_q_heads * splits;  // hkv * g = hq
+    const size_t slots = (size_t)batch * num_q_heads * splits * kMaxSub;  // hkv * g = hq
     return slots * (kHeadDim + 2) * sizeof(float);
 }
 
@@ -416,19 +585,20 @@ extern "C" int attn_decode_splitk(const void* q, const void* k_pages, const void
     a.num_pages = num_pages;
     a.max_splits = (max_kv_len + kps - 1) / kps;
     a.tiles_per_split = kps / kPage;
-    const size_t slots = (size_t)batch * num_q_heads * a.max_splits;
+    const size_t slots = (size_t)batch * num_q_heads * a.max_splits * kMaxSub;
     a.part_o = (float*)workspace;
     a.part_ml = (float*)workspace + slots * kHeadDim;
     const bool fp8 = kv_dtype == ATTN_FP8_E4M3;
+    a.sub = fp8 ? kFp8Waves : 1;
     a.scale_log2 = softmax_scale * 1.4426950408889634f * (fp8 ? k_scale : 1.f);
     a.v_scale = fp8 ? v_scale : 1.f;
     const long long grid = (long long)batch * num_kv_heads * a.max_splits;
     if (grid > 0x7fffffffLL || (long long)batch * num_q_heads > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     if (fp8)
-        hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)grid), dim3(kDecThreads), 0,
-                           stream, a);
+        hipLaunchKernelGGL(decode_split_fp8_kernel<kFp8Waves>, dim3((unsigned)grid),
+                           dim3(64 * kFp8Waves), 0, stream, a);
     else
-        hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)grid), dim3(kDecThreads), 0,
+        hipLaunchKernelGGL(decode_split_bf16_kernel, dim3((unsigned)grid), dim3(kDecThreads), 0,
                            stream, a);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
     if (out_dtype == ATTN_FP32)

@@ -10,9 +10,11 @@ namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 
 #define ATTN_LDS __attribute__((address_space(3)))
 #define ATTN_GLOBAL __attribute__((address_space(1)))
@@ -64,20 +66,34 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // bookkeeping would otherwise wait for every outstanding tile load before
 // any LDS read.  Callers order it with wait_vmcnt and lds_barrier.  M0 carries
 // the LDS address (one wait state after the SALU write); none of the kernels
-// built with these helpers use M0 for anything else.
-template <int SWZ, int REL>
+// built with these helpers use M0 for anything else.  The SALU add also
+// writes SCC, which the clobber list declares.
+template <int SWZ, int REL, bool NT = false>
 __device__ __forceinline__ void dma_row(u32x4 rsrc, uint32_t lds_base, uint32_t soff,
                                         int lane_off) {
     int voff;
-    asm volatile(
-        "v_xor_b32 %0, %1, %2\n\t"
-        "v_or_b32 %0, %3, %0\n\t"
-        "s_add_u32 m0, %4, %3\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %0, %5, %6 offen lds"
-        : "=&v"(voff)
-        : "i"(SWZ), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
-        : "memory", "m0");
+    // NT: non-temporal (streaming) cache policy, for data read exactly once
+    if constexpr (NT) {
+        asm volatile(
+            "v_xor_b32 %0, %1, %2\n\t"
+            "v_or_b32 %0, %3, %0\n\t"
+            "s_add_u32 m0, %4, %3\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %0, %5, %6 offen nt lds"
+            : "=&v"(voff)
+            : "i"(SWZ), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
+            : "memory", "m0", "scc");
+    } else {
+        asm volatile(
+            "v_xor_b32 %0, %1, %2\n\t"
+            "v_or_b32 %0, %3, %0\n\t"
+            "s_add_u32 m0, %4, %3\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %0, %5, %6 offen lds"
+            : "=&v"(voff)
+            : "i"(SWZ), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
+            : "memory", "m0", "scc");
+    }
 }
 
 // Compile-time loop: f(std::integral_constant<int, i>{}) for i = 0 .. N-1, so
@@ -93,13 +109,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // A wave's 16 rows of one tile, rows 16 wave .. 16 wave + 15 (row 16 wave + i
 // has swizzle swz(i)).
+template <bool NT>
 __device__ __forceinline__ void rows16_to_lds(u32x4 rsrc, const ATTN_LDS char* buf, int wave,
                                               int lane16) {
     const uint32_t off = (uint32_t)wave * 16 * kRowBytes;
     const uint32_t base = (uint32_t)(uintptr_t)buf + off;
     static_for<16>([&](auto I) {
         constexpr int i = decltype(I)::value;
-        dma_row<(swz(i) << 4), i * kRowBytes>(rsrc, base, off, lane16);
+        dma_row<(swz(i) << 4), i * kRowBytes, NT>(rsrc, base, off, lane16);
     });
 }
 

@@ -102,7 +102,7 @@ def test_decode_validation(L):
 
 def test_workspace_size(L):
     n = L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 1024)
-    assert n == 64 * 8 * 28 * (512 + 2) * 4
+    assert n == 64 * 8 * 28 * 4 * (512 + 2) * 4   # 4 partials per split
     assert L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 100) == 0
     assert L.attn_decode_splitk_workspace_size(0, 8, 4, 28672, 0) == 0
     assert L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 0) > 0
