@@ -23,18 +23,19 @@
 // 15, the scores meet in a small LDS buffer, every wave runs the softmax of
 // all 64 keys and accumulates its own 128 of the 512 output dims.
 //
-// FP8-E4M3 pool: the four waves of a workgroup work independently, each on
-// its own 32-key half pages (wave w takes half pages w, w + 4, ... of the
-// split) and each writing its own partial, so the loop has no workgroup
-// barrier.  K goes from HBM straight into the MFMA operand registers; V is
-// staged through registers into a per-wave LDS buffer as raw E4M3 bytes and
-// read back transposed (ds_read_b64_tr_b8).  Both are widened exactly to
-// bf16 (every E4M3 value is a bf16 value) just before their MFMA, k_scale is
-// folded into the softmax scale and v_scale into the partial (vLLM
-// flash-attention PR 199, "Summary": FP8 KV with 16-bit MMA).  Each wave
-// keeps a reference maximum and rescales O only when a score exceeds it by
-// more than kRefMargin (log2 units), so the 128-register O accumulator is
-// rarely touched by the softmax.
+// FP8-E4M3 pool: a split workgroup is one wave (the kernel takes any number
+// of waves, each on its own 32-key half pages and writing its own partial),
+// so the loop has no workgroup barrier and four independent waves per CU
+// hide each other's start-up.  The wave streams 32-key half pages: K goes
+// from HBM straight into the MFMA operand registers; V is DMA'd as raw E4M3
+// bytes into a per-wave double buffer in LDS and read back transposed
+// (ds_read_b64_tr_b8).  Both are widened exactly to bf16 (every E4M3 value
+// is a bf16 value) just before their MFMA, k_scale is folded into the
+// softmax scale and v_scale into the partial (vLLM flash-attention PR 199,
+// "Summary": FP8 KV with 16-bit MMA).  The wave keeps a reference maximum
+// and rescales O only when a score exceeds it by more than kRefMargin (log2
+// units), so the 128-register O accumulator is rarely touched by the
+// softmax.
 #include "device_common.h"
 #include "attn_host.h"
 
@@ -48,10 +49,7 @@ constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kSxStride = 272;      // bytes per score-exchange row (256 + 16 pad)
 constexpr int kDefaultTargetWgs = 4096;
 constexpr int kNonTemporal = 2;     // buffer-load cache policy: nt (read-once stream)
-#ifndef FP8_WAVES
-#define FP8_WAVES 1
-#endif
-constexpr int kFp8Waves = FP8_WAVES; // waves per FP8 split workgroup, one partial each
+constexpr int kFp8Waves = 1;       // waves per FP8 split workgroup, one partial each
 constexpr int kMaxSub = 4;          // partials per split workgroup (FP8: one per wave)
 constexpr int kHalfKeys = 32;       // FP8: keys per wave step
 constexpr int kHalfBytes = kHalfKeys * kHeadDim;   // FP8 rows are 512 bytes

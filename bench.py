@@ -31,6 +31,33 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (no sparsity)
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 
+# HBM bytes per launch of the headline prefill kernel, from two rocprofv3
+# counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of this script,
+# each scaled by what the same counter reads for the 1 GiB device-to-device
+# copy this script makes (profiles/prefill_hd512_chunk8192_at_8192.md).  The
+# figure is only valid for the kernel sources it was taken with: their
+# SHA-256 is checked at run time and traffic is reported as null otherwise.
+TRAFFIC_RECORD = {
+    "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
+                "attention_hd512_gqa_amd/csrc/device_common.h"],
+    "sha256": "d45101aeb6af71d83f50e036f7ffd83d173c5f3dd68b58c6be6771830854e66e",
+    "fetch_bytes": 2035786130,
+    "write_bytes": 286013312,
+    "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
+}
+
+
+def recorded_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_RECORD["sources"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    digest = h.hexdigest()
+    if TRAFFIC_RECORD["sha256"] != digest or TRAFFIC_RECORD["fetch_bytes"] is None:
+        return None, digest
+    return TRAFFIC_RECORD["fetch_bytes"] + TRAFFIC_RECORD["write_bytes"], digest
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -106,6 +133,16 @@ def main():
     del buf, sink
     torch.cuda.empty_cache()
     log(f"HBM read probe over 8 GiB: {hbm_read:.0f} GB/s")
+    # 1 GiB device-to-device copy: a rate for reference and, under rocprofv3,
+    # the calibration of the FETCH_SIZE / WRITE_SIZE counters (1 GiB each way)
+    cal_bytes = 1 << 30
+    src = torch.empty(cal_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src), 5, 2)
+    d2d = 2 * cal_bytes / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"D2D copy of 1 GiB: {d2d:.0f} GB/s (read + write)")
 
     # ---- headline: prefill of one 8192-row chunk at 8192..16383 ------------
     case = W.chunk_prefill_8k_at_8k(device="cuda")
@@ -226,6 +263,10 @@ def main():
                          f"fp32 C oracle, {cores} threads)"}
         log(f"CPU oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cores} threads")
 
+    traffic, digest = recorded_traffic()
+    # unique bytes of one launch: Q, the visible K and V rows of each KV head, O
+    algo_bytes = (lc.total_q * case.num_q_heads * W.HEAD_DIM * 2 * 2
+                  + 2 * lc.kv_lens[0] * case.num_kv_heads * W.HEAD_DIM * 2)
     result = {
         "metric": "hd512 causal prefill TFLOP/s + % of same-process bf16 MFMA GEMM peak",
         "value": tflops,
@@ -247,9 +288,13 @@ def main():
                           "frac": (tflops / gemm) if gemm else None,
                           "how": "torch.matmul bf16 8192^3 and 16384^3, best"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "prefill_hd512_kernel"},
-        "hbm": {"read_probe_GB_per_s": hbm_read, "probe_bytes": hbm_bytes},
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (FETCH + WRITE, calibrated)",
+                     "traffic_algorithmic_bytes": algo_bytes,
+                     "traffic_source": TRAFFIC_RECORD["profile"] if traffic else None,
+                     "kernel": "prefill_hd512_kernel", "kernel_sources_sha256": digest},
+        "hbm": {"read_probe_GB_per_s": hbm_read, "probe_bytes": hbm_bytes,
+                "d2d_copy_GB_per_s": d2d},
         "decode": decode,
         "prefill_other": extra,
         "cpu_baseline": cpu,

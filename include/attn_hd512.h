@@ -100,9 +100,10 @@ int attn_prefill_hd512(const void* q, const void* k_pages, const void* v_pages,
                        float softmax_scale, void* out, int out_dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace attn_decode_splitk needs for these sizes
- * (fp32 partial outputs plus (m, l) per split, query head and sequence).
- * keys_per_split = 0 selects the library default.  Returns 0 for invalid sizes.
+ * Bytes of device workspace attn_decode_splitk needs for these sizes: fp32
+ * partial outputs plus (m, l) for up to 4 partials per split, per query head
+ * and sequence (valid for either KV dtype).  keys_per_split = 0 selects the
+ * library default.  Returns 0 for invalid sizes.
  */
 size_t attn_decode_splitk_workspace_size(int batch, int num_q_heads, int num_kv_heads,
                                          int max_kv_len, int keys_per_split);
@@ -126,10 +127,13 @@ size_t attn_decode_splitk_workspace_size(int batch, int num_q_heads, int num_kv_
  *                entry are ignored; it must not be shared by concurrent calls.
  *   out          [batch][num_q_heads][512] of out_dtype (ATTN_BF16 or ATTN_FP32).
  *
- * Two kernels run back to back on `stream`: the split kernel writes one
- * partial per (sequence, KV head, split) for every query head of the group,
- * and the merge kernel combines them.  A split past a sequence's kv_len is
- * empty (m = -inf, l = 0) and contributes nothing.
+ * Two kernels run back to back on `stream`: the split kernel writes the
+ * partials of every (sequence, KV head, split) for every query head of the
+ * group (one per split for a bf16 pool, one per wave of the split workgroup
+ * for an FP8 pool), and the merge kernel combines them.  Splits that start
+ * at or past a sequence's kv_len are neither written nor read: the merge
+ * derives each sequence's split count from kv_lens.  A partial that saw no
+ * key (m = -inf, l = 0, O = 0) contributes nothing.
  */
 int attn_decode_splitk(const void* q, const void* k_pages, const void* v_pages, int kv_dtype,
                        float k_scale, float v_scale, const int32_t* page_table,
