@@ -38,6 +38,9 @@ def lib() -> ctypes.CDLL:
         P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.attn_prefill_hd512.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P]
         L.attn_prefill_hd512.restype = I
+        L.attn_prefill_hd512_e4m3.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I, I, I, I, I,
+                                              I, F, P, I, P]
+        L.attn_prefill_hd512_e4m3.restype = I
         L.attn_decode_splitk_workspace_size.argtypes = [I, I, I, I, I]
         L.attn_decode_splitk_workspace_size.restype = SZ
         L.attn_decode_splitk.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, F,
@@ -81,20 +84,32 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
 
 
 def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out, *,
-            total_q: int, max_q_len: int, softmax_scale: float, stream=None) -> None:
-    """Chunked causal prefill (attn_prefill_hd512).  Sizes are host ints: no sync."""
+            total_q: int, max_q_len: int, softmax_scale: float, kv_dtype: str = "bf16",
+            k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """Chunked causal prefill over a bf16 pool (attn_prefill_hd512) or an
+    FP8-E4M3 pool with per-tensor scales (attn_prefill_hd512_e4m3).  Sizes are
+    host ints: no sync."""
     num_pages, hkv, page, d = k_pages.shape
     hq = q.shape[1]
     batch = kv_lens.shape[0]
-    code = lib().attn_prefill_hd512(
-        _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.bfloat16),
-        _dev(v_pages, "v_pages", torch.bfloat16), _dev(page_table, "page_table", torch.int32),
-        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(q_start, "q_start", torch.int32),
-        _dev(kv_lens, "kv_lens", torch.int32), int(batch), int(total_q), int(max_q_len),
-        int(hq), int(hkv), int(d), int(page), int(num_pages), int(page_table.shape[1]),
-        float(softmax_scale), _dev(out, "out", (torch.bfloat16, torch.float32)),
-        _DTYPE_CODES[out.dtype], _stream(stream))
-    _check(code, "attn_prefill_hd512")
+    meta = (_dev(page_table, "page_table", torch.int32),
+            _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(q_start, "q_start", torch.int32),
+            _dev(kv_lens, "kv_lens", torch.int32), int(batch), int(total_q), int(max_q_len),
+            int(hq), int(hkv), int(d), int(page), int(num_pages), int(page_table.shape[1]),
+            float(softmax_scale), _dev(out, "out", (torch.bfloat16, torch.float32)),
+            _DTYPE_CODES[out.dtype], _stream(stream))
+    if kv_dtype == "bf16":
+        code = lib().attn_prefill_hd512(
+            _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.bfloat16),
+            _dev(v_pages, "v_pages", torch.bfloat16), *meta)
+        _check(code, "attn_prefill_hd512")
+    elif kv_dtype == "fp8_e4m3":
+        code = lib().attn_prefill_hd512_e4m3(
+            _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.uint8),
+            _dev(v_pages, "v_pages", torch.uint8), float(k_scale), float(v_scale), *meta)
+        _check(code, "attn_prefill_hd512_e4m3")
+    else:
+        raise AttnError(f"unsupported kv_dtype {kv_dtype!r}")
 
 
 def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_kv_len: int,

@@ -146,6 +146,19 @@ __device__ __forceinline__ void mfma32x32x16_vgpr_first(f32x16& acc, bf16x8 a, b
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 
+// The same two forms for an A operand that VALU instructions have just
+// written (e.g. widened FP8): the asm is opaque to the hazard recognizer, so
+// the VALU-write -> MFMA-read wait states are issued here (5, more than the
+// gfx950 requirement).
+__device__ __forceinline__ void mfma32x32x16_vgpr_va(f32x16& acc, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32x32x16_vgpr_first_va(f32x16& acc, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                 : "=&v"(acc) : "v"(a), "v"(b));
+}
+
 // Wait states covering an XDL MFMA write -> VALU/VMEM/DS read of its result
 // (at most 16 passes + a few on gfx950; 3 x 8 = 24 here), tied to the
 // accumulator so that no reader can be scheduled above it.

@@ -40,6 +40,8 @@
 #include "device_common.h"
 #include "attn_host.h"
 
+#include <type_traits>
+
 namespace attn {
 
 namespace {
@@ -52,6 +54,10 @@ constexpr int kRowsPerWaveLoad = kPage / kWaves;  // tile rows each wave moves
 // maximum: p <= 2^32 and l <= 2^32 * keys stay far inside fp32 and bf16.
 constexpr float kRescaleMargin = 32.f;
 constexpr int kPrefetch = 4;  // LDS operand reads in flight ahead of their MFMA
+// FP8 operands are widened in registers; one fewer read in flight keeps the
+// FP8 kernel inside the 256 VGPRs
+template <bool FP8>
+constexpr int kPrefetchOf = FP8 ? 3 : kPrefetch;
 // Page ids of the first kPagesInLds tiles are staged in LDS at the start of
 // the workgroup (reading them from the scalar cache inside the loop stalls
 // the wave: scalar loads share the LDS wait counter and return out of order).
@@ -59,6 +65,22 @@ constexpr int kPagesInLds = 4096;
 // Restarts per workgroup are capped so that non-finite inputs (a caller error)
 // cannot loop forever; each genuine restart raises a row's reference by > 32.
 constexpr int kMaxRestarts = 8;
+
+// K/V pool element: bf16 (1 KB key rows) or FP8-E4M3 bytes (512-byte rows).
+template <bool FP8>
+struct Kv {
+    static constexpr int kRowB = FP8 ? kHeadDim : kRowBytes;
+    static constexpr int kTileB = kPage * kRowB;
+    // buffer->LDS loads per wave per 32-key half refill: 8 bf16 rows of 1 KB,
+    // or 4 loads of two 512-byte FP8 rows
+    static constexpr int kDmaPerHalf = FP8 ? 4 : 8;
+};
+
+// LDS layout of an FP8 tile: row r (a key) is 512 bytes, its 16-byte chunk c
+// sits at chunk c ^ (r % 32).  The K operand reads (32 consecutive rows at one
+// chunk) and the transposed V reads (8 rows per 16-lane group at one chunk)
+// then hit distinct chunks.
+__host__ __device__ constexpr int swz8(int r) { return r & 31; }
 
 struct PrefillArgs {
     const __bf16* q;
@@ -72,7 +94,8 @@ struct PrefillArgs {
     int batch, total_q, hq, hkv, g, max_pages, num_pages;
     int tok_per_wg;     // tokens per workgroup = 128 / g (rounded down)
     int wgs_per_seq;    // ceil(max_q_len / tok_per_wg)
-    float scale_log2;   // softmax_scale * log2(e)
+    float scale_log2;   // softmax_scale * log2(e) (* k_scale for an FP8 pool)
+    float v_scale;      // FP8 pool: value dequantisation scale, applied to O (1 for bf16)
 };
 
 // Refill of one 32-key half (rows 32 half .. 32 half + 31) of a K or V tile
@@ -88,26 +111,67 @@ struct HalfDma {
     bool on;            // wave-uniform: this refill exists
 };
 
+template <bool FP8>
 __device__ __forceinline__ HalfDma half_dma(const char* pool, int page, int num_pages, int hkv,
                                             int kvh, int valid, const ATTN_LDS char* buf,
                                             int half, int wave, bool on) {
+    constexpr int kRowB = Kv<FP8>::kRowB;
     page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
-    const char* src = pool + ((size_t)page * hkv + kvh) * (size_t)kTileBytes;
+    const char* src = pool + ((size_t)page * hkv + kvh) * (size_t)Kv<FP8>::kTileB;
     HalfDma d;
-    d.rsrc = buffer_rsrc(src, (uint32_t)(valid > 0 ? valid : 0) * kRowBytes);
-    d.soff = (uint32_t)__builtin_amdgcn_readfirstlane((32 * half + 8 * wave) * kRowBytes);
+    d.rsrc = buffer_rsrc(src, (uint32_t)(valid > 0 ? valid : 0) * kRowB);
+    d.soff = (uint32_t)__builtin_amdgcn_readfirstlane((32 * half + 8 * wave) * kRowB);
     d.lds_base = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(uintptr_t)buf + d.soff));
     d.on = on;
     return d;
 }
 
-template <int J>
-__device__ __forceinline__ void half_dma_row(const HalfDma& d, int lane_off) {
-    dma_row<(swz(J) << 4), J * kRowBytes>(d.rsrc, d.lds_base, d.soff, lane_off);
+// One buffer->LDS load of 16 bytes per lane at LDS byte m0 + 16 lane, from
+// byte voff + soff of the resource.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t m0, uint32_t soff, int voff) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %2, %3 offen lds"
+        :
+        : "v"(voff), "s"(m0), "s"(rsrc), "s"(soff)
+        : "memory", "m0");
 }
 
-__device__ __forceinline__ void half_dma_all(const HalfDma& d, int lane_off) {
-    static_for<8>([&](auto J) { half_dma_row<decltype(J)::value>(d, lane_off); });
+// Refill load J of this wave's share of a half: bf16, row 8 wave + J of the
+// half (one 1 KB row); FP8, rows 8 wave + 2 J and + 1 (lanes 0-31 and 32-63),
+// each lane fetching the logical chunk that the swizzle stores at its LDS
+// position: chunk (lane % 32) ^ swz8(row).
+template <bool FP8, int J>
+__device__ __forceinline__ void half_dma_row(const HalfDma& d, int lane_off, int lane, int wave) {
+    if constexpr (FP8) {
+        const int rw = 2 * J + (lane >> 5);            // row within the wave's 8
+        const int f = (8 * wave + rw) & 31;            // swz8 of the tile row (32 half is 0 mod 32)
+        const int voff = rw * kHeadDim + (((lane & 31) ^ f) << 4);
+        dma16(d.rsrc, d.lds_base + 2 * J * kHeadDim, d.soff, voff);
+    } else {
+        dma_row<(swz(J) << 4), J * kRowBytes>(d.rsrc, d.lds_base, d.soff, lane_off);
+    }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void half_dma_all(const HalfDma& d, int lane_off, int lane, int wave) {
+    static_for<Kv<FP8>::kDmaPerHalf>([&](auto J) {
+        half_dma_row<FP8, decltype(J)::value>(d, lane_off, lane, wave);
+    });
+}
+
+// 8 E4M3 bytes -> 8 bf16 (exact: every E4M3 value is a bf16 value)
+__device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
+    const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+__device__ __forceinline__ bf16x8 operand(const bf16x8& x) { return x; }
+__device__ __forceinline__ bf16x8 operand(const v2i32& x) {
+    return widen8((uint32_t)x[0], (uint32_t)x[1]);
 }
 
 // Per-lane state of the softmax of one 32-key block.  Scores arrive already
@@ -173,35 +237,75 @@ struct VReader {
     }
 };
 
+// FP8 V^T operand reader (ds_read_b64_tr_b8): within each 16-lane group G,
+// lane 2 j + hh addresses key row 16 c + 8 (j / 4) + 4 (G / 2) + (j % 4) at
+// byte 32 db + 16 (G % 2) + 8 hh, and lane i of the group receives dim
+// 32 db + 16 (G % 2) + i of those 8 rows: the A operand of the 32x32x16 MFMA
+// (row = lane % 32, k-slot = 8 (lane / 32) + j) with the same keys per slot as
+// the bf16 reader, i.e. as the P^T operand.  The row's swizzle is
+// (k0 + 16 (c % 2)) for the in-block key k0, so the reader keeps one
+// precomputed address per parity of c and XORs in the dim block.
+struct VReader8 {
+    int w[2];
+    __device__ __forceinline__ explicit VReader8(int lane) {
+        const int G = lane >> 4, i = lane & 15, j = i >> 1, hh = i & 1;
+        const int k0 = 8 * (j >> 2) + 4 * (G >> 1) + (j & 3);
+        const int vbase = k0 * kHeadDim + 8 * hh;
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            w[par] = vbase | ((((G & 1) ^ swz8(k0 + 16 * par))) << 4);
+    }
+    // raw E4M3 bytes of the operand (widened to bf16 just before the MFMA)
+    __device__ __forceinline__ v2i32 read(const ATTN_LDS char* sV, int step) const {
+        const int c = step >> 4, db = step & 15;
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (ATTN_LDS v2i32*)(sV + 16 * c * kHeadDim + (w[c & 1] ^ (2 * db << 4))));
+    }
+};
+
 // Q.K^T of one 32-key block kb: 32 MFMAs (VGPR accumulator) over the 32
 // k-steps of head_dim.  When OVERLAP, one softmax element of the previous
 // block's scores `sp` is computed after every other MFMA; the half-tile
 // refill `dma` issues one row load after every fourth MFMA.
-template <bool OVERLAP>
+template <bool OVERLAP, bool FP8>
 __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[32],
                                          const ATTN_LDS char* sK, const int (&koff)[8],
                                          const f32x16& sp, const SoftmaxCtx& c, float& mx,
                                          float& psum, bf16x8& pf0, bf16x8& pf1,
-                                         const HalfDma& dma, int lane_off) {
-    // step ks reads chunk 2 ks + h of key row 32 kb + n; with ks = 8 u + v the
-    // byte offset is koff[v] + 256 u + 32 KiB kb.
-    auto kread = [&](int ks) -> bf16x8 {
-        return *(const ATTN_LDS bf16x8*)(sK + koff[ks & 7] + 256 * (ks >> 3) +
-                                          kb * 32 * kRowBytes);
+                                         const HalfDma& dma, int lane_off, int lane, int wave) {
+    // bf16: step ks reads chunk 2 ks + h of key row 32 kb + n; with ks = 8 u + v
+    // the byte offset is koff[v] + 256 u + 32 KiB kb.  FP8: bytes 16 ks + 8 h of
+    // row 32 kb + n, chunk ks at ks ^ n: koff[0] ^ (16 ks) + 16 KiB kb.
+    // FP8 operands are prefetched as raw bytes and widened at their MFMA
+    using Raw = typename std::conditional<FP8, v2i32, bf16x8>::type;
+    auto kread = [&](int ks) -> Raw {
+        if constexpr (FP8)
+            return *(const ATTN_LDS v2i32*)(sK + (koff[0] ^ (ks << 4)) + kb * 32 * kHeadDim);
+        else
+            return *(const ATTN_LDS bf16x8*)(sK + koff[ks & 7] + 256 * (ks >> 3) +
+                                              kb * 32 * kRowBytes);
     };
-    bf16x8 kbuf[kPrefetch];
+    constexpr int kDmaEvery = 32 / Kv<FP8>::kDmaPerHalf;
+    Raw kbuf[kPrefetchOf<FP8>];
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) kbuf[j] = kread(j);
+    for (int j = 0; j < kPrefetchOf<FP8>; ++j) kbuf[j] = kread(j);
     static_for<32>([&](auto KS) {
         constexpr int ks = decltype(KS)::value;
-        const bf16x8 cur = kbuf[ks % kPrefetch];
-        if (ks + kPrefetch < 32) kbuf[ks % kPrefetch] = kread(ks + kPrefetch);
-        if constexpr (ks == 0)
-            mfma32x32x16_vgpr_first(s, cur, qf[0]);
-        else
-            mfma32x32x16_vgpr(s, cur, qf[ks]);
-        if constexpr (ks % 4 == 0) {
-            if (dma.on) half_dma_row<ks / 4>(dma, lane_off);
+        const bf16x8 cur = operand(kbuf[ks % kPrefetchOf<FP8>]);
+        if (ks + kPrefetchOf<FP8> < 32) kbuf[ks % kPrefetchOf<FP8>] = kread(ks + kPrefetchOf<FP8>);
+        if constexpr (FP8) {   // cur was just written by the widening VALU ops
+            if constexpr (ks == 0)
+                mfma32x32x16_vgpr_first_va(s, cur, qf[0]);
+            else
+                mfma32x32x16_vgpr_va(s, cur, qf[ks]);
+        } else {
+            if constexpr (ks == 0)
+                mfma32x32x16_vgpr_first(s, cur, qf[0]);
+            else
+                mfma32x32x16_vgpr(s, cur, qf[ks]);
+        }
+        if constexpr (ks % kDmaEvery == 0) {
+            if (dma.on) half_dma_row<FP8, ks / kDmaEvery>(dma, lane_off, lane, wave);
         }
         if constexpr (OVERLAP && (ks & 1)) {
             constexpr int i = ks >> 1;
@@ -216,28 +320,30 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[3
 // only ever written by MFMAs.  When OVERLAP, one softmax element of the next
 // block's scores `sn` is computed after every other MFMA; the half-tile
 // refill `dma` issues one row load after every fourth MFMA.
-template <bool FIRST, bool OVERLAP>
+template <bool FIRST, bool OVERLAP, bool FP8, typename VR>
 __device__ __forceinline__ void pv_block(f32x16 (&o)[16], int kb, const bf16x8& p0,
                                          const bf16x8& p1, const ATTN_LDS char* sV,
-                                         const VReader& vr, const f32x16& sn,
+                                         const VR& vr, const f32x16& sn,
                                          const SoftmaxCtx& c, float& mx, float& psum,
                                          bf16x8& pn0, bf16x8& pn1, const HalfDma& dma,
-                                         int lane_off) {
+                                         int lane_off, int lane, int wave) {
     const int base = 32 * kb;   // steps 32 kb .. 32 kb + 31 of the tile
-    bf16x8 vbuf[kPrefetch];
+    constexpr int kDmaEvery = 32 / Kv<FP8>::kDmaPerHalf;
+    using Raw = typename std::conditional<FP8, v2i32, bf16x8>::type;
+    Raw vbuf[kPrefetchOf<FP8>];
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) vbuf[j] = vr.read(sV, base + j);
+    for (int j = 0; j < kPrefetchOf<FP8>; ++j) vbuf[j] = vr.read(sV, base + j);
     static_for<32>([&](auto ST) {
         constexpr int st = decltype(ST)::value;
-        const bf16x8 cur = vbuf[st % kPrefetch];
-        if (st + kPrefetch < 32) vbuf[st % kPrefetch] = vr.read(sV, base + st + kPrefetch);
+        const bf16x8 cur = operand(vbuf[st % kPrefetchOf<FP8>]);
+        if (st + kPrefetchOf<FP8> < 32) vbuf[st % kPrefetchOf<FP8>] = vr.read(sV, base + st + kPrefetchOf<FP8>);
         constexpr int db = st & 15;
         if constexpr (FIRST && st < 16)
             o[db] = mfma32x32x16(cur, p0, f32x16{});
         else
             o[db] = mfma32x32x16(cur, st < 16 ? p0 : p1, o[db]);
-        if constexpr (st % 4 == 0) {
-            if (dma.on) half_dma_row<st / 4>(dma, lane_off);
+        if constexpr (st % kDmaEvery == 0) {
+            if (dma.on) half_dma_row<FP8, st / kDmaEvery>(dma, lane_off, lane, wave);
         }
         if constexpr (OVERLAP && (st & 1)) {
             constexpr int i = st >> 1;
@@ -247,14 +353,16 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[16], int kb, const bf16x8& 
     });
 }
 
-template <bool OUT_FP32>
+template <bool OUT_FP32, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_hd512_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes];
+    constexpr int kTileB = Kv<FP8>::kTileB;
+    constexpr int kD = Kv<FP8>::kDmaPerHalf;   // loads per wave per half refill
+    __shared__ __attribute__((aligned(1024))) char smem[2 * kTileB];
     __shared__ int sFlag[kWaves];
     __shared__ int sPage[kPagesInLds];
     ATTN_LDS char* sK = (ATTN_LDS char*)smem;
-    ATTN_LDS char* sV = sK + kTileBytes;
+    ATTN_LDS char* sV = sK + kTileB;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -307,9 +415,17 @@ void prefill_hd512_kernel(PrefillArgs a) {
         }
     }
     int koff[8];
+    if constexpr (FP8) {
+        // row n, chunk 0 at n ^ 0, byte 8 h; step ks XORs in 16 ks
+        koff[0] = n * kHeadDim + (swz8(n) << 4) + 8 * h;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) koff[v] = n * kRowBytes + (((2 * v + h) ^ swz(n)) << 4);
-    const VReader vr(lane);
+        for (int v = 1; v < 8; ++v) koff[v] = koff[0];
+    } else {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) koff[v] = n * kRowBytes + (((2 * v + h) ^ swz(n)) << 4);
+    }
+    using VRd = typename std::conditional<FP8, VReader8, VReader>::type;
+    const VRd vr(lane);
 
     f32x16 o[16];  // written first by tile 0's P.V
     // Online softmax with a fixed per-row reference maximum: p = 2^(x - m_ref)
@@ -340,16 +456,16 @@ void prefill_hd512_kernel(PrefillArgs a) {
 
     // Vector-memory accounting: every wave issues its half-tile refills in the
     // order V1(j) [during QK0(j)], K0(j+1) [QK1(j)], K1(j+1) [PV0(j)],
-    // V0(j+1) [PV1(j)], 8 loads each; before each phase the half it reads was
-    // issued two refills (16 loads) before the newest, except where the tile
+    // V0(j+1) [PV1(j)], kD loads each; before each phase the half it reads was
+    // issued two refills (2 kD loads) before the newest, except where the tile
     // has no successor and those later refills do not exist.
     for (;;) {   // one pass over the key range; a restart begins a new pass
         if (ntiles > 0) {
             const int page0 = page_of(0);
             const int v0 = min(L, kPage);
-            half_dma_all(half_dma(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 0, wave, true), lane_off);
-            half_dma_all(half_dma(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 1, wave, true), lane_off);
-            half_dma_all(half_dma(a.v_pages, page0, a.num_pages, a.hkv, kvh, v0, sV, 0, wave, true), lane_off);
+            half_dma_all<FP8>(half_dma<FP8>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 0, wave, true), lane_off, lane, wave);
+            half_dma_all<FP8>(half_dma<FP8>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 1, wave, true), lane_off, lane, wave);
+            half_dma_all<FP8>(half_dma<FP8>(a.v_pages, page0, a.num_pages, a.hkv, kvh, v0, sV, 0, wave, true), lane_off, lane, wave);
         }
         bool restart = false;
         for (int kt = 0; kt < ntiles; ++kt) {
@@ -367,15 +483,15 @@ void prefill_hd512_kernel(PrefillArgs a) {
             f32x16 s0, s1;
 
             // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill
-            wait_vmcnt<16>();
+            wait_vmcnt<2 * kD>();
             lds_barrier();
             if (kt > 0 && restarts < kMaxRestarts && flags_set()) {
                 restart = true;   // a row of tile kt-1 overshot its reference
                 break;
             }
-            qk_block<false>(s0, 0, qf, sK, koff, s0, c0, mx, psum, pf[0], pf[1],
-                            half_dma(a.v_pages, page, a.num_pages, a.hkv, kvh, valid, sV, 1, wave, true),
-                            lane_off);
+            qk_block<false, FP8>(s0, 0, qf, sK, koff, s0, c0, mx, psum, pf[0], pf[1],
+                                 half_dma<FP8>(a.v_pages, page, a.num_pages, a.hkv, kvh, valid, sV, 1, wave, true),
+                                 lane_off, lane, wave);
             mfma_vgpr_drain(s0);
             if (mask) mask_block(s0, key0 + 4 * h, n_row);
             if (kt == 0) {
@@ -390,30 +506,30 @@ void prefill_hd512_kernel(PrefillArgs a) {
             }
 
             // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill
-            wait_vmcnt<16>();
+            wait_vmcnt<2 * kD>();
             lds_barrier();
-            qk_block<true>(s1, 1, qf, sK, koff, s0, c0, mx, psum, pf[0], pf[1],
-                           half_dma(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 0, wave, more),
-                           lane_off);
+            qk_block<true, FP8>(s1, 1, qf, sK, koff, s0, c0, mx, psum, pf[0], pf[1],
+                                half_dma<FP8>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 0, wave, more),
+                                lane_off, lane, wave);
             mfma_vgpr_drain(s1);
             if (mask) mask_block(s1, key0 + 32 + 4 * h, n_row);
 
             // ---- PV0 with block 1's softmax; K rows 32..63 of tile kt+1 refill
-            if (more) wait_vmcnt<16>(); else wait_vmcnt<8>();
+            if (more) wait_vmcnt<2 * kD>(); else wait_vmcnt<kD>();
             lds_barrier();
             const SoftmaxCtx& c1 = c0;
-            const HalfDma dk1 = half_dma(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 1, wave, more);
+            const HalfDma dk1 = half_dma<FP8>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 1, wave, more);
             if (kt == 0)
-                pv_block<true, true>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off);
+                pv_block<true, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
             else
-                pv_block<false, true>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off);
+                pv_block<false, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
 
             // ---- PV1; V rows 0..31 of tile kt+1 refill
-            if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
+            if (more) wait_vmcnt<2 * kD>(); else wait_vmcnt<0>();
             lds_barrier();
-            pv_block<false, false>(o, 1, pf[2], pf[3], sV, vr, s1, c1, mx, psum, pf[2], pf[3],
-                                   half_dma(a.v_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sV, 0, wave, more),
-                                   lane_off);
+            pv_block<false, false, FP8>(o, 1, pf[2], pf[3], sV, vr, s1, c1, mx, psum, pf[2], pf[3],
+                                        half_dma<FP8>(a.v_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sV, 0, wave, more),
+                                        lane_off, lane, wave);
             l_run += psum;
             mx *= a.scale_log2;
             m_seen = fmaxf(m_seen, mx);
@@ -440,6 +556,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // o = O / l with an IEEE division (not O * (1/l)), as the definition reads:
     // with V = 1 it returns exactly 1.
     float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float vs = a.v_scale;   // 1 for a bf16 pool
     if (ntiles == 0) {  // no visible key (empty cache): the output row is 0
         l_tot = 1.f;
 #pragma unroll
@@ -454,6 +571,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
                 const int d0 = 32 * db + 8 * q4 + 4 * h;
                 f32x4 v = {o[db][4 * q4] / l_tot, o[db][4 * q4 + 1] / l_tot,
                            o[db][4 * q4 + 2] / l_tot, o[db][4 * q4 + 3] / l_tot};
+                if constexpr (FP8) v *= vs;
                 if constexpr (OUT_FP32) {
                     *(f32x4*)((float*)a.out + obase + d0) = v;
                 } else {
@@ -469,20 +587,23 @@ void prefill_hd512_kernel(PrefillArgs a) {
 
 }  // namespace attn
 
-extern "C" int attn_prefill_hd512(const void* q, const void* k_pages, const void* v_pages,
-                                  const int32_t* page_table, const int32_t* cu_seqlens_q,
-                                  const int32_t* q_start_pos, const int32_t* kv_lens, int batch,
-                                  int total_q, int max_q_len, int num_q_heads,
-                                  int num_kv_heads, int head_dim, int page_size,
-                                  int num_pages, int max_pages_per_seq, float softmax_scale,
-                                  void* out, int out_dtype, hipStream_t stream) {
-    using namespace attn;
+namespace attn {
+namespace {
+
+int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool fp8,
+                   float k_scale, float v_scale, const int32_t* page_table,
+                   const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
+                   const int32_t* kv_lens, int batch, int total_q, int max_q_len,
+                   int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                   int num_pages, int max_pages_per_seq, float softmax_scale, void* out,
+                   int out_dtype, hipStream_t stream) {
     if (!q || !k_pages || !v_pages || !page_table || !cu_seqlens_q || !q_start_pos ||
         !kv_lens || !out)
         return ATTN_ERR_NULL;
     if (batch < 1 || total_q < 0 || max_q_len < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
         num_pages < 1 || max_pages_per_seq < 1 || !(softmax_scale == softmax_scale))
         return ATTN_ERR_SHAPE;
+    if (fp8 && (!(k_scale > 0.f) || !(v_scale > 0.f))) return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads) return ATTN_ERR_SHAPE;
     if (head_dim != kHeadDim || page_size != kPage) return ATTN_ERR_UNSUPPORTED;
     const int g = num_q_heads / num_kv_heads;
@@ -510,14 +631,51 @@ extern "C" int attn_prefill_hd512(const void* q, const void* k_pages, const void
     a.num_pages = num_pages;
     a.tok_per_wg = kRowsPerWg / g;
     a.wgs_per_seq = (max_q_len + a.tok_per_wg - 1) / a.tok_per_wg;
-    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f * (fp8 ? k_scale : 1.f);
+    a.v_scale = fp8 ? v_scale : 1.f;
     const long long grid = (long long)a.wgs_per_seq * batch * num_kv_heads;
     if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-    if (out_dtype == ATTN_FP32)
-        hipLaunchKernelGGL(prefill_hd512_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL(prefill_hd512_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0,
-                           stream, a);
+    const dim3 gd((unsigned)grid), bd(kThreads);
+    if (fp8) {
+        if (out_dtype == ATTN_FP32)
+            hipLaunchKernelGGL((prefill_hd512_kernel<true, true>), gd, bd, 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_hd512_kernel<false, true>), gd, bd, 0, stream, a);
+    } else {
+        if (out_dtype == ATTN_FP32)
+            hipLaunchKernelGGL((prefill_hd512_kernel<true, false>), gd, bd, 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_hd512_kernel<false, false>), gd, bd, 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" int attn_prefill_hd512(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                  const int32_t* q_start_pos, const int32_t* kv_lens, int batch,
+                                  int total_q, int max_q_len, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int page_size,
+                                  int num_pages, int max_pages_per_seq, float softmax_scale,
+                                  void* out, int out_dtype, hipStream_t stream) {
+    return attn::prefill_launch(q, k_pages, v_pages, false, 1.f, 1.f, page_table, cu_seqlens_q,
+                                q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
+                                num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
+                                softmax_scale, out, out_dtype, stream);
+}
+
+extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const void* v_pages,
+                                       float k_scale, float v_scale, const int32_t* page_table,
+                                       const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
+                                       const int32_t* kv_lens, int batch, int total_q,
+                                       int max_q_len, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int page_size, int num_pages,
+                                       int max_pages_per_seq, float softmax_scale, void* out,
+                                       int out_dtype, hipStream_t stream) {
+    return attn::prefill_launch(q, k_pages, v_pages, true, k_scale, v_scale, page_table,
+                                cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
+                                num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                                max_pages_per_seq, softmax_scale, out, out_dtype, stream);
 }

@@ -21,24 +21,30 @@ def tiny_prefill_mqa(device="cpu", seed=1) -> PagedCase:
                       seed=seed, out_dtype="fp32", device=device)
 
 
-def chunk_prefill_2k(device="cpu", seed=2) -> PagedCase:
+def _fp8_suffix(kv_dtype: str) -> str:
+    return "" if kv_dtype == "bf16" else "_fp8"
+
+
+def chunk_prefill_2k(device="cpu", seed=2, kv_dtype="bf16") -> PagedCase:
     """2048 rows causal over 2048 keys, 32 q heads over 4 KV heads, bf16 out."""
-    return build_case("chunk_prefill_2048", seqs=[(2048, 0, 2048)], hq=32, hkv=4,
-                      seed=seed, out_dtype="bf16", device=device)
+    return build_case("chunk_prefill_2048" + _fp8_suffix(kv_dtype), seqs=[(2048, 0, 2048)],
+                      hq=32, hkv=4, seed=seed, out_dtype="bf16", device=device,
+                      kv_dtype=kv_dtype)
 
 
-def chunk_prefill_8k_at_8k(device="cpu", seed=3) -> PagedCase:
+def chunk_prefill_8k_at_8k(device="cpu", seed=3, kv_dtype="bf16") -> PagedCase:
     """One 8192-row chunk at positions 8192..16383 over 16384 keys, 32/4 heads, bf16 out.
 
     Hostile padding: 64 NaN q rows past the chunk, three spare NaN pages, a
     NaN page behind the table's padding column.
     """
-    return build_case("chunk_prefill_8192_at_8192", seqs=[(8192, 8192, 16384)], hq=32, hkv=4,
-                      seed=seed, out_dtype="bf16", device=device, q_pad_rows=64,
-                      extra_pages=3, table_pad=2)
+    return build_case("chunk_prefill_8192_at_8192" + _fp8_suffix(kv_dtype),
+                      seqs=[(8192, 8192, 16384)], hq=32, hkv=4, seed=seed, out_dtype="bf16",
+                      device=device, q_pad_rows=64, extra_pages=3, table_pad=2,
+                      kv_dtype=kv_dtype)
 
 
-def long_mqa_32k(device="cpu", seed=4, q_zero=False, v_one=False) -> PagedCase:
+def long_mqa_32k(device="cpu", seed=4, q_zero=False, v_one=False, kv_dtype="bf16") -> PagedCase:
     """A 32768-token prompt as eight 4096-row causal chunks against the growing cache.
 
     16 q heads over 1 KV head; every (row, head) of Q, K and V carries its own
@@ -47,10 +53,10 @@ def long_mqa_32k(device="cpu", seed=4, q_zero=False, v_one=False) -> PagedCase:
     unread.  The q=0, V=1 variant must give exactly 1 everywhere.
     """
     chunks = [[(4096, 4096 * c, 4096 * (c + 1))] for c in range(8)]
-    name = "long_mqa_32k_8x4096" + ("_q0_v1" if (q_zero or v_one) else "")
+    name = "long_mqa_32k_8x4096" + ("_q0_v1" if (q_zero or v_one) else "") + _fp8_suffix(kv_dtype)
     return build_case(name, seqs=None, chunks=chunks, hq=16, hkv=1, seed=seed,
                       out_dtype="fp32", device=device, row_scale=(0.5, 2.0),
-                      q_zero=q_zero, v_one=v_one)
+                      q_zero=q_zero, v_one=v_one, kv_dtype=kv_dtype)
 
 
 def decode_b64(device="cpu", seed=5, kv_dtype="bf16", batch=64, lo=4096, hi=28672) -> PagedCase:

@@ -193,6 +193,20 @@ def main():
         extra["long_mqa_32k_8x4096"] = {"ms_per_prompt": ms4, "tflops": f4 / (ms4 * 1e-3) / 1e12}
         del c4, o4
         torch.cuda.empty_cache()
+        # the headline chunk over an FP8-E4M3 cache (same values, per-tensor scales)
+        c8 = W.chunk_prefill_8k_at_8k(device="cuda", kv_dtype="fp8_e4m3")
+        l8 = c8.launches[0]
+
+        def fp8_step():
+            A.prefill(l8.q, c8.k_pool, c8.v_pool, c8.page_table, l8.cu_seqlens_q, l8.q_start,
+                      l8.kv_len, out, total_q=l8.total_q, max_q_len=l8.max_q_len,
+                      softmax_scale=c8.softmax_scale, kv_dtype="fp8_e4m3", k_scale=c8.k_scale,
+                      v_scale=c8.v_scale, stream=stream)
+        ms8 = timed(fp8_step, args.steps, args.warmup)
+        extra["chunk_prefill_8192_at_8192_fp8"] = {"ms_per_launch": ms8,
+                                                   "tflops": flops / (ms8 * 1e-3) / 1e12}
+        del c8
+        torch.cuda.empty_cache()
         log(f"other prefill workloads: {json.dumps(extra)}")
 
     # ---- split-K decode ------------------------------------------------------

@@ -7,7 +7,8 @@
  * FlashAttention Prefill Kernel for Gemma 4, intro and "The starting point"):
  *   - attn_prefill_hd512: chunked causal prefill, one call per chunk; a chunk
  *     attends to every key before it in the cache (pegainfer issue 1051,
- *     "Description");
+ *     "Description"); attn_prefill_hd512_e4m3 is the same over an FP8-E4M3
+ *     cache;
  *   - attn_decode_splitk: Flash-Decoding for one query token per sequence:
  *     the key range is split across workgroups, each writes an unnormalised
  *     (O, m, l) partial, and a merge kernel combines them (Flash-Decoding for
@@ -98,6 +99,32 @@ int attn_prefill_hd512(const void* q, const void* k_pages, const void* v_pages,
                        int total_q, int max_q_len, int num_q_heads, int num_kv_heads,
                        int head_dim, int page_size, int num_pages, int max_pages_per_seq,
                        float softmax_scale, void* out, int out_dtype, hipStream_t stream);
+
+/*
+ * Chunked causal prefill over an FP8-E4M3 KV cache (OCP E4M3, the "fn"
+ * variant: max 448, no infinities).  Same arguments and semantics as
+ * attn_prefill_hd512, except:
+ *
+ *   k_pages,
+ *   v_pages      E4M3 byte pools [num_pages][num_kv_heads][64][512] whose real
+ *                values are byte * k_scale (keys) and byte * v_scale (values).
+ *   k_scale,
+ *   v_scale      per-tensor fp32 dequantisation scales, both > 0
+ *                (ATTN_ERR_SHAPE otherwise).
+ *
+ * The bytes are widened exactly to bf16 inside the kernel (every E4M3 value
+ * is a bf16 value); products and the softmax run as in the bf16 path, k_scale
+ * folded into the softmax scale and v_scale applied to the output (vLLM
+ * flash-attention PR 199, "Summary": FP8 KV with 16-bit MMA; P accumulated in
+ * fp32 per key block as in commit 3 of the first review).
+ */
+int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const void* v_pages,
+                            float k_scale, float v_scale, const int32_t* page_table,
+                            const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
+                            const int32_t* kv_lens, int batch, int total_q, int max_q_len,
+                            int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                            int num_pages, int max_pages_per_seq, float softmax_scale,
+                            void* out, int out_dtype, hipStream_t stream);
 
 /*
  * Bytes of device workspace attn_decode_splitk needs for these sizes: fp32

@@ -1,0 +1,117 @@
+"""GPU parity of attn_prefill_hd512_e4m3 (FP8-E4M3 KV cache) against the CPU oracle.
+
+The oracle reads the same E4M3 bytes, widened exactly and multiplied by the
+per-tensor scales in fp32 (vLLM flash-attention PR 199, "Summary"), so the
+parity gate is the bf16 path's: only the bf16 rounding of P and the
+summation order differ.  Small shapes are checked on every output, the
+measured shapes on sampled rows, with the same NaN-poisoned padding,
+spare pages and table padding as the bf16 tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_workloads as W
+import oracle
+from _gpu_helpers import check_parity, library, run_prefill, sample_rows, sentinel_intact
+
+pytestmark = pytest.mark.gpu
+
+FP8 = "fp8_e4m3"
+
+
+@pytest.fixture(scope="module")
+def A():
+    return library()
+
+
+def _full_check(A, case, out_dtype=None, pad_rows=5, li=0):
+    out = run_prefill(A, case, li=li, out_dtype=out_dtype, pad_rows=pad_rows)
+    lc = case.launches[li]
+    ref = oracle.attend_all(case.to("cpu"), launch_idx=li)
+    assert sentinel_intact(out[lc.total_q:]), "rows past total_q were written"
+    return check_parity(out[:lc.total_q], ref, f"{case.name}[{li}] out={out.dtype}")
+
+
+SMALL = [
+    ([(1, 0, 1)], 8, 1),
+    ([(37, 0, 37)], 8, 1),
+    ([(100, 28, 128)], 4, 4),
+    ([(64, 64, 200)], 16, 8),
+    ([(19, 5, 24), (70, 130, 200), (1, 63, 64)], 12, 4),
+    ([(130, 0, 130), (7, 300, 307)], 16, 1),
+    ([(129, 2000, 2129)], 32, 4),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: f"{s[0]}-{s[1]}x{s[2]}")
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_small_shapes_fp8(A, shape, out_dtype):
+    seqs, hq, hkv = shape
+    case = W.build_case("small_fp8", seqs=seqs, hq=hq, hkv=hkv, seed=19, out_dtype=out_dtype,
+                        device="cuda", q_pad_rows=3, extra_pages=2, table_pad=2, kv_dtype=FP8)
+    _full_check(A, case)
+
+
+def test_chunk_prefill_2048_fp8(A):
+    _full_check(A, W.chunk_prefill_2k(device="cuda", kv_dtype=FP8))
+
+
+def test_chunk_prefill_8192_at_8192_fp8_sampled(A):
+    case = W.chunk_prefill_8k_at_8k(device="cuda", kv_dtype=FP8)
+    lc = case.launches[0]
+    out = run_prefill(A, case, pad_rows=64)
+    assert sentinel_intact(out[lc.total_q:])
+    g = np.random.default_rng(5)
+    tokens = list(range(0, 16)) + list(range(lc.total_q - 16, lc.total_q)) + \
+        g.integers(0, lc.total_q, 32).tolist()
+    rows, toks = sample_rows(lc, case.num_q_heads, tokens)
+    ref = oracle.attend_rows(case.to("cpu"), rows).reshape(len(toks), case.num_q_heads, -1)
+    check_parity(out[torch.as_tensor(toks, device="cuda")], ref, "chunk_8192_at_8192_fp8 sampled")
+
+
+def test_long_mqa_32k_last_chunk_fp8_sampled(A):
+    case = W.long_mqa_32k(device="cuda", kv_dtype=FP8)
+    li = len(case.launches) - 1
+    lc = case.launches[li]
+    out = run_prefill(A, case, li=li)
+    g = np.random.default_rng(6)
+    tokens = [0, 1, 2, lc.total_q - 1] + g.integers(0, lc.total_q, 12).tolist()
+    rows, toks = sample_rows(lc, case.num_q_heads, tokens)
+    ref = oracle.attend_rows(case.to("cpu"), rows, launch_idx=li).reshape(
+        len(toks), case.num_q_heads, -1)
+    check_parity(out[torch.as_tensor(toks, device="cuda")], ref, "long_mqa_32k last chunk fp8")
+
+
+def test_fp8_q0_v1_matches_dequantised_one(A):
+    # q = 0 gives uniform weights; every V element dequantises to the same
+    # value v = byte(1 / v_scale) * v_scale, so the output is v (within the
+    # fp32 rounding of the final scale multiply), whatever the weights.
+    case = W.long_mqa_32k(device="cuda", q_zero=True, v_one=True, kv_dtype=FP8)
+    li = 3
+    out = run_prefill(A, case, li=li).float().cpu().numpy()
+    page0 = int(case.page_table[0, 0].item())
+    code = case.v_pool.view(torch.uint8)[page0, 0, 0, 0].item()
+    v = float(oracle.e4m3_to_f32(np.array([code], dtype=np.uint8))[0] * np.float32(case.v_scale))
+    assert np.isfinite(out).all()
+    np.testing.assert_allclose(out, v, rtol=2e-7, atol=0)
+
+
+def test_fp8_deterministic(A):
+    case = W.build_case("det_fp8", seqs=[(300, 100, 400)], hq=32, hkv=4, seed=23,
+                        out_dtype="fp32", device="cuda", kv_dtype=FP8)
+    a = run_prefill(A, case)
+    b = run_prefill(A, case)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_fp8_bad_scales(A):
+    case = W.build_case("bad_fp8", seqs=[(8, 0, 8)], hq=8, hkv=1, seed=1, out_dtype="fp32",
+                        device="cuda", kv_dtype=FP8)
+    lc = case.launches[0]
+    out = torch.zeros((lc.total_q, 8, 512), device="cuda")
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("nan"), 1.0)):
+        with pytest.raises(A.AttnError, match="status 2"):
+            A.prefill(lc.q, case.k_pool, case.v_pool, case.page_table, lc.cu_seqlens_q,
+                      lc.q_start, lc.kv_len, out, total_q=lc.total_q, max_q_len=lc.max_q_len,
+                      softmax_scale=case.softmax_scale, kv_dtype=FP8, k_scale=ks, v_scale=vs)
