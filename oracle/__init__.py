@@ -6,9 +6,12 @@ code: the C source here (oracle_attn.c) is the plain fp32 definition, and
 brute.py is an independent float64 brute force for tiny inputs.
 
 Parity status: every function here is pinned by the CPU test suite
-(tests/test_oracle_pins.py) against brute force, closed forms, a library
-routine special case (torch's CPU scaled_dot_product_attention with an
-explicit mask) and torch's float8_e4m3fn decoding.
+(tests/test_oracle_pins.py, tests/test_oracle_sinks_lse.py) against brute
+force, closed forms, a library routine special case (torch's CPU
+scaled_dot_product_attention with an explicit mask) and torch's
+float8_e4m3fn decoding; the log-sum-exp and sink outputs against the float64
+brute force, the equal-scores and single-key closed forms and the split-K
+merge identity.
 """
 from __future__ import annotations
 
@@ -48,6 +51,10 @@ def lib():
         common = [P, I64, P, P, I, F, F, P, I, I, P, P, P, I, I, I, I, I, F]
         L.oracle_attn_rows.argtypes = common + [P, I64, P, I]
         L.oracle_attn_rows.restype = I
+        L.oracle_attn_rows_ex.argtypes = common + [P, P, I64, P, P, I]
+        L.oracle_attn_rows_ex.restype = I
+        L.oracle_merge_ex.argtypes = [P, P, P, I, I, F, P, P]
+        L.oracle_merge_ex.restype = None
         L.oracle_attn_partial.argtypes = common + [I64, I, I, I, P, P, P]
         L.oracle_attn_partial.restype = I
         L.oracle_merge.argtypes = [P, P, P, I, I, P]
@@ -96,6 +103,39 @@ def attend_rows(case, rows: Sequence[int], launch_idx: int = 0,
     return out
 
 
+def attend_rows_lse(case, rows: Sequence[int], launch_idx: int = 0,
+                    sinks: Optional[Sequence[float]] = None,
+                    threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Outputs [n, D] and log-sum-exps [n] (natural log) of the given entries
+    (q_row * Hq + head), with optional per-query-head sink logits."""
+    keep = []
+    args = _common_args(case, launch_idx, keep)
+    D = args[16]
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.zeros((len(r), D), dtype=np.float32)
+    lse = np.zeros(len(r), dtype=np.float32)
+    snk = None
+    if sinks is not None:
+        snk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32))
+        assert snk.shape == (case.num_q_heads,)
+    nthreads = threads if threads is not None else (os.cpu_count() or 1)
+    rc = lib().oracle_attn_rows_ex(*args, snk.ctypes.data if snk is not None else None,
+                                   r.ctypes.data, len(r), out.ctypes.data, lse.ctypes.data,
+                                   int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_rows_ex failed with code {rc}")
+    return out, lse
+
+
+def attend_all_lse(case, launch_idx: int = 0, sinks=None,
+                   threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Every output [total_q, Hq, D] and log-sum-exp [total_q, Hq] of one launch."""
+    lc = case.launches[launch_idx]
+    n = lc.total_q * case.num_q_heads
+    out, lse = attend_rows_lse(case, range(n), launch_idx, sinks, threads)
+    return out.reshape(lc.total_q, case.num_q_heads, -1), lse.reshape(lc.total_q, -1)
+
+
 def attend_all(case, launch_idx: int = 0, threads: Optional[int] = None) -> np.ndarray:
     """Every output of one launch as float32 [total_q, Hq, D]."""
     lc = case.launches[launch_idx]
@@ -129,6 +169,20 @@ def merge(O: np.ndarray, m: np.ndarray, l: np.ndarray) -> np.ndarray:
     lib().oracle_merge(O.ctypes.data, m.ctypes.data, l.ctypes.data, int(O.shape[0]),
                        int(O.shape[1]), out.ctypes.data)
     return out
+
+
+def merge_lse(O: np.ndarray, m: np.ndarray, l: np.ndarray,
+              sink: Optional[float] = None) -> Tuple[np.ndarray, float]:
+    """merge() with an optional sink logit; also returns the log-sum-exp."""
+    O = np.ascontiguousarray(O, dtype=np.float32)
+    m = np.ascontiguousarray(m, dtype=np.float32)
+    l = np.ascontiguousarray(l, dtype=np.float32)
+    out = np.zeros(O.shape[1], dtype=np.float32)
+    lse = ctypes.c_float()
+    lib().oracle_merge_ex(O.ctypes.data, m.ctypes.data, l.ctypes.data, int(O.shape[0]),
+                          int(O.shape[1]), float("nan") if sink is None else float(sink),
+                          out.ctypes.data, ctypes.addressof(lse))
+    return out, lse.value
 
 
 def e4m3_to_f32(codes: np.ndarray) -> np.ndarray:

@@ -38,10 +38,18 @@ def depage(case, launch_idx: int = 0) -> List[Tuple[np.ndarray, np.ndarray]]:
 
 def attention(case, launch_idx: int = 0) -> np.ndarray:
     """float64 [total_q, Hq, D] outputs of one launch."""
+    return attention_lse(case, launch_idx)[0]
+
+
+def attention_lse(case, launch_idx: int = 0, sinks=None):
+    """float64 outputs [total_q, Hq, D] and log-sum-exps [total_q, Hq] of one
+    launch; `sinks` (one logit per query head, or None) joins each softmax as a
+    term with no value row."""
     lc = case.launches[launch_idx]
     q = lc.q[:lc.total_q].float().double().numpy()
     g = case.num_q_heads // case.num_kv_heads
     out = np.zeros_like(q)
+    lse = np.full(q.shape[:2], -np.inf)
     dense = depage(case, launch_idx)
     row0 = 0
     for b, (ql, st, L) in enumerate(zip(lc.q_lens, lc.q_starts, lc.kv_lens)):
@@ -53,8 +61,15 @@ def attention(case, launch_idx: int = 0) -> np.ndarray:
             kvh = h // g
             s = (q[row0:row0 + ql, h, :] @ K[:, kvh, :].T) * float(np.float32(case.softmax_scale))
             s = np.where(visible, s, -np.inf)
-            mx = s.max(axis=1, keepdims=True)
-            w = np.exp(s - mx)
-            out[row0:row0 + ql, h, :] = (w @ V[:, kvh, :]) / w.sum(axis=1, keepdims=True)
+            if sinks is not None:   # one more softmax column, weight only
+                s = np.concatenate([s, np.full((ql, 1), float(sinks[h]))], axis=1)
+            mx = s.max(axis=1, keepdims=True) if s.shape[1] else np.full((ql, 1), -np.inf)
+            ok = np.isfinite(mx[:, 0])
+            w = np.exp(s - np.where(np.isfinite(mx), mx, 0.0))
+            den = w.sum(axis=1)
+            vals = V[:, kvh, :]
+            num = w[:, :L] @ vals if L else np.zeros((ql, vals.shape[-1]))
+            out[row0:row0 + ql, h, :] = np.where(ok[:, None], num / np.where(ok, den, 1.0)[:, None], 0.0)
+            lse[row0:row0 + ql, h] = np.where(ok, mx[:, 0] + np.log(np.where(ok, den, 1.0)), -np.inf)
         row0 += ql
-    return out
+    return out, lse

@@ -34,6 +34,14 @@
  * combine as  mu = max_i m_i,  o = sum_i e^{m_i-mu} O_i / sum_i e^{m_i-mu} l_i;
  * an empty range is (0, -inf, 0) and contributes nothing.
  *
+ * Attention sinks and the log-sum-exp (vLLM flash-attention PR 199, second
+ * review, finding F4): a head may carry a sink logit s_h, an extra softmax
+ * term with no value row.  Then
+ *     o   = (sum_j e^{S[j]} V[j]) / (e^{s_h} + sum_j e^{S[j]})
+ *     lse = log(e^{s_h} + sum_j e^{S[j]})
+ * (both evaluated around the larger of max S and s_h).  A row with no visible
+ * key gives o = 0 and lse = s_h, or lse = -inf without a sink.
+ *
  * Precision: inputs are widened exactly (bf16 -> fp32; e4m3 -> fp32, then
  * times the per-tensor scale in fp32); dot products, exponentials and sums
  * run in fp32 in plain sequential order.  Built without -ffast-math.
@@ -201,17 +209,38 @@ static void row_partial(const problem_t* p, int64_t row, int h, int k0, int k1, 
                    max_pages, num_pages, cu_seqlens_q, q_start, kv_len, batch, hq, hkv,  \
                    head_dim, page_size, softmax_scale};
 
+/* Normalises one row's (O, m, l) with an optional sink logit (NAN = none):
+ * writes o[d] and, when lse is not NULL, the log-sum-exp. */
+static void finish_row(const float* O, float m, float l, float sink, int d_len, float* o,
+                       float* lse) {
+    float top = m;
+    if (!isnan(sink) && sink > top) top = sink;
+    if (top == -INFINITY) { /* nothing visible and no sink */
+        for (int d = 0; d < d_len; ++d) o[d] = 0.0f;
+        if (lse) *lse = -INFINITY;
+        return;
+    }
+    float w = (m == -INFINITY) ? 0.0f : expf(m - top); /* rescales O and l to `top` */
+    float den = w * l + (isnan(sink) ? 0.0f : expf(sink - top));
+    for (int d = 0; d < d_len; ++d) o[d] = (w * O[d]) / den;
+    if (lse) *lse = top + logf(den);
+}
+
 /*
- * out[r, :] = attention output of entry rows[r] = q_row * Hq + head.
- * A row with no visible key gives 0.  Returns 0, or an error code without
- * writing anything when an argument or a page id is out of range.
+ * out[r, :] = attention output of entry rows[r] = q_row * Hq + head, and, when
+ * lse is not NULL, lse[r] = its log-sum-exp.  sinks (NULL = none) holds one
+ * logit per query head.  A row with no visible key gives 0 (lse = the sink,
+ * or -inf).  Returns 0, or an error code without writing anything when an
+ * argument or a page id is out of range.
  */
-int oracle_attn_rows(const uint16_t* q, int64_t q_rows, const void* k_pool, const void* v_pool,
-                     int kv_format, float k_scale, float v_scale, const int32_t* page_table,
-                     int max_pages, int num_pages, const int32_t* cu_seqlens_q,
-                     const int32_t* q_start, const int32_t* kv_len, int batch, int hq, int hkv,
-                     int head_dim, int page_size, float softmax_scale, const int64_t* rows,
-                     int64_t n_rows, float* out, int num_threads) {
+int oracle_attn_rows_ex(const uint16_t* q, int64_t q_rows, const void* k_pool,
+                        const void* v_pool, int kv_format, float k_scale, float v_scale,
+                        const int32_t* page_table, int max_pages, int num_pages,
+                        const int32_t* cu_seqlens_q, const int32_t* q_start,
+                        const int32_t* kv_len, int batch, int hq, int hkv, int head_dim,
+                        int page_size, float softmax_scale, const float* sinks,
+                        const int64_t* rows, int64_t n_rows, float* out, float* lse,
+                        int num_threads) {
     FILL_PROBLEM
     int rc = check_problem(&p);
     if (rc) return rc;
@@ -239,14 +268,27 @@ int oracle_attn_rows(const uint16_t* q, int64_t q_rows, const void* k_pool, cons
                 int b = seq_of_row(&p, row);
                 float m, l;
                 row_partial(&p, row, h, 0, kv_len[b], S, O, &m, &l);
-                float* dst = out + r * (int64_t)head_dim;
-                for (int d = 0; d < head_dim; ++d) dst[d] = (l > 0.0f) ? O[d] / l : 0.0f;
+                finish_row(O, m, l, sinks ? sinks[h] : NAN, head_dim,
+                           out + r * (int64_t)head_dim, lse ? lse + r : NULL);
             }
         }
         free(S);
         free(O);
     }
     return failed ? ERR_NOMEM : OK;
+}
+
+/* oracle_attn_rows_ex without sinks and without the log-sum-exp. */
+int oracle_attn_rows(const uint16_t* q, int64_t q_rows, const void* k_pool, const void* v_pool,
+                     int kv_format, float k_scale, float v_scale, const int32_t* page_table,
+                     int max_pages, int num_pages, const int32_t* cu_seqlens_q,
+                     const int32_t* q_start, const int32_t* kv_len, int batch, int hq, int hkv,
+                     int head_dim, int page_size, float softmax_scale, const int64_t* rows,
+                     int64_t n_rows, float* out, int num_threads) {
+    return oracle_attn_rows_ex(q, q_rows, k_pool, v_pool, kv_format, k_scale, v_scale,
+                               page_table, max_pages, num_pages, cu_seqlens_q, q_start, kv_len,
+                               batch, hq, hkv, head_dim, page_size, softmax_scale, NULL, rows,
+                               n_rows, out, NULL, num_threads);
 }
 
 /* Unnormalised partial of one row (q_row, head) over keys [k0, k1). */
@@ -269,19 +311,29 @@ int oracle_attn_partial(const uint16_t* q, int64_t q_rows, const void* k_pool,
     return OK;
 }
 
-/* Merge n partials (O_i [d], m_i, l_i) into one normalised output row. */
-void oracle_merge(const float* O, const float* m, const float* l, int n, int head_dim,
-                  float* out) {
+/* Merge n partials (O_i [d], m_i, l_i) into one normalised output row, with
+ * an optional sink logit (NAN = none) and log-sum-exp (lse may be NULL). */
+void oracle_merge_ex(const float* O, const float* m, const float* l, int n, int head_dim,
+                     float sink, float* out, float* lse) {
     float mu = -INFINITY;
     for (int i = 0; i < n; ++i) if (m[i] > mu) mu = m[i];
-    for (int d = 0; d < head_dim; ++d) out[d] = 0.0f;
-    if (mu == -INFINITY) return; /* nothing visible anywhere */
+    float* acc = (float*)calloc((size_t)head_dim, sizeof(float));
     float den = 0.0f;
-    for (int i = 0; i < n; ++i) {
-        if (m[i] == -INFINITY) continue; /* empty split: identity */
-        float w = expf(m[i] - mu);
-        den += w * l[i];
-        for (int d = 0; d < head_dim; ++d) out[d] += w * O[(int64_t)i * head_dim + d];
+    if (mu != -INFINITY) {
+        for (int i = 0; i < n; ++i) {
+            if (m[i] == -INFINITY) continue; /* empty split: identity */
+            float w = expf(m[i] - mu);
+            den += w * l[i];
+            for (int d = 0; d < head_dim; ++d) acc[d] += w * O[(int64_t)i * head_dim + d];
+        }
     }
-    for (int d = 0; d < head_dim; ++d) out[d] /= den;
+    /* the merged partial is (acc, mu, den); normalise it like one row */
+    finish_row(acc, mu, den, sink, head_dim, out, lse);
+    free(acc);
+}
+
+/* oracle_merge_ex without a sink and without the log-sum-exp. */
+void oracle_merge(const float* O, const float* m, const float* l, int n, int head_dim,
+                  float* out) {
+    oracle_merge_ex(O, m, l, n, head_dim, NAN, out, NULL);
 }

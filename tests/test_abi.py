@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_prefill_hd512", "attn_decode_splitk", "attn_decode_splitk_workspace_size",
+    for n in ("attn_prefill_hd512", "attn_prefill_hd512_e4m3", "attn_decode_splitk",
+              "attn_decode_splitk_workspace_size",
               "attn_status_string", "attn_hbm_read_probe", "attn_hbm_probe_sink_words"):
         assert n in names
 
@@ -72,6 +73,29 @@ def test_prefill_validation(L):
     assert prefill(L, scale=float("nan")) == 2
     assert prefill(L, max_q_len=5) == 2          # larger than total_q
     assert prefill(L, total_q=0, max_q_len=0) == 0  # empty call: nothing to launch
+
+
+def prefill_e4m3(L, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=0.01, vs=0.01, pt=FAKE, cu=FAKE, qs=FAKE, kl=FAKE,
+             batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=512, page=64, num_pages=4,
+             max_pages=4, scale=0.04, out=FAKE, out_dtype=1, stream=None)
+    a.update(over)
+    return L.attn_prefill_hd512_e4m3(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["pt"], a["cu"],
+                                     a["qs"], a["kl"], a["batch"], a["total_q"], a["max_q_len"],
+                                     a["hq"], a["hkv"], a["d"], a["page"], a["num_pages"],
+                                     a["max_pages"], a["scale"], a["out"], a["out_dtype"],
+                                     a["stream"])
+
+
+def test_prefill_e4m3_validation(L):
+    assert prefill_e4m3(L, v=None) == 1
+    assert prefill_e4m3(L, ks=0.0) == 2
+    assert prefill_e4m3(L, vs=-1.0) == 2
+    assert prefill_e4m3(L, ks=float("nan")) == 2
+    assert prefill_e4m3(L, batch=0) == 2
+    assert prefill_e4m3(L, d=256) == 3
+    assert prefill_e4m3(L, out_dtype=2) == 3
+    assert prefill_e4m3(L, total_q=0, max_q_len=0) == 0
 
 
 def decode(L, **over):
