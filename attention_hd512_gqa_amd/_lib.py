@@ -41,6 +41,14 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_hd512_e4m3.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I, I, I, I, I,
                                               I, F, P, I, P]
         L.attn_prefill_hd512_e4m3.restype = I
+        L.attn_prefill_hd512_ex.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I, I,
+                                            I, I, F, P, P, I, P, P]
+        L.attn_prefill_hd512_ex.restype = I
+        L.attn_decode_splitk_ex_workspace_size.argtypes = [I, I, I, I, I, I]
+        L.attn_decode_splitk_ex_workspace_size.restype = SZ
+        L.attn_decode_splitk_ex.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, I,
+                                            F, P, P, SZ, P, I, P, P]
+        L.attn_decode_splitk_ex.restype = I
         L.attn_decode_splitk_workspace_size.argtypes = [I, I, I, I, I]
         L.attn_decode_splitk_workspace_size.restype = SZ
         L.attn_decode_splitk.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, F,
@@ -83,12 +91,23 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
+def _opt(t, name, dtype, numel):
+    if t is None:
+        return None
+    if t.numel() != numel:
+        raise AttnError(f"{name} must have {numel} elements, has {t.numel()}")
+    return _dev(t, name, dtype)
+
+
 def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out, *,
             total_q: int, max_q_len: int, softmax_scale: float, kv_dtype: str = "bf16",
-            k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+            k_scale: float = 1.0, v_scale: float = 1.0, sinks=None, lse=None,
+            stream=None) -> None:
     """Chunked causal prefill over a bf16 pool (attn_prefill_hd512) or an
-    FP8-E4M3 pool with per-tensor scales (attn_prefill_hd512_e4m3).  Sizes are
-    host ints: no sync."""
+    FP8-E4M3 pool with per-tensor scales (attn_prefill_hd512_e4m3); with
+    per-head sink logits `sinks` (fp32 [Hq]) or a log-sum-exp output `lse`
+    (fp32 [total_q, Hq]) it calls attn_prefill_hd512_ex.  Sizes are host ints:
+    no sync."""
     num_pages, hkv, page, d = k_pages.shape
     hq = q.shape[1]
     batch = kv_lens.shape[0]
@@ -98,7 +117,17 @@ def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out
             int(hq), int(hkv), int(d), int(page), int(num_pages), int(page_table.shape[1]),
             float(softmax_scale), _dev(out, "out", (torch.bfloat16, torch.float32)),
             _DTYPE_CODES[out.dtype], _stream(stream))
-    if kv_dtype == "bf16":
+    if kv_dtype not in _KV_CODES:
+        raise AttnError(f"unsupported kv_dtype {kv_dtype!r}")
+    kvt = torch.bfloat16 if kv_dtype == "bf16" else torch.uint8
+    if sinks is not None or lse is not None:
+        code = lib().attn_prefill_hd512_ex(
+            _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
+            _dev(v_pages, "v_pages", kvt), _KV_CODES[kv_dtype], float(k_scale), float(v_scale),
+            *meta[:14], _opt(sinks, "sinks", torch.float32, hq), meta[14], meta[15],
+            _opt(lse, "lse", torch.float32, int(total_q) * hq), meta[16])
+        _check(code, "attn_prefill_hd512_ex")
+    elif kv_dtype == "bf16":
         code = lib().attn_prefill_hd512(
             _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.bfloat16),
             _dev(v_pages, "v_pages", torch.bfloat16), *meta)
@@ -108,34 +137,47 @@ def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out
             _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.uint8),
             _dev(v_pages, "v_pages", torch.uint8), float(k_scale), float(v_scale), *meta)
         _check(code, "attn_prefill_hd512_e4m3")
-    else:
-        raise AttnError(f"unsupported kv_dtype {kv_dtype!r}")
 
 
 def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_kv_len: int,
-                          keys_per_split: int = 0) -> int:
-    return int(lib().attn_decode_splitk_workspace_size(int(batch), int(num_q_heads),
-                                                       int(num_kv_heads), int(max_kv_len),
-                                                       int(keys_per_split)))
+                          keys_per_split: int = 0, q_len: int = 1) -> int:
+    return int(lib().attn_decode_splitk_ex_workspace_size(
+        int(batch), int(q_len), int(num_q_heads), int(num_kv_heads), int(max_kv_len),
+        int(keys_per_split)))
 
 
 def decode(q, k_pages, v_pages, page_table, kv_lens, out, workspace, *, max_kv_len: int,
            softmax_scale: float, kv_dtype: str = "bf16", k_scale: float = 1.0,
-           v_scale: float = 1.0, keys_per_split: int = 0, stream=None) -> None:
-    """Split-K decode (attn_decode_splitk): split kernel then merge kernel."""
+           v_scale: float = 1.0, keys_per_split: int = 0, q_len: int = 1, sinks=None,
+           lse=None, stream=None) -> None:
+    """Split-K decode (split kernel then merge kernel).  q holds q_len tokens per
+    sequence, [batch * q_len, Hq, 512], at positions kv_len - q_len ..; with
+    q_len > 1, sinks (fp32 [Hq]) or lse (fp32 [batch * q_len, Hq]) it calls
+    attn_decode_splitk_ex, else attn_decode_splitk."""
     num_pages, hkv, page, d = k_pages.shape
-    batch, hq = q.shape[0], q.shape[1]
+    hq = q.shape[1]
+    batch = kv_lens.shape[0]
+    if q.shape[0] != batch * q_len:
+        raise AttnError(f"q has {q.shape[0]} rows, expected batch * q_len = {batch * q_len}")
     kvt = torch.bfloat16 if kv_dtype == "bf16" else torch.uint8
-    code = lib().attn_decode_splitk(
-        _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt), _dev(v_pages, "v_pages", kvt),
-        _KV_CODES[kv_dtype], float(k_scale), float(v_scale),
-        _dev(page_table, "page_table", torch.int32), _dev(kv_lens, "kv_lens", torch.int32),
-        int(batch), int(hq), int(hkv), int(d), int(page), int(num_pages),
-        int(page_table.shape[1]), int(max_kv_len), int(keys_per_split), float(softmax_scale),
-        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
-        _stream(stream))
-    _check(code, "attn_decode_splitk")
+    head = (_dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
+            _dev(v_pages, "v_pages", kvt), _KV_CODES[kv_dtype], float(k_scale), float(v_scale),
+            _dev(page_table, "page_table", torch.int32), _dev(kv_lens, "kv_lens", torch.int32))
+    ws = (_dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+          _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype])
+    if q_len != 1 or sinks is not None or lse is not None:
+        code = lib().attn_decode_splitk_ex(
+            *head, int(batch), int(q_len), int(hq), int(hkv), int(d), int(page), int(num_pages),
+            int(page_table.shape[1]), int(max_kv_len), int(keys_per_split), float(softmax_scale),
+            _opt(sinks, "sinks", torch.float32, hq), *ws,
+            _opt(lse, "lse", torch.float32, int(batch) * int(q_len) * hq), _stream(stream))
+        _check(code, "attn_decode_splitk_ex")
+    else:
+        code = lib().attn_decode_splitk(
+            *head, int(batch), int(hq), int(hkv), int(d), int(page), int(num_pages),
+            int(page_table.shape[1]), int(max_kv_len), int(keys_per_split), float(softmax_scale),
+            *ws, _stream(stream))
+        _check(code, "attn_decode_splitk")
 
 
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -64,15 +64,20 @@ struct DecodeArgs {
     float* part_o;      // [batch][hkv][max_splits][sub][g][512]
     float* part_ml;     // [batch][hkv][max_splits][sub][g][2]  (m in log2 units, l)
     int batch, hq, hkv, g, max_pages, num_pages;
+    int q_len;          // query tokens per sequence, at positions kv_len - q_len ..
+    int cols;           // q_len * g MFMA columns: column c = token c / g, head c % g
     int max_splits, tiles_per_split, sub;
     float scale_log2;   // softmax_scale * log2(e) * k_scale
     float v_scale;
+    const float* sinks; // per query head sink logit (natural-log units), or null
+    float* lse;         // [batch * q_len][hq] natural-log log-sum-exp, or null
 };
 
 // The key range of one split workgroup and where its tiles live.
 struct SplitPlan {
     int b, kvh, split;
     int k_begin, k_end, ntiles;
+    int L;              // the sequence's cache length
     const int* ptab;    // this sequence's row of the page table
 };
 
@@ -93,6 +98,7 @@ __device__ __forceinline__ bool plan_split(const DecodeArgs& a, SplitPlan& p) {
     if (p.k_begin >= L) return false;  // empty split: the merge never reads it
     p.k_end = min(p.k_begin + a.tiles_per_split * kPage, L);
     p.ntiles = (p.k_end - p.k_begin + kPage - 1) / kPage;
+    p.L = L;
     p.ptab = a.page_table + (size_t)p.b * a.max_pages;
     return true;
 }
@@ -125,6 +131,29 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int voff) {
                                                                           kNonTemporal));
 }
 
+// MFMA column c of a split: token c / g at position L - q_len + c / g and
+// query head kvh g + c % g.  Columns past q_len g are zero padding.
+struct Column {
+    bool ok;            // a real (token, head)
+    size_t q_row;       // row of q / out: (b q_len + token) hq + head
+    int k_lim;          // keys of the split this column may see: [k_begin, k_lim)
+};
+
+__device__ __forceinline__ Column column_of(const DecodeArgs& a, const SplitPlan& p, int c) {
+    Column col;
+    col.ok = c < a.cols;
+    const int t = col.ok ? c / a.g : 0;
+    const int h = col.ok ? c - t * a.g : 0;
+    col.q_row = ((size_t)p.b * a.q_len + t) * a.hq + (size_t)p.kvh * a.g + h;
+    // causal: the token at position L - q_len + t sees keys j <= that position
+    col.k_lim = col.ok ? min(p.k_end, p.L - a.q_len + t + 1) : p.k_end;
+    return col;
+}
+
+// exp2 reference that is finite whenever possible: a column that has seen
+// no key yet keeps m = -inf, and its p = 2^(-inf - 0) = 0, alpha = 1.
+__device__ __forceinline__ float finite_or_zero(float m) { return m == -__builtin_inff() ? 0.f : m; }
+
 // Unnormalised partial of head n: O^T element i of block db is dim
 // 16 db + 4 kq + i (db over NB blocks, starting at dim d0); l sums over the
 // four k-groups.
@@ -133,7 +162,7 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, size_t slot, 
                                               int d0, const f32x4 (&o)[NB], float m, float l) {
     float l_row = l + __shfl_xor(l, 16);
     l_row += __shfl_xor(l_row, 32);
-    if (n < a.g) {
+    if (n < a.cols) {
         float* dst = a.part_o + slot * kHeadDim + d0 + 4 * kq;
 #pragma unroll
         for (int db = 0; db < NB; ++db) *(f32x4*)(dst + 16 * db) = o[db] * a.v_scale;
@@ -166,15 +195,15 @@ void decode_split_bf16_kernel(DecodeArgs a) {
     const int kq = lane >> 4;  // k-group
     const int lane16 = lane * 16;
 
+    const Column col = column_of(a, p, n);
     // Q^T operand, k-step ks covers dims 32 ks .. 32 ks + 31; lane holds 32 ks + 8 kq .. + 7
     bf16x8 qf[16];
     {
-        const bf16x8* qp = (const bf16x8*)(a.q + ((size_t)p.b * a.hq + p.kvh * a.g +
-                                                  (n < a.g ? n : 0)) * kHeadDim) + kq;
+        const bf16x8* qp = (const bf16x8*)(a.q + col.q_row * kHeadDim) + kq;
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
             const bf16x8 v = qp[4 * ks];
-            qf[ks] = n < a.g ? v : bf16x8{};
+            qf[ks] = col.ok ? v : bf16x8{};
         }
     }
     // K operand: row 16 wave + n, chunk 4 ks + kq; with ks = 4 u + v the byte
@@ -242,22 +271,25 @@ void decode_split_bf16_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int key = key0 + 32 * c + 8 * kq + j;
-                const float v = key < p.k_end ? x[c][j] * a.scale_log2 : -__builtin_inff();
+                const float v = key < col.k_lim ? x[c][j] * a.scale_log2 : -__builtin_inff();
                 x[c][j] = v;
                 mt = fmaxf(mt, v);
             }
         }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);   // finite: every tile has a visible key
-        const float alpha = fast_exp2(m_run - m_new);
+        // -inf until the column's first visible key (a later token of a
+        // multi-token decode can see keys an earlier one cannot)
+        const float m_new = fmaxf(m_run, mt);
+        const float m_use = finite_or_zero(m_new);
+        const float alpha = fast_exp2(m_run - m_use);
         bf16x8 pf[2];
         float psum = 0.f;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float pv = fast_exp2(x[c][j] - m_new);
+                const float pv = fast_exp2(x[c][j] - m_use);
                 psum += pv;
                 pf[c][j] = (__bf16)pv;
             }
@@ -288,7 +320,7 @@ void decode_split_bf16_kernel(DecodeArgs a) {
             issue_tile_bf16(tile_base(a.v_pages, a, pg_next, p.kvh, kTileBytes), valid_of(t + 1),
                             sV, wave, lane16);
     }
-    const size_t slot = (((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub * a.g + n;
+    const size_t slot = (((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub * a.cols + n;
     write_partial<8>(a, slot, n, kq, 128 * wave, o, m_run, l_run);
 }
 
@@ -367,13 +399,14 @@ void decode_split_fp8_kernel(DecodeArgs a) {
 
     // Q^T operand of k-step ks: dims 64 (ks / 2) + 16 kq + 8 (ks % 2) .. + 7,
     // the order in which the K loads deliver them
+    const Column col = column_of(a, p, n);
     bf16x8 qf[16];
     {
-        const __bf16* qrow = a.q + ((size_t)p.b * a.hq + p.kvh * a.g + (n < a.g ? n : 0)) * kHeadDim;
+        const __bf16* qrow = a.q + col.q_row * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
             const bf16x8 v = *(const bf16x8*)(qrow + 64 * (ks >> 1) + 16 * kq + 8 * (ks & 1));
-            qf[ks] = n < a.g ? v : bf16x8{};
+            qf[ks] = col.ok ? v : bf16x8{};
         }
     }
     // V^T operand, read transposed: within each 16-lane group kq, lane
@@ -436,14 +469,16 @@ void decode_split_fp8_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = key0 + 16 * gm + 4 * kq + i;
-                const float v = key < p.k_end ? s[gm][i] * a.scale_log2 : -__builtin_inff();
+                const float v = key < col.k_lim ? s[gm][i] * a.scale_log2 : -__builtin_inff();
                 x[4 * gm + i] = v;
                 mt = fmaxf(mt, v);
             }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        // every half page has a live key, so mt is finite; the first one
-        // always moves the reference (alpha = 0 on the zero O)
+        // the first half page with a visible key moves the reference (alpha
+        // = 0 on the zero O); before it mt = m_ref = -inf and nothing changes
+        // (a later token of a multi-token decode can see keys an earlier one
+        // cannot)
         const bool up = mt > m_ref + kRefMargin;
         if (__builtin_amdgcn_ballot_w64(up)) {
             const float m_new = up ? mt : m_ref;
@@ -455,9 +490,10 @@ void decode_split_fp8_kernel(DecodeArgs a) {
         }
         bf16x8 pf;
         float psum = 0.f;
+        const float m_use = finite_or_zero(m_ref);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float pv = fast_exp2(x[j] - m_ref);
+            const float pv = fast_exp2(x[j] - m_use);
             psum += pv;
             pf[j] = (__bf16)pv;
         }
@@ -475,45 +511,60 @@ void decode_split_fp8_kernel(DecodeArgs a) {
     }
     wait_vmcnt<0>();   // the last (zero-length) loads
     const size_t slot =
-        ((((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub + wave) * a.g + n;
+        ((((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub + wave) * a.cols + n;
     write_partial<32>(a, slot, n, kq, 0, o, m_ref, l_run);
 }
 
-// One workgroup per (sequence, query head): combine the sequence's partials,
-// mu = max m_i, o = sum 2^(m_i - mu) O_i / sum 2^(m_i - mu) l_i.  A partial
-// that saw no key (m = -inf, l = 0, O = 0) adds nothing.
+// One workgroup per (sequence, token, query head): combine the partials,
+// mu = max(m_i, sink), o = sum 2^(m_i - mu) O_i / (sum 2^(m_i - mu) l_i +
+// 2^(sink - mu)), in log2 units (m_i already are; the sink logit is scaled by
+// log2(e)).  A partial that saw no key (m = -inf, l = 0, O = 0) adds nothing;
+// with no key at all the output is 0 and the log-sum-exp is the sink logit,
+// or -inf without a sink (vLLM flash-attention PR 199, second review,
+// finding F4).
 template <bool OUT_FP32>
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, void* out) {
-    const int b = blockIdx.x / a.hq;
-    const int h = blockIdx.x - b * a.hq;
+    const int h = blockIdx.x % a.hq;
+    const int bt = blockIdx.x / a.hq;     // b q_len + token
+    const int b = bt / a.q_len;
+    const int t = bt - b * a.q_len;
     const int kvh = h / a.g;
-    const int r = h - kvh * a.g;
+    const int c = t * a.g + (h - kvh * a.g);
     int L = a.kv_lens[b];
     L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
     const int split_keys = a.tiles_per_split * kPage;
     int ns = (L + split_keys - 1) / split_keys;
     ns = (ns > a.max_splits ? a.max_splits : ns) * a.sub;   // every non-empty split wrote a.sub
-    const size_t slot0 = (((size_t)b * a.hkv + kvh) * a.max_splits) * a.sub * a.g + r;
-    float mu = -__builtin_inff();
-    for (int i = 0; i < ns; ++i) mu = fmaxf(mu, a.part_ml[2 * (slot0 + (size_t)i * a.g)]);
+    const size_t slot0 = (((size_t)b * a.hkv + kvh) * a.max_splits) * a.sub * a.cols + c;
+    const float sink2 = a.sinks ? a.sinks[h] * 1.4426950408889634f : -__builtin_inff();
+    float mu = sink2;
+    for (int i = 0; i < ns; ++i) mu = fmaxf(mu, a.part_ml[2 * (slot0 + (size_t)i * a.cols)]);
     f32x4 acc = f32x4{};
     float den = 0.f;
     const int d0 = 4 * threadIdx.x;
-    for (int i = 0; i < ns; ++i) {
-        const size_t slot = slot0 + (size_t)i * a.g;
-        const float w = fast_exp2(a.part_ml[2 * slot] - mu);
-        den += w * a.part_ml[2 * slot + 1];
-        acc += w * *(const f32x4*)(a.part_o + slot * kHeadDim + d0);
+    if (mu != -__builtin_inff()) {
+        for (int i = 0; i < ns; ++i) {
+            const size_t slot = slot0 + (size_t)i * a.cols;
+            const float m = a.part_ml[2 * slot];
+            if (m == -__builtin_inff()) continue;   // empty partial
+            const float w = fast_exp2(m - mu);
+            den += w * a.part_ml[2 * slot + 1];
+            acc += w * *(const f32x4*)(a.part_o + slot * kHeadDim + d0);
+        }
+        den += fast_exp2(sink2 - mu);   // 0 without a sink
     }
-    // IEEE division, as in prefill; no visible key gives 0
+    // IEEE division, as in prefill; no key and no sink gives 0
     const float dd = den > 0.f ? den : 1.f;
-    const size_t obase = ((size_t)b * a.hq + h) * kHeadDim + d0;
+    const size_t obase = ((size_t)bt * a.hq + h) * kHeadDim + d0;
     const f32x4 v = {acc[0] / dd, acc[1] / dd, acc[2] / dd, acc[3] / dd};
     if constexpr (OUT_FP32) {
         *(f32x4*)((float*)out + obase) = v;
     } else {
         *(bf16x4*)((__bf16*)out + obase) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     }
+    if (a.lse && threadIdx.x == 0)
+        a.lse[(size_t)bt * a.hq + h] =
+            den > 0.f ? (mu + __builtin_log2f(den)) * 0.6931471805599453f : -__builtin_inff();
 }
 
 int default_keys_per_split(int batch, int hkv, int max_kv_len) {
@@ -528,30 +579,39 @@ int default_keys_per_split(int batch, int hkv, int max_kv_len) {
 
 }  // namespace attn
 
-extern "C" size_t attn_decode_splitk_workspace_size(int batch, int num_q_heads, int num_kv_heads,
-                                                    int max_kv_len, int keys_per_split) {
+extern "C" size_t attn_decode_splitk_ex_workspace_size(int batch, int q_len, int num_q_heads,
+                                                       int num_kv_heads, int max_kv_len,
+                                                       int keys_per_split) {
     using namespace attn;
-    if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_kv_len < 1 ||
+    if (batch < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_kv_len < 1 ||
         num_q_heads % num_kv_heads || keys_per_split < 0 || keys_per_split % kPage)
         return 0;
     const int kps = keys_per_split ? keys_per_split
                                    : default_keys_per_split(batch, num_kv_heads, max_kv_len);
     const size_t splits = (size_t)(max_kv_len + kps - 1) / kps;
-    const size_t slots = (size_t)batch * num_q_heads * splits * kMaxSub;  // hkv * g = hq
+    // hkv * (q_len * g) columns = q_len * hq
+    const size_t slots = (size_t)batch * q_len * num_q_heads * splits * kMaxSub;
     return slots * (kHeadDim + 2) * sizeof(float);
 }
 
-extern "C" int attn_decode_splitk(const void* q, const void* k_pages, const void* v_pages,
-                                  int kv_dtype, float k_scale, float v_scale,
-                                  const int32_t* page_table, const int32_t* kv_lens, int batch,
-                                  int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                                  int num_pages, int max_pages_per_seq, int max_kv_len,
-                                  int keys_per_split, float softmax_scale, void* workspace,
-                                  size_t workspace_bytes, void* out, int out_dtype,
-                                  hipStream_t stream) {
+extern "C" size_t attn_decode_splitk_workspace_size(int batch, int num_q_heads, int num_kv_heads,
+                                                    int max_kv_len, int keys_per_split) {
+    return attn_decode_splitk_ex_workspace_size(batch, 1, num_q_heads, num_kv_heads, max_kv_len,
+                                                keys_per_split);
+}
+
+extern "C" int attn_decode_splitk_ex(const void* q, const void* k_pages, const void* v_pages,
+                                     int kv_dtype, float k_scale, float v_scale,
+                                     const int32_t* page_table, const int32_t* kv_lens,
+                                     int batch, int q_len, int num_q_heads, int num_kv_heads,
+                                     int head_dim, int page_size, int num_pages,
+                                     int max_pages_per_seq, int max_kv_len, int keys_per_split,
+                                     float softmax_scale, const float* sinks, void* workspace,
+                                     size_t workspace_bytes, void* out, int out_dtype,
+                                     float* lse, hipStream_t stream) {
     using namespace attn;
     if (!q || !k_pages || !v_pages || !page_table || !kv_lens || !out) return ATTN_ERR_NULL;
-    if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_pages < 1 ||
+    if (batch < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_pages < 1 ||
         max_pages_per_seq < 1 || max_kv_len < 1 || keys_per_split < 0 ||
         !(softmax_scale == softmax_scale))
         return ATTN_ERR_SHAPE;
@@ -559,12 +619,13 @@ extern "C" int attn_decode_splitk(const void* q, const void* k_pages, const void
     if ((long long)max_kv_len > (long long)max_pages_per_seq * kPage) return ATTN_ERR_SHAPE;
     if (head_dim != kHeadDim || page_size != kPage) return ATTN_ERR_UNSUPPORTED;
     const int g = num_q_heads / num_kv_heads;
-    if (g > kDecRows) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)q_len * g > kDecRows) return ATTN_ERR_UNSUPPORTED;
     if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
     if (out_dtype != ATTN_BF16 && out_dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
     if (kv_dtype == ATTN_FP8_E4M3 && (!(k_scale > 0.f) || !(v_scale > 0.f))) return ATTN_ERR_SHAPE;
-    const size_t need = attn_decode_splitk_workspace_size(batch, num_q_heads, num_kv_heads,
-                                                          max_kv_len, keys_per_split);
+    const size_t need = attn_decode_splitk_ex_workspace_size(batch, q_len, num_q_heads,
+                                                             num_kv_heads, max_kv_len,
+                                                             keys_per_split);
     if (!workspace || workspace_bytes < need || need == 0) return ATTN_ERR_WORKSPACE;
 
     const int kps = keys_per_split ? keys_per_split
@@ -579,19 +640,24 @@ extern "C" int attn_decode_splitk(const void* q, const void* k_pages, const void
     a.hq = num_q_heads;
     a.hkv = num_kv_heads;
     a.g = g;
+    a.q_len = q_len;
+    a.cols = q_len * g;
     a.max_pages = max_pages_per_seq;
     a.num_pages = num_pages;
     a.max_splits = (max_kv_len + kps - 1) / kps;
     a.tiles_per_split = kps / kPage;
-    const size_t slots = (size_t)batch * num_q_heads * a.max_splits * kMaxSub;
+    const size_t slots = (size_t)batch * q_len * num_q_heads * a.max_splits * kMaxSub;
     a.part_o = (float*)workspace;
     a.part_ml = (float*)workspace + slots * kHeadDim;
     const bool fp8 = kv_dtype == ATTN_FP8_E4M3;
     a.sub = fp8 ? kFp8Waves : 1;
     a.scale_log2 = softmax_scale * 1.4426950408889634f * (fp8 ? k_scale : 1.f);
     a.v_scale = fp8 ? v_scale : 1.f;
+    a.sinks = sinks;
+    a.lse = lse;
     const long long grid = (long long)batch * num_kv_heads * a.max_splits;
-    if (grid > 0x7fffffffLL || (long long)batch * num_q_heads > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    const long long mgrid = (long long)batch * q_len * num_q_heads;
+    if (grid > 0x7fffffffLL || mgrid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     if (fp8)
         hipLaunchKernelGGL(decode_split_fp8_kernel<kFp8Waves>, dim3((unsigned)grid),
                            dim3(64 * kFp8Waves), 0, stream, a);
@@ -600,10 +666,25 @@ extern "C" int attn_decode_splitk(const void* q, const void* k_pages, const void
                            stream, a);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
     if (out_dtype == ATTN_FP32)
-        hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)(batch * num_q_heads)),
-                           dim3(128), 0, stream, a, out);
+        hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)mgrid), dim3(128), 0, stream,
+                           a, out);
     else
-        hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((unsigned)(batch * num_q_heads)),
-                           dim3(128), 0, stream, a, out);
+        hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((unsigned)mgrid), dim3(128), 0,
+                           stream, a, out);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" int attn_decode_splitk(const void* q, const void* k_pages, const void* v_pages,
+                                  int kv_dtype, float k_scale, float v_scale,
+                                  const int32_t* page_table, const int32_t* kv_lens, int batch,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                                  int num_pages, int max_pages_per_seq, int max_kv_len,
+                                  int keys_per_split, float softmax_scale, void* workspace,
+                                  size_t workspace_bytes, void* out, int out_dtype,
+                                  hipStream_t stream) {
+    return attn_decode_splitk_ex(q, k_pages, v_pages, kv_dtype, k_scale, v_scale, page_table,
+                                 kv_lens, batch, 1, num_q_heads, num_kv_heads, head_dim,
+                                 page_size, num_pages, max_pages_per_seq, max_kv_len,
+                                 keys_per_split, softmax_scale, nullptr, workspace,
+                                 workspace_bytes, out, out_dtype, nullptr, stream);
 }

@@ -96,6 +96,8 @@ struct PrefillArgs {
     int wgs_per_seq;    // ceil(max_q_len / tok_per_wg)
     float scale_log2;   // softmax_scale * log2(e) (* k_scale for an FP8 pool)
     float v_scale;      // FP8 pool: value dequantisation scale, applied to O (1 for bf16)
+    const float* sinks; // per query head sink logit (natural-log units), or null
+    float* lse;         // [total_q][hq] natural-log log-sum-exp, or null
 };
 
 // Refill of one 32-key half (rows 32 half .. 32 half + 31) of a K or V tile
@@ -557,11 +559,25 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // with V = 1 it returns exactly 1.
     float l_tot = l_run + __shfl_xor(l_run, 32);
     const float vs = a.v_scale;   // 1 for a bf16 pool
+    // A sink (vLLM flash-attention PR 199, second review, finding F4) adds
+    // 2^(sink - m_ref) to the denominator in the units of l (log2 units,
+    // relative to the row's reference maximum); 0 without one, so that the
+    // division below is then exactly O / l.
+    const float sink2 = a.sinks ? a.sinks[head] * 1.4426950408889634f : -__builtin_inff();
+    float lse2 = -__builtin_inff();   // log2-sum-exp of the row
     if (ntiles == 0) {  // no visible key (empty cache): the output row is 0
         l_tot = 1.f;
+        lse2 = sink2;
 #pragma unroll
         for (int db = 0; db < 16; ++db) o[db] = f32x16{};
+    } else {
+        const float a2 = m_ref + __builtin_log2f(l_tot);
+        const float top = fmaxf(a2, sink2);
+        lse2 = top + __builtin_log2f(fast_exp2(a2 - top) + fast_exp2(sink2 - top));
+        l_tot += fast_exp2(sink2 - m_ref);
     }
+    if (a.lse && valid && h == 0)
+        a.lse[(size_t)(q0 + t) * a.hq + head] = lse2 * 0.6931471805599453f;
     if (valid) {
         const size_t obase = ((size_t)(q0 + t) * a.hq + head) * kHeadDim;
 #pragma unroll
@@ -595,8 +611,9 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
                    const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
                    const int32_t* kv_lens, int batch, int total_q, int max_q_len,
                    int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                   int num_pages, int max_pages_per_seq, float softmax_scale, void* out,
-                   int out_dtype, hipStream_t stream) {
+                   int num_pages, int max_pages_per_seq, float softmax_scale,
+                   const float* sinks, void* out, int out_dtype, float* lse,
+                   hipStream_t stream) {
     if (!q || !k_pages || !v_pages || !page_table || !cu_seqlens_q || !q_start_pos ||
         !kv_lens || !out)
         return ATTN_ERR_NULL;
@@ -633,6 +650,8 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     a.wgs_per_seq = (max_q_len + a.tok_per_wg - 1) / a.tok_per_wg;
     a.scale_log2 = softmax_scale * 1.4426950408889634f * (fp8 ? k_scale : 1.f);
     a.v_scale = fp8 ? v_scale : 1.f;
+    a.sinks = sinks;
+    a.lse = lse;
     const long long grid = (long long)a.wgs_per_seq * batch * num_kv_heads;
     if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     const dim3 gd((unsigned)grid), bd(kThreads);
@@ -663,7 +682,7 @@ extern "C" int attn_prefill_hd512(const void* q, const void* k_pages, const void
     return attn::prefill_launch(q, k_pages, v_pages, false, 1.f, 1.f, page_table, cu_seqlens_q,
                                 q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
-                                softmax_scale, out, out_dtype, stream);
+                                softmax_scale, nullptr, out, out_dtype, nullptr, stream);
 }
 
 extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const void* v_pages,
@@ -677,5 +696,24 @@ extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const
     return attn::prefill_launch(q, k_pages, v_pages, true, k_scale, v_scale, page_table,
                                 cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
                                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                                max_pages_per_seq, softmax_scale, out, out_dtype, stream);
+                                max_pages_per_seq, softmax_scale, nullptr, out, out_dtype,
+                                nullptr, stream);
+}
+
+extern "C" int attn_prefill_hd512_ex(const void* q, const void* k_pages, const void* v_pages,
+                                     int kv_dtype, float k_scale, float v_scale,
+                                     const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                     const int32_t* q_start_pos, const int32_t* kv_lens,
+                                     int batch, int total_q, int max_q_len, int num_q_heads,
+                                     int num_kv_heads, int head_dim, int page_size,
+                                     int num_pages, int max_pages_per_seq, float softmax_scale,
+                                     const float* sinks, void* out, int out_dtype, float* lse,
+                                     hipStream_t stream) {
+    using namespace attn;
+    if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+    const bool fp8 = kv_dtype == ATTN_FP8_E4M3;
+    return prefill_launch(q, k_pages, v_pages, fp8, fp8 ? k_scale : 1.f, fp8 ? v_scale : 1.f,
+                          page_table, cu_seqlens_q, q_start_pos, kv_lens, batch, total_q,
+                          max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                          max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, stream);
 }

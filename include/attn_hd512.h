@@ -127,6 +127,30 @@ int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const void* v_pa
                             void* out, int out_dtype, hipStream_t stream);
 
 /*
+ * Chunked causal prefill with every option: a bf16 or FP8-E4M3 pool
+ * (kv_dtype ATTN_BF16 or ATTN_FP8_E4M3; the scales are used for FP8 only),
+ * attention sinks and a log-sum-exp output.  Other arguments as for
+ * attn_prefill_hd512.
+ *
+ *   sinks        fp32 [num_q_heads] or NULL: one logit per query head, an
+ *                extra softmax term with no value row, in the units of
+ *                softmax_scale * q.k (natural log).  o = sum_j e^{S_j} V_j /
+ *                (e^{sink} + sum_j e^{S_j}).
+ *   lse          fp32 [total_q][num_q_heads] or NULL: log(e^{sink} +
+ *                sum_j e^{S_j}) (natural log) of every written row.  A row
+ *                with no visible key gets the sink logit, or -inf without a
+ *                sink (vLLM flash-attention PR 199, second review, finding F4).
+ */
+int attn_prefill_hd512_ex(const void* q, const void* k_pages, const void* v_pages, int kv_dtype,
+                          float k_scale, float v_scale, const int32_t* page_table,
+                          const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
+                          const int32_t* kv_lens, int batch, int total_q, int max_q_len,
+                          int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                          int num_pages, int max_pages_per_seq, float softmax_scale,
+                          const float* sinks, void* out, int out_dtype, float* lse,
+                          hipStream_t stream);
+
+/*
  * Bytes of device workspace attn_decode_splitk needs for these sizes: fp32
  * partial outputs plus (m, l) for up to 4 partials per split, per query head
  * and sequence (valid for either KV dtype).  keys_per_split = 0 selects the
@@ -169,6 +193,34 @@ int attn_decode_splitk(const void* q, const void* k_pages, const void* v_pages, 
                        int max_kv_len, int keys_per_split, float softmax_scale,
                        void* workspace, size_t workspace_bytes, void* out, int out_dtype,
                        hipStream_t stream);
+
+/*
+ * Split-K decode with every option: q_len query tokens per sequence
+ * (multi-token decode, e.g. verifying q_len - 1 draft tokens; vLLM
+ * flash-attention PR 199, second review: "MTP decode"), attention sinks and
+ * a log-sum-exp output.  Other arguments as for attn_decode_splitk.
+ *
+ *   q            bf16 [batch * q_len][num_q_heads][512]: token t of sequence
+ *                b is row b * q_len + t, at position kv_lens[b] - q_len + t,
+ *                and sees keys j <= that position.  1 <= q_len and
+ *                q_len * (num_q_heads / num_kv_heads) <= 16 (ATTN_ERR_UNSUPPORTED
+ *                otherwise); kv_lens[b] >= q_len is a precondition.
+ *   sinks, lse   as for attn_prefill_hd512_ex; lse is [batch * q_len][num_q_heads].
+ *   out          [batch * q_len][num_q_heads][512].
+ *   workspace    at least attn_decode_splitk_ex_workspace_size(...) bytes.
+ */
+size_t attn_decode_splitk_ex_workspace_size(int batch, int q_len, int num_q_heads,
+                                            int num_kv_heads, int max_kv_len,
+                                            int keys_per_split);
+
+int attn_decode_splitk_ex(const void* q, const void* k_pages, const void* v_pages, int kv_dtype,
+                          float k_scale, float v_scale, const int32_t* page_table,
+                          const int32_t* kv_lens, int batch, int q_len, int num_q_heads,
+                          int num_kv_heads, int head_dim, int page_size, int num_pages,
+                          int max_pages_per_seq, int max_kv_len, int keys_per_split,
+                          float softmax_scale, const float* sinks, void* workspace,
+                          size_t workspace_bytes, void* out, int out_dtype, float* lse,
+                          hipStream_t stream);
 
 /*
  * Measurement helper: streams `bytes` (a multiple of 16) of device memory

@@ -124,12 +124,50 @@ def test_decode_validation(L):
     assert decode(L, ws_bytes=16) == 4
 
 
+def decode_ex(L, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kvd=0, ks=1.0, vs=1.0, pt=FAKE, kl=FAKE, batch=2, q_len=2,
+             hq=8, hkv=4, d=512, page=64, num_pages=8, max_pages=4, max_kv=256, kps=0,
+             scale=0.04, sinks=None, ws=FAKE, ws_bytes=1 << 30, out=FAKE, out_dtype=0,
+             lse=None, stream=None)
+    a.update(over)
+    return L.attn_decode_splitk_ex(a["q"], a["k"], a["v"], a["kvd"], a["ks"], a["vs"], a["pt"],
+                                   a["kl"], a["batch"], a["q_len"], a["hq"], a["hkv"], a["d"],
+                                   a["page"], a["num_pages"], a["max_pages"], a["max_kv"],
+                                   a["kps"], a["scale"], a["sinks"], a["ws"], a["ws_bytes"],
+                                   a["out"], a["out_dtype"], a["lse"], a["stream"])
+
+
+def test_decode_ex_validation(L):
+    assert decode_ex(L, q=None) == 1
+    assert decode_ex(L, q_len=0) == 2
+    assert decode_ex(L, q_len=9) == 3            # 9 tokens x g=2 columns > 16
+    assert decode_ex(L, kvd=1) == 3
+    assert decode_ex(L, ws_bytes=16) == 4
+
+
+def test_prefill_ex_validation(L):
+    def pf(**over):
+        a = dict(kvd=0, ks=1.0, vs=1.0, batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=512,
+                 page=64, out_dtype=1)
+        a.update(over)
+        return L.attn_prefill_hd512_ex(FAKE, FAKE, FAKE, a["kvd"], a["ks"], a["vs"], FAKE, FAKE,
+                                       FAKE, FAKE, a["batch"], a["total_q"], a["max_q_len"],
+                                       a["hq"], a["hkv"], a["d"], a["page"], 4, 4, 0.04, None,
+                                       FAKE, a["out_dtype"], None, None)
+    assert pf(kvd=1) == 3
+    assert pf(kvd=2, ks=0.0) == 2
+    assert pf(d=128) == 3
+    assert pf(total_q=0, max_q_len=0) == 0
+
+
 def test_workspace_size(L):
     n = L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 1024)
     assert n == 64 * 8 * 28 * 4 * (512 + 2) * 4   # 4 partials per split
     assert L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 100) == 0
     assert L.attn_decode_splitk_workspace_size(0, 8, 4, 28672, 0) == 0
     assert L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 0) > 0
+    assert L.attn_decode_splitk_ex_workspace_size(64, 3, 8, 4, 28672, 1024) == 3 * n
+    assert L.attn_decode_splitk_ex_workspace_size(64, 0, 8, 4, 28672, 1024) == 0
 
 
 def test_probe_validation(L):
