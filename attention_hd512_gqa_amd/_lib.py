@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_splitk_ex.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, I,
                                             F, P, P, SZ, P, I, P, P]
         L.attn_decode_splitk_ex.restype = I
+        L.attn_append_kv.argtypes = [P, P, I, F, F, P, P, P, I, I, I, I, I, I, I, P, P, P]
+        L.attn_append_kv.restype = I
         L.attn_decode_splitk_workspace_size.argtypes = [I, I, I, I, I]
         L.attn_decode_splitk_workspace_size.restype = SZ
         L.attn_decode_splitk.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, F,
@@ -178,6 +180,25 @@ def decode(q, k_pages, v_pages, page_table, kv_lens, out, workspace, *, max_kv_l
             int(page_table.shape[1]), int(max_kv_len), int(keys_per_split), float(softmax_scale),
             *ws, _stream(stream))
         _check(code, "attn_decode_splitk")
+
+
+def append_kv(k_new, v_new, page_table, cu_seqlens, q_start, k_pages, v_pages, *,
+              kv_dtype: str = "bf16", k_scale: float = 1.0, v_scale: float = 1.0,
+              stream=None) -> None:
+    """Paged KV append (attn_append_kv): writes the bf16 rows k_new, v_new
+    [total_q, Hkv, 512] into their page slots, as bf16 or as E4M3 codes
+    (x / scale, saturated, round to nearest even)."""
+    num_pages, hkv, page, d = k_pages.shape
+    batch = q_start.shape[0]
+    kvt = torch.bfloat16 if kv_dtype == "bf16" else torch.uint8
+    code = lib().attn_append_kv(
+        _dev(k_new, "k_new", torch.bfloat16), _dev(v_new, "v_new", torch.bfloat16),
+        _KV_CODES[kv_dtype], float(k_scale), float(v_scale),
+        _dev(page_table, "page_table", torch.int32), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(q_start, "q_start", torch.int32), int(batch), int(k_new.shape[0]), int(hkv), int(d),
+        int(page), int(num_pages), int(page_table.shape[1]), _dev(k_pages, "k_pages", kvt),
+        _dev(v_pages, "v_pages", kvt), _stream(stream))
+    _check(code, "attn_append_kv")
 
 
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

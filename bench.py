@@ -245,6 +245,29 @@ def main():
             del dc, dout, ws, qd
             torch.cuda.empty_cache()
 
+    # ---- paged KV append of the headline chunk (HBM-bound data movement) -----
+    append = {}
+    if not args.no_decode:
+        for kv_dtype in ("bf16", "fp8_e4m3"):
+            ac = W.chunk_prefill_8k_at_8k(device="cuda", kv_dtype=kv_dtype)
+            al = ac.launches[0]
+            kn = torch.randn(al.total_q, ac.num_kv_heads, W.HEAD_DIM, device="cuda").to(torch.bfloat16)
+            vn = torch.randn_like(kn)
+            kp, vp = ac.k_pool.clone(), ac.v_pool.clone()
+
+            def append_call():
+                A.append_kv(kn, vn, ac.page_table, al.cu_seqlens_q, al.q_start, kp, vp,
+                            kv_dtype=kv_dtype, k_scale=ac.k_scale, v_scale=ac.v_scale,
+                            stream=stream)
+            ms = timed(append_call, 20, 5)
+            moved = 2 * kn.numel() * 2 + 2 * kn.numel() * (2 if kv_dtype == "bf16" else 1)
+            append[kv_dtype] = {"us_per_call": ms * 1e3, "bytes": moved,
+                                "GB_per_s": moved / (ms * 1e-3) / 1e9}
+            log(f"append_kv {kv_dtype} (8192 rows x {ac.num_kv_heads} KV heads): "
+                f"{ms * 1e3:.1f} us, {moved / (ms * 1e-3) / 1e9:.0f} GB/s")
+            del ac, kn, vn, kp, vp
+            torch.cuda.empty_cache()
+
     gemm_after = 0.0 if args.no_gemm else gemm_rate()
     log(f"bf16 GEMM roofline (after): {gemm_after:.1f} TFLOP/s")
     gemm = max(gemm_before, gemm_after)
@@ -310,6 +333,7 @@ def main():
         "hbm": {"read_probe_GB_per_s": hbm_read, "probe_bytes": hbm_bytes,
                 "d2d_copy_GB_per_s": d2d},
         "decode": decode,
+        "append_kv": append,
         "prefill_other": extra,
         "cpu_baseline": cpu,
     }

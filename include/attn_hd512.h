@@ -223,6 +223,31 @@ int attn_decode_splitk_ex(const void* q, const void* k_pages, const void* v_page
                           hipStream_t stream);
 
 /*
+ * Paged KV append: writes a chunk's new key and value rows into their cache
+ * slots (the pool paged at the attention key block: pegainfer issue 1051,
+ * "Proposed Plan").
+ *
+ *   k_new, v_new   bf16 [total_q][num_kv_heads][512]; row order as q.
+ *   kv_dtype       ATTN_BF16 (rows copied) or ATTN_FP8_E4M3 (each element
+ *                  stored as the E4M3FN code of x / scale (fp32 division),
+ *                  saturated to +-448, rounded to nearest even; NaN stays NaN).
+ *   page_table, cu_seqlens, q_start_pos   as for prefill: token i of sequence
+ *                  b goes to position q_start_pos[b] + i, i.e. page
+ *                  page_table[b][p / 64], slot p % 64.
+ *   k_pages, v_pages   the pools written (layout above).
+ *
+ * Rows whose position falls outside the table, or whose page id falls
+ * outside the pool, are skipped.  Rows must not share a slot (no two tokens
+ * at one position of one sequence, no page shared by two sequences'
+ * written slots); then the result does not depend on execution order.
+ */
+int attn_append_kv(const void* k_new, const void* v_new, int kv_dtype, float k_scale,
+                   float v_scale, const int32_t* page_table, const int32_t* cu_seqlens,
+                   const int32_t* q_start_pos, int batch, int total_q, int num_kv_heads,
+                   int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                   void* k_pages, void* v_pages, hipStream_t stream);
+
+/*
  * Measurement helper: streams `bytes` (a multiple of 16) of device memory
  * once with 16-byte loads and writes one word per workgroup to `sink`
  * (at least attn_hbm_probe_sink_words(bytes) uint32 values).  Used to take

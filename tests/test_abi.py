@@ -160,6 +160,22 @@ def test_prefill_ex_validation(L):
     assert pf(total_q=0, max_q_len=0) == 0
 
 
+def test_append_validation(L):
+    def ap(**over):
+        a = dict(kn=FAKE, kvd=0, ks=1.0, vs=1.0, batch=1, total_q=4, hkv=2, d=512, page=64,
+                 num_pages=4, max_pages=4)
+        a.update(over)
+        return L.attn_append_kv(a["kn"], FAKE, a["kvd"], a["ks"], a["vs"], FAKE, FAKE, FAKE,
+                                a["batch"], a["total_q"], a["hkv"], a["d"], a["page"],
+                                a["num_pages"], a["max_pages"], FAKE, FAKE, None)
+    assert ap(kn=None) == 1
+    assert ap(kvd=1) == 3
+    assert ap(kvd=2, vs=0.0) == 2
+    assert ap(d=256) == 3
+    assert ap(batch=0) == 2
+    assert ap(total_q=0) == 0
+
+
 def test_workspace_size(L):
     n = L.attn_decode_splitk_workspace_size(64, 8, 4, 28672, 1024)
     assert n == 64 * 8 * 28 * 4 * (512 + 2) * 4   # 4 partials per split
