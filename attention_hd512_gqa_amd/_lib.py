@@ -44,6 +44,11 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_hd512_ex.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I, I,
                                             I, I, F, P, P, I, P, P]
         L.attn_prefill_hd512_ex.restype = I
+        L.attn_prefill_hd512_splitk_workspace_size.argtypes = [I, I, I, I, I, I, I]
+        L.attn_prefill_hd512_splitk_workspace_size.restype = SZ
+        L.attn_prefill_hd512_splitk.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I,
+                                                I, I, I, I, I, F, P, P, SZ, P, I, P, P]
+        L.attn_prefill_hd512_splitk.restype = I
         L.attn_decode_splitk_ex_workspace_size.argtypes = [I, I, I, I, I, I]
         L.attn_decode_splitk_ex_workspace_size.restype = SZ
         L.attn_decode_splitk_ex.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, I,
@@ -139,6 +144,48 @@ def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out
             _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.uint8),
             _dev(v_pages, "v_pages", torch.uint8), float(k_scale), float(v_scale), *meta)
         _check(code, "attn_prefill_hd512_e4m3")
+
+
+def prefill_splitk_workspace_size(batch: int, max_q_len: int, total_q: int, num_q_heads: int,
+                                  num_kv_heads: int, max_kv_len: int,
+                                  keys_per_split: int = 0) -> int:
+    """Bytes of workspace attn_prefill_hd512_splitk needs (0: a single pass)."""
+    return int(lib().attn_prefill_hd512_splitk_workspace_size(
+        int(batch), int(max_q_len), int(total_q), int(num_q_heads), int(num_kv_heads),
+        int(max_kv_len), int(keys_per_split)))
+
+
+def prefill_splitk(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out,
+                   workspace, *, total_q: int, max_q_len: int, max_kv_len: int,
+                   softmax_scale: float, keys_per_split: int = 0, kv_dtype: str = "bf16",
+                   k_scale: float = 1.0, v_scale: float = 1.0, sinks=None, lse=None,
+                   stream=None) -> None:
+    """Chunked causal prefill with the key range split across workgroups
+    (attn_prefill_hd512_splitk): split kernel then merge kernel, for short
+    chunks over long prefixes.  `workspace` may be None when
+    prefill_splitk_workspace_size(...) is 0."""
+    num_pages, hkv, page, d = k_pages.shape
+    hq = q.shape[1]
+    batch = kv_lens.shape[0]
+    if kv_dtype not in _KV_CODES:
+        raise AttnError(f"unsupported kv_dtype {kv_dtype!r}")
+    kvt = torch.bfloat16 if kv_dtype == "bf16" else torch.uint8
+    if workspace is None:
+        ws, ws_bytes = None, 0
+    else:
+        ws, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    code = lib().attn_prefill_hd512_splitk(
+        _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
+        _dev(v_pages, "v_pages", kvt), _KV_CODES[kv_dtype], float(k_scale), float(v_scale),
+        _dev(page_table, "page_table", torch.int32),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(q_start, "q_start", torch.int32),
+        _dev(kv_lens, "kv_lens", torch.int32), int(batch), int(total_q), int(max_q_len),
+        int(hq), int(hkv), int(d), int(page), int(num_pages), int(page_table.shape[1]),
+        int(max_kv_len), int(keys_per_split), float(softmax_scale),
+        _opt(sinks, "sinks", torch.float32, hq), ws, ws_bytes,
+        _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
+        _opt(lse, "lse", torch.float32, int(total_q) * hq), _stream(stream))
+    _check(code, "attn_prefill_hd512_splitk")
 
 
 def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_kv_len: int,

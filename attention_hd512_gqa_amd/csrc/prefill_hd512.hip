@@ -98,6 +98,11 @@ struct PrefillArgs {
     float v_scale;      // FP8 pool: value dequantisation scale, applied to O (1 for bf16)
     const float* sinks; // per query head sink logit (natural-log units), or null
     float* lse;         // [total_q][hq] natural-log log-sum-exp, or null
+    // split-K over keys: workgroup split s covers key tiles
+    // [s split_tiles, (s + 1) split_tiles) and writes unnormalised partials
+    int nsplit, split_tiles;
+    float* part_o;      // [nsplit][total_q][hq][512] fp32, O * v_scale
+    float* part_ml;     // [nsplit][total_q][hq][2]  (m in log2 units, l)
 };
 
 // Refill of one 32-key half (rows 32 half .. 32 half + 31) of a K or V tile
@@ -355,7 +360,7 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[16], int kb, const bf16x8& 
     });
 }
 
-template <bool OUT_FP32, bool FP8>
+template <bool OUT_FP32, bool FP8, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_hd512_kernel(PrefillArgs a) {
     constexpr int kTileB = Kv<FP8>::kTileB;
@@ -373,8 +378,11 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // consecutive workgroups (spread round-robin over the XCDs) share a KV
     // head per XCD whenever the KV head count divides 8.
     const int per_rank = a.batch * a.hkv;
-    const int rank = blockIdx.x / per_rank;
-    const int rem = blockIdx.x - rank * per_rank;
+    const int per_split = a.wgs_per_seq * per_rank;
+    const int split = SPLIT ? blockIdx.x / per_split : 0;
+    const int in_split = blockIdx.x - split * per_split;
+    const int rank = in_split / per_rank;
+    const int rem = in_split - rank * per_rank;
     const int kvh = rem % a.hkv;
     const int b = rem / a.hkv;
     const int wg_in_seq = a.wgs_per_seq - 1 - rank;
@@ -392,7 +400,11 @@ void prefill_hd512_kernel(PrefillArgs a) {
     const int qs = max(a.q_start[b], 0);   // every row then sees key 0
     const int n_max = min(qs + t_last + 1, L);   // keys the last row sees
     const int n_min = min(qs + t0 + 1, L);       // keys the first row sees
-    const int ntiles = n_max > 0 ? (n_max + kPage - 1) / kPage : 0;
+    const int ntiles_all = n_max > 0 ? (n_max + kPage - 1) / kPage : 0;
+    // this workgroup's key tiles [kt_lo, ntiles): all of them, or one split
+    const int kt_lo = SPLIT ? split * a.split_tiles : 0;
+    const int ntiles = SPLIT ? min(ntiles_all, kt_lo + a.split_tiles) : ntiles_all;
+    if (SPLIT && kt_lo >= ntiles) return;   // no row of this unit needs the split
 
     // ---- this lane's query row: n = column of the MFMA tiles, h = k-half
     const int n = lane & 31;
@@ -447,12 +459,12 @@ void prefill_hd512_kernel(PrefillArgs a) {
     const int* ptab = a.page_table + (size_t)b * a.max_pages;
     const int lane16 = lane * 16;
     const int lane_off = lane16 ^ ((wave & 1) << 7);
-    const int staged = min(ntiles, kPagesInLds);
-    for (int i = threadIdx.x; i < staged; i += kThreads) sPage[i] = ptab[i];
+    const int staged = min(ntiles - kt_lo, kPagesInLds);
+    for (int i = threadIdx.x; i < staged; i += kThreads) sPage[i] = ptab[kt_lo + i];
     __syncthreads();
     auto page_of = [&](int tile) -> int {
-        return tile < kPagesInLds ? __builtin_amdgcn_readfirstlane(sPage[tile])
-                                  : load_uniform(ptab, tile);
+        return tile - kt_lo < kPagesInLds ? __builtin_amdgcn_readfirstlane(sPage[tile - kt_lo])
+                                          : load_uniform(ptab, tile);
     };
     auto flags_set = [&]() -> bool { return (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0; };
 
@@ -462,15 +474,15 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // issued two refills (2 kD loads) before the newest, except where the tile
     // has no successor and those later refills do not exist.
     for (;;) {   // one pass over the key range; a restart begins a new pass
-        if (ntiles > 0) {
-            const int page0 = page_of(0);
-            const int v0 = min(L, kPage);
+        if (ntiles > kt_lo) {
+            const int page0 = page_of(kt_lo);
+            const int v0 = min(L - kt_lo * kPage, kPage);
             half_dma_all<FP8>(half_dma<FP8>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 0, wave, true), lane_off, lane, wave);
             half_dma_all<FP8>(half_dma<FP8>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 1, wave, true), lane_off, lane, wave);
             half_dma_all<FP8>(half_dma<FP8>(a.v_pages, page0, a.num_pages, a.hkv, kvh, v0, sV, 0, wave, true), lane_off, lane, wave);
         }
         bool restart = false;
-        for (int kt = 0; kt < ntiles; ++kt) {
+        for (int kt = kt_lo; kt < ntiles; ++kt) {
             const bool more = kt + 1 < ntiles;
             const int key0 = kt * kPage;
             const int valid = min(L - key0, kPage);
@@ -487,7 +499,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
             // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill
             wait_vmcnt<2 * kD>();
             lds_barrier();
-            if (kt > 0 && restarts < kMaxRestarts && flags_set()) {
+            if (kt > kt_lo && restarts < kMaxRestarts && flags_set()) {
                 restart = true;   // a row of tile kt-1 overshot its reference
                 break;
             }
@@ -496,13 +508,16 @@ void prefill_hd512_kernel(PrefillArgs a) {
                                  lane_off, lane, wave);
             mfma_vgpr_drain(s0);
             if (mask) mask_block(s0, key0 + 4 * h, n_row);
-            if (kt == 0) {
-                // reference maximum: the row's maximum over keys 0..31 (key 0 is
-                // visible to every row, so it is finite)
+            if (kt == kt_lo && restarts == 0) {
+                // reference maximum: the row's maximum over the range's first 32
+                // keys (a restarted pass keeps the raised one).  Without split-K key 0 is visible to every row, so it is
+                // finite; a split can start past a row's causal limit, and that
+                // row then takes 0 (every p = 0, an empty partial).
                 float m0 = -__builtin_inff();
 #pragma unroll
                 for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
                 m0 = fmaxf(m0, __shfl_xor(m0, 32)) * a.scale_log2;
+                m0 = m0 == -__builtin_inff() ? 0.f : m0;
                 m_ref = m0;
                 c0.neg_m_ref = -m0;
             }
@@ -521,7 +536,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
             lds_barrier();
             const SoftmaxCtx& c1 = c0;
             const HalfDma dk1 = half_dma<FP8>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 1, wave, more);
-            if (kt == 0)
+            if (kt == kt_lo)
                 pv_block<true, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
             else
                 pv_block<false, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
@@ -536,11 +551,12 @@ void prefill_hd512_kernel(PrefillArgs a) {
             mx *= a.scale_log2;
             m_seen = fmaxf(m_seen, mx);
             // restart flag of this tile: any row whose scores exceeded
-            // m_ref + margin (non-finite sums included); read after the next barrier
-            if (lane == 0)
-                sFlag[wave] = __any(!(mx <= m_ref + kRescaleMargin) || !(psum == psum)) ? 1 : 0;
+            // m_ref + margin (non-finite sums included); read after the next
+            // barrier.  The vote runs on every lane, outside the lane-0 store.
+            const bool over = __any(!(mx <= m_ref + kRescaleMargin) || !(psum == psum));
+            if (lane == 0) sFlag[wave] = over ? 1 : 0;
         }
-        if (!restart && ntiles > 0) {
+        if (!restart && ntiles > kt_lo) {
             lds_barrier();   // the last tile's flags are visible
             restart = restarts < kMaxRestarts && flags_set();
         }
@@ -549,15 +565,39 @@ void prefill_hd512_kernel(PrefillArgs a) {
         ++restarts;
         wait_vmcnt<0>();     // refills still landing in sK / sV
         lds_barrier();
-        m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));
+        // (a row that saw no key keeps its reference; the reference only rises)
+        m_ref = fmaxf(m_ref, fmaxf(m_seen, __shfl_xor(m_seen, 32)));
         m_seen = m_ref;
         l_run = 0.f;         // O restarts too: tile 0's P.V overwrites it
     }
 
     // ---- epilogue: lane holds d = 32 db + 8 (i/4) + 4 h + (i%4) of its row.
+    float l_tot = l_run + __shfl_xor(l_run, 32);
+    if constexpr (SPLIT) {
+        // split-K partial: O * v_scale, m (log2 units) and l; a row that saw
+        // no key of the split gives (0, -inf, 0) and adds nothing in the merge
+        if (valid) {
+            const size_t slot = ((size_t)split * a.total_q + (q0 + t)) * a.hq + head;
+            float* dst = a.part_o + slot * kHeadDim;
+            const float vs = a.v_scale;
+#pragma unroll
+            for (int db = 0; db < 16; ++db) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d0 = 32 * db + 8 * q4 + 4 * h;
+                    *(f32x4*)(dst + d0) = f32x4{o[db][4 * q4], o[db][4 * q4 + 1],
+                                                o[db][4 * q4 + 2], o[db][4 * q4 + 3]} * vs;
+                }
+            }
+            if (h == 0) {
+                a.part_ml[2 * slot] = l_tot > 0.f ? m_ref : -__builtin_inff();
+                a.part_ml[2 * slot + 1] = l_tot;
+            }
+        }
+        return;
+    }
     // o = O / l with an IEEE division (not O * (1/l)), as the definition reads:
     // with V = 1 it returns exactly 1.
-    float l_tot = l_run + __shfl_xor(l_run, 32);
     const float vs = a.v_scale;   // 1 for a bf16 pool
     // A sink (vLLM flash-attention PR 199, second review, finding F4) adds
     // 2^(sink - m_ref) to the denominator in the units of l (log2 units,
@@ -599,12 +639,117 @@ void prefill_hd512_kernel(PrefillArgs a) {
     }
 }
 
+
+// Merge of the split-K partials of one (query row, query head): the partial
+// of split s is O_s (times v_scale), m_s (log2 units) and l_s, with O_s and
+// l_s relative to 2^{m_s}; the row's result is sum_s 2^{m_s - top} O_s /
+// (2^{sink - top} + sum_s 2^{m_s - top} l_s), top the largest exponent.
+// Grid: one 128-lane workgroup per (row, head); lane i owns dims 4i .. 4i+3.
+template <bool OUT_FP32>
+__global__ __launch_bounds__(128) void prefill_merge_kernel(PrefillArgs a, int rows_cap) {
+    const int head = blockIdx.x % a.hq;
+    const int row = blockIdx.x / a.hq;
+    auto cu = [&](int i) {
+        const int v = a.cu_seqlens_q[i];
+        return v < 0 ? 0 : (v > a.total_q ? a.total_q : v);
+    };
+    // the sequence holding the row: the last b with cu[b] <= row
+    int lo = 0, hi = a.batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu(mid) <= row) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int q0 = cu(b);
+    const int q1 = max(q0, cu(b + 1));
+    const int t = row - q0;
+    if (row < q0 || row >= q1 || t >= rows_cap) return;   // a row the split kernel skipped
+    int L = a.kv_lens[b];
+    L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
+    const int n_row = min(max(a.q_start[b], 0) + t + 1, L);
+    const int split_keys = a.split_tiles * kPage;
+    const int ns = min((n_row + split_keys - 1) / split_keys, a.nsplit);
+    const size_t slot0 = (size_t)row * a.hq + head;
+    const size_t stride = (size_t)a.total_q * a.hq;
+    const float sink2 = a.sinks ? a.sinks[head] * 1.4426950408889634f : -__builtin_inff();
+    float top = sink2;
+    for (int s = 0; s < ns; ++s) top = fmaxf(top, a.part_ml[2 * (slot0 + s * stride)]);
+    f32x4 acc = f32x4{};
+    float den = 0.f;
+    const int d0 = 4 * threadIdx.x;
+    if (top != -__builtin_inff()) {
+        for (int s = 0; s < ns; ++s) {
+            const size_t slot = slot0 + s * stride;
+            const float m = a.part_ml[2 * slot];
+            if (m == -__builtin_inff()) continue;   // a split the row saw no key of
+            const float w = fast_exp2(m - top);
+            den += w * a.part_ml[2 * slot + 1];
+            acc += w * *(const f32x4*)(a.part_o + slot * kHeadDim + d0);
+        }
+        den += fast_exp2(sink2 - top);   // 0 without a sink
+    }
+    // IEEE division as in the single-pass epilogue; no key and no sink gives 0
+    const float dd = den > 0.f ? den : 1.f;
+    const size_t obase = slot0 * kHeadDim + d0;
+    const f32x4 v = {acc[0] / dd, acc[1] / dd, acc[2] / dd, acc[3] / dd};
+    if constexpr (OUT_FP32) {
+        *(f32x4*)((float*)a.out + obase) = v;
+    } else {
+        *(bf16x4*)((__bf16*)a.out + obase) =
+            bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    }
+    if (a.lse && threadIdx.x == 0)
+        a.lse[slot0] = den > 0.f ? (top + __builtin_log2f(den)) * 0.6931471805599453f
+                                 : -__builtin_inff();
+}
+
 }  // namespace
 
 }  // namespace attn
 
 namespace attn {
 namespace {
+
+// Split-K plan of a prefill launch: nsplit ranges of split_tiles key tiles.
+// A workgroup fills a compute unit (its LDS and registers), so a launch of
+// u equal workgroups takes ceil(u / kCus) rounds of one workgroup's time,
+// which shrinks as 1 / nsplit.  The default picks the split count that
+// minimises ceil(u / kCus) / u, charged kSplitCost per range for the
+// partial traffic, the merge and each range's pipeline start; ranges keep
+// at least kMinSplitTiles tiles.  One range means the single-pass kernel.
+constexpr int kCus = 256;               // compute units of a gfx950 part
+constexpr int kMinSplitTiles = 8;
+constexpr int kMaxAutoSplits = 64;
+constexpr double kSplitCost = 0.02;
+
+struct SplitPlanK {
+    int nsplit, split_tiles;
+};
+
+SplitPlanK prefill_split_plan(long long base_wgs, int max_kv_len, int keys_per_split) {
+    const int max_tiles = (max_kv_len + kPage - 1) / kPage;
+    if (max_tiles < 1 || base_wgs < 1) return {1, max_tiles > 0 ? max_tiles : 1};
+    int st = max_tiles;
+    if (keys_per_split > 0) {
+        st = keys_per_split / kPage;
+    } else {
+        const int cap = min(kMaxAutoSplits, max(1, max_tiles / kMinSplitTiles));
+        double best = 0.0;
+        for (int ns = 1; ns <= cap; ++ns) {
+            const int t = (max_tiles + ns - 1) / ns;
+            const int real = (max_tiles + t - 1) / t;   // ranges after rounding
+            if (real != ns) continue;
+            const double u = (double)base_wgs * ns;
+            const double rounds = (double)((long long)(u + kCus - 1) / kCus);
+            const double cost = rounds / u * (ns == 1 ? 1.0 : 1.0 + kSplitCost * ns);
+            if (ns == 1 || cost < best) {
+                best = cost;
+                st = t;
+            }
+        }
+    }
+    return {(max_tiles + st - 1) / st, st};
+}
 
 int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool fp8,
                    float k_scale, float v_scale, const int32_t* page_table,
@@ -613,7 +758,8 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
                    int num_q_heads, int num_kv_heads, int head_dim, int page_size,
                    int num_pages, int max_pages_per_seq, float softmax_scale,
                    const float* sinks, void* out, int out_dtype, float* lse,
-                   hipStream_t stream) {
+                   bool splitk, int max_kv_len, int keys_per_split, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
     if (!q || !k_pages || !v_pages || !page_table || !cu_seqlens_q || !q_start_pos ||
         !kv_lens || !out)
         return ATTN_ERR_NULL;
@@ -627,6 +773,9 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     if (g > kRowsPerWg) return ATTN_ERR_UNSUPPORTED;
     if (out_dtype != ATTN_BF16 && out_dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
     if ((long long)max_pages_per_seq * kPage > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if (splitk && (max_kv_len < 1 || keys_per_split < 0 || keys_per_split % kPage ||
+                   (long long)max_kv_len > (long long)max_pages_per_seq * kPage))
+        return ATTN_ERR_SHAPE;
     if (total_q == 0 || max_q_len == 0) return ATTN_OK;
     if (max_q_len > total_q) return ATTN_ERR_SHAPE;
 
@@ -652,19 +801,53 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     a.v_scale = fp8 ? v_scale : 1.f;
     a.sinks = sinks;
     a.lse = lse;
-    const long long grid = (long long)a.wgs_per_seq * batch * num_kv_heads;
+    a.nsplit = 1;
+    a.split_tiles = 0;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    const long long base = (long long)a.wgs_per_seq * batch * num_kv_heads;
+    if (splitk) {
+        const SplitPlanK sp = prefill_split_plan(base, max_kv_len, keys_per_split);
+        if (sp.nsplit > 1) {
+            const size_t slots = (size_t)sp.nsplit * total_q * num_q_heads;
+            if (!workspace || workspace_bytes < slots * (kHeadDim + 2) * sizeof(float))
+                return ATTN_ERR_WORKSPACE;
+            a.nsplit = sp.nsplit;
+            a.split_tiles = sp.split_tiles;
+            a.part_o = (float*)workspace;
+            a.part_ml = (float*)workspace + slots * kHeadDim;
+            const long long grid = base * sp.nsplit;
+            const long long mgrid = (long long)total_q * num_q_heads;
+            if (grid > 0x7fffffffLL || mgrid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+            if (fp8)
+                hipLaunchKernelGGL((prefill_hd512_kernel<false, true, true>), dim3((unsigned)grid),
+                                   dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((prefill_hd512_kernel<false, false, true>), dim3((unsigned)grid),
+                                   dim3(kThreads), 0, stream, a);
+            const int rows_cap = a.wgs_per_seq * a.tok_per_wg;
+            if (out_dtype == ATTN_FP32)
+                hipLaunchKernelGGL(prefill_merge_kernel<true>, dim3((unsigned)mgrid), dim3(128), 0,
+                                   stream, a, rows_cap);
+            else
+                hipLaunchKernelGGL(prefill_merge_kernel<false>, dim3((unsigned)mgrid), dim3(128), 0,
+                                   stream, a, rows_cap);
+            return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+        }
+    }
+    const long long grid = base;
     if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     const dim3 gd((unsigned)grid), bd(kThreads);
     if (fp8) {
         if (out_dtype == ATTN_FP32)
-            hipLaunchKernelGGL((prefill_hd512_kernel<true, true>), gd, bd, 0, stream, a);
+            hipLaunchKernelGGL((prefill_hd512_kernel<true, true, false>), gd, bd, 0, stream, a);
         else
-            hipLaunchKernelGGL((prefill_hd512_kernel<false, true>), gd, bd, 0, stream, a);
+            hipLaunchKernelGGL((prefill_hd512_kernel<false, true, false>), gd, bd, 0, stream, a);
     } else {
         if (out_dtype == ATTN_FP32)
-            hipLaunchKernelGGL((prefill_hd512_kernel<true, false>), gd, bd, 0, stream, a);
+            hipLaunchKernelGGL((prefill_hd512_kernel<true, false, false>), gd, bd, 0, stream, a);
         else
-            hipLaunchKernelGGL((prefill_hd512_kernel<false, false>), gd, bd, 0, stream, a);
+            hipLaunchKernelGGL((prefill_hd512_kernel<false, false, false>), gd, bd, 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -682,7 +865,8 @@ extern "C" int attn_prefill_hd512(const void* q, const void* k_pages, const void
     return attn::prefill_launch(q, k_pages, v_pages, false, 1.f, 1.f, page_table, cu_seqlens_q,
                                 q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
-                                softmax_scale, nullptr, out, out_dtype, nullptr, stream);
+                                softmax_scale, nullptr, out, out_dtype, nullptr, false, 0, 0, nullptr,
+                                0, stream);
 }
 
 extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const void* v_pages,
@@ -697,7 +881,7 @@ extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const
                                 cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
                                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                                 max_pages_per_seq, softmax_scale, nullptr, out, out_dtype,
-                                nullptr, stream);
+                                nullptr, false, 0, 0, nullptr, 0, stream);
 }
 
 extern "C" int attn_prefill_hd512_ex(const void* q, const void* k_pages, const void* v_pages,
@@ -715,5 +899,45 @@ extern "C" int attn_prefill_hd512_ex(const void* q, const void* k_pages, const v
     return prefill_launch(q, k_pages, v_pages, fp8, fp8 ? k_scale : 1.f, fp8 ? v_scale : 1.f,
                           page_table, cu_seqlens_q, q_start_pos, kv_lens, batch, total_q,
                           max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                          max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, stream);
+                          max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, false, 0,
+                          0, nullptr, 0, stream);
+}
+
+extern "C" size_t attn_prefill_hd512_splitk_workspace_size(int batch, int max_q_len,
+                                                           int total_q, int num_q_heads,
+                                                           int num_kv_heads, int max_kv_len,
+                                                           int keys_per_split) {
+    using namespace attn;
+    if (batch < 1 || max_q_len < 1 || total_q < max_q_len || num_q_heads < 1 ||
+        num_kv_heads < 1 || num_q_heads % num_kv_heads || max_kv_len < 1 ||
+        keys_per_split < 0 || keys_per_split % kPage)
+        return 0;
+    const int g = num_q_heads / num_kv_heads;
+    if (g > kRowsPerWg) return 0;
+    const int tok = kRowsPerWg / g;
+    const long long base = (long long)((max_q_len + tok - 1) / tok) * batch * num_kv_heads;
+    const SplitPlanK sp = prefill_split_plan(base, max_kv_len, keys_per_split);
+    if (sp.nsplit < 2) return 0;
+    return (size_t)sp.nsplit * total_q * num_q_heads * (kHeadDim + 2) * sizeof(float);
+}
+
+extern "C" int attn_prefill_hd512_splitk(const void* q, const void* k_pages, const void* v_pages,
+                                         int kv_dtype, float k_scale, float v_scale,
+                                         const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                         const int32_t* q_start_pos, const int32_t* kv_lens,
+                                         int batch, int total_q, int max_q_len, int num_q_heads,
+                                         int num_kv_heads, int head_dim, int page_size,
+                                         int num_pages, int max_pages_per_seq, int max_kv_len,
+                                         int keys_per_split, float softmax_scale,
+                                         const float* sinks, void* workspace,
+                                         size_t workspace_bytes, void* out, int out_dtype,
+                                         float* lse, hipStream_t stream) {
+    using namespace attn;
+    if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+    const bool fp8 = kv_dtype == ATTN_FP8_E4M3;
+    return prefill_launch(q, k_pages, v_pages, fp8, fp8 ? k_scale : 1.f, fp8 ? v_scale : 1.f,
+                          page_table, cu_seqlens_q, q_start_pos, kv_lens, batch, total_q,
+                          max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                          max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, true,
+                          max_kv_len, keys_per_split, workspace, workspace_bytes, stream);
 }

@@ -6,9 +6,9 @@ from .gen import (HEAD_DIM, PAGE_SIZE, BF16_NAN_BITS, E4M3_NAN_BYTE, E4M3_MAX, L
                   PagedCase, build_case, decode_lengths, quantize_e4m3)
 from .count import causal_pairs, decode_kv_bytes, prefill_flops
 from .cases import (WORKLOADS, chunk_prefill_2k, chunk_prefill_8k_at_8k, decode_b64,
-                    long_mqa_32k, tiny_prefill_mqa)
+                    long_mqa_32k, prefix_prefill_512_at_32k, tiny_prefill_mqa)
 
 __all__ = ["HEAD_DIM", "PAGE_SIZE", "BF16_NAN_BITS", "E4M3_NAN_BYTE", "E4M3_MAX", "Launch",
            "PagedCase", "build_case", "decode_lengths", "quantize_e4m3", "WORKLOADS",
            "chunk_prefill_2k", "chunk_prefill_8k_at_8k", "decode_b64", "long_mqa_32k",
-           "tiny_prefill_mqa", "causal_pairs", "decode_kv_bytes", "prefill_flops"]
+           "prefix_prefill_512_at_32k", "tiny_prefill_mqa", "causal_pairs", "decode_kv_bytes", "prefill_flops"]

@@ -59,6 +59,20 @@ def long_mqa_32k(device="cpu", seed=4, q_zero=False, v_one=False, kv_dtype="bf16
                       q_zero=q_zero, v_one=v_one, kv_dtype=kv_dtype)
 
 
+def prefix_prefill_512_at_32k(device="cpu", seed=6, kv_dtype="bf16") -> PagedCase:
+    """A short chunk over a long prefix: 512 rows at positions 32256..32767 over
+    32768 keys, 32 q heads over 4 KV heads, bf16 out.
+
+    The single-pass launch has 32 row blocks x 4 KV heads = 128 workgroups,
+    each walking all 512 key tiles; the split-K entry point spreads the key
+    range over the compute units.  Hostile padding as in the 8192-row chunk.
+    """
+    return build_case("prefix_prefill_512_at_32k" + _fp8_suffix(kv_dtype),
+                      seqs=[(512, 32256, 32768)], hq=32, hkv=4, seed=seed, out_dtype="bf16",
+                      device=device, q_pad_rows=16, extra_pages=3, table_pad=2,
+                      kv_dtype=kv_dtype)
+
+
 def decode_b64(device="cpu", seed=5, kv_dtype="bf16", batch=64, lo=4096, hi=28672) -> PagedCase:
     """Batch-64 single-token decode, 8 q heads over 4 KV heads, lengths U{4096..28672}.
 
@@ -77,5 +91,6 @@ WORKLOADS: Dict[str, Callable[..., PagedCase]] = {
     "chunk_prefill_2048": chunk_prefill_2k,
     "chunk_prefill_8192_at_8192": chunk_prefill_8k_at_8k,
     "long_mqa_32k_8x4096": long_mqa_32k,
+    "prefix_prefill_512_at_32k": prefix_prefill_512_at_32k,
     "decode_b64_splitk": decode_b64,
 }

@@ -151,6 +151,55 @@ int attn_prefill_hd512_ex(const void* q, const void* k_pages, const void* v_page
                           hipStream_t stream);
 
 /*
+ * Bytes of device workspace attn_prefill_hd512_splitk needs for these sizes:
+ * fp32 partial outputs plus (m, l) per split, query row and query head.
+ * Returns 0 when the plan has a single key range (the call then runs the
+ * single-pass kernel and needs no workspace) and for invalid sizes.
+ */
+size_t attn_prefill_hd512_splitk_workspace_size(int batch, int max_q_len, int total_q,
+                                                int num_q_heads, int num_kv_heads,
+                                                int max_kv_len, int keys_per_split);
+
+/*
+ * Chunked causal prefill with the key range split across workgroups, for
+ * short chunks over long prefixes, where one workgroup per block of query
+ * rows would leave most compute units idle while each walks the whole
+ * prefix (vLLM flash-attention PR 199, second review: vLLM's call shapes
+ * include prefix prefill and explicit split counts; the partials combine as
+ * in split-K decode).  Arguments as for attn_prefill_hd512_ex, plus:
+ *
+ *   max_kv_len       host bound on kv_lens[b], 1 <= max_kv_len <=
+ *                    max_pages_per_seq * 64; keys past the last split of
+ *                    the plan (nsplit * keys_per_split >= max_kv_len) are
+ *                    not read.
+ *   keys_per_split   keys per range, a positive multiple of 64, or 0 for the
+ *                    library default: the range count (at most 64, ranges of
+ *                    at least 512 keys) that keeps the 256 compute units
+ *                    busiest, each range charged 2% for its partials.
+ *   workspace        device buffer of at least
+ *                    attn_prefill_hd512_splitk_workspace_size(...) bytes
+ *                    (may be NULL when that is 0); contents on entry are
+ *                    ignored; not to be shared by concurrent calls.
+ *
+ * The split kernel writes, for every (query row, query head, range) whose
+ * range holds at least one key the row sees, O * v_scale, m and l of that
+ * range; the merge kernel combines a row's ranges (the count follows from
+ * q_start_pos, kv_lens and the row's position) with the sink, divides, and
+ * writes out (and lse).  Results equal attn_prefill_hd512_ex's up to
+ * rounding order.
+ */
+int attn_prefill_hd512_splitk(const void* q, const void* k_pages, const void* v_pages,
+                              int kv_dtype, float k_scale, float v_scale,
+                              const int32_t* page_table, const int32_t* cu_seqlens_q,
+                              const int32_t* q_start_pos, const int32_t* kv_lens, int batch,
+                              int total_q, int max_q_len, int num_q_heads, int num_kv_heads,
+                              int head_dim, int page_size, int num_pages,
+                              int max_pages_per_seq, int max_kv_len, int keys_per_split,
+                              float softmax_scale, const float* sinks, void* workspace,
+                              size_t workspace_bytes, void* out, int out_dtype, float* lse,
+                              hipStream_t stream);
+
+/*
  * Bytes of device workspace attn_decode_splitk needs for these sizes: fp32
  * partial outputs plus (m, l) for up to 4 partials per split, per query head
  * and sequence (valid for either KV dtype).  keys_per_split = 0 selects the

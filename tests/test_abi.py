@@ -160,6 +160,44 @@ def test_prefill_ex_validation(L):
     assert pf(total_q=0, max_q_len=0) == 0
 
 
+def test_prefill_splitk_validation(L):
+    def pf(**over):
+        a = dict(kvd=0, ks=1.0, vs=1.0, batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=512,
+                 page=64, max_pages=4, max_kv=256, kps=64, ws=FAKE, ws_bytes=16, out_dtype=1)
+        a.update(over)
+        return L.attn_prefill_hd512_splitk(
+            FAKE, FAKE, FAKE, a["kvd"], a["ks"], a["vs"], FAKE, FAKE, FAKE, FAKE, a["batch"],
+            a["total_q"], a["max_q_len"], a["hq"], a["hkv"], a["d"], a["page"], 4,
+            a["max_pages"], a["max_kv"], a["kps"], 0.04, None, a["ws"], a["ws_bytes"], FAKE,
+            a["out_dtype"], None, None)
+    assert pf() == 4                       # four 64-key ranges need a workspace
+    assert pf(ws=None) == 4
+    assert pf(kps=100) == 2                # not a multiple of 64
+    assert pf(kps=-64) == 2
+    assert pf(max_kv=0) == 2
+    assert pf(max_kv=257) == 2             # beyond max_pages * 64
+    assert pf(kvd=1) == 3
+    assert pf(kvd=2, ks=0.0) == 2
+    assert pf(d=256) == 3
+    assert pf(total_q=0, max_q_len=0) == 0
+
+
+def test_prefill_splitk_workspace_size(L):
+    f = L.attn_prefill_hd512_splitk_workspace_size
+    # 512 rows x g = 8 -> 32 row blocks x 4 KV heads = 128 workgroups; two
+    # ranges fill the 256 compute units in one round
+    assert f(1, 512, 512, 32, 4, 32768, 0) == 2 * 512 * 32 * (512 + 2) * 4
+    # 256 rows: 64 workgroups, four ranges
+    assert f(1, 256, 256, 32, 4, 32768, 0) == 4 * 256 * 32 * (512 + 2) * 4
+    assert f(1, 512, 512, 32, 4, 32768, 4096) == 8 * 512 * 32 * (512 + 2) * 4
+    assert f(1, 512, 600, 32, 4, 32768, 4096) == 8 * 600 * 32 * (512 + 2) * 4
+    # enough workgroups already: a single pass, no workspace
+    assert f(1, 8192, 8192, 32, 4, 16384, 0) == 0
+    assert f(1, 512, 512, 32, 4, 32768, 32768) == 0
+    assert f(1, 512, 512, 32, 4, 32768, 100) == 0      # invalid: not a multiple of 64
+    assert f(1, 512, 256, 32, 4, 32768, 0) == 0        # invalid: total_q < max_q_len
+
+
 def test_append_validation(L):
     def ap(**over):
         a = dict(kn=FAKE, kvd=0, ks=1.0, vs=1.0, batch=1, total_q=4, hkv=2, d=512, page=64,
