@@ -53,6 +53,8 @@ constexpr int kRowsPerWaveLoad = kPage / kWaves;  // tile rows each wave moves
 // Largest allowed excess (log2 units) of a row's scores over its reference
 // maximum: p <= 2^32 and l <= 2^32 * keys stay far inside fp32 and bf16.
 constexpr float kRescaleMargin = 32.f;
+constexpr float kOverSum = 4294967296.f;   // 2^kRescaleMargin
+constexpr float kBlindRaise = 123.f;       // log2(FLT_MAX / 32), rounded down
 constexpr int kPrefetch = 4;  // LDS operand reads in flight ahead of their MFMA
 // FP8 operands are widened in registers; one fewer read in flight keeps the
 // FP8 kernel inside the 256 VGPRs
@@ -188,21 +190,21 @@ struct SoftmaxCtx {
     float neg_m_ref;  // -m_ref
 };
 
-// One softmax element: p = 2^(s * scale - m_ref) (0 for masked keys).  Tracks
-// the lane's running maximum of the raw scores (the scale is positive, so the
-// scaled maximum is mx * scale) and its sum; packs p into the P^T operand.
+// One softmax element: p = 2^(s * scale - m_ref) (0 for masked keys).  Adds p
+// to the lane's running sum and packs it into the P^T operand.  No running
+// maximum is kept: the sum bounds every p of the tile, which is all the
+// reference check needs.
 // The empty asms pin the element to the MFMA step it is issued with (inputs
 // taken and running values produced inside the step): without them, IR
 // passes gather the softmax arithmetic into one cluster after the MFMA chain
 // and the matrix core idles while it runs.
-__device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float s, int i, float& mx,
-                                             float& psum, bf16x8& pf) {
+__device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float s, int i, float& psum,
+                                             bf16x8& pf) {
     asm volatile("" : "+v"(s));
-    mx = fmaxf(mx, s);
     const float p = fast_exp2(__builtin_fmaf(s, c.scale_log2, c.neg_m_ref));
     psum += p;
     pf[i & 7] = (__bf16)p;
-    asm volatile("" : "+v"(mx), "+v"(psum));
+    asm volatile("" : "+v"(psum));
 }
 
 // Masks one block's raw scores in place: element i is key
@@ -277,8 +279,7 @@ struct VReader8 {
 template <bool OVERLAP, bool FP8>
 __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[32],
                                          const ATTN_LDS char* sK, const int (&koff)[8],
-                                         const f32x16& sp, const SoftmaxCtx& c, float& mx,
-                                         float& psum, bf16x8& pf0, bf16x8& pf1,
+                                         const f32x16& sp, const SoftmaxCtx& c, float& psum, bf16x8& pf0, bf16x8& pf1,
                                          const HalfDma& dma, int lane_off, int lane, int wave) {
     // bf16: step ks reads chunk 2 ks + h of key row 32 kb + n; with ks = 8 u + v
     // the byte offset is koff[v] + 256 u + 32 KiB kb.  FP8: bytes 16 ks + 8 h of
@@ -316,7 +317,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[3
         }
         if constexpr (OVERLAP && (ks & 1)) {
             constexpr int i = ks >> 1;
-            softmax_elem(c, sp[i], i, mx, psum, i < 8 ? pf0 : pf1);
+            softmax_elem(c, sp[i], i, psum, i < 8 ? pf0 : pf1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -331,7 +332,7 @@ template <bool FIRST, bool OVERLAP, bool FP8, typename VR>
 __device__ __forceinline__ void pv_block(f32x16 (&o)[16], int kb, const bf16x8& p0,
                                          const bf16x8& p1, const ATTN_LDS char* sV,
                                          const VR& vr, const f32x16& sn,
-                                         const SoftmaxCtx& c, float& mx, float& psum,
+                                         const SoftmaxCtx& c, float& psum,
                                          bf16x8& pn0, bf16x8& pn1, const HalfDma& dma,
                                          int lane_off, int lane, int wave) {
     const int base = 32 * kb;   // steps 32 kb .. 32 kb + 31 of the tile
@@ -354,7 +355,7 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[16], int kb, const bf16x8& 
         }
         if constexpr (OVERLAP && (st & 1)) {
             constexpr int i = st >> 1;
-            softmax_elem(c, sn[i], i, mx, psum, i < 8 ? pn0 : pn1);
+            softmax_elem(c, sn[i], i, psum, i < 8 ? pn0 : pn1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -445,14 +446,16 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // Online softmax with a fixed per-row reference maximum: p = 2^(x - m_ref)
     // where m_ref is the row's maximum over its first 32 keys.  O and l carry
     // the same factor 2^(m_true - m_ref), which cancels in O / l.  A row whose
-    // scores climb more than kRescaleMargin above m_ref would push p past
-    // 2^kRescaleMargin, so the workgroup then restarts its key loop with every
-    // row's reference raised to the maximum seen so far: the rescale of O is
-    // replaced by a recompute that typical inputs never trigger.  This keeps
-    // the 256 O accumulators (AGPRs, which VALU cannot address) out of all
-    // VALU code in the loop.
+    // scores climb more than kRescaleMargin above m_ref pushes a lane's tile
+    // sum of p past 2^kRescaleMargin, and the workgroup then restarts its key
+    // loop with every row's reference raised by log2 of its largest tile sum
+    // so far (which bounds every p seen from above and exceeds the largest p
+    // by at most 32x): the rescale of O is replaced by a recompute that
+    // typical inputs never trigger.  This keeps the 256 O accumulators (AGPRs,
+    // which VALU cannot address) out of all VALU code in the loop, and the
+    // per-element work to one exp2, one add and a conversion.
     float m_ref = -__builtin_inff();
-    float m_seen = -__builtin_inff();
+    float l_peak = 0.f;   // largest tile sum of p of this lane in the pass
     float l_run = 0.f;
     int restarts = 0;
 
@@ -491,7 +494,6 @@ void prefill_hd512_kernel(PrefillArgs a) {
             const int page_n = more ? page_of(kt + 1) : page;
             const bool mask = key0 + kPage > n_min;   // the tile crosses a row's causal limit
             SoftmaxCtx c0{a.scale_log2, -m_ref};
-            float mx = -__builtin_inff();   // raw-score maximum of the tile
             float psum = 0.f;
             bf16x8 pf[4];
             f32x16 s0, s1;
@@ -503,7 +505,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
                 restart = true;   // a row of tile kt-1 overshot its reference
                 break;
             }
-            qk_block<false, FP8>(s0, 0, qf, sK, koff, s0, c0, mx, psum, pf[0], pf[1],
+            qk_block<false, FP8>(s0, 0, qf, sK, koff, s0, c0, psum, pf[0], pf[1],
                                  half_dma<FP8>(a.v_pages, page, a.num_pages, a.hkv, kvh, valid, sV, 1, wave, true),
                                  lane_off, lane, wave);
             mfma_vgpr_drain(s0);
@@ -525,7 +527,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
             // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill
             wait_vmcnt<2 * kD>();
             lds_barrier();
-            qk_block<true, FP8>(s1, 1, qf, sK, koff, s0, c0, mx, psum, pf[0], pf[1],
+            qk_block<true, FP8>(s1, 1, qf, sK, koff, s0, c0, psum, pf[0], pf[1],
                                 half_dma<FP8>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 0, wave, more),
                                 lane_off, lane, wave);
             mfma_vgpr_drain(s1);
@@ -537,23 +539,22 @@ void prefill_hd512_kernel(PrefillArgs a) {
             const SoftmaxCtx& c1 = c0;
             const HalfDma dk1 = half_dma<FP8>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 1, wave, more);
             if (kt == kt_lo)
-                pv_block<true, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
+                pv_block<true, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
             else
-                pv_block<false, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, mx, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
+                pv_block<false, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
 
             // ---- PV1; V rows 0..31 of tile kt+1 refill
             if (more) wait_vmcnt<2 * kD>(); else wait_vmcnt<0>();
             lds_barrier();
-            pv_block<false, false, FP8>(o, 1, pf[2], pf[3], sV, vr, s1, c1, mx, psum, pf[2], pf[3],
+            pv_block<false, false, FP8>(o, 1, pf[2], pf[3], sV, vr, s1, c1, psum, pf[2], pf[3],
                                         half_dma<FP8>(a.v_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sV, 0, wave, more),
                                         lane_off, lane, wave);
             l_run += psum;
-            mx *= a.scale_log2;
-            m_seen = fmaxf(m_seen, mx);
-            // restart flag of this tile: any row whose scores exceeded
-            // m_ref + margin (non-finite sums included); read after the next
+            l_peak = fmaxf(l_peak, psum);
+            // restart flag of this tile: any lane whose sum of p exceeded
+            // 2^margin (non-finite sums included); read after the next
             // barrier.  The vote runs on every lane, outside the lane-0 store.
-            const bool over = __any(!(mx <= m_ref + kRescaleMargin) || !(psum == psum));
+            const bool over = __any(!(psum <= kOverSum));
             if (lane == 0) sFlag[wave] = over ? 1 : 0;
         }
         if (!restart && ntiles > kt_lo) {
@@ -565,9 +566,15 @@ void prefill_hd512_kernel(PrefillArgs a) {
         ++restarts;
         wait_vmcnt<0>();     // refills still landing in sK / sV
         lds_barrier();
-        // (a row that saw no key keeps its reference; the reference only rises)
-        m_ref = fmaxf(m_ref, fmaxf(m_seen, __shfl_xor(m_seen, 32)));
-        m_seen = m_ref;
+        // by log2 of the row's largest tile sum (>= its largest p); a sum that
+        // overflowed says only that some p passed 2^123, so the reference rises
+        // by that much and the pass may restart again.  Rows that saw no key,
+        // or none above the reference, keep it: the reference only rises.
+        {
+            const float lp = fmaxf(l_peak, __shfl_xor(l_peak, 32));
+            m_ref += !(lp <= 3.0e38f) ? kBlindRaise : (lp > 1.f ? __builtin_log2f(lp) : 0.f);
+        }
+        l_peak = 0.f;
         l_run = 0.f;         // O restarts too: tile 0's P.V overwrites it
     }
 
