@@ -13,7 +13,10 @@ Storage conventions (the boundary's, stated in the C header):
               is one contiguous 64-key tile (the pool is paged at the key-tile
               size, as the pegainfer issue 1051 "Proposed Plan" asks)
   page_table  int32 [batch, max_pages]; logical key j of sequence b lives in
-              page page_table[b][j // 64], slot j % 64
+              page page_table[b][j // 64], slot j % 64; in a ring cache of
+              C = ring_pages * 64 slots (sliding-window layers) key j lives at
+              cache slot j % C instead, i.e. page page_table[b][(j % C) // 64],
+              and only the last C keys are held
 Hostile padding (pegainfer issue 1051, "Acceptance Criteria"; Flash-Decoding
 for MQA in CUDA, "The test that catches what parity misses"): unused page
 slots, spare pages and q padding rows hold NaN; table entries past a
@@ -80,6 +83,12 @@ class PagedCase:
     out_dtype: str              # "bf16" or "fp32"
     launches: List[Launch]
     nan_page: int               # id of an all-NaN page that padding entries point at
+    window: int = 0             # sliding window in keys (0: none)
+    ring_pages: int = 0         # ring cache pages per sequence (0: unbounded cache)
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k_pool.shape[-1])
 
     @property
     def num_pages(self) -> int:
@@ -95,7 +104,7 @@ class PagedCase:
 
     def kv_bytes_per_key_head(self) -> int:
         """Bytes of K plus V per (key, kv head)."""
-        return 2 * HEAD_DIM * (1 if self.kv_dtype == "fp8_e4m3" else 2)
+        return 2 * self.head_dim * (1 if self.kv_dtype == "fp8_e4m3" else 2)
 
     def to(self, device) -> "PagedCase":
         """Copy of the case with every tensor on `device` (same bytes)."""
@@ -130,7 +139,8 @@ def build_case(name: str, *, seqs: Sequence[Tuple[int, int, int]], hq: int, hkv:
                page_size: int = PAGE_SIZE,
                shuffle_pages: bool = True, kv_len_total: Optional[Sequence[int]] = None,
                softmax_scale: Optional[float] = None,
-               page_seed: Optional[int] = None) -> PagedCase:
+               page_seed: Optional[int] = None, head_dim: int = HEAD_DIM,
+               window: int = 0, ring_pages: int = 0) -> PagedCase:
     """Build one paged workload.
 
     seqs: per sequence (q_len, q_start, kv_len) of the (single) launch.  When
@@ -144,8 +154,13 @@ def build_case(name: str, *, seqs: Sequence[Tuple[int, int, int]], hq: int, hkv:
     before rounding.  The CPU generator (page_seed, default seed) draws the page
     permutation.
     Storage rounding is round-to-nearest-even.
+
+    head_dim sets D (512 for the global layers, 256 for sliding-window ones).
+    window is recorded in the case for the consumers.  ring_pages > 0 stores
+    each sequence in a ring of C = ring_pages * page_size slots: key j of the
+    resident band [max(0, L - C), L) at slot j % C, other slots NaN.
     """
-    D, P = HEAD_DIM, page_size
+    D, P = head_dim, page_size
     assert hq % hkv == 0
     if chunks is None:
         chunks = [list(seqs)]
@@ -201,7 +216,10 @@ def build_case(name: str, *, seqs: Sequence[Tuple[int, int, int]], hq: int, hkv:
         raise ValueError(kv_dtype)
 
     # --- pages -------------------------------------------------------------
-    n_pages = [math.ceil(L / P) for L in kv_len_total]
+    if ring_pages:
+        n_pages = [ring_pages] * B
+    else:
+        n_pages = [math.ceil(L / P) for L in kv_len_total]
     n_logical = sum(n_pages)
     num_pages = n_logical + max(1, extra_pages)
     if shuffle_pages:
@@ -227,10 +245,16 @@ def build_case(name: str, *, seqs: Sequence[Tuple[int, int, int]], hq: int, hkv:
             L = src.shape[0]
             if kv_dtype == "bf16":
                 padded = _nan_bf16((n_pages[b] * P, hkv, D), device)
-                padded[:L] = src
+                stored = src
             else:
                 padded = torch.full((n_pages[b] * P, hkv, D), E4M3_NAN_BYTE, dtype=torch.uint8, device=device)
-                padded[:L] = quantize_e4m3(src, scale)
+                stored = quantize_e4m3(src, scale)
+            if ring_pages:
+                C = ring_pages * P
+                j = torch.arange(max(0, L - C), L, device=device)
+                padded[j % C] = stored[j]
+            else:
+                padded[:L] = stored
             pool[idx] = padded.view(n_pages[b], P, hkv, D).permute(0, 2, 1, 3)
         base += n_pages[b]
     del kb, vb
@@ -266,7 +290,8 @@ def build_case(name: str, *, seqs: Sequence[Tuple[int, int, int]], hq: int, hkv:
     return PagedCase(name=name, num_q_heads=hq, num_kv_heads=hkv, softmax_scale=scale,
                      kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale,
                      k_pool=k_pool, v_pool=v_pool, page_table=table.to(device),
-                     out_dtype=out_dtype, launches=launches, nan_page=nan_page)
+                     out_dtype=out_dtype, launches=launches, nan_page=nan_page,
+                     window=window, ring_pages=ring_pages)
 
 
 def decode_lengths(batch: int, lo: int, hi: int, seed: int) -> List[int]:

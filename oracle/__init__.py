@@ -6,12 +6,16 @@ code: the C source here (oracle_attn.c) is the plain fp32 definition, and
 brute.py is an independent float64 brute force for tiny inputs.
 
 Parity status: every function here is pinned by the CPU test suite
-(tests/test_oracle_pins.py, tests/test_oracle_sinks_lse.py) against brute
+(tests/test_oracle_pins.py, tests/test_oracle_sinks_lse.py,
+tests/test_oracle_window.py) against brute
 force, closed forms, a library routine special case (torch's CPU
 scaled_dot_product_attention with an explicit mask) and torch's
 float8_e4m3fn decoding; the log-sum-exp and sink outputs against the float64
 brute force, the equal-scores and single-key closed forms and the split-K
-merge identity.
+merge identity; the sliding window and the ring cache against the float64
+brute force (which de-pages through the ring independently), the window-1
+identity o = V[pos], the q = 0 mean over the band, a window covering every
+key equal to no window, and a wrapped ring equal to the unbounded layout.
 """
 from __future__ import annotations
 
@@ -53,6 +57,8 @@ def lib():
         L.oracle_attn_rows.restype = I
         L.oracle_attn_rows_ex.argtypes = common + [P, P, I64, P, P, I]
         L.oracle_attn_rows_ex.restype = I
+        L.oracle_attn_rows_full.argtypes = common + [I, I, P, P, I64, P, P, I]
+        L.oracle_attn_rows_full.restype = I
         L.oracle_merge_ex.argtypes = [P, P, P, I, I, F, P, P]
         L.oracle_merge_ex.restype = None
         L.oracle_attn_partial.argtypes = common + [I64, I, I, I, P, P, P]
@@ -88,6 +94,12 @@ def _common_args(case, launch_idx: int, keep):
             page_size, float(case.softmax_scale)]
 
 
+def _window_args(case):
+    """(window, ring slots) of a case: 0 for none / an unbounded cache."""
+    ring = int(getattr(case, "ring_pages", 0) or 0)
+    return int(getattr(case, "window", 0) or 0), ring * int(case.k_pool.shape[2])
+
+
 def attend_rows(case, rows: Sequence[int], launch_idx: int = 0,
                 threads: Optional[int] = None) -> np.ndarray:
     """Outputs of the given entries (q_row * Hq + head) as float32 [n, D]."""
@@ -97,7 +109,13 @@ def attend_rows(case, rows: Sequence[int], launch_idx: int = 0,
     r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     out = np.zeros((len(r), D), dtype=np.float32)
     nthreads = threads if threads is not None else (os.cpu_count() or 1)
-    rc = lib().oracle_attn_rows(*args, r.ctypes.data, len(r), out.ctypes.data, int(nthreads))
+    window, ring_slots = _window_args(case)
+    if window or ring_slots:
+        rc = lib().oracle_attn_rows_full(*args, window, ring_slots, None, r.ctypes.data,
+                                         len(r), out.ctypes.data, None, int(nthreads))
+    else:
+        rc = lib().oracle_attn_rows(*args, r.ctypes.data, len(r), out.ctypes.data,
+                                    int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_attn_rows failed with code {rc}")
     return out
@@ -119,9 +137,11 @@ def attend_rows_lse(case, rows: Sequence[int], launch_idx: int = 0,
         snk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32))
         assert snk.shape == (case.num_q_heads,)
     nthreads = threads if threads is not None else (os.cpu_count() or 1)
-    rc = lib().oracle_attn_rows_ex(*args, snk.ctypes.data if snk is not None else None,
-                                   r.ctypes.data, len(r), out.ctypes.data, lse.ctypes.data,
-                                   int(nthreads))
+    window, ring_slots = _window_args(case)
+    rc = lib().oracle_attn_rows_full(*args, window, ring_slots,
+                                     snk.ctypes.data if snk is not None else None,
+                                     r.ctypes.data, len(r), out.ctypes.data, lse.ctypes.data,
+                                     int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_attn_rows_ex failed with code {rc}")
     return out, lse
@@ -146,7 +166,10 @@ def attend_all(case, launch_idx: int = 0, threads: Optional[int] = None) -> np.n
 
 def partial(case, q_row: int, head: int, k0: int, k1: int,
             launch_idx: int = 0) -> Tuple[np.ndarray, float, float]:
-    """Unnormalised (O, m, l) of one row over keys [k0, k1); m in natural-log units."""
+    """Unnormalised (O, m, l) of one row over keys [k0, k1); m in natural-log units
+    (unbounded cache, no window)."""
+    if any(_window_args(case)):
+        raise ValueError("partial() covers the unbounded cache without a window only")
     keep = []
     args = _common_args(case, launch_idx, keep)
     D = args[16]

@@ -1,10 +1,13 @@
 """Float64 brute force for tiny inputs -- TEST INFRASTRUCTURE ONLY.
 
 Independent of oracle_attn.c: it de-pages the pools with numpy indexing into
-dense per-sequence K and V, builds the full score matrix of each (sequence,
-head) with an explicit causal mask aligned at absolute positions, and applies
-softmax and the value product in float64.  It pins the C oracle on small
-shapes; it is far too slow and memory-hungry for the measured workloads.
+dense per-sequence K and V (through the ring when the cache is one: key j at
+slot j % C, keys older than the last C marked NaN), builds the full score
+matrix of each (sequence, head) with an explicit causal mask aligned at
+absolute positions, cut to the last `window` positions when there is a
+window, and applies softmax and the value product in float64.  It pins the C
+oracle on small shapes; it is far too slow and memory-hungry for the measured
+workloads.
 """
 from __future__ import annotations
 
@@ -27,12 +30,18 @@ def depage(case, launch_idx: int = 0) -> List[Tuple[np.ndarray, np.ndarray]]:
     P = int(case.k_pool.shape[2])
     kp = _to_f64(case.k_pool.cpu(), case.kv_dtype, case.k_scale)
     vp = _to_f64(case.v_pool.cpu(), case.kv_dtype, case.v_scale)
+    C = int(getattr(case, "ring_pages", 0) or 0) * P
     out = []
     for b, L in enumerate(lc.kv_lens):
         j = np.arange(L)
-        pages = table[b, j // P]
-        slots = j % P
-        out.append((kp[pages, :, slots, :], vp[pages, :, slots, :]))
+        c = j % C if C else j
+        pages = table[b, c // P]
+        slots = c % P
+        K, V = kp[pages, :, slots, :], vp[pages, :, slots, :]
+        if C and L > C:            # overwritten by later keys of the ring
+            K[:L - C] = np.nan
+            V[:L - C] = np.nan
+        out.append((K, V))
     return out
 
 
@@ -57,6 +66,9 @@ def attention_lse(case, launch_idx: int = 0, sinks=None):
         pos = st + np.arange(ql)[:, None]          # absolute query positions
         keys = np.arange(L)[None, :]
         visible = keys <= pos                         # causal, bottom-right aligned
+        W = int(getattr(case, "window", 0) or 0)
+        if W:
+            visible &= keys > pos - W                  # the last W positions
         for h in range(case.num_q_heads):
             kvh = h // g
             s = (q[row0:row0 + ql, h, :] @ K[:, kvh, :].T) * float(np.float32(case.softmax_scale))
@@ -64,10 +76,12 @@ def attention_lse(case, launch_idx: int = 0, sinks=None):
             if sinks is not None:   # one more softmax column, weight only
                 s = np.concatenate([s, np.full((ql, 1), float(sinks[h]))], axis=1)
             mx = s.max(axis=1, keepdims=True) if s.shape[1] else np.full((ql, 1), -np.inf)
-            ok = np.isfinite(mx[:, 0])
+            ok = ~np.isneginf(mx[:, 0])   # a row with a visible key (NaN stays NaN)
             w = np.exp(s - np.where(np.isfinite(mx), mx, 0.0))
             den = w.sum(axis=1)
-            vals = V[:, kvh, :]
+            # rows the ring no longer holds are NaN: a visible one poisons its
+            # score, a masked one must not leak through a zero weight
+            vals = np.nan_to_num(V[:, kvh, :], nan=0.0)
             num = w[:, :L] @ vals if L else np.zeros((ql, vals.shape[-1]))
             out[row0:row0 + ql, h, :] = np.where(ok[:, None], num / np.where(ok, den, 1.0)[:, None], 0.0)
             lse[row0:row0 + ql, h] = np.where(ok, mx[:, 0] + np.log(np.where(ok, den, 1.0)), -np.inf)

@@ -42,6 +42,18 @@
  * (both evaluated around the larger of max S and s_h).  A row with no visible
  * key gives o = 0 and lse = s_h, or lse = -inf without a sink.
  *
+ * Sliding-window layers and the ring cache (Flash-Decoding for MQA in CUDA,
+ * "One KV head breaks the textbook": the walk is over absolute positions, the
+ * slot of a position is position % capacity, and only the live band
+ * [max(0, len - window), len) is read; A custom attention kernel for Gemma 4
+ * on the RTX PRO 6000, "The deployment": local layers attend to the last
+ * 1,024 tokens).  With a window W a row at pos sees keys
+ *     max(0, pos - W + 1) <= j <= pos,  j < kv_len,
+ * i.e. its own position and the W - 1 before it; with a ring of C slots, key
+ * j is read from slot j % C (page table entry (j % C) / page_size), which
+ * holds it as long as j >= kv_len - C.  W = 0 means no window and C = 0 an
+ * unbounded cache (slot = position).
+ *
  * Precision: inputs are widened exactly (bf16 -> fp32; e4m3 -> fp32, then
  * times the per-tensor scale in fp32); dot products, exponentials and sums
  * run in fp32 in plain sequential order.  Built without -ffast-math.
@@ -103,13 +115,17 @@ typedef struct {
     const int32_t* kv_len;
     int batch, hq, hkv, d, page_size;
     float scale;
+    int window;      /* 0: none */
+    int ring_slots;  /* 0: unbounded cache */
 } problem_t;
 
 /* Index of element 0 of key (or value) row j of sequence b, KV head kvh:
- * logical key j lives in page page_table[b][j / page_size], slot j % page_size. */
+ * logical key j has cache slot c = j (or j % C in a ring of C slots), which
+ * lives in page page_table[b][c / page_size] at offset c % page_size. */
 static int64_t kv_row_index(const problem_t* p, int b, int kvh, int j) {
-    int page = p->page_table[(int64_t)b * p->max_pages + j / p->page_size];
-    int slot = j % p->page_size;
+    int c = p->ring_slots > 0 ? j % p->ring_slots : j;
+    int page = p->page_table[(int64_t)b * p->max_pages + c / p->page_size];
+    int slot = c % p->page_size;
     return (((int64_t)page * p->hkv + kvh) * p->page_size + slot) * p->d;
 }
 
@@ -132,15 +148,16 @@ static int seq_of_row(const problem_t* p, int64_t row) {
 /* Checks every page id a row could read; rejects indexes outside the pool. */
 static int check_problem(const problem_t* p) {
     if (p->batch < 1 || p->hq < 1 || p->hkv < 1 || p->hq % p->hkv || p->d < 1 ||
-        p->page_size < 1 || p->max_pages < 1)
+        p->page_size < 1 || p->max_pages < 1 || p->window < 0 || p->ring_slots < 0)
         return ERR_ARG;
     if (p->cu_seqlens_q[0] != 0) return ERR_ARG;
     for (int b = 0; b < p->batch; ++b) {
         int ql = p->cu_seqlens_q[b + 1] - p->cu_seqlens_q[b];
         int L = p->kv_len[b];
         if (ql < 0 || L < 0 || p->q_start[b] < 0) return ERR_ARG;
-        if ((L + p->page_size - 1) / p->page_size > p->max_pages) return ERR_INDEX;
-        for (int j = 0; j < (L + p->page_size - 1) / p->page_size; ++j) {
+        int slots = p->ring_slots > 0 && p->ring_slots < L ? p->ring_slots : L;
+        if ((slots + p->page_size - 1) / p->page_size > p->max_pages) return ERR_INDEX;
+        for (int j = 0; j < (slots + p->page_size - 1) / p->page_size; ++j) {
             int pg = p->page_table[(int64_t)b * p->max_pages + j];
             if (pg < 0 || pg >= p->num_pages) return ERR_INDEX;
         }
@@ -161,6 +178,7 @@ static void row_partial(const problem_t* p, int64_t row, int h, int k0, int k1, 
     int pos = p->q_start[b] + i;
     int L = p->kv_len[b];
     int n = pos + 1 < L ? pos + 1 : L;
+    int lo = p->window > 0 && pos - p->window + 1 > 0 ? pos - p->window + 1 : 0;
     int kvh = h / (p->hq / p->hkv);
     const uint16_t* qrow = p->q + (row * p->hq + h) * (int64_t)p->d;
     if (k1 > L) k1 = L;
@@ -168,7 +186,7 @@ static void row_partial(const problem_t* p, int64_t row, int h, int k0, int k1, 
 
     /* scores, materialised over the whole range (masked entries -inf) */
     for (int j = k0; j < k1; ++j) {
-        if (j < n) {
+        if (j >= lo && j < n) {
             int64_t kr = kv_row_index(p, b, kvh, j);
             float dot = 0.0f;
             for (int d = 0; d < p->d; ++d)
@@ -193,8 +211,8 @@ static void row_partial(const problem_t* p, int64_t row, int h, int k0, int k1, 
         S[j - k0] = e;
         l += e;
     }
-    /* masked keys (j >= n) have weight exactly zero and are left out */
-    for (int j = k0; j < (k1 < n ? k1 : n); ++j) {
+    /* masked keys (j < lo, j >= n) have weight exactly zero and are left out */
+    for (int j = (k0 > lo ? k0 : lo); j < (k1 < n ? k1 : n); ++j) {
         float e = S[j - k0];
         int64_t vr = kv_row_index(p, b, kvh, j);
         for (int d = 0; d < p->d; ++d)
@@ -207,7 +225,7 @@ static void row_partial(const problem_t* p, int64_t row, int h, int k0, int k1, 
 #define FILL_PROBLEM                                                                     \
     problem_t p = {q, q_rows, k_pool, v_pool, kv_format, k_scale, v_scale, page_table,   \
                    max_pages, num_pages, cu_seqlens_q, q_start, kv_len, batch, hq, hkv,  \
-                   head_dim, page_size, softmax_scale};
+                   head_dim, page_size, softmax_scale, 0, 0};
 
 /* Normalises one row's (O, m, l) with an optional sink logit (NAN = none):
  * writes o[d] and, when lse is not NULL, the log-sum-exp. */
@@ -233,15 +251,17 @@ static void finish_row(const float* O, float m, float l, float sink, int d_len, 
  * or -inf).  Returns 0, or an error code without writing anything when an
  * argument or a page id is out of range.
  */
-int oracle_attn_rows_ex(const uint16_t* q, int64_t q_rows, const void* k_pool,
-                        const void* v_pool, int kv_format, float k_scale, float v_scale,
-                        const int32_t* page_table, int max_pages, int num_pages,
-                        const int32_t* cu_seqlens_q, const int32_t* q_start,
-                        const int32_t* kv_len, int batch, int hq, int hkv, int head_dim,
-                        int page_size, float softmax_scale, const float* sinks,
-                        const int64_t* rows, int64_t n_rows, float* out, float* lse,
-                        int num_threads) {
+int oracle_attn_rows_full(const uint16_t* q, int64_t q_rows, const void* k_pool,
+                          const void* v_pool, int kv_format, float k_scale, float v_scale,
+                          const int32_t* page_table, int max_pages, int num_pages,
+                          const int32_t* cu_seqlens_q, const int32_t* q_start,
+                          const int32_t* kv_len, int batch, int hq, int hkv, int head_dim,
+                          int page_size, float softmax_scale, int window, int ring_slots,
+                          const float* sinks, const int64_t* rows, int64_t n_rows, float* out,
+                          float* lse, int num_threads) {
     FILL_PROBLEM
+    p.window = window;
+    p.ring_slots = ring_slots;
     int rc = check_problem(&p);
     if (rc) return rc;
     int total_q = cu_seqlens_q[batch];
@@ -276,6 +296,21 @@ int oracle_attn_rows_ex(const uint16_t* q, int64_t q_rows, const void* k_pool,
         free(O);
     }
     return failed ? ERR_NOMEM : OK;
+}
+
+/* oracle_attn_rows_full without a window, over an unbounded cache. */
+int oracle_attn_rows_ex(const uint16_t* q, int64_t q_rows, const void* k_pool,
+                        const void* v_pool, int kv_format, float k_scale, float v_scale,
+                        const int32_t* page_table, int max_pages, int num_pages,
+                        const int32_t* cu_seqlens_q, const int32_t* q_start,
+                        const int32_t* kv_len, int batch, int hq, int hkv, int head_dim,
+                        int page_size, float softmax_scale, const float* sinks,
+                        const int64_t* rows, int64_t n_rows, float* out, float* lse,
+                        int num_threads) {
+    return oracle_attn_rows_full(q, q_rows, k_pool, v_pool, kv_format, k_scale, v_scale,
+                                 page_table, max_pages, num_pages, cu_seqlens_q, q_start,
+                                 kv_len, batch, hq, hkv, head_dim, page_size, softmax_scale, 0,
+                                 0, sinks, rows, n_rows, out, lse, num_threads);
 }
 
 /* oracle_attn_rows_ex without sinks and without the log-sum-exp. */
