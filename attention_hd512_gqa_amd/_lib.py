@@ -44,6 +44,9 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_hd512_ex.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I, I,
                                             I, I, F, P, P, I, P, P]
         L.attn_prefill_hd512_ex.restype = I
+        L.attn_prefill_swa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, F,
+                                       P, I, P]
+        L.attn_prefill_swa.restype = I
         L.attn_prefill_hd512_splitk_workspace_size.argtypes = [I, I, I, I, I, I, I]
         L.attn_prefill_hd512_splitk_workspace_size.restype = SZ
         L.attn_prefill_hd512_splitk.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I,
@@ -144,6 +147,28 @@ def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out
             _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.uint8),
             _dev(v_pages, "v_pages", torch.uint8), float(k_scale), float(v_scale), *meta)
         _check(code, "attn_prefill_hd512_e4m3")
+
+
+def prefill_swa(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out, *,
+                total_q: int, max_q_len: int, softmax_scale: float, window: int,
+                ring_pages: int = 0, stream=None) -> None:
+    """Chunked causal prefill of a sliding-window layer (attn_prefill_swa): a
+    row at position p sees keys max(0, p - window + 1) .. p (window 0: no
+    window), over a bf16 pool of head dim 256 or 512, optionally a ring cache
+    of ring_pages pages per sequence (key j at slot j % (64 ring_pages))."""
+    num_pages, hkv, page, d = k_pages.shape
+    hq = q.shape[1]
+    batch = kv_lens.shape[0]
+    code = lib().attn_prefill_swa(
+        _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", torch.bfloat16),
+        _dev(v_pages, "v_pages", torch.bfloat16), _dev(page_table, "page_table", torch.int32),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(q_start, "q_start", torch.int32),
+        _dev(kv_lens, "kv_lens", torch.int32), int(batch), int(total_q), int(max_q_len),
+        int(hq), int(hkv), int(d), int(page), int(num_pages), int(page_table.shape[1]),
+        int(window), int(ring_pages), float(softmax_scale),
+        _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
+        _stream(stream))
+    _check(code, "attn_prefill_swa")
 
 
 def prefill_splitk_workspace_size(batch: int, max_q_len: int, total_q: int, num_q_heads: int,

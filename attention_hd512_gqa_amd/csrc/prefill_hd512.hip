@@ -68,14 +68,20 @@ constexpr int kPagesInLds = 4096;
 // cannot loop forever; each genuine restart raises a row's reference by > 32.
 constexpr int kMaxRestarts = 8;
 
-// K/V pool element: bf16 (1 KB key rows) or FP8-E4M3 bytes (512-byte rows).
-template <bool FP8>
+// K/V tile geometry for a pool element (bf16, or FP8-E4M3 bytes) and a head
+// dim D (512 for the global layers, 256 for the sliding-window ones).  Rows
+// are 1 KB (bf16 at 512) or 512 bytes (FP8 at 512, bf16 at 256: "narrow").
+template <bool FP8, int D = kHeadDim>
 struct Kv {
-    static constexpr int kRowB = FP8 ? kHeadDim : kRowBytes;
+    static_assert(D == 512 || (D == 256 && !FP8), "head dims 512 (bf16, FP8) and 256 (bf16)");
+    static constexpr int kRowB = FP8 ? D : 2 * D;
     static constexpr int kTileB = kPage * kRowB;
-    // buffer->LDS loads per wave per 32-key half refill: 8 bf16 rows of 1 KB,
-    // or 4 loads of two 512-byte FP8 rows
-    static constexpr int kDmaPerHalf = FP8 ? 4 : 8;
+    static constexpr bool kNarrow = kRowB == 512;
+    // buffer->LDS loads per wave per 32-key half refill: 8 rows of 1 KB, or 4
+    // loads of two 512-byte rows
+    static constexpr int kDmaPerHalf = kNarrow ? 4 : 8;
+    static constexpr int kSteps = D / 16;       // Q.K^T MFMAs (k-steps) per 32-key block
+    static constexpr int kDimBlocks = D / 32;   // 32-dim output blocks (P.V MFMAs per k-step)
 };
 
 // LDS layout of an FP8 tile: row r (a key) is 512 bytes, its 16-byte chunk c
@@ -83,6 +89,16 @@ struct Kv {
 // chunk) and the transposed V reads (8 rows per 16-lane group at one chunk)
 // then hit distinct chunks.
 __host__ __device__ constexpr int swz8(int r) { return r & 31; }
+
+// LDS layout of a bf16 head-dim-256 tile: row r is 512 bytes, its 16-byte
+// chunk c sits at chunk c ^ swzN(r).  swzN swaps the two 2-bit fields of r's
+// low nibble (bit 4 kept): a bijection on r mod 16, so 16 consecutive rows
+// at one chunk (the K operand reads) hit distinct bank groups, and its bits
+// 2..3 separate the 4 rows of an aligned quad, so a transposed V read (4 rows
+// x 4 chunks per half wave) does too.
+__host__ __device__ constexpr int swzN(int r) {
+    return ((r & 3) << 2) | ((r >> 2) & 3) | (r & 16);
+}
 
 struct PrefillArgs {
     const __bf16* q;
@@ -105,6 +121,8 @@ struct PrefillArgs {
     int nsplit, split_tiles;
     float* part_o;      // [nsplit][total_q][hq][512] fp32, O * v_scale
     float* part_ml;     // [nsplit][total_q][hq][2]  (m in log2 units, l)
+    int window;         // sliding window in keys (0: none)
+    int ring_pages;     // ring cache pages per sequence (0: unbounded cache)
 };
 
 // Refill of one 32-key half (rows 32 half .. 32 half + 31) of a K or V tile
@@ -120,13 +138,13 @@ struct HalfDma {
     bool on;            // wave-uniform: this refill exists
 };
 
-template <bool FP8>
+template <bool FP8, int D>
 __device__ __forceinline__ HalfDma half_dma(const char* pool, int page, int num_pages, int hkv,
                                             int kvh, int valid, const ATTN_LDS char* buf,
                                             int half, int wave, bool on) {
-    constexpr int kRowB = Kv<FP8>::kRowB;
+    constexpr int kRowB = Kv<FP8, D>::kRowB;
     page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
-    const char* src = pool + ((size_t)page * hkv + kvh) * (size_t)Kv<FP8>::kTileB;
+    const char* src = pool + ((size_t)page * hkv + kvh) * (size_t)Kv<FP8, D>::kTileB;
     HalfDma d;
     d.rsrc = buffer_rsrc(src, (uint32_t)(valid > 0 ? valid : 0) * kRowB);
     d.soff = (uint32_t)__builtin_amdgcn_readfirstlane((32 * half + 8 * wave) * kRowB);
@@ -147,26 +165,27 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t m0, uint32_t soff, in
         : "memory", "m0");
 }
 
-// Refill load J of this wave's share of a half: bf16, row 8 wave + J of the
-// half (one 1 KB row); FP8, rows 8 wave + 2 J and + 1 (lanes 0-31 and 32-63),
+// Refill load J of this wave's share of a half: 1 KB rows, row 8 wave + J of
+// the half; narrow rows, rows 8 wave + 2 J and + 1 (lanes 0-31 and 32-63),
 // each lane fetching the logical chunk that the swizzle stores at its LDS
-// position: chunk (lane % 32) ^ swz8(row).
-template <bool FP8, int J>
+// position: chunk (lane % 32) ^ swz8(row) (FP8) or ^ swzN(row) (bf16 at 256).
+template <bool FP8, int D, int J>
 __device__ __forceinline__ void half_dma_row(const HalfDma& d, int lane_off, int lane, int wave) {
-    if constexpr (FP8) {
+    if constexpr (Kv<FP8, D>::kNarrow) {
         const int rw = 2 * J + (lane >> 5);            // row within the wave's 8
-        const int f = (8 * wave + rw) & 31;            // swz8 of the tile row (32 half is 0 mod 32)
-        const int voff = rw * kHeadDim + (((lane & 31) ^ f) << 4);
-        dma16(d.rsrc, d.lds_base + 2 * J * kHeadDim, d.soff, voff);
+        const int tr = 8 * wave + rw;                  // tile row mod 32 (32 half is 0 mod 32)
+        const int f = FP8 ? swz8(tr) : swzN(tr);
+        const int voff = rw * 512 + (((lane & 31) ^ f) << 4);
+        dma16(d.rsrc, d.lds_base + 2 * J * 512, d.soff, voff);
     } else {
         dma_row<(swz(J) << 4), J * kRowBytes>(d.rsrc, d.lds_base, d.soff, lane_off);
     }
 }
 
-template <bool FP8>
+template <bool FP8, int D>
 __device__ __forceinline__ void half_dma_all(const HalfDma& d, int lane_off, int lane, int wave) {
-    static_for<Kv<FP8>::kDmaPerHalf>([&](auto J) {
-        half_dma_row<FP8, decltype(J)::value>(d, lane_off, lane, wave);
+    static_for<Kv<FP8, D>::kDmaPerHalf>([&](auto J) {
+        half_dma_row<FP8, D, decltype(J)::value>(d, lane_off, lane, wave);
     });
 }
 
@@ -208,17 +227,36 @@ __device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float s, int i
 }
 
 // Masks one block's raw scores in place: element i is key
-// key_base + 8(i/4) + (i%4) (key_base includes 4h); keys >= n_row get -inf.
-__device__ __forceinline__ void mask_block(f32x16& s, int key_base, int n_row) {
+// key_base + 8(i/4) + (i%4) (key_base includes 4h); keys >= n_row get -inf,
+// and with a window so do keys < lo_row.
+template <bool WINDOW>
+__device__ __forceinline__ void mask_block(f32x16& s, int key_base, int n_row, int lo_row) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int key = key_base + 8 * (i >> 2) + (i & 3);
-        s[i] = key < n_row ? s[i] : -__builtin_inff();
+        const bool vis = WINDOW ? (key < n_row && key >= lo_row) : key < n_row;
+        s[i] = vis ? s[i] : -__builtin_inff();
     }
 }
 
-// V^T operand reader for the P.V MFMAs: step = 16 c + db reads keys
-// 16c + 8(j/4) + 4h + (j%4) (j = operand slot) of output-dim block db.
+// Sliding window: a row's reference maximum is the maximum of the first
+// 32-key block in which it sees a key (rows start their windows at different
+// keys, so the workgroup's first block may be empty for some).  Until then
+// m_ref stays -inf and p = 2^(s - 0) = 0 for its (masked) scores.
+__device__ __forceinline__ void lazy_reference(const f32x16& s, float scale_log2, float& m_ref,
+                                               SoftmaxCtx& c) {
+    if (__builtin_amdgcn_ballot_w64(m_ref == -__builtin_inff()) == 0) return;
+    float m0 = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s[i]);
+    m0 = fmaxf(m0, __shfl_xor(m0, 32)) * scale_log2;
+    if (m_ref == -__builtin_inff()) m_ref = m0;
+    c.neg_m_ref = m_ref == -__builtin_inff() ? 0.f : -m_ref;
+}
+
+// V^T operand reader for the P.V MFMAs (bf16, 1 KB rows): k-step c of the
+// tile and dim block db read keys 16c + 8(j/4) + 4h + (j%4) (j = operand
+// slot) of output dims 32 db .. 32 db + 31.
 struct VReader {
     int voffA[4], voffB[4];
     __device__ __forceinline__ explicit VReader(int lane) {
@@ -237,11 +275,38 @@ struct VReader {
             voffB[w] = (krow + 8) * kRowBytes + (((4 * w + cb) ^ swz(krow + 8)) << 4) + within;
         }
     }
-    __device__ __forceinline__ bf16x8 read(const ATTN_LDS char* sV, int step) const {
-        const int c = step >> 4, db = step & 15;
+    __device__ __forceinline__ bf16x8 read(const ATTN_LDS char* sV, int c, int db) const {
         const int rel = 16 * c * kRowBytes + 256 * (db >> 2);  // swz(16c + k) == swz(k)
         const bf16x4 va = lds_read_tr16(sV + voffA[db & 3] + rel);
         const bf16x4 vb = lds_read_tr16(sV + voffB[db & 3] + rel);
+        return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+// The same reader for bf16 head-dim-256 tiles (512-byte rows, swzN): the lane
+// reads chunk 4 db + cb of rows krow (+ 8) + 16 c.  krow < 16, so the row's
+// swizzle is swzN(krow) ^ 16 (c % 2); with cb < 4 the chunk field is
+// (4 db) ^ (cb ^ swizzle), so one address per parity of c takes the dim block
+// by XOR (bits 6..8) and the k-step by adding 16 rows.
+struct VReaderN {
+    int offA[2], offB[2];
+    __device__ __forceinline__ explicit VReaderN(int lane) {
+        const int h = lane >> 5;
+        const int grp = lane & 15;
+        const int dsub = (lane >> 4) & 1;
+        const int krow = 4 * h + (grp >> 2);
+        const int cb = 2 * dsub + ((grp & 3) >> 1);
+        const int within = 8 * (grp & 1);
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            offA[par] = krow * 512 + within + ((cb ^ swzN(krow) ^ (16 * par)) << 4);
+            offB[par] = (krow + 8) * 512 + within + ((cb ^ swzN(krow + 8) ^ (16 * par)) << 4);
+        }
+    }
+    __device__ __forceinline__ bf16x8 read(const ATTN_LDS char* sV, int c, int db) const {
+        const int rel = 16 * c * 512;
+        const bf16x4 va = lds_read_tr16(sV + ((offA[c & 1] ^ (64 * db)) + rel));
+        const bf16x4 vb = lds_read_tr16(sV + ((offB[c & 1] ^ (64 * db)) + rel));
         return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 };
@@ -265,42 +330,48 @@ struct VReader8 {
             w[par] = vbase | ((((G & 1) ^ swz8(k0 + 16 * par))) << 4);
     }
     // raw E4M3 bytes of the operand (widened to bf16 just before the MFMA)
-    __device__ __forceinline__ v2i32 read(const ATTN_LDS char* sV, int step) const {
-        const int c = step >> 4, db = step & 15;
+    __device__ __forceinline__ v2i32 read(const ATTN_LDS char* sV, int c, int db) const {
         return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (ATTN_LDS v2i32*)(sV + 16 * c * kHeadDim + (w[c & 1] ^ (2 * db << 4))));
     }
 };
 
-// Q.K^T of one 32-key block kb: 32 MFMAs (VGPR accumulator) over the 32
-// k-steps of head_dim.  When OVERLAP, one softmax element of the previous
-// block's scores `sp` is computed after every other MFMA; the half-tile
-// refill `dma` issues one row load after every fourth MFMA.
-template <bool OVERLAP, bool FP8>
-__device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[32],
+// Q.K^T of one 32-key block kb: D / 16 MFMAs (VGPR accumulator) over the
+// k-steps of head_dim.  When OVERLAP, the 16 softmax elements of the previous
+// block's scores `sp` are spread evenly over the MFMAs (one after every other
+// at D = 512, one after each at 256); the half-tile refill `dma` issues one
+// row load after every fourth MFMA.
+template <bool OVERLAP, bool FP8, int D>
+__device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(Kv<FP8, D>::kSteps)],
                                          const ATTN_LDS char* sK, const int (&koff)[8],
                                          const f32x16& sp, const SoftmaxCtx& c, float& psum, bf16x8& pf0, bf16x8& pf1,
                                          const HalfDma& dma, int lane_off, int lane, int wave) {
-    // bf16: step ks reads chunk 2 ks + h of key row 32 kb + n; with ks = 8 u + v
-    // the byte offset is koff[v] + 256 u + 32 KiB kb.  FP8: bytes 16 ks + 8 h of
-    // row 32 kb + n, chunk ks at ks ^ n: koff[0] ^ (16 ks) + 16 KiB kb.
-    // FP8 operands are prefetched as raw bytes and widened at their MFMA
+    // bf16 at 512: step ks reads chunk 2 ks + h of key row 32 kb + n; with
+    // ks = 8 u + v the byte offset is koff[v] + 256 u + 32 KiB kb.  bf16 at
+    // 256: chunk (2 ks + h) ^ swzN(n) = (2 ks) ^ (h ^ swzN(n)): koff[0] ^ (32 ks)
+    // + 16 KiB kb.  FP8: bytes 16 ks + 8 h of row 32 kb + n, chunk ks at
+    // ks ^ n: koff[0] ^ (16 ks) + 16 KiB kb.  FP8 operands are prefetched as
+    // raw bytes and widened at their MFMA.
+    constexpr int kSteps = Kv<FP8, D>::kSteps;
     using Raw = typename std::conditional<FP8, v2i32, bf16x8>::type;
     auto kread = [&](int ks) -> Raw {
         if constexpr (FP8)
-            return *(const ATTN_LDS v2i32*)(sK + (koff[0] ^ (ks << 4)) + kb * 32 * kHeadDim);
+            return *(const ATTN_LDS v2i32*)(sK + (koff[0] ^ (ks << 4)) + kb * 32 * 512);
+        else if constexpr (Kv<FP8, D>::kNarrow)
+            return *(const ATTN_LDS bf16x8*)(sK + (koff[0] ^ (ks << 5)) + kb * 32 * 512);
         else
             return *(const ATTN_LDS bf16x8*)(sK + koff[ks & 7] + 256 * (ks >> 3) +
                                               kb * 32 * kRowBytes);
     };
-    constexpr int kDmaEvery = 32 / Kv<FP8>::kDmaPerHalf;
+    constexpr int kDmaEvery = kSteps / Kv<FP8, D>::kDmaPerHalf;
+    constexpr int kSmEvery = kSteps / 16;
     Raw kbuf[kPrefetchOf<FP8>];
 #pragma unroll
     for (int j = 0; j < kPrefetchOf<FP8>; ++j) kbuf[j] = kread(j);
-    static_for<32>([&](auto KS) {
+    static_for<kSteps>([&](auto KS) {
         constexpr int ks = decltype(KS)::value;
         const bf16x8 cur = operand(kbuf[ks % kPrefetchOf<FP8>]);
-        if (ks + kPrefetchOf<FP8> < 32) kbuf[ks % kPrefetchOf<FP8>] = kread(ks + kPrefetchOf<FP8>);
+        if (ks + kPrefetchOf<FP8> < kSteps) kbuf[ks % kPrefetchOf<FP8>] = kread(ks + kPrefetchOf<FP8>);
         if constexpr (FP8) {   // cur was just written by the widening VALU ops
             if constexpr (ks == 0)
                 mfma32x32x16_vgpr_first_va(s, cur, qf[0]);
@@ -313,59 +384,65 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[3
                 mfma32x32x16_vgpr(s, cur, qf[ks]);
         }
         if constexpr (ks % kDmaEvery == 0) {
-            if (dma.on) half_dma_row<FP8, ks / kDmaEvery>(dma, lane_off, lane, wave);
+            if (dma.on) half_dma_row<FP8, D, ks / kDmaEvery>(dma, lane_off, lane, wave);
         }
-        if constexpr (OVERLAP && (ks & 1)) {
-            constexpr int i = ks >> 1;
+        if constexpr (OVERLAP && (ks % kSmEvery == kSmEvery - 1)) {
+            constexpr int i = ks / kSmEvery;
             softmax_elem(c, sp[i], i, psum, i < 8 ? pf0 : pf1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
 }
 
-// P.V of one 32-key block (k-steps c = 2 kb, 2 kb + 1, all 16 dim blocks).
-// FIRST: the tile's first k-step starts O from zero (inline c = 0), so O is
-// only ever written by MFMAs.  When OVERLAP, one softmax element of the next
-// block's scores `sn` is computed after every other MFMA; the half-tile
-// refill `dma` issues one row load after every fourth MFMA.
-template <bool FIRST, bool OVERLAP, bool FP8, typename VR>
-__device__ __forceinline__ void pv_block(f32x16 (&o)[16], int kb, const bf16x8& p0,
-                                         const bf16x8& p1, const ATTN_LDS char* sV,
-                                         const VR& vr, const f32x16& sn,
+// P.V of one 32-key block (k-steps c = 2 kb, 2 kb + 1 of the tile, all D / 32
+// dim blocks).  FIRST: the tile's first k-step starts O from zero (inline
+// c = 0), so O is only ever written by MFMAs.  When OVERLAP, the 16 softmax
+// elements of the next block's scores `sn` are spread evenly over the MFMAs;
+// the half-tile refill `dma` issues one row load after every fourth MFMA.
+template <bool FIRST, bool OVERLAP, bool FP8, int D, typename VR>
+__device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], int kb,
+                                         const bf16x8& p0, const bf16x8& p1,
+                                         const ATTN_LDS char* sV, const VR& vr, const f32x16& sn,
                                          const SoftmaxCtx& c, float& psum,
                                          bf16x8& pn0, bf16x8& pn1, const HalfDma& dma,
                                          int lane_off, int lane, int wave) {
-    const int base = 32 * kb;   // steps 32 kb .. 32 kb + 31 of the tile
-    constexpr int kDmaEvery = 32 / Kv<FP8>::kDmaPerHalf;
+    constexpr int kDB = Kv<FP8, D>::kDimBlocks;
+    constexpr int kMfma = 2 * kDB;
+    constexpr int kDmaEvery = kMfma / Kv<FP8, D>::kDmaPerHalf;
+    constexpr int kSmEvery = kMfma / 16;
     using Raw = typename std::conditional<FP8, v2i32, bf16x8>::type;
+    auto vread = [&](int st) -> Raw { return vr.read(sV, 2 * kb + st / kDB, st % kDB); };
     Raw vbuf[kPrefetchOf<FP8>];
 #pragma unroll
-    for (int j = 0; j < kPrefetchOf<FP8>; ++j) vbuf[j] = vr.read(sV, base + j);
-    static_for<32>([&](auto ST) {
+    for (int j = 0; j < kPrefetchOf<FP8>; ++j) vbuf[j] = vread(j);
+    static_for<kMfma>([&](auto ST) {
         constexpr int st = decltype(ST)::value;
         const bf16x8 cur = operand(vbuf[st % kPrefetchOf<FP8>]);
-        if (st + kPrefetchOf<FP8> < 32) vbuf[st % kPrefetchOf<FP8>] = vr.read(sV, base + st + kPrefetchOf<FP8>);
-        constexpr int db = st & 15;
-        if constexpr (FIRST && st < 16)
+        if (st + kPrefetchOf<FP8> < kMfma) vbuf[st % kPrefetchOf<FP8>] = vread(st + kPrefetchOf<FP8>);
+        constexpr int db = st % kDB;
+        if constexpr (FIRST && st < kDB)
             o[db] = mfma32x32x16(cur, p0, f32x16{});
         else
-            o[db] = mfma32x32x16(cur, st < 16 ? p0 : p1, o[db]);
+            o[db] = mfma32x32x16(cur, st < kDB ? p0 : p1, o[db]);
         if constexpr (st % kDmaEvery == 0) {
-            if (dma.on) half_dma_row<FP8, st / kDmaEvery>(dma, lane_off, lane, wave);
+            if (dma.on) half_dma_row<FP8, D, st / kDmaEvery>(dma, lane_off, lane, wave);
         }
-        if constexpr (OVERLAP && (st & 1)) {
-            constexpr int i = st >> 1;
+        if constexpr (OVERLAP && (st % kSmEvery == kSmEvery - 1)) {
+            constexpr int i = st / kSmEvery;
             softmax_elem(c, sn[i], i, psum, i < 8 ? pn0 : pn1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
 }
 
-template <bool OUT_FP32, bool FP8, bool SPLIT>
+template <bool OUT_FP32, bool FP8, bool SPLIT, int D = kHeadDim, bool WINDOW = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_hd512_kernel(PrefillArgs a) {
-    constexpr int kTileB = Kv<FP8>::kTileB;
-    constexpr int kD = Kv<FP8>::kDmaPerHalf;   // loads per wave per half refill
+    static_assert(!(SPLIT && (WINDOW || D != kHeadDim)), "split-K: head dim 512, no window");
+    constexpr int kTileB = Kv<FP8, D>::kTileB;
+    constexpr int kD = Kv<FP8, D>::kDmaPerHalf;   // loads per wave per half refill
+    constexpr int kSteps = Kv<FP8, D>::kSteps;
+    constexpr int kDB = Kv<FP8, D>::kDimBlocks;
     __shared__ __attribute__((aligned(1024))) char smem[2 * kTileB];
     __shared__ int sFlag[kWaves];
     __shared__ int sPage[kPagesInLds];
@@ -397,13 +474,22 @@ void prefill_hd512_kernel(PrefillArgs a) {
     if (t0 >= q_len) return;
     const int t_last = min(t0 + a.tok_per_wg, q_len) - 1;
     int L = a.kv_lens[b];
-    L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
-    const int qs = max(a.q_start[b], 0);   // every row then sees key 0
+    // positions index the page table directly unless the cache is a ring
+    // (then any tile maps to table entry tile % ring_pages; windowed kernels only)
+    const int ring = WINDOW ? a.ring_pages : 0;
+    const int L_cap = ring > 0 ? 0x7fffffff - kPage : a.max_pages * kPage;
+    L = L < 0 ? 0 : (L > L_cap ? L_cap : L);
+    const int qs = max(a.q_start[b], 0);   // every row then sees key 0 (or its window)
     const int n_max = min(qs + t_last + 1, L);   // keys the last row sees
     const int n_min = min(qs + t0 + 1, L);       // keys the first row sees
+    // window: row at position p sees keys [p - window + 1, p]; lo_first and
+    // lo_last are the first and last rows' lower ends
+    const int lo_first = WINDOW ? max(0, qs + t0 - a.window + 1) : 0;
+    const int lo_last = WINDOW ? max(0, qs + t_last - a.window + 1) : 0;
     const int ntiles_all = n_max > 0 ? (n_max + kPage - 1) / kPage : 0;
-    // this workgroup's key tiles [kt_lo, ntiles): all of them, or one split
-    const int kt_lo = SPLIT ? split * a.split_tiles : 0;
+    // this workgroup's key tiles [kt_lo, ntiles): all of them, one split, or
+    // those from the first row's window start
+    const int kt_lo = SPLIT ? split * a.split_tiles : (WINDOW ? lo_first / kPage : 0);
     const int ntiles = SPLIT ? min(ntiles_all, kt_lo + a.split_tiles) : ntiles_all;
     if (SPLIT && kt_lo >= ntiles) return;   // no row of this unit needs the split
 
@@ -416,15 +502,16 @@ void prefill_hd512_kernel(PrefillArgs a) {
     const int t = valid ? t0 + tr : t_last;      // padding rows shadow the last real token
     const int head = kvh * a.g + (valid ? r - tr * a.g : 0);
     const int n_row = min(qs + t + 1, L);
+    const int lo_row = WINDOW ? max(0, qs + t - a.window + 1) : 0;
 
     // ---- Q^T operand: k-step ks covers head dims 16 ks .. 16 ks + 15; this
     // lane holds dims 16 ks + 8 h .. + 7 of its row.
-    bf16x8 qf[32];
+    bf16x8 qf[kSteps];
     {
         const bf16x8* qp =
-            (const bf16x8*)(a.q + ((size_t)(q0 + t) * a.hq + head) * kHeadDim) + h;
+            (const bf16x8*)(a.q + ((size_t)(q0 + t) * a.hq + head) * D) + h;
 #pragma unroll
-        for (int ks = 0; ks < 32; ++ks) {
+        for (int ks = 0; ks < kSteps; ++ks) {
             bf16x8 v = qp[2 * ks];
             qf[ks] = valid ? v : bf16x8{};
         }
@@ -432,17 +519,23 @@ void prefill_hd512_kernel(PrefillArgs a) {
     int koff[8];
     if constexpr (FP8) {
         // row n, chunk 0 at n ^ 0, byte 8 h; step ks XORs in 16 ks
-        koff[0] = n * kHeadDim + (swz8(n) << 4) + 8 * h;
+        koff[0] = n * 512 + (swz8(n) << 4) + 8 * h;
+#pragma unroll
+        for (int v = 1; v < 8; ++v) koff[v] = koff[0];
+    } else if constexpr (Kv<FP8, D>::kNarrow) {
+        // row n, chunk h at h ^ swzN(n); step ks XORs in 32 ks
+        koff[0] = n * 512 + ((h ^ swzN(n)) << 4);
 #pragma unroll
         for (int v = 1; v < 8; ++v) koff[v] = koff[0];
     } else {
 #pragma unroll
         for (int v = 0; v < 8; ++v) koff[v] = n * kRowBytes + (((2 * v + h) ^ swz(n)) << 4);
     }
-    using VRd = typename std::conditional<FP8, VReader8, VReader>::type;
+    using VRd = typename std::conditional<
+        FP8, VReader8, typename std::conditional<Kv<FP8, D>::kNarrow, VReaderN, VReader>::type>::type;
     const VRd vr(lane);
 
-    f32x16 o[16];  // written first by tile 0's P.V
+    f32x16 o[kDB];  // written first by the range's first P.V
     // Online softmax with a fixed per-row reference maximum: p = 2^(x - m_ref)
     // where m_ref is the row's maximum over its first 32 keys.  O and l carry
     // the same factor 2^(m_true - m_ref), which cancels in O / l.  A row whose
@@ -463,11 +556,12 @@ void prefill_hd512_kernel(PrefillArgs a) {
     const int lane16 = lane * 16;
     const int lane_off = lane16 ^ ((wave & 1) << 7);
     const int staged = min(ntiles - kt_lo, kPagesInLds);
-    for (int i = threadIdx.x; i < staged; i += kThreads) sPage[i] = ptab[kt_lo + i];
+    for (int i = threadIdx.x; i < staged; i += kThreads)
+        sPage[i] = ptab[ring > 0 ? (kt_lo + i) % ring : kt_lo + i];
     __syncthreads();
     auto page_of = [&](int tile) -> int {
         return tile - kt_lo < kPagesInLds ? __builtin_amdgcn_readfirstlane(sPage[tile - kt_lo])
-                                          : load_uniform(ptab, tile);
+                                          : load_uniform(ptab, ring > 0 ? tile % ring : tile);
     };
     auto flags_set = [&]() -> bool { return (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0; };
 
@@ -480,9 +574,9 @@ void prefill_hd512_kernel(PrefillArgs a) {
         if (ntiles > kt_lo) {
             const int page0 = page_of(kt_lo);
             const int v0 = min(L - kt_lo * kPage, kPage);
-            half_dma_all<FP8>(half_dma<FP8>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 0, wave, true), lane_off, lane, wave);
-            half_dma_all<FP8>(half_dma<FP8>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 1, wave, true), lane_off, lane, wave);
-            half_dma_all<FP8>(half_dma<FP8>(a.v_pages, page0, a.num_pages, a.hkv, kvh, v0, sV, 0, wave, true), lane_off, lane, wave);
+            half_dma_all<FP8, D>(half_dma<FP8, D>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 0, wave, true), lane_off, lane, wave);
+            half_dma_all<FP8, D>(half_dma<FP8, D>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 1, wave, true), lane_off, lane, wave);
+            half_dma_all<FP8, D>(half_dma<FP8, D>(a.v_pages, page0, a.num_pages, a.hkv, kvh, v0, sV, 0, wave, true), lane_off, lane, wave);
         }
         bool restart = false;
         for (int kt = kt_lo; kt < ntiles; ++kt) {
@@ -492,8 +586,9 @@ void prefill_hd512_kernel(PrefillArgs a) {
             const int valid_n = more ? min(L - key0 - kPage, kPage) : 0;
             const int page = page_of(kt);
             const int page_n = more ? page_of(kt + 1) : page;
-            const bool mask = key0 + kPage > n_min;   // the tile crosses a row's causal limit
-            SoftmaxCtx c0{a.scale_log2, -m_ref};
+            // the tile crosses a row's causal limit (or a row's window start)
+            const bool mask = key0 + kPage > n_min || (WINDOW && key0 < lo_last);
+            SoftmaxCtx c0{a.scale_log2, WINDOW && m_ref == -__builtin_inff() ? 0.f : -m_ref};
             float psum = 0.f;
             bf16x8 pf[4];
             f32x16 s0, s1;
@@ -505,12 +600,13 @@ void prefill_hd512_kernel(PrefillArgs a) {
                 restart = true;   // a row of tile kt-1 overshot its reference
                 break;
             }
-            qk_block<false, FP8>(s0, 0, qf, sK, koff, s0, c0, psum, pf[0], pf[1],
-                                 half_dma<FP8>(a.v_pages, page, a.num_pages, a.hkv, kvh, valid, sV, 1, wave, true),
-                                 lane_off, lane, wave);
+            qk_block<false, FP8, D>(s0, 0, qf, sK, koff, s0, c0, psum, pf[0], pf[1],
+                                    half_dma<FP8, D>(a.v_pages, page, a.num_pages, a.hkv, kvh, valid, sV, 1, wave, true),
+                                    lane_off, lane, wave);
             mfma_vgpr_drain(s0);
-            if (mask) mask_block(s0, key0 + 4 * h, n_row);
-            if (kt == kt_lo && restarts == 0) {
+            if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
+            if constexpr (WINDOW) lazy_reference(s0, a.scale_log2, m_ref, c0);
+            if (!WINDOW && kt == kt_lo && restarts == 0) {
                 // reference maximum: the row's maximum over the range's first 32
                 // keys (a restarted pass keeps the raised one).  Without split-K key 0 is visible to every row, so it is
                 // finite; a split can start past a row's causal limit, and that
@@ -527,28 +623,29 @@ void prefill_hd512_kernel(PrefillArgs a) {
             // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill
             wait_vmcnt<2 * kD>();
             lds_barrier();
-            qk_block<true, FP8>(s1, 1, qf, sK, koff, s0, c0, psum, pf[0], pf[1],
-                                half_dma<FP8>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 0, wave, more),
-                                lane_off, lane, wave);
+            qk_block<true, FP8, D>(s1, 1, qf, sK, koff, s0, c0, psum, pf[0], pf[1],
+                                   half_dma<FP8, D>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 0, wave, more),
+                                   lane_off, lane, wave);
             mfma_vgpr_drain(s1);
-            if (mask) mask_block(s1, key0 + 32 + 4 * h, n_row);
+            if (mask) mask_block<WINDOW>(s1, key0 + 32 + 4 * h, n_row, lo_row);
+            if constexpr (WINDOW) lazy_reference(s1, a.scale_log2, m_ref, c0);
 
             // ---- PV0 with block 1's softmax; K rows 32..63 of tile kt+1 refill
             if (more) wait_vmcnt<2 * kD>(); else wait_vmcnt<kD>();
             lds_barrier();
             const SoftmaxCtx& c1 = c0;
-            const HalfDma dk1 = half_dma<FP8>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 1, wave, more);
+            const HalfDma dk1 = half_dma<FP8, D>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 1, wave, more);
             if (kt == kt_lo)
-                pv_block<true, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
+                pv_block<true, true, FP8, D>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
             else
-                pv_block<false, true, FP8>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
+                pv_block<false, true, FP8, D>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
 
             // ---- PV1; V rows 0..31 of tile kt+1 refill
             if (more) wait_vmcnt<2 * kD>(); else wait_vmcnt<0>();
             lds_barrier();
-            pv_block<false, false, FP8>(o, 1, pf[2], pf[3], sV, vr, s1, c1, psum, pf[2], pf[3],
-                                        half_dma<FP8>(a.v_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sV, 0, wave, more),
-                                        lane_off, lane, wave);
+            pv_block<false, false, FP8, D>(o, 1, pf[2], pf[3], sV, vr, s1, c1, psum, pf[2], pf[3],
+                                           half_dma<FP8, D>(a.v_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sV, 0, wave, more),
+                                           lane_off, lane, wave);
             l_run += psum;
             l_peak = fmaxf(l_peak, psum);
             // restart flag of this tile: any lane whose sum of p exceeded
@@ -585,10 +682,10 @@ void prefill_hd512_kernel(PrefillArgs a) {
         // no key of the split gives (0, -inf, 0) and adds nothing in the merge
         if (valid) {
             const size_t slot = ((size_t)split * a.total_q + (q0 + t)) * a.hq + head;
-            float* dst = a.part_o + slot * kHeadDim;
+            float* dst = a.part_o + slot * D;
             const float vs = a.v_scale;
 #pragma unroll
-            for (int db = 0; db < 16; ++db) {
+            for (int db = 0; db < kDB; ++db) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int d0 = 32 * db + 8 * q4 + 4 * h;
@@ -612,11 +709,14 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // division below is then exactly O / l.
     const float sink2 = a.sinks ? a.sinks[head] * 1.4426950408889634f : -__builtin_inff();
     float lse2 = -__builtin_inff();   // log2-sum-exp of the row
-    if (ntiles == 0) {  // no visible key (empty cache): the output row is 0
+    if (ntiles <= kt_lo) {  // no tile with a visible key (empty cache): the output is 0
         l_tot = 1.f;
         lse2 = sink2;
 #pragma unroll
-        for (int db = 0; db < 16; ++db) o[db] = f32x16{};
+        for (int db = 0; db < kDB; ++db) o[db] = f32x16{};
+    } else if (l_tot == 0.f) {  // this row saw no key (its band is past the cache end)
+        l_tot = 1.f;            // O is 0
+        lse2 = sink2;
     } else {
         const float a2 = m_ref + __builtin_log2f(l_tot);
         const float top = fmaxf(a2, sink2);
@@ -626,9 +726,9 @@ void prefill_hd512_kernel(PrefillArgs a) {
     if (a.lse && valid && h == 0)
         a.lse[(size_t)(q0 + t) * a.hq + head] = lse2 * 0.6931471805599453f;
     if (valid) {
-        const size_t obase = ((size_t)(q0 + t) * a.hq + head) * kHeadDim;
+        const size_t obase = ((size_t)(q0 + t) * a.hq + head) * D;
 #pragma unroll
-        for (int db = 0; db < 16; ++db) {
+        for (int db = 0; db < kDB; ++db) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int d0 = 32 * db + 8 * q4 + 4 * h;
@@ -758,6 +858,16 @@ SplitPlanK prefill_split_plan(long long base_wgs, int max_kv_len, int keys_per_s
     return {(max_tiles + st - 1) / st, st};
 }
 
+template <bool FP8, int D, bool WINDOW>
+void launch_single(const PrefillArgs& a, bool out_fp32, dim3 gd, hipStream_t stream) {
+    if (out_fp32)
+        hipLaunchKernelGGL((prefill_hd512_kernel<true, FP8, false, D, WINDOW>), gd, dim3(kThreads),
+                           0, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_hd512_kernel<false, FP8, false, D, WINDOW>), gd,
+                           dim3(kThreads), 0, stream, a);
+}
+
 int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool fp8,
                    float k_scale, float v_scale, const int32_t* page_table,
                    const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
@@ -766,7 +876,10 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
                    int num_pages, int max_pages_per_seq, float softmax_scale,
                    const float* sinks, void* out, int out_dtype, float* lse,
                    bool splitk, int max_kv_len, int keys_per_split, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+                   size_t workspace_bytes, bool swa, int window, int ring_pages,
+                   hipStream_t stream) {
+    // the sliding-window entry is bf16 and single-pass
+    if (swa && (fp8 || splitk)) return ATTN_ERR_UNSUPPORTED;
     if (!q || !k_pages || !v_pages || !page_table || !cu_seqlens_q || !q_start_pos ||
         !kv_lens || !out)
         return ATTN_ERR_NULL;
@@ -775,7 +888,12 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
         return ATTN_ERR_SHAPE;
     if (fp8 && (!(k_scale > 0.f) || !(v_scale > 0.f))) return ATTN_ERR_SHAPE;
     if (num_q_heads % num_kv_heads) return ATTN_ERR_SHAPE;
-    if (head_dim != kHeadDim || page_size != kPage) return ATTN_ERR_UNSUPPORTED;
+    if (window < 0 || ring_pages < 0 || ring_pages > max_pages_per_seq) return ATTN_ERR_SHAPE;
+    if (page_size != kPage) return ATTN_ERR_UNSUPPORTED;
+    // head dim 256, windows and rings come only through attn_prefill_swa
+    if (head_dim != kHeadDim && (head_dim != 256 || !swa)) return ATTN_ERR_UNSUPPORTED;
+    if (!swa && (window != 0 || ring_pages != 0)) return ATTN_ERR_UNSUPPORTED;
+    if (ring_pages > 0 && window == 0) return ATTN_ERR_SHAPE;   // a ring needs a window
     const int g = num_q_heads / num_kv_heads;
     if (g > kRowsPerWg) return ATTN_ERR_UNSUPPORTED;
     if (out_dtype != ATTN_BF16 && out_dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
@@ -812,6 +930,8 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     a.split_tiles = 0;
     a.part_o = nullptr;
     a.part_ml = nullptr;
+    a.window = window;
+    a.ring_pages = ring_pages;
     const long long base = (long long)a.wgs_per_seq * batch * num_kv_heads;
     if (splitk) {
         const SplitPlanK sp = prefill_split_plan(base, max_kv_len, keys_per_split);
@@ -844,18 +964,14 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     }
     const long long grid = base;
     if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-    const dim3 gd((unsigned)grid), bd(kThreads);
-    if (fp8) {
-        if (out_dtype == ATTN_FP32)
-            hipLaunchKernelGGL((prefill_hd512_kernel<true, true, false>), gd, bd, 0, stream, a);
-        else
-            hipLaunchKernelGGL((prefill_hd512_kernel<false, true, false>), gd, bd, 0, stream, a);
-    } else {
-        if (out_dtype == ATTN_FP32)
-            hipLaunchKernelGGL((prefill_hd512_kernel<true, false, false>), gd, bd, 0, stream, a);
-        else
-            hipLaunchKernelGGL((prefill_hd512_kernel<false, false, false>), gd, bd, 0, stream, a);
-    }
+    const dim3 gd((unsigned)grid);
+    const bool f32 = out_dtype == ATTN_FP32;
+    if (fp8)
+        launch_single<true, kHeadDim, false>(a, f32, gd, stream);
+    else if (head_dim == 256)
+        (window > 0 ? launch_single<false, 256, true> : launch_single<false, 256, false>)(a, f32, gd, stream);
+    else
+        (window > 0 ? launch_single<false, kHeadDim, true> : launch_single<false, kHeadDim, false>)(a, f32, gd, stream);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -873,7 +989,7 @@ extern "C" int attn_prefill_hd512(const void* q, const void* k_pages, const void
                                 q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
                                 softmax_scale, nullptr, out, out_dtype, nullptr, false, 0, 0, nullptr,
-                                0, stream);
+                                0, false, 0, 0, stream);
 }
 
 extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const void* v_pages,
@@ -888,7 +1004,7 @@ extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const
                                 cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
                                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                                 max_pages_per_seq, softmax_scale, nullptr, out, out_dtype,
-                                nullptr, false, 0, 0, nullptr, 0, stream);
+                                nullptr, false, 0, 0, nullptr, 0, false, 0, 0, stream);
 }
 
 extern "C" int attn_prefill_hd512_ex(const void* q, const void* k_pages, const void* v_pages,
@@ -907,7 +1023,7 @@ extern "C" int attn_prefill_hd512_ex(const void* q, const void* k_pages, const v
                           page_table, cu_seqlens_q, q_start_pos, kv_lens, batch, total_q,
                           max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                           max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, false, 0,
-                          0, nullptr, 0, stream);
+                          0, nullptr, 0, false, 0, 0, stream);
 }
 
 extern "C" size_t attn_prefill_hd512_splitk_workspace_size(int batch, int max_q_len,
@@ -946,5 +1062,20 @@ extern "C" int attn_prefill_hd512_splitk(const void* q, const void* k_pages, con
                           page_table, cu_seqlens_q, q_start_pos, kv_lens, batch, total_q,
                           max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                           max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, true,
-                          max_kv_len, keys_per_split, workspace, workspace_bytes, stream);
+                          max_kv_len, keys_per_split, workspace, workspace_bytes, false, 0, 0, stream);
+}
+
+extern "C" int attn_prefill_swa(const void* q, const void* k_pages, const void* v_pages,
+                                const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                const int32_t* q_start_pos, const int32_t* kv_lens, int batch,
+                                int total_q, int max_q_len, int num_q_heads, int num_kv_heads,
+                                int head_dim, int page_size, int num_pages,
+                                int max_pages_per_seq, int window, int ring_pages,
+                                float softmax_scale, void* out, int out_dtype,
+                                hipStream_t stream) {
+    return attn::prefill_launch(q, k_pages, v_pages, false, 1.f, 1.f, page_table, cu_seqlens_q,
+                                q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
+                                num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
+                                softmax_scale, nullptr, out, out_dtype, nullptr, false, 0, 0,
+                                nullptr, 0, true, window, ring_pages, stream);
 }

@@ -73,6 +73,28 @@ def prefix_prefill_512_at_32k(device="cpu", seed=6, kv_dtype="bf16") -> PagedCas
                       kv_dtype=kv_dtype)
 
 
+def swa_prefill_hd256_8k_at_8k(device="cpu", seed=7) -> PagedCase:
+    """A sliding-window (local) layer: one 8192-row chunk at positions
+    8192..16383, window 1024, head_dim 256, 32 q heads over 4 KV heads, bf16
+    out, in a ring cache of 144 pages (9216 slots = chunk + window) that has
+    wrapped: the 16384 keys were written through it, so only the last 9216
+    are resident and the table holds 144 entries."""
+    return build_case("swa_prefill_hd256_8192_at_8192_w1024", seqs=[(8192, 8192, 16384)],
+                      hq=32, hkv=4, seed=seed, out_dtype="bf16", device=device,
+                      q_pad_rows=16, extra_pages=3, table_pad=2, head_dim=256, window=1024,
+                      ring_pages=144)
+
+
+def swa_decode_hd256_b64(device="cpu", seed=8, batch=64, lo=4096, hi=28672) -> PagedCase:
+    """Single-token decode of a sliding-window layer: batch 64, window 1024,
+    head_dim 256, 32 q heads over 4 KV heads, lengths U{4096..28672}, each
+    sequence in a ring of 16 pages (1024 slots = the window)."""
+    lens = decode_lengths(batch, lo, hi, seed)
+    return build_case(f"swa_decode_hd256_b{batch}_w1024", seqs=[(1, L - 1, L) for L in lens],
+                      hq=32, hkv=4, seed=seed, out_dtype="bf16", device=device, head_dim=256,
+                      window=1024, ring_pages=16)
+
+
 def decode_b64(device="cpu", seed=5, kv_dtype="bf16", batch=64, lo=4096, hi=28672) -> PagedCase:
     """Batch-64 single-token decode, 8 q heads over 4 KV heads, lengths U{4096..28672}.
 
@@ -93,4 +115,6 @@ WORKLOADS: Dict[str, Callable[..., PagedCase]] = {
     "long_mqa_32k_8x4096": long_mqa_32k,
     "prefix_prefill_512_at_32k": prefix_prefill_512_at_32k,
     "decode_b64_splitk": decode_b64,
+    "swa_prefill_hd256_8192_at_8192_w1024": swa_prefill_hd256_8k_at_8k,
+    "swa_decode_hd256_b64_w1024": swa_decode_hd256_b64,
 }

@@ -239,6 +239,41 @@ def main():
                               "splitk_workspace_bytes": nb}
             del cp, op, wsp
             torch.cuda.empty_cache()
+        # sliding-window (local) layers: head dim 256, window 1024, ring caches
+        cs = W.swa_prefill_hd256_8k_at_8k(device="cuda")
+        ls = cs.launches[0]
+        os_ = torch.empty((ls.total_q, cs.num_q_heads, cs.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+
+        def swa_prefill(c=cs, l=ls, o=os_):
+            A.prefill_swa(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q, l.q_start,
+                          l.kv_len, o, total_q=l.total_q, max_q_len=l.max_q_len,
+                          softmax_scale=c.softmax_scale, window=c.window,
+                          ring_pages=c.ring_pages, stream=stream)
+        ms_w = timed(swa_prefill, 20, 5)
+        f_w = W.prefill_flops(ls.q_lens, ls.q_starts, ls.kv_lens, cs.num_q_heads,
+                              head_dim=cs.head_dim, window=cs.window)
+        extra[cs.name] = {"ms_per_launch": ms_w, "tflops": f_w / (ms_w * 1e-3) / 1e12,
+                          "flop_per_launch": f_w}
+        del cs, os_
+        cd = W.swa_decode_hd256_b64(device="cuda")
+        ld = cd.launches[0]
+        od = torch.empty((ld.total_q, cd.num_q_heads, cd.head_dim), dtype=torch.bfloat16,
+                         device="cuda")
+
+        def swa_decode(c=cd, l=ld, o=od):
+            A.prefill_swa(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q, l.q_start,
+                          l.kv_len, o, total_q=l.total_q, max_q_len=l.max_q_len,
+                          softmax_scale=c.softmax_scale, window=c.window,
+                          ring_pages=c.ring_pages, stream=stream)
+        for _ in range(10):
+            swa_decode()
+        wins = sorted(timed(swa_decode, 20, 0) for _ in range(7))
+        nb_d = W.decode_kv_bytes(ld.kv_lens, cd.num_kv_heads, cd.head_dim, 2, cd.window)
+        extra[cd.name] = {"us_per_call": wins[3] * 1e3, "kv_bytes": nb_d,
+                          "GB_per_s": nb_d / (wins[3] * 1e-3) / 1e9}
+        del cd, od
+        torch.cuda.empty_cache()
         log(f"other prefill workloads: {json.dumps(extra)}")
 
     # ---- split-K decode ------------------------------------------------------

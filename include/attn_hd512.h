@@ -151,6 +151,39 @@ int attn_prefill_hd512_ex(const void* q, const void* k_pages, const void* v_page
                           hipStream_t stream);
 
 /*
+ * Chunked causal prefill of a sliding-window (local) layer over a bf16 pool,
+ * at head_dim 256 (the local layers' heads; A custom attention kernel for
+ * Gemma 4 on the RTX PRO 6000, "The deployment": local layers attend to the
+ * last 1,024 tokens with 256-dimensional heads) or 512.  Arguments as for
+ * attn_prefill_hd512, with pools [num_pages][num_kv_heads][64][head_dim] and
+ * q / out [total_q][num_q_heads][head_dim], plus:
+ *
+ *   window       >= 0: a row at absolute position p sees keys
+ *                max(0, p - window + 1) <= j <= p (and j < kv_lens[b]); 0 means
+ *                no window.
+ *   ring_pages   >= 0, <= max_pages_per_seq: 0 for a cache indexed by
+ *                position; otherwise (window > 0 required) the sequence's
+ *                cache is a ring of
+ *                C = 64 ring_pages slots and key j is read from slot j % C,
+ *                i.e. page page_table[b][(j % C) / 64] (Flash-Decoding for MQA
+ *                in CUDA, "One KV head breaks the textbook": slot = position %
+ *                capacity, only the live band is read).  The caller keeps the
+ *                band every row needs resident: C >= q_len + window - 1 for a
+ *                chunk, C >= window for one token.
+ *
+ * ATTN_ERR_UNSUPPORTED for head_dim other than 256 or 512 or page_size other
+ * than 64; ATTN_ERR_SHAPE for a negative window or ring size, a ring longer
+ * than the table, or a ring without a window.  Decode is the case q_len = 1.
+ */
+int attn_prefill_swa(const void* q, const void* k_pages, const void* v_pages,
+                     const int32_t* page_table, const int32_t* cu_seqlens_q,
+                     const int32_t* q_start_pos, const int32_t* kv_lens, int batch, int total_q,
+                     int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int page_size, int num_pages, int max_pages_per_seq, int window,
+                     int ring_pages, float softmax_scale, void* out, int out_dtype,
+                     hipStream_t stream);
+
+/*
  * Bytes of device workspace attn_prefill_hd512_splitk needs for these sizes:
  * fp32 partial outputs plus (m, l) per split, query row and query head.
  * Returns 0 when the plan has a single key range (the call then runs the

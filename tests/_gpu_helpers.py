@@ -23,12 +23,13 @@ def library():
     return A
 
 
-def out_tensor(rows: int, hq: int, dtype: str, pad_rows: int = 0) -> torch.Tensor:
+def out_tensor(rows: int, hq: int, dtype: str, pad_rows: int = 0,
+               head_dim: int = W.HEAD_DIM) -> torch.Tensor:
     if dtype == "fp32":
-        t = torch.empty((rows + pad_rows, hq, W.HEAD_DIM), dtype=torch.float32, device="cuda")
+        t = torch.empty((rows + pad_rows, hq, head_dim), dtype=torch.float32, device="cuda")
         t.view(torch.int32).fill_(SENTINEL_F32)
     else:
-        t = torch.empty((rows + pad_rows, hq, W.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+        t = torch.empty((rows + pad_rows, hq, head_dim), dtype=torch.bfloat16, device="cuda")
         t.view(torch.int16).fill_(SENTINEL_BF16)
     return t
 

@@ -160,6 +160,29 @@ def test_prefill_ex_validation(L):
     assert pf(total_q=0, max_q_len=0) == 0
 
 
+def test_prefill_swa_validation(L):
+    def sw(**over):
+        a = dict(q=FAKE, batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=256, page=64,
+                 max_pages=4, window=16, ring=0, out_dtype=1)
+        a.update(over)
+        return L.attn_prefill_swa(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["batch"],
+                                  a["total_q"], a["max_q_len"], a["hq"], a["hkv"], a["d"],
+                                  a["page"], 4, a["max_pages"], a["window"], a["ring"], 0.06,
+                                  FAKE, a["out_dtype"], None)
+    assert sw(q=None) == 1
+    assert sw(d=128) == 3
+    assert sw(page=16) == 3
+    assert sw(window=-1) == 2
+    assert sw(ring=-1) == 2
+    assert sw(ring=5) == 2                 # longer than the table
+    assert sw(window=0, ring=2) == 2       # a ring needs a window
+    assert sw(out_dtype=2) == 3
+    assert sw(hq=6, hkv=4) == 2
+    assert sw(total_q=0, max_q_len=0) == 0
+    # head dim 256 and windows are refused by the head-dim-512 entry points
+    assert prefill(L, d=256) == 3
+
+
 def test_prefill_splitk_validation(L):
     def pf(**over):
         a = dict(kvd=0, ks=1.0, vs=1.0, batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=512,
