@@ -571,8 +571,9 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // issued two refills (2 kD loads) before the newest, except where the tile
     // has no successor and those later refills do not exist.
     for (;;) {   // one pass over the key range; a restart begins a new pass
+        int page_cur = ntiles > kt_lo ? page_of(kt_lo) : 0;   // page of tile kt
         if (ntiles > kt_lo) {
-            const int page0 = page_of(kt_lo);
+            const int page0 = page_cur;
             const int v0 = min(L - kt_lo * kPage, kPage);
             half_dma_all<FP8, D>(half_dma<FP8, D>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 0, wave, true), lane_off, lane, wave);
             half_dma_all<FP8, D>(half_dma<FP8, D>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 1, wave, true), lane_off, lane, wave);
@@ -584,8 +585,9 @@ void prefill_hd512_kernel(PrefillArgs a) {
             const int key0 = kt * kPage;
             const int valid = min(L - key0, kPage);
             const int valid_n = more ? min(L - key0 - kPage, kPage) : 0;
-            const int page = page_of(kt);
+            const int page = page_cur;
             const int page_n = more ? page_of(kt + 1) : page;
+            page_cur = page_n;
             // the tile crosses a row's causal limit (or a row's window start)
             const bool mask = key0 + kPage > n_min || (WINDOW && key0 < lo_last);
             SoftmaxCtx c0{a.scale_log2, WINDOW && m_ref == -__builtin_inff() ? 0.f : -m_ref};
@@ -596,14 +598,18 @@ void prefill_hd512_kernel(PrefillArgs a) {
             // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill
             wait_vmcnt<2 * kD>();
             lds_barrier();
-            if (kt > kt_lo && restarts < kMaxRestarts && flags_set()) {
-                restart = true;   // a row of tile kt-1 overshot its reference
-                break;
-            }
+            // restart flags of tile kt-1: read now, acted on after this block's
+            // MFMAs so that the read's latency hides under them (an aborted
+            // block only wrote scores and refilled V rows the restart reloads)
+            const bool over_prev = kt > kt_lo && restarts < kMaxRestarts && flags_set();
             qk_block<false, FP8, D>(s0, 0, qf, sK, koff, s0, c0, psum, pf[0], pf[1],
                                     half_dma<FP8, D>(a.v_pages, page, a.num_pages, a.hkv, kvh, valid, sV, 1, wave, true),
                                     lane_off, lane, wave);
             mfma_vgpr_drain(s0);
+            if (over_prev) {
+                restart = true;   // a row of tile kt-1 overshot its reference
+                break;
+            }
             if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
             if constexpr (WINDOW) lazy_reference(s0, a.scale_log2, m_ref, c0);
             if (!WINDOW && kt == kt_lo && restarts == 0) {
