@@ -40,9 +40,9 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "74d1dd7ad664e10e4b4bddb8d31ed4d2ff5415a6c807f4b48e2164a71e13aa03",
-    "fetch_bytes": 2018617303,
-    "write_bytes": 284921958,
+    "sha256": "cc29a3ad66d928b5d514990e58ac3c74302dc9455c95eb761a565a0cce81f5c4",
+    "fetch_bytes": 2029180246,
+    "write_bytes": 287539200,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
 
