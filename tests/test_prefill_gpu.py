@@ -115,3 +115,17 @@ def test_empty_launch_and_bad_arguments(A):
               lc.kv_len, out, total_q=0, max_q_len=0, softmax_scale=case.softmax_scale)
     torch.cuda.synchronize()
     assert not out.any()
+
+
+def test_many_ragged_sequences(A):
+    # 40 sequences with every kind of offset: chunks at 0, mid-page, on page
+    # boundaries, single rows, rows longer than one workgroup's 16 tokens
+    g = np.random.default_rng(79)
+    seqs = []
+    for i in range(40):
+        ql = int(g.integers(1, 200))
+        st = int(g.choice([0, 63, 64, 65, int(g.integers(0, 3000))]))
+        seqs.append((ql, st, st + ql))
+    case = W.build_case("ragged40", seqs=seqs, hq=16, hkv=2, seed=79, out_dtype="fp32",
+                        device="cuda", q_pad_rows=3, extra_pages=2, table_pad=2)
+    _full_check(A, case, pad_rows=3)

@@ -182,3 +182,22 @@ def test_reference_restart_on_hot_key(A, kv_dtype, path):
     ref = oracle.attend_all(case.to("cpu"))
     assert np.isfinite(ref).all()
     check_parity(out[:lc.total_q], ref, f"hot key {kv_dtype} {path}")
+
+
+@pytest.mark.parametrize("path", ["single", "splitk"])
+def test_context_past_the_staged_page_ids(A, path):
+    # 300000 keys = 4688 key tiles: past the 4096 page ids a workgroup stages
+    # in LDS, so the tail tiles take the page-table path in the loop
+    case = W.build_case("long300k", seqs=[(64, 299936, 300000)], hq=8, hkv=1, seed=73,
+                        out_dtype="fp32", device="cuda", q_pad_rows=2)
+    lc = case.launches[0]
+    if path == "single":
+        out = run_prefill(A, case, pad_rows=2)
+    else:
+        out, _, nbytes = run_splitk(A, case, 0, pad_rows=2)
+        assert nbytes > 0
+    assert sentinel_intact(out[lc.total_q:])
+    tokens = [0, 1, 31, 62, 63]
+    rows, toks = sample_rows(lc, case.num_q_heads, tokens)
+    ref = oracle.attend_rows(case.to("cpu"), rows).reshape(len(toks), case.num_q_heads, -1)
+    check_parity(out[torch.as_tensor(toks, device="cuda")], ref, f"300000 keys {path}")
