@@ -9,10 +9,10 @@
 // group, so every K/V tile brought into LDS serves all g heads of the group
 // (A custom attention kernel for Gemma 4 on the RTX PRO 6000, "The kernel in
 // three steps", step 1).  Wave w owns packed rows 32w .. 32w+31 with the full
-// 512-wide Q row in VGPRs and the full 512-wide O row in accumulators: a
+// Q row in VGPRs and the full O row in accumulators (head dim 512: a
 // gfx950 wave has up to 512 registers, so the register ceiling that pushed
 // the Ada and Blackwell kernels to split head_dim across warps does not bind
-// here, and no score partials need exchanging between waves.
+// here, and no score partials need exchanging between waves).
 //
 // Per 64-key tile (= one page of one KV head):
 //   K and V arrive in two separate 64 KB LDS buffers (no time-sharing of one
@@ -37,6 +37,16 @@
 // tile that needs it two phases later, with the wave's 8 row loads spread one
 // per four MFMAs over the next phase (a burst of 1 KB buffer->LDS loads would
 // stall the wave's instruction issue and starve the matrix core).
+//
+// The same kernel, by template parameters, also covers: an FP8-E4M3 pool
+// (512-byte tile rows, bytes widened exactly to bf16 at their MFMA); head dim
+// 256 for the sliding-window local layers (512-byte bf16 rows, half the
+// MFMAs per tile; A custom attention kernel for Gemma 4 on the RTX PRO 6000,
+// "The deployment"), with a window that bounds each row's keys from below and
+// a ring cache (Flash-Decoding for MQA in CUDA, "One KV head breaks the
+// textbook": slot = position % capacity); and split-K, where workgroups of
+// one row block take disjoint key ranges and write unnormalised partials
+// that prefill_merge_kernel combines.
 #include "device_common.h"
 #include "attn_host.h"
 

@@ -40,7 +40,7 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "cc29a3ad66d928b5d514990e58ac3c74302dc9455c95eb761a565a0cce81f5c4",
+    "sha256": "ce778464405fc9091ebbcb84ffb17dc56a473402bb2e6734e9ab5325982daef3",
     "fetch_bytes": 2029180246,
     "write_bytes": 287539200,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
