@@ -13,6 +13,10 @@
  *     the key range is split across workgroups, each writes an unnormalised
  *     (O, m, l) partial, and a merge kernel combines them (Flash-Decoding for
  *     MQA in CUDA, "One KV head breaks the textbook").
+ * Around them: _ex forms with sinks, a log-sum-exp output and multi-token
+ * decode; split-K prefill for short chunks over long prefixes; the paged KV
+ * append; sliding-window (local) layers at head dim 256 over ring caches
+ * (attn_prefill_swa); a measurement helper (the HBM read probe).
  *
  * Common conventions
  *   Pointers are device pointers unless stated otherwise; the caller owns and
@@ -26,7 +30,8 @@
  *   the kernels so that bad values cannot read outside the buffers, but the
  *   results are then undefined.
  *
- *   head_dim must be 512 and page_size 64.  num_q_heads must be a multiple
+ *   head_dim must be 512 (256 is accepted by attn_prefill_swa only) and
+ *   page_size 64.  num_q_heads must be a multiple
  *   of num_kv_heads, with group g = num_q_heads / num_kv_heads <= 128; query
  *   head h uses KV head h / g (consecutive grouping, so that [B, 1, Hq*D] and
  *   [B*Hkv, g, D] are one layout: Flash-Decoding for MQA in CUDA, "One KV head
