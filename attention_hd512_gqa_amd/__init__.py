@@ -5,8 +5,10 @@ this package only marshals torch tensors into that ABI.
 """
 from ._lib import (ATTN_BF16, ATTN_FP32, ATTN_FP8_E4M3, AttnError, LIB_PATH, append_kv, decode,
                    decode_workspace_size, hbm_probe_sink_words, hbm_read_probe, lib, prefill,
-                   prefill_splitk, prefill_splitk_workspace_size, prefill_swa, status_string)
+                   prefill_append, prefill_splitk, prefill_splitk_workspace_size, prefill_swa,
+                   status_string)
 
 __all__ = ["ATTN_BF16", "ATTN_FP32", "ATTN_FP8_E4M3", "AttnError", "LIB_PATH", "append_kv", "decode",
            "decode_workspace_size", "hbm_probe_sink_words", "hbm_read_probe", "lib", "prefill",
-           "prefill_splitk", "prefill_splitk_workspace_size", "prefill_swa", "status_string"]
+           "prefill_append", "prefill_splitk", "prefill_splitk_workspace_size", "prefill_swa",
+           "status_string"]

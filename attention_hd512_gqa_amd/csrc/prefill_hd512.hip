@@ -133,6 +133,9 @@ struct PrefillArgs {
     float* part_ml;     // [nsplit][total_q][hq][2]  (m in log2 units, l)
     int window;         // sliding window in keys (0: none)
     int ring_pages;     // ring cache pages per sequence (0: unbounded cache)
+    // fused append: the chunk's new K and V rows, bf16 [total_q][hkv][512]
+    const char* k_new;
+    const char* v_new;
 };
 
 // Refill of one 32-key half (rows 32 half .. 32 half + 31) of a K or V tile
@@ -146,6 +149,12 @@ struct HalfDma {
     uint32_t lds_base;  // LDS address of this wave's first row
     uint32_t soff;      // byte offset of this wave's first row in the tile
     bool on;            // wave-uniform: this refill exists
+    // Fused append only (app is a compile-time false everywhere else): row J
+    // of the wave's 8 is read J * stride bytes past soff, so that rsrc / soff
+    // / stride can name either the pool tile (1 KB rows) or the chunk's
+    // new-row buffer (rows of one KV head Hkv KB apart).
+    bool app;
+    int stride;
 };
 
 template <bool FP8, int D>
@@ -160,6 +169,8 @@ __device__ __forceinline__ HalfDma half_dma(const char* pool, int page, int num_
     d.soff = (uint32_t)__builtin_amdgcn_readfirstlane((32 * half + 8 * wave) * kRowB);
     d.lds_base = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(uintptr_t)buf + d.soff));
     d.on = on;
+    d.app = false;
+    d.stride = kRowB;
     return d;
 }
 
@@ -175,6 +186,25 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t m0, uint32_t soff, in
         : "memory", "m0");
 }
 
+// Row J of a wave's 8 at J * stride bytes past byte soff of the resource (a
+// runtime row stride), to LDS at lds_base + REL, 16-byte chunks placed like
+// dma_row's.
+template <int SWZ, int J, int REL>
+__device__ __forceinline__ void dma_row_strided(u32x4 rsrc, uint32_t lds_base, uint32_t soff,
+                                                int stride, int lane_off) {
+    int voff;
+    asm volatile(
+        "v_xor_b32 %0, %1, %2\n\t"
+        "v_mad_u32_u24 %0, %3, %4, %0\n\t"
+        "s_add_u32 m0, %5, %6\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %7, %8 offen lds"
+        : "=&v"(voff)
+        : "i"(SWZ), "v"(lane_off), "i"(J), "s"(stride), "s"(lds_base), "i"(REL), "s"(rsrc),
+          "s"(soff)
+        : "memory", "m0", "scc");
+}
+
 // Refill load J of this wave's share of a half: 1 KB rows, row 8 wave + J of
 // the half; narrow rows, rows 8 wave + 2 J and + 1 (lanes 0-31 and 32-63),
 // each lane fetching the logical chunk that the swizzle stores at its LDS
@@ -188,12 +218,25 @@ __device__ __forceinline__ void half_dma_row(const HalfDma& d, int lane_off, int
         const int voff = rw * 512 + (((lane & 31) ^ f) << 4);
         dma16(d.rsrc, d.lds_base + 2 * J * 512, d.soff, voff);
     } else {
+        if (d.app) {
+            dma_row_strided<(swz(J) << 4), J, J * kRowBytes>(d.rsrc, d.lds_base, d.soff,
+                                                              d.stride, lane_off);
+            return;
+        }
         dma_row<(swz(J) << 4), J * kRowBytes>(d.rsrc, d.lds_base, d.soff, lane_off);
     }
 }
 
+// Keeps the instructions before it (a refill's address work) ahead of the
+// wait and barrier that follow, where they overlap the wait.
+template <bool ON>
+__device__ __forceinline__ void hold_before_wait() {
+    if constexpr (ON) __builtin_amdgcn_sched_barrier(0);
+}
+
 template <bool FP8, int D>
 __device__ __forceinline__ void half_dma_all(const HalfDma& d, int lane_off, int lane, int wave) {
+    if (!d.on) return;
     static_for<Kv<FP8, D>::kDmaPerHalf>([&](auto J) {
         half_dma_row<FP8, D, decltype(J)::value>(d, lane_off, lane, wave);
     });
@@ -445,10 +488,13 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
     });
 }
 
-template <bool OUT_FP32, bool FP8, bool SPLIT, int D = kHeadDim, bool WINDOW = false>
+template <bool OUT_FP32, bool FP8, bool SPLIT, int D = kHeadDim, bool WINDOW = false,
+          bool APPEND = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_hd512_kernel(PrefillArgs a) {
     static_assert(!(SPLIT && (WINDOW || D != kHeadDim)), "split-K: head dim 512, no window");
+    static_assert(!APPEND || (!FP8 && !SPLIT && !WINDOW && D == kHeadDim),
+                  "fused append: bf16 pool, head dim 512, single pass");
     constexpr int kTileB = Kv<FP8, D>::kTileB;
     constexpr int kD = Kv<FP8, D>::kDmaPerHalf;   // loads per wave per half refill
     constexpr int kSteps = Kv<FP8, D>::kSteps;
@@ -568,6 +614,57 @@ void prefill_hd512_kernel(PrefillArgs a) {
     const int staged = min(ntiles - kt_lo, kPagesInLds);
     for (int i = threadIdx.x; i < staged; i += kThreads)
         sPage[i] = ptab[ring > 0 ? (kt_lo + i) % ring : kt_lo + i];
+    // Fused append.  The chunk's keys are positions [qs, hi).  A wave's 8
+    // refill rows (an aligned group of 8 positions) that all lie there come
+    // from the new-row buffer; every other group comes from the pool.  This
+    // workgroup writes its own tokens' K and V rows into their cache slots,
+    // and also the chunk rows of the groups that straddle qs or hi in the
+    // tiles it walks: those it then reads from the pool, so it waits for its
+    // own writes before the barrier.  Workgroups that write one row write
+    // the same bytes, and no workgroup reads a chunk row it has not written.
+    if constexpr (APPEND) {
+        const int hi = min(qs + q_len, L);
+        const int lo8 = min((qs + 7) & ~7, hi);                    // [qs, lo8): first group
+        const int hi8 = max(hi & ~7, lo8);                         // [hi8, hi): last group
+        const int walked = ntiles_all * kPage;
+        const int ntok = t_last - t0 + 1;
+        const int nlo = max(lo8 - qs, 0);                          // none when hi <= qs
+        const int nhi = max(min(hi, walked) - hi8, 0);
+        const int nrow = ntok + nlo + nhi;
+        // wave w moves rows w, w + 4, ... (one 1 KB row per wave instruction,
+        // 16 bytes a lane), four rows of K and V in flight per batch; a row's
+        // position and page are wave-uniform
+        for (int r0 = wave; r0 < nrow; r0 += 16) {
+            u32x4 kr[4], vr4[4];
+            size_t dst[4];
+            bool ok[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = r0 + 4 * i;
+                const int pos = rr < ntok ? qs + t0 + rr
+                                          : (rr < ntok + nlo ? qs + rr - ntok : hi8 + rr - ntok - nlo);
+                const int pg = rr < nrow && pos / kPage < a.max_pages ? ptab[pos / kPage] : -1;
+                ok[i] = pg >= 0 && pg < a.num_pages;
+                dst[i] = (((size_t)pg * a.hkv + kvh) * kPage + pos % kPage) * kRowBytes + lane16;
+                const size_t src = ((size_t)(q0 + pos - qs) * a.hkv + kvh) * kRowBytes + lane16;
+                if (ok[i]) {
+                    kr[i] = *(const u32x4*)(a.k_new + src);
+                    vr4[i] = *(const u32x4*)(a.v_new + src);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (ok[i]) {
+                    *(u32x4*)((char*)a.k_pages + dst[i]) = kr[i];
+                    *(u32x4*)((char*)a.v_pages + dst[i]) = vr4[i];
+                }
+            }
+        }
+        // the straddling rows must be in memory before this workgroup's
+        // refills read them; its own rows need no wait (their stores are
+        // older than every refill load, so the loop's counted waits stay safe)
+        if (nlo + nhi > 0) wait_vmcnt<0>();
+    }
     __syncthreads();
     auto page_of = [&](int tile) -> int {
         return tile - kt_lo < kPagesInLds ? __builtin_amdgcn_readfirstlane(sPage[tile - kt_lo])
@@ -575,19 +672,66 @@ void prefill_hd512_kernel(PrefillArgs a) {
     };
     auto flags_set = [&]() -> bool { return (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0; };
 
+    // Fused append: a group of 8 refill rows starting at position p comes
+    // from the new-row buffer when qs <= p and p + 8 <= hi, i.e. when
+    // p - qs_g <= g_lim unsigned (qs_g pushed out of reach when no group
+    // qualifies); its bytes start (p - qs) * n_stride + n_base into the buffer.
+    int qs_g = 0, g_lim = 0, n_stride = kRowBytes;
+    uint32_t n_base = 0, n_bytes = 0;
+    if constexpr (APPEND) {
+        const int hi = min(qs + q_len, L);
+        qs_g = hi - 8 - qs >= 0 ? qs : 0x40000000;
+        g_lim = max(hi - 8 - qs, 0);
+        n_stride = a.hkv * kRowBytes;
+        n_base = ((uint32_t)q0 * (uint32_t)a.hkv + (uint32_t)kvh) * kRowBytes;
+        n_bytes = (uint32_t)a.total_q * a.hkv * kRowBytes;
+    }
+    // refill descriptor of half `half` of tile `tile` (K or V)
+    auto refill = [&](bool is_k, int page, int valid_rows, int tile, int half, bool on) -> HalfDma {
+        if constexpr (!APPEND) {
+            return half_dma<FP8, D>(is_k ? a.k_pages : a.v_pages, page, a.num_pages, a.hkv, kvh,
+                                    valid_rows, is_k ? sK : sV, half, wave, on);
+        } else {
+            // the same pool descriptor as half_dma's, with the source chosen
+            // by selects (no branch in the loop)
+            const char* pool = is_k ? a.k_pages : a.v_pages;
+            page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+            const char* psrc = pool + ((size_t)page * a.hkv + kvh) * (size_t)kTileB;
+            const uint32_t pbytes = (uint32_t)(valid_rows > 0 ? valid_rows : 0) * kRowBytes;
+            const int row0 = 32 * half + 8 * wave;
+            const int p = tile * kPage + row0;
+            const bool in = (uint32_t)(p - qs_g) <= (uint32_t)g_lim;
+            const char* nsrc = is_k ? a.k_new : a.v_new;
+            HalfDma d;
+            d.rsrc = buffer_rsrc(in ? nsrc : psrc, in ? n_bytes : pbytes);
+            d.soff = (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)(in ? (uint32_t)(p - qs) * (uint32_t)n_stride + n_base
+                         : (uint32_t)row0 * kRowBytes));
+            d.lds_base = (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)((uint32_t)(uintptr_t)(is_k ? sK : sV) + (uint32_t)row0 * kRowBytes));
+            d.stride = __builtin_amdgcn_readfirstlane(in ? n_stride : kRowBytes);
+            d.on = on;
+            d.app = true;
+            return d;
+        }
+    };
+
     // Vector-memory accounting: every wave issues its half-tile refills in the
     // order V1(j) [during QK0(j)], K0(j+1) [QK1(j)], K1(j+1) [PV0(j)],
     // V0(j+1) [PV1(j)], kD loads each; before each phase the half it reads was
-    // issued two refills (2 kD loads) before the newest, except where the tile
-    // has no successor and those later refills do not exist.
+    // issued two refills (2 kD loads) before the newest.  The last tile's
+    // successor refills are issued too, over an empty key range (a resource
+    // with no records lands zeros, fetching nothing) into halves nothing reads
+    // again, so that every refill site is unconditional and every count the
+    // same; the pass's end waits for them.
     for (;;) {   // one pass over the key range; a restart begins a new pass
         int page_cur = ntiles > kt_lo ? page_of(kt_lo) : 0;   // page of tile kt
         if (ntiles > kt_lo) {
             const int page0 = page_cur;
             const int v0 = min(L - kt_lo * kPage, kPage);
-            half_dma_all<FP8, D>(half_dma<FP8, D>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 0, wave, true), lane_off, lane, wave);
-            half_dma_all<FP8, D>(half_dma<FP8, D>(a.k_pages, page0, a.num_pages, a.hkv, kvh, v0, sK, 1, wave, true), lane_off, lane, wave);
-            half_dma_all<FP8, D>(half_dma<FP8, D>(a.v_pages, page0, a.num_pages, a.hkv, kvh, v0, sV, 0, wave, true), lane_off, lane, wave);
+            half_dma_all<FP8, D>(refill(true, page0, v0, kt_lo, 0, true), lane_off, lane, wave);
+            half_dma_all<FP8, D>(refill(true, page0, v0, kt_lo, 1, true), lane_off, lane, wave);
+            half_dma_all<FP8, D>(refill(false, page0, v0, kt_lo, 0, true), lane_off, lane, wave);
         }
         bool restart = false;
         for (int kt = kt_lo; kt < ntiles; ++kt) {
@@ -606,14 +750,18 @@ void prefill_hd512_kernel(PrefillArgs a) {
             f32x16 s0, s1;
 
             // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill
+            // (each refill is named before the wait that precedes its block, so
+            // that the address work overlaps the wait rather than delaying the
+            // block's first MFMA)
+            const HalfDma dv1 = refill(false, page, valid, kt, 1, true);
+            hold_before_wait<APPEND>();
             wait_vmcnt<2 * kD>();
             lds_barrier();
             // restart flags of tile kt-1: read now, acted on after this block's
             // MFMAs so that the read's latency hides under them (an aborted
             // block only wrote scores and refilled V rows the restart reloads)
             const bool over_prev = kt > kt_lo && restarts < kMaxRestarts && flags_set();
-            qk_block<false, FP8, D>(s0, 0, qf, sK, koff, s0, c0, psum, pf[0], pf[1],
-                                    half_dma<FP8, D>(a.v_pages, page, a.num_pages, a.hkv, kvh, valid, sV, 1, wave, true),
+            qk_block<false, FP8, D>(s0, 0, qf, sK, koff, s0, c0, psum, pf[0], pf[1], dv1,
                                     lane_off, lane, wave);
             mfma_vgpr_drain(s0);
             if (over_prev) {
@@ -637,31 +785,34 @@ void prefill_hd512_kernel(PrefillArgs a) {
             }
 
             // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill
+            const HalfDma dk0 = refill(true, page_n, valid_n, kt + 1, 0, true);
+            hold_before_wait<APPEND>();
             wait_vmcnt<2 * kD>();
             lds_barrier();
-            qk_block<true, FP8, D>(s1, 1, qf, sK, koff, s0, c0, psum, pf[0], pf[1],
-                                   half_dma<FP8, D>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 0, wave, more),
+            qk_block<true, FP8, D>(s1, 1, qf, sK, koff, s0, c0, psum, pf[0], pf[1], dk0,
                                    lane_off, lane, wave);
             mfma_vgpr_drain(s1);
             if (mask) mask_block<WINDOW>(s1, key0 + 32 + 4 * h, n_row, lo_row);
             if constexpr (WINDOW) lazy_reference(s1, a.scale_log2, m_ref, c0);
 
             // ---- PV0 with block 1's softmax; K rows 32..63 of tile kt+1 refill
-            if (more) wait_vmcnt<2 * kD>(); else wait_vmcnt<kD>();
+            const HalfDma dk1 = refill(true, page_n, valid_n, kt + 1, 1, true);
+            hold_before_wait<APPEND>();
+            wait_vmcnt<2 * kD>();
             lds_barrier();
             const SoftmaxCtx& c1 = c0;
-            const HalfDma dk1 = half_dma<FP8, D>(a.k_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sK, 1, wave, more);
             if (kt == kt_lo)
                 pv_block<true, true, FP8, D>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
             else
                 pv_block<false, true, FP8, D>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
 
             // ---- PV1; V rows 0..31 of tile kt+1 refill
-            if (more) wait_vmcnt<2 * kD>(); else wait_vmcnt<0>();
+            const HalfDma dv0 = refill(false, page_n, valid_n, kt + 1, 0, true);
+            hold_before_wait<APPEND>();
+            wait_vmcnt<2 * kD>();
             lds_barrier();
             pv_block<false, false, FP8, D>(o, 1, pf[2], pf[3], sV, vr, s1, c1, psum, pf[2], pf[3],
-                                           half_dma<FP8, D>(a.v_pages, page_n, a.num_pages, a.hkv, kvh, valid_n, sV, 0, wave, more),
-                                           lane_off, lane, wave);
+                                           dv0, lane_off, lane, wave);
             l_run += psum;
             l_peak = fmaxf(l_peak, psum);
             // restart flag of this tile: any lane whose sum of p exceeded
@@ -690,6 +841,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
         l_peak = 0.f;
         l_run = 0.f;         // O restarts too: tile 0's P.V overwrites it
     }
+    wait_vmcnt<0>();   // the empty refills past the last tile
 
     // ---- epilogue: lane holds d = 32 db + 8 (i/4) + 4 h + (i%4) of its row.
     float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -893,9 +1045,13 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
                    const float* sinks, void* out, int out_dtype, float* lse,
                    bool splitk, int max_kv_len, int keys_per_split, void* workspace,
                    size_t workspace_bytes, bool swa, int window, int ring_pages,
-                   hipStream_t stream) {
-    // the sliding-window entry is bf16 and single-pass
+                   const void* k_new, const void* v_new, hipStream_t stream) {
+    // the sliding-window entry is bf16 and single-pass; so is the fused append
+    // (given both new-row buffers or neither), at head dim 512 with no window
+    const bool append = k_new || v_new;
     if (swa && (fp8 || splitk)) return ATTN_ERR_UNSUPPORTED;
+    if (append && (!k_new || !v_new)) return ATTN_ERR_NULL;
+    if (append && (fp8 || splitk || swa)) return ATTN_ERR_UNSUPPORTED;
     if (!q || !k_pages || !v_pages || !page_table || !cu_seqlens_q || !q_start_pos ||
         !kv_lens || !out)
         return ATTN_ERR_NULL;
@@ -948,6 +1104,11 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     a.part_ml = nullptr;
     a.window = window;
     a.ring_pages = ring_pages;
+    a.k_new = (const char*)k_new;
+    a.v_new = (const char*)v_new;
+    // the new-row buffers are addressed by 32-bit buffer offsets
+    if (append && (long long)total_q * num_kv_heads * kRowBytes > 0xffffffffLL)
+        return ATTN_ERR_SHAPE;
     const long long base = (long long)a.wgs_per_seq * batch * num_kv_heads;
     if (splitk) {
         const SplitPlanK sp = prefill_split_plan(base, max_kv_len, keys_per_split);
@@ -982,7 +1143,14 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     const dim3 gd((unsigned)grid);
     const bool f32 = out_dtype == ATTN_FP32;
-    if (fp8)
+    if (append) {
+        if (f32)
+            hipLaunchKernelGGL((prefill_hd512_kernel<true, false, false, kHeadDim, false, true>),
+                               gd, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_hd512_kernel<false, false, false, kHeadDim, false, true>),
+                               gd, dim3(kThreads), 0, stream, a);
+    } else if (fp8)
         launch_single<true, kHeadDim, false>(a, f32, gd, stream);
     else if (head_dim == 256)
         (window > 0 ? launch_single<false, 256, true> : launch_single<false, 256, false>)(a, f32, gd, stream);
@@ -1005,7 +1173,7 @@ extern "C" int attn_prefill_hd512(const void* q, const void* k_pages, const void
                                 q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
                                 softmax_scale, nullptr, out, out_dtype, nullptr, false, 0, 0, nullptr,
-                                0, false, 0, 0, stream);
+                                0, false, 0, 0, nullptr, nullptr, stream);
 }
 
 extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const void* v_pages,
@@ -1020,7 +1188,7 @@ extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const
                                 cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
                                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                                 max_pages_per_seq, softmax_scale, nullptr, out, out_dtype,
-                                nullptr, false, 0, 0, nullptr, 0, false, 0, 0, stream);
+                                nullptr, false, 0, 0, nullptr, 0, false, 0, 0, nullptr, nullptr, stream);
 }
 
 extern "C" int attn_prefill_hd512_ex(const void* q, const void* k_pages, const void* v_pages,
@@ -1039,7 +1207,7 @@ extern "C" int attn_prefill_hd512_ex(const void* q, const void* k_pages, const v
                           page_table, cu_seqlens_q, q_start_pos, kv_lens, batch, total_q,
                           max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                           max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, false, 0,
-                          0, nullptr, 0, false, 0, 0, stream);
+                          0, nullptr, 0, false, 0, 0, nullptr, nullptr, stream);
 }
 
 extern "C" size_t attn_prefill_hd512_splitk_workspace_size(int batch, int max_q_len,
@@ -1078,7 +1246,8 @@ extern "C" int attn_prefill_hd512_splitk(const void* q, const void* k_pages, con
                           page_table, cu_seqlens_q, q_start_pos, kv_lens, batch, total_q,
                           max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                           max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, true,
-                          max_kv_len, keys_per_split, workspace, workspace_bytes, false, 0, 0, stream);
+                          max_kv_len, keys_per_split, workspace, workspace_bytes, false, 0, 0, nullptr,
+                          nullptr, stream);
 }
 
 extern "C" int attn_prefill_swa(const void* q, const void* k_pages, const void* v_pages,
@@ -1093,5 +1262,22 @@ extern "C" int attn_prefill_swa(const void* q, const void* k_pages, const void* 
                                 q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
                                 softmax_scale, nullptr, out, out_dtype, nullptr, false, 0, 0,
-                                nullptr, 0, true, window, ring_pages, stream);
+                                nullptr, 0, true, window, ring_pages, nullptr, nullptr, stream);
+}
+
+extern "C" int attn_prefill_hd512_append(const void* q, const void* k_new, const void* v_new,
+                                         void* k_pages, void* v_pages,
+                                         const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                         const int32_t* q_start_pos, const int32_t* kv_lens,
+                                         int batch, int total_q, int max_q_len, int num_q_heads,
+                                         int num_kv_heads, int head_dim, int page_size,
+                                         int num_pages, int max_pages_per_seq,
+                                         float softmax_scale, const float* sinks, void* out,
+                                         int out_dtype, float* lse, hipStream_t stream) {
+    if (!k_new || !v_new) return ATTN_ERR_NULL;
+    return attn::prefill_launch(q, k_pages, v_pages, false, 1.f, 1.f, page_table, cu_seqlens_q,
+                                q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
+                                num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
+                                softmax_scale, sinks, out, out_dtype, lse, false, 0, 0, nullptr,
+                                0, false, 0, 0, k_new, v_new, stream);
 }

@@ -332,6 +332,36 @@ def main():
                                 "GB_per_s": moved / (ms * 1e-3) / 1e9}
             log(f"append_kv {kv_dtype} (8192 rows x {ac.num_kv_heads} KV heads): "
                 f"{ms * 1e3:.1f} us, {moved / (ms * 1e-3) / 1e9:.0f} GB/s")
+            if kv_dtype == "bf16":
+                # the append fused into the prefill launch against the two
+                # launches, with the chunk's own rows as the new rows
+                pos = torch.arange(al.q_starts[0], al.q_starts[0] + al.total_q, device="cuda")
+                pg = ac.page_table[0, pos // 64].long()
+                kn = ac.k_pool[pg, :, pos % 64, :].contiguous()
+                vn = ac.v_pool[pg, :, pos % 64, :].contiguous()
+                ao = torch.empty((al.total_q, ac.num_q_heads, W.HEAD_DIM),
+                                 dtype=torch.bfloat16, device="cuda")
+
+                def fused_call():
+                    A.prefill_append(al.q, kn, vn, kp, vp, ac.page_table, al.cu_seqlens_q,
+                                     al.q_start, al.kv_len, ao, total_q=al.total_q,
+                                     max_q_len=al.max_q_len, softmax_scale=ac.softmax_scale,
+                                     stream=stream)
+
+                def unfused_call():
+                    append_call()
+                    A.prefill(al.q, kp, vp, ac.page_table, al.cu_seqlens_q, al.q_start,
+                              al.kv_len, ao, total_q=al.total_q, max_q_len=al.max_q_len,
+                              softmax_scale=ac.softmax_scale, stream=stream)
+                ms_f = timed(fused_call, 10, 3)
+                ms_u = timed(unfused_call, 10, 3)
+                append["prefill_with_append_bf16"] = {
+                    "fused_ms": ms_f, "append_then_prefill_ms": ms_u,
+                    "fused_tflops": flops / (ms_f * 1e-3) / 1e12}
+                log(f"prefill 8192@8192 with the append fused: {ms_f:.3f} ms "
+                    f"({flops / (ms_f * 1e-3) / 1e12:.1f} TFLOP/s); append_kv + prefill: "
+                    f"{ms_u:.3f} ms")
+                del ao
             del ac, kn, vn, kp, vp
             torch.cuda.empty_cache()
 

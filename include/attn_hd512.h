@@ -15,8 +15,9 @@
  *     MQA in CUDA, "One KV head breaks the textbook").
  * Around them: _ex forms with sinks, a log-sum-exp output and multi-token
  * decode; split-K prefill for short chunks over long prefixes; the paged KV
- * append; sliding-window (local) layers at head dim 256 over ring caches
- * (attn_prefill_swa); a measurement helper (the HBM read probe).
+ * append, alone or fused into the prefill launch; sliding-window (local)
+ * layers at head dim 256 over ring caches (attn_prefill_swa); a measurement
+ * helper (the HBM read probe).
  *
  * Common conventions
  *   Pointers are device pointers unless stated otherwise; the caller owns and
@@ -333,6 +334,38 @@ int attn_append_kv(const void* k_new, const void* v_new, int kv_dtype, float k_s
                    const int32_t* q_start_pos, int batch, int total_q, int num_kv_heads,
                    int head_dim, int page_size, int num_pages, int max_pages_per_seq,
                    void* k_pages, void* v_pages, hipStream_t stream);
+
+/*
+ * Chunked causal prefill with the chunk's paged KV append fused into the same
+ * launch, over a bf16 pool at head_dim 512: the pool is paged at the
+ * attention key block, so a key tile is one copy (pegainfer issue 1051,
+ * "Proposed Plan"), and the rows a chunk appends are the keys it attends to
+ * last.  Arguments as for attn_prefill_hd512_ex with kv_dtype ATTN_BF16,
+ * plus:
+ *
+ *   k_new, v_new   bf16 [total_q][num_kv_heads][512], row order as q: the
+ *                  chunk's new key and value rows, token i of sequence b at
+ *                  position q_start_pos[b] + i.
+ *   k_pages, v_pages   written as attn_append_kv(ATTN_BF16) writes them,
+ *                  and read for the keys before the chunk.
+ *
+ * Keys at the chunk's own positions are read from k_new / v_new, so the
+ * result and the pool afterwards are bitwise those of attn_append_kv followed
+ * by attn_prefill_hd512_ex, provided every chunk position maps to a page of
+ * the pool (a row whose page id falls outside it is skipped by both writes,
+ * but the fused call still attends to its new row), q_start_pos[b] >= 0,
+ * and no page slot the call writes is visible to another sequence of the
+ * call (the writes are not ordered with the other workgroups' reads).  ATTN_ERR_NULL for a missing k_new or v_new;
+ * ATTN_ERR_SHAPE when total_q * num_kv_heads * 1024 exceeds 2^32 - 1 bytes.
+ */
+int attn_prefill_hd512_append(const void* q, const void* k_new, const void* v_new,
+                              void* k_pages, void* v_pages, const int32_t* page_table,
+                              const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
+                              const int32_t* kv_lens, int batch, int total_q, int max_q_len,
+                              int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                              int num_pages, int max_pages_per_seq, float softmax_scale,
+                              const float* sinks, void* out, int out_dtype, float* lse,
+                              hipStream_t stream);
 
 /*
  * Measurement helper: streams `bytes` (a multiple of 16) of device memory

@@ -183,6 +183,26 @@ def test_prefill_swa_validation(L):
     assert prefill(L, d=256) == 3
 
 
+def test_prefill_append_validation(L):
+    def pa(**over):
+        a = dict(kn=FAKE, vn=FAKE, batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=512,
+                 page=64, out_dtype=1)
+        a.update(over)
+        return L.attn_prefill_hd512_append(
+            FAKE, a["kn"], a["vn"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["batch"],
+            a["total_q"], a["max_q_len"], a["hq"], a["hkv"], a["d"], a["page"], 4, 4, 0.04,
+            None, FAKE, a["out_dtype"], None, None)
+    assert pa(kn=None) == 1
+    assert pa(vn=None) == 1
+    assert pa(d=256) == 3
+    assert pa(page=16) == 3
+    assert pa(hq=6, hkv=4) == 2
+    assert pa(out_dtype=2) == 3
+    # new-row buffers past 32-bit buffer offsets
+    assert pa(total_q=1 << 22, max_q_len=4) == 2
+    assert pa(total_q=0, max_q_len=0) == 0
+
+
 def test_prefill_splitk_validation(L):
     def pf(**over):
         a = dict(kvd=0, ks=1.0, vs=1.0, batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=512,
