@@ -680,11 +680,12 @@ void prefill_hd512_kernel(PrefillArgs a) {
     uint32_t n_base = 0, n_bytes = 0;
     if constexpr (APPEND) {
         const int hi = min(qs + q_len, L);
-        qs_g = hi - 8 - qs >= 0 ? qs : 0x40000000;
-        g_lim = max(hi - 8 - qs, 0);
-        n_stride = a.hkv * kRowBytes;
-        n_base = ((uint32_t)q0 * (uint32_t)a.hkv + (uint32_t)kvh) * kRowBytes;
-        n_bytes = (uint32_t)a.total_q * a.hkv * kRowBytes;
+        qs_g = __builtin_amdgcn_readfirstlane(hi - 8 - qs >= 0 ? qs : 0x40000000);
+        g_lim = __builtin_amdgcn_readfirstlane(max(hi - 8 - qs, 0));
+        n_stride = __builtin_amdgcn_readfirstlane(a.hkv * kRowBytes);
+        n_base = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(((uint32_t)q0 * (uint32_t)a.hkv + (uint32_t)kvh) * kRowBytes));
+        n_bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)a.total_q * a.hkv * kRowBytes));
     }
     // refill descriptor of half `half` of tile `tile` (K or V)
     auto refill = [&](bool is_k, int page, int valid_rows, int tile, int half, bool on) -> HalfDma {
@@ -692,25 +693,36 @@ void prefill_hd512_kernel(PrefillArgs a) {
             return half_dma<FP8, D>(is_k ? a.k_pages : a.v_pages, page, a.num_pages, a.hkv, kvh,
                                     valid_rows, is_k ? sK : sV, half, wave, on);
         } else {
-            // the same pool descriptor as half_dma's, with the source chosen
-            // by selects (no branch in the loop)
-            const char* pool = is_k ? a.k_pages : a.v_pages;
-            page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-            const char* psrc = pool + ((size_t)page * a.hkv + kvh) * (size_t)kTileB;
-            const uint32_t pbytes = (uint32_t)(valid_rows > 0 ? valid_rows : 0) * kRowBytes;
-            const int row0 = 32 * half + 8 * wave;
-            const int p = tile * kPage + row0;
-            const bool in = (uint32_t)(p - qs_g) <= (uint32_t)g_lim;
-            const char* nsrc = is_k ? a.k_new : a.v_new;
-            HalfDma d;
-            d.rsrc = buffer_rsrc(in ? nsrc : psrc, in ? n_bytes : pbytes);
-            d.soff = (uint32_t)__builtin_amdgcn_readfirstlane(
-                (int)(in ? (uint32_t)(p - qs) * (uint32_t)n_stride + n_base
-                         : (uint32_t)row0 * kRowBytes));
-            d.lds_base = (uint32_t)__builtin_amdgcn_readfirstlane(
-                (int)((uint32_t)(uintptr_t)(is_k ? sK : sV) + (uint32_t)row0 * kRowBytes));
-            d.stride = __builtin_amdgcn_readfirstlane(in ? n_stride : kRowBytes);
-            d.on = on;
+            // the pool descriptor half_dma would build, then the source chosen
+            // by scalar selects on one compare (written out so that the choice
+            // costs no branch in the loop)
+            const HalfDma pd = half_dma<FP8, D>(is_k ? a.k_pages : a.v_pages, page, a.num_pages,
+                                                a.hkv, kvh, valid_rows, is_k ? sK : sV, half,
+                                                wave, on);
+            const int p = tile * kPage + 32 * half + 8 * wave;
+            const uint32_t nsoff = (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)((uint32_t)(p - qs) * (uint32_t)n_stride + n_base));
+            const uint64_t np = (uint64_t)(uintptr_t)(is_k ? a.k_new : a.v_new);
+            const uint32_t n0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)np);
+            const uint32_t n1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)((np >> 32) & 0xffffu));
+            const uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane(p);
+            HalfDma d = pd;
+            uint32_t t;
+            asm volatile(
+                "s_sub_u32 %[t], %[pos], %[qsg]\n\t"
+                "s_cmp_le_u32 %[t], %[glim]\n\t"
+                "s_cselect_b32 %[r0], %[n0], %[p0]\n\t"
+                "s_cselect_b32 %[r1], %[n1], %[p1]\n\t"
+                "s_cselect_b32 %[r2], %[nb], %[p2]\n\t"
+                "s_cselect_b32 %[so], %[nso], %[pso]\n\t"
+                "s_cselect_b32 %[st], %[nst], %[pst]"
+                : [t] "=&s"(t), [r0] "=&s"(d.rsrc[0]), [r1] "=&s"(d.rsrc[1]),
+                  [r2] "=&s"(d.rsrc[2]), [so] "=&s"(d.soff), [st] "=&s"(d.stride)
+                : [pos] "s"(pos), [qsg] "s"(qs_g), [glim] "s"(g_lim), [n0] "s"(n0),
+                  [p0] "s"(pd.rsrc[0]), [n1] "s"(n1), [p1] "s"(pd.rsrc[1]), [nb] "s"(n_bytes),
+                  [p2] "s"(pd.rsrc[2]), [nso] "s"(nsoff), [pso] "s"(pd.soff),
+                  [nst] "s"(n_stride), [pst] "s"(pd.stride)
+                : "scc");
             d.app = true;
             return d;
         }
