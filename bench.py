@@ -40,9 +40,9 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "ce778464405fc9091ebbcb84ffb17dc56a473402bb2e6734e9ab5325982daef3",
-    "fetch_bytes": 2029180246,
-    "write_bytes": 287539200,
+    "sha256": "22fff9a9b6a10ba45c070a6f0f87b93693640ff86c635a85f0b93544da1ef1cf",
+    "fetch_bytes": 1992367844,
+    "write_bytes": 287287706,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
 
