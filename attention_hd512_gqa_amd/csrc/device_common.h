@@ -65,7 +65,9 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // Issued from asm so that the compiler does not track it: its LDS-DMA
 // bookkeeping would otherwise wait for every outstanding tile load before
 // any LDS read.  Callers order it with wait_vmcnt and lds_barrier.  M0 carries
-// the LDS address (one wait state after the SALU write); none of the kernels
+// the LDS address; it is written first so that the two VALU ops forming the
+// lane offset fill the wait state the load needs after the SALU write; none
+// of the kernels
 // built with these helpers use M0 for anything else.  The SALU add also
 // writes SCC, which the clobber list declares.
 template <int SWZ, int REL, bool NT = false>
@@ -75,20 +77,18 @@ __device__ __forceinline__ void dma_row(u32x4 rsrc, uint32_t lds_base, uint32_t 
     // NT: non-temporal (streaming) cache policy, for data read exactly once
     if constexpr (NT) {
         asm volatile(
+            "s_add_u32 m0, %4, %3\n\t"
             "v_xor_b32 %0, %1, %2\n\t"
             "v_or_b32 %0, %3, %0\n\t"
-            "s_add_u32 m0, %4, %3\n\t"
-            "s_nop 0\n\t"
             "buffer_load_dwordx4 %0, %5, %6 offen nt lds"
             : "=&v"(voff)
             : "i"(SWZ), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
             : "memory", "m0", "scc");
     } else {
         asm volatile(
+            "s_add_u32 m0, %4, %3\n\t"
             "v_xor_b32 %0, %1, %2\n\t"
             "v_or_b32 %0, %3, %0\n\t"
-            "s_add_u32 m0, %4, %3\n\t"
-            "s_nop 0\n\t"
             "buffer_load_dwordx4 %0, %5, %6 offen lds"
             : "=&v"(voff)
             : "i"(SWZ), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)

@@ -188,16 +188,15 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t m0, uint32_t soff, in
 
 // Row J of a wave's 8 at J * stride bytes past byte soff of the resource (a
 // runtime row stride), to LDS at lds_base + REL, 16-byte chunks placed like
-// dma_row's.
+// dma_row's (M0 written first, as there).
 template <int SWZ, int J, int REL>
 __device__ __forceinline__ void dma_row_strided(u32x4 rsrc, uint32_t lds_base, uint32_t soff,
                                                 int stride, int lane_off) {
     int voff;
     asm volatile(
+        "s_add_u32 m0, %5, %6\n\t"
         "v_xor_b32 %0, %1, %2\n\t"
         "v_mad_u32_u24 %0, %3, %4, %0\n\t"
-        "s_add_u32 m0, %5, %6\n\t"
-        "s_nop 0\n\t"
         "buffer_load_dwordx4 %0, %7, %8 offen lds"
         : "=&v"(voff)
         : "i"(SWZ), "v"(lane_off), "i"(J), "s"(stride), "s"(lds_base), "i"(REL), "s"(rsrc),
@@ -262,21 +261,32 @@ struct SoftmaxCtx {
     float neg_m_ref;  // -m_ref
 };
 
-// One softmax element: p = 2^(s * scale - m_ref) (0 for masked keys).  Adds p
-// to the lane's running sum and packs it into the P^T operand.  No running
-// maximum is kept: the sum bounds every p of the tile, which is all the
-// reference check needs.
+// One softmax element: p = 2^(s * scale - m_ref) (0 for masked keys).  The
+// lane's running sum and the P^T operand take p one element later (the
+// previous element's p, `pend`, is added and packed here), so that no
+// instruction reads an exp2 result right after it is written (that read
+// costs a wait state); softmax_flush finishes the block's last element.  No
+// running maximum is kept: the sum bounds every p of the tile, which is all
+// the reference check needs.
 // The empty asms pin the element to the MFMA step it is issued with (inputs
 // taken and running values produced inside the step): without them, IR
 // passes gather the softmax arithmetic into one cluster after the MFMA chain
 // and the matrix core idles while it runs.
 __device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float s, int i, float& psum,
-                                             bf16x8& pf) {
+                                             float& pend, bf16x8& pf_prev) {
     asm volatile("" : "+v"(s));
     const float p = fast_exp2(__builtin_fmaf(s, c.scale_log2, c.neg_m_ref));
-    psum += p;
-    pf[i & 7] = (__bf16)p;
+    if (i > 0) {
+        psum += pend;
+        pf_prev[(i - 1) & 7] = (__bf16)pend;
+    }
+    pend = p;
     asm volatile("" : "+v"(psum));
+}
+
+__device__ __forceinline__ void softmax_flush(float& psum, float pend, bf16x8& pf1) {
+    psum += pend;
+    pf1[7] = (__bf16)pend;
 }
 
 // Masks one block's raw scores in place: element i is key
@@ -419,6 +429,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(
     constexpr int kDmaEvery = kSteps / Kv<FP8, D>::kDmaPerHalf;
     constexpr int kSmEvery = kSteps / 16;
     Raw kbuf[kPrefetchOf<FP8>];
+    float pend = 0.f;   // p of the previous softmax element
 #pragma unroll
     for (int j = 0; j < kPrefetchOf<FP8>; ++j) kbuf[j] = kread(j);
     static_for<kSteps>([&](auto KS) {
@@ -441,10 +452,11 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(
         }
         if constexpr (OVERLAP && (ks % kSmEvery == kSmEvery - 1)) {
             constexpr int i = ks / kSmEvery;
-            softmax_elem(c, sp[i], i, psum, i < 8 ? pf0 : pf1);
+            softmax_elem(c, sp[i], i, psum, pend, i - 1 < 8 ? pf0 : pf1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
+    if constexpr (OVERLAP) softmax_flush(psum, pend, pf1);
 }
 
 // P.V of one 32-key block (k-steps c = 2 kb, 2 kb + 1 of the tile, all D / 32
@@ -466,6 +478,7 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
     using Raw = typename std::conditional<FP8, v2i32, bf16x8>::type;
     auto vread = [&](int st) -> Raw { return vr.read(sV, 2 * kb + st / kDB, st % kDB); };
     Raw vbuf[kPrefetchOf<FP8>];
+    float pend = 0.f;   // p of the previous softmax element
 #pragma unroll
     for (int j = 0; j < kPrefetchOf<FP8>; ++j) vbuf[j] = vread(j);
     static_for<kMfma>([&](auto ST) {
@@ -482,10 +495,11 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
         }
         if constexpr (OVERLAP && (st % kSmEvery == kSmEvery - 1)) {
             constexpr int i = st / kSmEvery;
-            softmax_elem(c, sn[i], i, psum, i < 8 ? pn0 : pn1);
+            softmax_elem(c, sn[i], i, psum, pend, i - 1 < 8 ? pn0 : pn1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
+    if constexpr (OVERLAP) softmax_flush(psum, pend, pn1);
 }
 
 template <bool OUT_FP32, bool FP8, bool SPLIT, int D = kHeadDim, bool WINDOW = false,
