@@ -58,40 +58,41 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // past LDS byte `lds_base`.  Lane i's 16 bytes land at LDS row start + 16 i,
 // so lane i fetches the logical chunk the swizzle stores at chunk i: lane
 // offset lane_off ^ SWZ, with lane_off = 16 i (possibly pre-XORed with a
-// wave-dependent part of the row's swizzle) and SWZ the row's remaining
-// swizzle bits, shifted to bytes.  Bytes past the resource's extent arrive as
-// zeros, which is how keys past the cache length are zero-filled.
+// wave-dependent part of the row's swizzle; below 1 KB either way) and SWZ
+// the row's remaining swizzle bits, shifted to bytes.  Bytes past the
+// resource's extent arrive as zeros, which is how keys past the cache length
+// are zero-filled.
 //
 // Issued from asm so that the compiler does not track it: its LDS-DMA
 // bookkeeping would otherwise wait for every outstanding tile load before
 // any LDS read.  Callers order it with wait_vmcnt and lds_barrier.  M0 carries
-// the LDS address; it is written first so that the two VALU ops forming the
-// lane offset fill the wait state the load needs after the SALU write; none
-// of the kernels
-// built with these helpers use M0 for anything else.  The SALU add also
-// writes SCC, which the clobber list declares.
+// the LDS address; it is written first so that the VALU op forming the lane
+// offset fills the wait state the load needs after the SALU write; none of
+// the kernels built with these helpers use M0 for anything else.  The SALU
+// add also writes SCC, which the clobber list declares.
 template <int SWZ, int REL, bool NT = false>
 __device__ __forceinline__ void dma_row(u32x4 rsrc, uint32_t lds_base, uint32_t soff,
                                         int lane_off) {
+    // lane_off and SWZ lie below 1 KB and REL is whole rows, so
+    // (lane_off ^ SWZ) + REL is one XOR with the constant SWZ | REL
+    static_assert(SWZ >= 0 && SWZ < kRowBytes && REL % kRowBytes == 0, "row offset layout");
     int voff;
     // NT: non-temporal (streaming) cache policy, for data read exactly once
     if constexpr (NT) {
         asm volatile(
             "s_add_u32 m0, %4, %3\n\t"
             "v_xor_b32 %0, %1, %2\n\t"
-            "v_or_b32 %0, %3, %0\n\t"
             "buffer_load_dwordx4 %0, %5, %6 offen nt lds"
             : "=&v"(voff)
-            : "i"(SWZ), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
+            : "i"(SWZ | REL), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
             : "memory", "m0", "scc");
     } else {
         asm volatile(
             "s_add_u32 m0, %4, %3\n\t"
             "v_xor_b32 %0, %1, %2\n\t"
-            "v_or_b32 %0, %3, %0\n\t"
             "buffer_load_dwordx4 %0, %5, %6 offen lds"
             : "=&v"(voff)
-            : "i"(SWZ), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
+            : "i"(SWZ | REL), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
             : "memory", "m0", "scc");
     }
 }
