@@ -610,11 +610,11 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // where m_ref is the row's maximum over its first 32 keys.  O and l carry
     // the same factor 2^(m_true - m_ref), which cancels in O / l.  A row whose
     // scores climb more than kRescaleMargin above m_ref pushes a lane's tile
-    // sum of p past 2^kRescaleMargin, and the workgroup then restarts its key
-    // loop with every row's reference raised by log2 of its largest tile sum
-    // so far (which bounds every p seen from above and exceeds the largest p
-    // by at most 32x): the rescale of O is replaced by a recompute that
-    // typical inputs never trigger.  This keeps the 256 O accumulators (AGPRs,
+    // sum of p past 2^kRescaleMargin, and at the end of the pass the
+    // workgroup then restarts its key loop with every row's reference raised
+    // by log2 of its largest tile sum (which bounds every p seen from above
+    // and exceeds the largest p by at most 32x): the rescale of O is replaced
+    // by a recompute that typical inputs never trigger.  This keeps the 256 O accumulators (AGPRs,
     // which VALU cannot address) out of all VALU code in the loop, and the
     // per-element work to one exp2, one add and a conversion.
     float m_ref = -__builtin_inff();
@@ -752,6 +752,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // same; the pass's end waits for them.
     for (;;) {   // one pass over the key range; a restart begins a new pass
         int page_cur = ntiles > kt_lo ? page_of(kt_lo) : 0;   // page of tile kt
+        int page_nx = kt_lo + 1 < ntiles ? page_of(kt_lo + 1) : page_cur;   // of tile kt + 1
         if (ntiles > kt_lo) {
             const int page0 = page_cur;
             const int v0 = min(L - kt_lo * kPage, kPage);
@@ -766,8 +767,14 @@ void prefill_hd512_kernel(PrefillArgs a) {
             const int valid = min(L - key0, kPage);
             const int valid_n = more ? min(L - key0 - kPage, kPage) : 0;
             const int page = page_cur;
-            const int page_n = more ? page_of(kt + 1) : page;
-            page_cur = page_n;
+            const int page_n = page_nx;
+            // page id of tile kt + 2: the LDS read is issued here and its value
+            // taken after QK0, so that its latency hides under QK0's MFMAs (the
+            // index is clamped into the staged range; past it the id comes from
+            // the table after QK0)
+            const int t2 = kt + 2;
+            const bool t2_staged = t2 - kt_lo < kPagesInLds;
+            const int page_nn_raw = sPage[min(t2 - kt_lo, kPagesInLds - 1)];
             // the tile crosses a row's causal limit (or a row's window start)
             const bool mask = key0 + kPage > n_min || (WINDOW && key0 < lo_last);
             SoftmaxCtx c0{a.scale_log2, WINDOW && m_ref == -__builtin_inff() ? 0.f : -m_ref};
@@ -783,17 +790,13 @@ void prefill_hd512_kernel(PrefillArgs a) {
             hold_before_wait<APPEND>();
             wait_vmcnt<2 * kD>();
             lds_barrier();
-            // restart flags of tile kt-1: read now, acted on after this block's
-            // MFMAs so that the read's latency hides under them (an aborted
-            // block only wrote scores and refilled V rows the restart reloads)
-            const bool over_prev = kt > kt_lo && restarts < kMaxRestarts && flags_set();
             qk_block<false, FP8, D>(s0, 0, qf, sK, koff, s0, c0, psum, pf[0], pf[1], dv1,
                                     lane_off, lane, wave);
             mfma_vgpr_drain(s0);
-            if (over_prev) {
-                restart = true;   // a row of tile kt-1 overshot its reference
-                break;
-            }
+            page_cur = page_n;
+            page_nx = t2 >= ntiles ? page_n
+                    : (t2_staged ? __builtin_amdgcn_readfirstlane(page_nn_raw)
+                                 : load_uniform(ptab, ring > 0 ? t2 % ring : t2));
             if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
             if constexpr (WINDOW) lazy_reference(s0, a.scale_log2, m_ref, c0);
             if (!WINDOW && kt == kt_lo && restarts == 0) {
@@ -841,14 +844,17 @@ void prefill_hd512_kernel(PrefillArgs a) {
                                            dv0, lane_off, lane, wave);
             l_run += psum;
             l_peak = fmaxf(l_peak, psum);
-            // restart flag of this tile: any lane whose sum of p exceeded
-            // 2^margin (non-finite sums included); read after the next
-            // barrier.  The vote runs on every lane, outside the lane-0 store.
-            const bool over = __any(!(psum <= kOverSum));
-            if (lane == 0) sFlag[wave] = over ? 1 : 0;
         }
-        if (!restart && ntiles > kt_lo) {
-            lds_barrier();   // the last tile's flags are visible
+        // Restart vote, once per pass: a lane whose sum of p passed 2^margin
+        // in some tile (l_peak), or whose sums were not finite (l_run; NaN
+        // does not reach l_peak through fmaxf).  A pass that overshot may
+        // have overflowed O, which the restart recomputes from the start, so
+        // no per-tile vote is needed; typical inputs never restart.  The vote
+        // runs on every lane, outside the lane-0 store.
+        if (ntiles > kt_lo) {
+            const bool over = __any(!(l_peak <= kOverSum) || !(l_run <= 3.0e38f));
+            if (lane == 0) sFlag[wave] = over ? 1 : 0;
+            lds_barrier();   // every wave's flag is visible
             restart = restarts < kMaxRestarts && flags_set();
         }
         if (!restart) break;
