@@ -40,9 +40,9 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "22fff9a9b6a10ba45c070a6f0f87b93693640ff86c635a85f0b93544da1ef1cf",
-    "fetch_bytes": 1992367844,
-    "write_bytes": 287287706,
+    "sha256": "357e637ef3359f7f5198a5ba2f9d29e5557dbd484e824a720a1363120d780e1d",
+    "fetch_bytes": 1993815134,
+    "write_bytes": 287395226,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
 
@@ -190,8 +190,25 @@ def main():
         ms4 = timed(long_prompt, 3, 1)
         f4 = sum(W.prefill_flops(l.q_lens, l.q_starts, l.kv_lens, c4.num_q_heads)
                  for l in c4.launches)
-        extra["long_mqa_32k_8x4096"] = {"ms_per_prompt": ms4, "tflops": f4 / (ms4 * 1e-3) / 1e12}
+        per_chunk = []
+        for l4 in c4.launches:
+            msc = timed(lambda l4=l4: prefill_step(c4, l4, o4), 10, 2)
+            fc = W.prefill_flops(l4.q_lens, l4.q_starts, l4.kv_lens, c4.num_q_heads)
+            per_chunk.append({"ms": msc, "tflops": fc / (msc * 1e-3) / 1e12})
+        extra["long_mqa_32k_8x4096"] = {"ms_per_prompt": ms4, "tflops": f4 / (ms4 * 1e-3) / 1e12,
+                                        "per_chunk": per_chunk}
         del c4, o4
+        # the tiny MQA prefill (256 rows, one workgroup per 16 tokens): launch-bound
+        c1 = W.tiny_prefill_mqa(device="cuda")
+        l1 = c1.launches[0]
+        o1 = torch.empty((l1.total_q, c1.num_q_heads, W.HEAD_DIM), dtype=torch.float32,
+                         device="cuda")
+        ms1 = timed(lambda: prefill_step(c1, l1, o1), 100, 20)
+        f1 = W.prefill_flops(l1.q_lens, l1.q_starts, l1.kv_lens, c1.num_q_heads)
+        extra["tiny_prefill_mqa_256"] = {"us_per_launch": ms1 * 1e3,
+                                         "tflops": f1 / (ms1 * 1e-3) / 1e12,
+                                         "note": "launch-bound (16 workgroups)"}
+        del c1, o1
         torch.cuda.empty_cache()
         # the headline chunk over an FP8-E4M3 cache (same values, per-tensor scales)
         c8 = W.chunk_prefill_8k_at_8k(device="cuda", kv_dtype="fp8_e4m3")
