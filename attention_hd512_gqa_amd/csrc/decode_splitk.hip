@@ -48,7 +48,6 @@ constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kSxStride = 272;      // bytes per score-exchange row (256 + 16 pad)
 constexpr int kDefaultTargetWgs = 4096;
-constexpr int kNonTemporal = 2;     // buffer-load cache policy: nt (read-once stream)
 constexpr int kFp8Waves = 1;       // waves per FP8 split workgroup, one partial each
 constexpr int kMaxSub = 4;          // partials per split workgroup (FP8: one per wave)
 constexpr int kHalfKeys = 32;       // FP8: keys per wave step
@@ -113,22 +112,6 @@ __device__ __forceinline__ int split_page(const DecodeArgs& a, const SplitPlan& 
 __device__ __forceinline__ const char* tile_base(const char* pool, const DecodeArgs& a, int page,
                                                  int kvh, int tile_bytes) {
     return pool + ((size_t)page * a.hkv + kvh) * (size_t)tile_bytes;
-}
-
-// Buffer resource over `bytes` bytes at `base`; both wave-uniform, kept in
-// SGPRs by readfirstlane.  Loads at offsets >= bytes return zeros and touch
-// no memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
-    const uint64_t a = (uint64_t)base;
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0,
-                                             __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int voff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0,
-                                                                          kNonTemporal));
 }
 
 // MFMA column c of a split: token c / g at position L - q_len + c / g and
@@ -332,11 +315,12 @@ void decode_split_bf16_kernel(DecodeArgs a) {
 // of each half of a wave.
 __host__ __device__ constexpr int swz8(int r) { return (r & 15) ^ (((r >> 4) & 1) << 2); }
 
-// V half page (32 rows of 512 E4M3 bytes) -> this wave's LDS buffer by DMA, 2
-// rows per instruction: lane l lands at LDS byte 16 l of rows 2 i, 2 i + 1,
-// i.e. row 2 i + l / 32 at chunk position l % 32, and so fetches logical
-// chunk (l % 32) ^ swz8(row).  Rows past `rows` arrive as zeros.
-__device__ __forceinline__ void dma_v_half(const char* src, int rows, ATTN_LDS char* buf,
+// K or V half page (32 rows of 512 E4M3 bytes) -> this wave's LDS buffer by
+// DMA, 2 whole rows (8 full 128-byte lines) per instruction: lane l lands at
+// LDS byte 16 l of rows 2 i, 2 i + 1, i.e. row 2 i + l / 32 at chunk position
+// l % 32, and so fetches logical chunk (l % 32) ^ swz8(row).  Rows past
+// `rows` arrive as zeros.
+__device__ __forceinline__ void dma_half(const char* src, int rows, ATTN_LDS char* buf,
                                            int lane) {
     const u32x4 rsrc = buffer_rsrc(src, (uint32_t)rows * kHeadDim);
     const uint32_t lds = (uint32_t)(uintptr_t)buf;
@@ -355,20 +339,14 @@ __device__ __forceinline__ void dma_v_half(const char* src, int rows, ATTN_LDS c
     }
 }
 
-// K half page straight into MFMA A-operand registers: key group gm (keys
-// 16 gm .. 16 gm + 15), load i: key 16 gm + n, bytes 64 i + 16 kq .. + 15,
-// i.e. the lane's operands of k-steps 2 i and 2 i + 1 (8 dims each).
-struct KHalf {
-    u32x4 r[16];
-};
-
-__device__ __forceinline__ void load_k_half(KHalf& k, const char* src, int rows, int n, int kq) {
-    const __amdgpu_buffer_rsrc_t rsrc = uniform_rsrc(src, rows * kHeadDim);
-    const int ko = n * kHeadDim + 16 * kq;
-#pragma unroll
-    for (int gm = 0; gm < 2; ++gm)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) k.r[8 * gm + i] = load16(rsrc, ko + gm * 16 * kHeadDim + 64 * i);
+// K operand of key group gm (keys 16 gm .. 16 gm + 15), read i: key
+// 16 gm + n, bytes 64 i + 16 kq .. + 15 (logical chunk 4 i + kq), i.e. the
+// lane's operands of k-steps 2 i and 2 i + 1 (8 dims each).  Within each 8
+// lanes of one read the rows differ in their low 3 bits, so swz8 puts their
+// chunks in distinct bank groups.
+__device__ __forceinline__ u32x4 k_read(const ATTN_LDS char* sk, int gm, int i, int n, int kq) {
+    const int row = 16 * gm + n;
+    return *(const ATTN_LDS u32x4*)(sk + row * kHeadDim + (((4 * i + kq) ^ swz8(row)) << 4));
 }
 
 __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
@@ -379,12 +357,13 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
     return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 }
 
-// Per wave step (half page u of this wave, V buffer c % 2):
-//   QK(u) from the K registers (their loads, and V(u)'s DMA issued before
-//   them, are waited for here), then V(u + 4) DMA -> the other buffer (its
-//   last readers, PV two steps back, are complete) and K(u + 4) -> the K
-//   registers, then softmax and PV(u).  Past the split's end the loads are
-//   zero-length.
+// Per wave step (half page u of this wave; one K and one V half-page buffer
+// in LDS, both filled by whole-row DMA):
+//   wait for K(u), QK(u) from the K buffer, then K(u + NW) -> the K buffer
+//   (its reads have returned); softmax; wait for V(u), PV(u) from the V
+//   buffer, then V(u + NW) -> the V buffer.  Every wait leaves exactly the
+//   other buffer's kHalfKeys / 2 loads in flight.  Past the split's end the
+//   loads are zero-length.
 template <int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_split_fp8_kernel(DecodeArgs a) {
@@ -395,7 +374,9 @@ void decode_split_fp8_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;   // query head of the group (MFMA column)
     const int kq = lane >> 4;  // k-group
-    ATTN_LDS char* sv0 = (ATTN_LDS char*)smem + wave * 2 * kHalfBytes;
+    // this wave's K and V half-page buffers
+    ATTN_LDS char* sk = (ATTN_LDS char*)smem + wave * 2 * kHalfBytes;
+    ATTN_LDS char* sv = sk + kHalfBytes;
 
     // Q^T operand of k-step ks: dims 64 (ks / 2) + 16 kq + 8 (ks % 2) .. + 7,
     // the order in which the K loads deliver them
@@ -427,20 +408,23 @@ void decode_split_fp8_kernel(DecodeArgs a) {
 
     const int nhalf = (p.k_end - p.k_begin + kHalfKeys - 1) / kHalfKeys;
     const int count = nhalf > wave ? (nhalf - wave + NW - 1) / NW : 0;
-    KHalf kr;
-    auto issue = [&](int u, ATTN_LDS char* vbuf) {
+    // half page u of the split: rows past its end (or past the split) are
+    // zero-length loads, so every step issues the same count
+    auto issue = [&](int u, bool is_k) {
         int rows = p.k_end - (p.k_begin + u * kHalfKeys);
         rows = rows < 0 ? 0 : (rows > kHalfKeys ? kHalfKeys : rows);
         const int pg = split_page(a, p, u >> 1);
         const int off = (u & 1) * kHalfBytes;
-        dma_v_half(tile_base(a.v_pages, a, pg, p.kvh, kTileBytes / 2) + off, rows, vbuf, lane);
-        load_k_half(kr, tile_base(a.k_pages, a, pg, p.kvh, kTileBytes / 2) + off, rows, n, kq);
+        dma_half(tile_base(is_k ? a.k_pages : a.v_pages, a, pg, p.kvh, kTileBytes / 2) + off,
+                 rows, is_k ? sk : sv, lane);
     };
-    issue(wave, sv0);
+    issue(wave, true);
+    issue(wave, false);
     for (int c = 0; c < count; ++c) {
         const int u = wave + NW * c;
         const int key0 = p.k_begin + u * kHalfKeys;
-        ATTN_LDS char* sv = sv0 + (c & 1) * kHalfBytes;
+        // K(u) landed; V(u), issued after it, may still be in flight
+        wait_vmcnt<kHalfKeys / 2>();
         // S^T[32 keys][16 heads]: key group gm = keys 16 gm .. 16 gm + 15
         f32x4 s[2];
 #pragma unroll
@@ -448,18 +432,17 @@ void decode_split_fp8_kernel(DecodeArgs a) {
             f32x4 s0 = f32x4{}, s1 = f32x4{};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const u32x4 w = kr.r[8 * gm + i];
+                const u32x4 w = k_read(sk, gm, i, n, kq);
                 s0 = mfma16x16x32(widen8(w[0], w[1]), qf[2 * i], s0);
                 s1 = mfma16x16x32(widen8(w[2], w[3]), qf[2 * i + 1], s1);
             }
             s[gm] = s0 + s1;   // element i: key 16 gm + 4 kq + i of head n
         }
-        wait_vmcnt<0>();   // V(u) landed too (its DMA was issued before K(u))
-        // refill for this wave's next half page; the K registers are reused
-        // in place, so keep the loads below QK
-        asm volatile("" ::: "memory");
+        // the K buffer is free once its reads have returned: refill it with
+        // this wave's next half page (one wave per buffer, so no barrier)
+        wait_lgkmcnt0();
         __builtin_amdgcn_sched_barrier(0);
-        issue(u + NW, sv0 + ((c + 1) & 1) * kHalfBytes);
+        issue(u + NW, true);
 
         // softmax against the reference maximum
         float x[8];
@@ -499,7 +482,9 @@ void decode_split_fp8_kernel(DecodeArgs a) {
         }
         l_run += psum;
 
-        // O^T[512 dims][16 heads] += V^T P^T over the 32 keys
+        // O^T[512 dims][16 heads] += V^T P^T over the 32 keys; V(u) landed
+        // (K(u + NW), issued after it, may still be in flight)
+        wait_vmcnt<kHalfKeys / 2>();
 #pragma unroll
         for (int db = 0; db < 32; ++db) {
             const v2i32 t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -508,6 +493,10 @@ void decode_split_fp8_kernel(DecodeArgs a) {
             // bound the operands in flight
             if ((db & 7) == 7 && db < 31) __builtin_amdgcn_sched_barrier(0);
         }
+        // the V buffer is free once its reads have returned
+        wait_lgkmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(u + NW, false);
     }
     wait_vmcnt<0>();   // the last (zero-length) loads
     const size_t slot =

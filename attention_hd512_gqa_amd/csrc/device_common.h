@@ -43,6 +43,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until this wave's LDS (and scalar-memory) operations have completed,
+// vector memory left in flight.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Words of a raw buffer resource over `bytes` bytes at `base` (gfx9: stride 0,
 // 32-bit data format).  Loads at offsets >= bytes return zeros.
 __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
