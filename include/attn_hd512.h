@@ -45,7 +45,11 @@
  *   keys j < kv_lens[b] are ever read: page slots and table entries past the
  *   live band may hold anything, NaN included, without affecting results
  *   (pegainfer issue 1051, "Acceptance Criteria"; Flash-Decoding for MQA in
- *   CUDA, "The test that catches what parity misses").
+ *   CUDA, "The test that catches what parity misses").  Inside the live band
+ *   a NaN key row makes exactly the rows that attend to it NaN; a NaN or
+ *   infinite value row does the same and may also reach rows that share its
+ *   64-key tile without attending to it (masked keys enter P.V with p = 0,
+ *   and 0 x NaN is NaN).
  */
 #ifndef ATTN_HD512_H
 #define ATTN_HD512_H
