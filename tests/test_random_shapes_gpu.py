@@ -1,0 +1,152 @@
+"""Seeded random shapes through every prefill entry point, against the oracle.
+
+Each case draws a ragged batch (1-4 sequences, chunk lengths 1-150 at
+offsets 0-2000), a GQA group g in {1, 2, 3, 4, 8, 16} over 1, 2 or 4 KV
+heads, the pool and output dtypes, and one entry point: the plain or _ex
+prefill (random sinks, log-sum-exp), the split-K prefill (random range
+length or the default plan), the prefill with the KV append fused (bf16
+pool; also bitwise against append_kv + prefill), or the sliding-window
+prefill (head dim 256 or 512, random window, unbounded or ring cache).
+Every element of every written row is held to the parity gate; rows past
+total_q must stay untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_workloads as W
+import oracle
+from _gpu_helpers import check_parity, library, out_tensor, sentinel_intact
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 64
+LSE_ATOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def A():
+    return library()
+
+
+def draw(i):
+    g_rng = np.random.default_rng(1000 + i)
+    mode = ["prefill", "splitk", "append", "swa"][i % 4]
+    batch = int(g_rng.integers(1, 5))
+    seqs = []
+    for _ in range(batch):
+        ql = int(g_rng.integers(1, 151))
+        st = int(g_rng.integers(0, 2001)) if g_rng.random() < 0.8 else 0
+        seqs.append((ql, st, st + ql))
+    g = int(g_rng.choice([1, 2, 3, 4, 8, 16]))
+    hkv = int(g_rng.choice([1, 2, 4]))
+    while g * hkv > 32:
+        hkv //= 2
+    kv = "bf16" if mode in ("append", "swa") else str(g_rng.choice(["bf16", "fp8_e4m3"]))
+    out = str(g_rng.choice(["fp32", "bf16"]))
+    extra = {}
+    if mode == "prefill":
+        extra["sinks"] = g_rng.random() < 0.5
+        extra["lse"] = g_rng.random() < 0.5
+    elif mode == "splitk":
+        extra["kps"] = int(g_rng.choice([0, 64, 128, 320, 1024]))
+        extra["sinks"] = g_rng.random() < 0.5
+    elif mode == "swa":
+        d = int(g_rng.choice([256, 512]))
+        window = int(g_rng.integers(1, 1500))
+        max_ql = max(s[0] for s in seqs)
+        ring = 0
+        if g_rng.random() < 0.5:
+            # the ring must hold every row's band: q_len + window - 1 slots
+            ring = -(-(max_ql + window - 1) // 64) + int(g_rng.integers(0, 3))
+            max_pages = max(-(-s[2] // 64) for s in seqs)
+            if ring >= max_pages:
+                ring = 0
+        extra.update(d=d, window=window, ring=ring)
+    return mode, seqs, g * hkv, hkv, kv, out, extra
+
+
+def _check_lse(got, ref, what):
+    gl = got.cpu().numpy()
+    assert np.array_equal(np.isinf(gl), np.isinf(ref)), f"{what}: lse infinities differ"
+    fin = np.isfinite(ref)
+    err = float(np.abs(gl[fin] - ref[fin]).max()) if fin.any() else 0.0
+    assert err <= LSE_ATOL, f"{what}: lse error {err}"
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape(A, i):
+    mode, seqs, hq, hkv, kv, out_dtype, ex = draw(i)
+    what = f"case {i}: {mode} {seqs} {hq}/{hkv} {kv} out={out_dtype} {ex}"
+    print(f"[case] {what}", flush=True)
+    kw = dict(seqs=seqs, hq=hq, hkv=hkv, seed=2000 + i, out_dtype=out_dtype, device="cuda",
+              kv_dtype=kv, q_pad_rows=2, extra_pages=2, table_pad=2)
+    if mode == "swa":
+        kw.update(head_dim=ex["d"], window=ex["window"], ring_pages=ex["ring"])
+    case = W.build_case(f"rand{i}", **kw)
+    lc = case.launches[0]
+    d = case.head_dim
+    out = out_tensor(lc.total_q, hq, out_dtype, 2, head_dim=d)
+    common = dict(total_q=lc.total_q, max_q_len=lc.max_q_len, softmax_scale=case.softmax_scale)
+    sinks = None
+    lse = None
+    if ex.get("sinks"):
+        sinks = np.random.default_rng(i).uniform(-2.0, 6.0, hq).astype(np.float32)
+    sk = None if sinks is None else torch.as_tensor(sinks, device="cuda")
+    if mode == "prefill":
+        if ex.get("lse"):
+            lse = torch.full((lc.total_q, hq), float("nan"), device="cuda")
+        A.prefill(lc.q, case.k_pool, case.v_pool, case.page_table, lc.cu_seqlens_q,
+                  lc.q_start, lc.kv_len, out, kv_dtype=kv, k_scale=case.k_scale,
+                  v_scale=case.v_scale, sinks=sk, lse=lse, **common)
+    elif mode == "splitk":
+        nb = A.prefill_splitk_workspace_size(lc.batch, lc.max_q_len, lc.total_q, hq, hkv,
+                                             lc.max_kv_len, ex["kps"])
+        ws = torch.full((max(nb, 4) // 4,), float("nan"), device="cuda") if nb else None
+        A.prefill_splitk(lc.q, case.k_pool, case.v_pool, case.page_table, lc.cu_seqlens_q,
+                         lc.q_start, lc.kv_len, out, ws, max_kv_len=lc.max_kv_len,
+                         keys_per_split=ex["kps"], kv_dtype=kv, k_scale=case.k_scale,
+                         v_scale=case.v_scale, sinks=sk, **common)
+    elif mode == "append":
+        # the chunk's own rows, gathered from the built cache; their slots
+        # are then poisoned in the pools the two calls start from
+        pages, slots = [], []
+        for b, (ql, st) in enumerate(zip(lc.q_lens, lc.q_starts)):
+            pos = torch.arange(st, st + ql, device="cuda")
+            pages.append(case.page_table[b, pos // 64].long())
+            slots.append(pos % 64)
+        pages, slots = torch.cat(pages), torch.cat(slots)
+        kn = case.k_pool[pages, :, slots, :].contiguous()
+        vn = case.v_pool[pages, :, slots, :].contiguous()
+        pools = []
+        for _ in range(2):
+            kp, vp = case.k_pool.clone(), case.v_pool.clone()
+            kp[pages, :, slots, :] = float("nan")
+            vp[pages, :, slots, :] = float("nan")
+            pools.append((kp, vp))
+        A.prefill_append(lc.q, kn, vn, pools[0][0], pools[0][1], case.page_table,
+                         lc.cu_seqlens_q, lc.q_start, lc.kv_len, out, **common)
+        out2 = out_tensor(lc.total_q, hq, out_dtype, 2, head_dim=d)
+        A.append_kv(kn, vn, case.page_table, lc.cu_seqlens_q, lc.q_start, pools[1][0],
+                    pools[1][1])
+        A.prefill(lc.q, pools[1][0], pools[1][1], case.page_table, lc.cu_seqlens_q,
+                  lc.q_start, lc.kv_len, out2, **common)
+        torch.cuda.synchronize()
+        view = torch.int32 if out.dtype == torch.float32 else torch.int16
+        assert torch.equal(out.view(view), out2.view(view)), f"{what}: fused != append + prefill"
+        assert torch.equal(pools[0][0].view(torch.int16), pools[1][0].view(torch.int16))
+        assert torch.equal(pools[0][1].view(torch.int16), pools[1][1].view(torch.int16))
+    else:
+        A.prefill_swa(lc.q, case.k_pool, case.v_pool, case.page_table, lc.cu_seqlens_q,
+                      lc.q_start, lc.kv_len, out, window=case.window,
+                      ring_pages=case.ring_pages, **common)
+    torch.cuda.synchronize()
+    assert sentinel_intact(out[lc.total_q:]), f"{what}: rows past total_q were written"
+    cpu = case.to("cpu")
+    if sinks is not None or lse is not None:
+        ref, ref_lse = oracle.attend_all_lse(cpu, sinks=sinks)
+    else:
+        ref, ref_lse = oracle.attend_all(cpu), None
+    check_parity(out[:lc.total_q], ref, what)
+    if lse is not None:
+        _check_lse(lse, ref_lse, what)
