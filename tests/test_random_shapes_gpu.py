@@ -1,4 +1,5 @@
-"""Seeded random shapes through every prefill entry point, against the oracle.
+"""Seeded random shapes through every prefill entry point and the split-K
+decode, against the oracle.
 
 Each case draws a ragged batch (1-4 sequences, chunk lengths 1-150 at
 offsets 0-2000), a GQA group g in {1, 2, 3, 4, 8, 16} over 1, 2 or 4 KV
@@ -7,8 +8,10 @@ prefill (random sinks, log-sum-exp), the split-K prefill (random range
 length or the default plan), the prefill with the KV append fused (bf16
 pool; also bitwise against append_kv + prefill), or the sliding-window
 prefill (head dim 256 or 512, random window, unbounded or ring cache).
-Every element of every written row is held to the parity gate; rows past
-total_q must stay untouched.
+Decode cases draw 1-8 sequences of 1-6000 keys, 1 to 16 / g tokens each,
+the range length (or the default plan), both pools, sinks and the
+log-sum-exp.  Every element of every written row is held to the parity
+gate; rows past the written ones must stay untouched.
 """
 import numpy as np
 import pytest
@@ -150,3 +153,43 @@ def test_random_shape(A, i):
     check_parity(out[:lc.total_q], ref, what)
     if lse is not None:
         _check_lse(lse, ref_lse, what)
+
+
+def draw_decode(i):
+    g_rng = np.random.default_rng(5000 + i)
+    g = int(g_rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(g_rng.choice([1, 2, 4]))
+    q_len = int(g_rng.integers(1, min(16 // g, 5) + 1))
+    batch = int(g_rng.integers(1, 9))
+    lens = [int(g_rng.integers(q_len, 6001)) for _ in range(batch)]
+    kps = int(g_rng.choice([0, 64, 256, 1024]))
+    kv = str(g_rng.choice(["bf16", "fp8_e4m3"]))
+    out = str(g_rng.choice(["fp32", "bf16"]))
+    sinks = bool(g_rng.random() < 0.5)
+    return lens, q_len, g * hkv, hkv, kps, kv, out, sinks
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_decode_shape(A, i):
+    lens, q_len, hq, hkv, kps, kv, out_dtype, with_sinks = draw_decode(i)
+    what = f"decode case {i}: lens={lens} q_len={q_len} {hq}/{hkv} kps={kps} {kv} {out_dtype}"
+    print(f"[case] {what}", flush=True)
+    case = W.build_case(f"rdec{i}", seqs=[(q_len, L - q_len, L) for L in lens], hq=hq, hkv=hkv,
+                        seed=6000 + i, out_dtype=out_dtype, device="cuda", kv_dtype=kv)
+    lc = case.launches[0]
+    B = lc.batch
+    out = out_tensor(B * q_len, hq, out_dtype, 2)
+    lse = torch.full((B * q_len, hq), float("nan"), device="cuda")
+    sinks = np.random.default_rng(i).uniform(-2.0, 6.0, hq).astype(np.float32) if with_sinks \
+        else None
+    nbytes = A.decode_workspace_size(B, hq, hkv, lc.max_kv_len, kps, q_len=q_len)
+    ws = torch.full((nbytes // 4,), float("nan"), device="cuda")
+    A.decode(lc.q[:B * q_len], case.k_pool, case.v_pool, case.page_table, lc.kv_len, out, ws,
+             max_kv_len=lc.max_kv_len, softmax_scale=case.softmax_scale, kv_dtype=kv,
+             k_scale=case.k_scale, v_scale=case.v_scale, keys_per_split=kps, q_len=q_len,
+             sinks=None if sinks is None else torch.as_tensor(sinks, device="cuda"), lse=lse)
+    torch.cuda.synchronize()
+    assert sentinel_intact(out[B * q_len:]), f"{what}: rows past the batch were written"
+    ref, ref_lse = oracle.attend_all_lse(case.to("cpu"), sinks=sinks)
+    check_parity(out[:B * q_len], ref, what)
+    _check_lse(lse, ref_lse, what)
