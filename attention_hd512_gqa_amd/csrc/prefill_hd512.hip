@@ -925,6 +925,49 @@ void prefill_hd512_kernel(PrefillArgs a) {
     }
     if (a.lse && valid && h == 0)
         a.lse[(size_t)(q0 + t) * a.hq + head] = lse2 * 0.6931471805599453f;
+    // bf16 output through LDS: a lane holds 4-dim pieces of its row spread
+    // over the row, so storing them directly puts 16-byte pieces of 32 rows
+    // in every store instruction.  Each wave instead writes its 32 rows into
+    // its own part of the (then free) tile buffers and stores them back one
+    // whole row per instruction.  16-byte chunk c of a staged row r sits at
+    // chunk c ^ (r & 15), so the 16 rows one write instruction covers fall in
+    // distinct bank groups.
+    constexpr int kOutRowB = D * 2;
+    constexpr bool kStageOut = !OUT_FP32 && 2 * kTileB >= kWaves * 32 * kOutRowB;
+    if constexpr (kStageOut) {
+        wait_vmcnt<0>();     // every wave's refills have landed ...
+        __syncthreads();     // ... and no wave reads the tiles any more
+        ATTN_LDS char* stage = (ATTN_LDS char*)smem + wave * 32 * kOutRowB;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                f32x4 v = {o[db][4 * q4] / l_tot, o[db][4 * q4 + 1] / l_tot,
+                           o[db][4 * q4 + 2] / l_tot, o[db][4 * q4 + 3] / l_tot};
+                if constexpr (FP8) v *= vs;
+                const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+                const int c = 4 * db + q4;   // dims 32 db + 8 q4 .. + 7; this lane's half: 4 h
+                *(ATTN_LDS bf16x4*)(stage + n * kOutRowB + ((c ^ (n & 15)) << 4) + 8 * h) = w;
+            }
+        }
+        // lane l moves chunk l % (kOutRowB / 16) of staged row
+        // 64 i / (kOutRowB / 16) + l / (kOutRowB / 16)
+        constexpr int kChunks = kOutRowB / 16;
+        constexpr int kRowsPerStore = 64 / kChunks;
+        const int cl = lane % kChunks;
+#pragma unroll 4
+        for (int i = 0; i < 32 / kRowsPerStore; ++i) {
+            const int rr = i * kRowsPerStore + lane / kChunks;   // staged row
+            const int pr = wave * 32 + rr;                       // packed row of the workgroup
+            const int trr = pr / a.g;
+            const bf16x8 x = *(const ATTN_LDS bf16x8*)(stage + rr * kOutRowB + ((cl ^ (rr & 15)) << 4));
+            if (trr < a.tok_per_wg && t0 + trr <= t_last) {
+                const size_t ob = ((size_t)(q0 + t0 + trr) * a.hq + kvh * a.g + (pr - trr * a.g)) * D;
+                *(bf16x8*)((__bf16*)a.out + ob + 8 * cl) = x;
+            }
+        }
+        return;
+    }
     if (valid) {
         const size_t obase = ((size_t)(q0 + t) * a.hq + head) * D;
 #pragma unroll
