@@ -40,9 +40,9 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "357e637ef3359f7f5198a5ba2f9d29e5557dbd484e824a720a1363120d780e1d",
-    "fetch_bytes": 1993815134,
-    "write_bytes": 287395226,
+    "sha256": "bc6c041faba515c8917d8205823ce85193d1d43bd5705a2e600e356b6f8297c0",
+    "fetch_bytes": 2005256880,
+    "write_bytes": 268435456,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
 
