@@ -44,6 +44,9 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_hd512_ex.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I, I,
                                             I, I, F, P, P, I, P, P]
         L.attn_prefill_hd512_ex.restype = I
+        L.attn_prefill_hd512_e4m3_mma.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I, I, I,
+                                                  I, I, I, F, P, P, I, P, P]
+        L.attn_prefill_hd512_e4m3_mma.restype = I
         L.attn_prefill_hd512_append.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
                                                 I, I, I, F, P, P, I, P, P]
         L.attn_prefill_hd512_append.restype = I
@@ -115,12 +118,13 @@ def _opt(t, name, dtype, numel):
 def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out, *,
             total_q: int, max_q_len: int, softmax_scale: float, kv_dtype: str = "bf16",
             k_scale: float = 1.0, v_scale: float = 1.0, sinks=None, lse=None,
-            stream=None) -> None:
+            fp8_mma: bool = False, stream=None) -> None:
     """Chunked causal prefill over a bf16 pool (attn_prefill_hd512) or an
     FP8-E4M3 pool with per-tensor scales (attn_prefill_hd512_e4m3); with
     per-head sink logits `sinks` (fp32 [Hq]) or a log-sum-exp output `lse`
-    (fp32 [total_q, Hq]) it calls attn_prefill_hd512_ex.  Sizes are host ints:
-    no sync."""
+    (fp32 [total_q, Hq]) it calls attn_prefill_hd512_ex.  fp8_mma (FP8 pool
+    only) runs both products on the block-scaled FP8 matrix core instead
+    (attn_prefill_hd512_e4m3_mma).  Sizes are host ints: no sync."""
     num_pages, hkv, page, d = k_pages.shape
     hq = q.shape[1]
     batch = kv_lens.shape[0]
@@ -133,7 +137,16 @@ def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out
     if kv_dtype not in _KV_CODES:
         raise AttnError(f"unsupported kv_dtype {kv_dtype!r}")
     kvt = torch.bfloat16 if kv_dtype == "bf16" else torch.uint8
-    if sinks is not None or lse is not None:
+    if fp8_mma:
+        if kv_dtype != "fp8_e4m3":
+            raise AttnError("fp8_mma needs kv_dtype 'fp8_e4m3'")
+        code = lib().attn_prefill_hd512_e4m3_mma(
+            _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
+            _dev(v_pages, "v_pages", kvt), float(k_scale), float(v_scale), *meta[:14],
+            _opt(sinks, "sinks", torch.float32, hq), meta[14], meta[15],
+            _opt(lse, "lse", torch.float32, int(total_q) * hq), meta[16])
+        _check(code, "attn_prefill_hd512_e4m3_mma")
+    elif sinks is not None or lse is not None:
         code = lib().attn_prefill_hd512_ex(
             _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
             _dev(v_pages, "v_pages", kvt), _KV_CODES[kv_dtype], float(k_scale), float(v_scale),

@@ -49,6 +49,7 @@
 // that prefill_merge_kernel combines.
 #include "device_common.h"
 #include "attn_host.h"
+#include "prefill_common.h"
 
 #include <type_traits>
 
@@ -56,27 +57,12 @@ namespace attn {
 
 namespace {
 
-constexpr int kRowsPerWg = 128;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWaveLoad = kPage / kWaves;  // tile rows each wave moves
-// Largest allowed excess (log2 units) of a row's scores over its reference
-// maximum: p <= 2^32 and l <= 2^32 * keys stay far inside fp32 and bf16.
-constexpr float kRescaleMargin = 32.f;
-constexpr float kOverSum = 4294967296.f;   // 2^kRescaleMargin
-constexpr float kBlindRaise = 123.f;       // log2(FLT_MAX / 32), rounded down
 constexpr int kPrefetch = 4;  // LDS operand reads in flight ahead of their MFMA
 // FP8 operands are widened in registers; one fewer read in flight keeps the
 // FP8 kernel inside the 256 VGPRs
 template <bool FP8>
 constexpr int kPrefetchOf = FP8 ? 3 : kPrefetch;
-// Page ids of the first kPagesInLds tiles are staged in LDS at the start of
-// the workgroup (reading them from the scalar cache inside the loop stalls
-// the wave: scalar loads share the LDS wait counter and return out of order).
-constexpr int kPagesInLds = 4096;
-// Restarts per workgroup are capped so that non-finite inputs (a caller error)
-// cannot loop forever; each genuine restart raises a row's reference by > 32.
-constexpr int kMaxRestarts = 8;
 
 // K/V tile geometry for a pool element (bf16, or FP8-E4M3 bytes) and a head
 // dim D (512 for the global layers, 256 for the sliding-window ones).  Rows
@@ -110,33 +96,6 @@ __host__ __device__ constexpr int swzN(int r) {
     return ((r & 3) << 2) | ((r >> 2) & 3) | (r & 16);
 }
 
-struct PrefillArgs {
-    const __bf16* q;
-    const char* k_pages;
-    const char* v_pages;
-    const int* page_table;
-    const int* cu_seqlens_q;
-    const int* q_start;
-    const int* kv_lens;
-    void* out;
-    int batch, total_q, hq, hkv, g, max_pages, num_pages;
-    int tok_per_wg;     // tokens per workgroup = 128 / g (rounded down)
-    int wgs_per_seq;    // ceil(max_q_len / tok_per_wg)
-    float scale_log2;   // softmax_scale * log2(e) (* k_scale for an FP8 pool)
-    float v_scale;      // FP8 pool: value dequantisation scale, applied to O (1 for bf16)
-    const float* sinks; // per query head sink logit (natural-log units), or null
-    float* lse;         // [total_q][hq] natural-log log-sum-exp, or null
-    // split-K over keys: workgroup split s covers key tiles
-    // [s split_tiles, (s + 1) split_tiles) and writes unnormalised partials
-    int nsplit, split_tiles;
-    float* part_o;      // [nsplit][total_q][hq][512] fp32, O * v_scale
-    float* part_ml;     // [nsplit][total_q][hq][2]  (m in log2 units, l)
-    int window;         // sliding window in keys (0: none)
-    int ring_pages;     // ring cache pages per sequence (0: unbounded cache)
-    // fused append: the chunk's new K and V rows, bf16 [total_q][hkv][512]
-    const char* k_new;
-    const char* v_new;
-};
 
 // Refill of one 32-key half (rows 32 half .. 32 half + 31) of a K or V tile
 // buffer from one (page, KV head) tile: each wave moves rows
@@ -289,18 +248,6 @@ __device__ __forceinline__ void softmax_flush(float& psum, float pend, bf16x8& p
     pf1[7] = (__bf16)pend;
 }
 
-// Masks one block's raw scores in place: element i is key
-// key_base + 8(i/4) + (i%4) (key_base includes 4h); keys >= n_row get -inf,
-// and with a window so do keys < lo_row.
-template <bool WINDOW>
-__device__ __forceinline__ void mask_block(f32x16& s, int key_base, int n_row, int lo_row) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int key = key_base + 8 * (i >> 2) + (i & 3);
-        const bool vis = WINDOW ? (key < n_row && key >= lo_row) : key < n_row;
-        s[i] = vis ? s[i] : -__builtin_inff();
-    }
-}
 
 // Sliding window: a row's reference maximum is the maximum of the first
 // 32-key block in which it sees a key (rows start their windows at different
@@ -1120,10 +1067,12 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
                    const float* sinks, void* out, int out_dtype, float* lse,
                    bool splitk, int max_kv_len, int keys_per_split, void* workspace,
                    size_t workspace_bytes, bool swa, int window, int ring_pages,
-                   const void* k_new, const void* v_new, hipStream_t stream) {
+                   const void* k_new, const void* v_new, bool fp8_mma, hipStream_t stream) {
     // the sliding-window entry is bf16 and single-pass; so is the fused append
-    // (given both new-row buffers or neither), at head dim 512 with no window
+    // (given both new-row buffers or neither), at head dim 512 with no window;
+    // the FP8-MFMA form is FP8, single-pass, at head dim 512
     const bool append = k_new || v_new;
+    if (fp8_mma && (!fp8 || splitk || swa || append)) return ATTN_ERR_UNSUPPORTED;
     if (swa && (fp8 || splitk)) return ATTN_ERR_UNSUPPORTED;
     if (append && (!k_new || !v_new)) return ATTN_ERR_NULL;
     if (append && (fp8 || splitk || swa)) return ATTN_ERR_UNSUPPORTED;
@@ -1218,7 +1167,9 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     const dim3 gd((unsigned)grid);
     const bool f32 = out_dtype == ATTN_FP32;
-    if (append) {
+    if (fp8_mma) {
+        launch_prefill_fp8mma(a, f32, (unsigned)grid, stream);
+    } else if (append) {
         if (f32)
             hipLaunchKernelGGL((prefill_hd512_kernel<true, false, false, kHeadDim, false, true>),
                                gd, dim3(kThreads), 0, stream, a);
@@ -1248,7 +1199,7 @@ extern "C" int attn_prefill_hd512(const void* q, const void* k_pages, const void
                                 q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
                                 softmax_scale, nullptr, out, out_dtype, nullptr, false, 0, 0, nullptr,
-                                0, false, 0, 0, nullptr, nullptr, stream);
+                                0, false, 0, 0, nullptr, nullptr, false, stream);
 }
 
 extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const void* v_pages,
@@ -1263,7 +1214,7 @@ extern "C" int attn_prefill_hd512_e4m3(const void* q, const void* k_pages, const
                                 cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
                                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                                 max_pages_per_seq, softmax_scale, nullptr, out, out_dtype,
-                                nullptr, false, 0, 0, nullptr, 0, false, 0, 0, nullptr, nullptr, stream);
+                                nullptr, false, 0, 0, nullptr, 0, false, 0, 0, nullptr, nullptr, false, stream);
 }
 
 extern "C" int attn_prefill_hd512_ex(const void* q, const void* k_pages, const void* v_pages,
@@ -1282,7 +1233,7 @@ extern "C" int attn_prefill_hd512_ex(const void* q, const void* k_pages, const v
                           page_table, cu_seqlens_q, q_start_pos, kv_lens, batch, total_q,
                           max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                           max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, false, 0,
-                          0, nullptr, 0, false, 0, 0, nullptr, nullptr, stream);
+                          0, nullptr, 0, false, 0, 0, nullptr, nullptr, false, stream);
 }
 
 extern "C" size_t attn_prefill_hd512_splitk_workspace_size(int batch, int max_q_len,
@@ -1322,7 +1273,7 @@ extern "C" int attn_prefill_hd512_splitk(const void* q, const void* k_pages, con
                           max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                           max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, true,
                           max_kv_len, keys_per_split, workspace, workspace_bytes, false, 0, 0, nullptr,
-                          nullptr, stream);
+                          nullptr, false, stream);
 }
 
 extern "C" int attn_prefill_swa(const void* q, const void* k_pages, const void* v_pages,
@@ -1337,7 +1288,7 @@ extern "C" int attn_prefill_swa(const void* q, const void* k_pages, const void* 
                                 q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
                                 softmax_scale, nullptr, out, out_dtype, nullptr, false, 0, 0,
-                                nullptr, 0, true, window, ring_pages, nullptr, nullptr, stream);
+                                nullptr, 0, true, window, ring_pages, nullptr, nullptr, false, stream);
 }
 
 extern "C" int attn_prefill_hd512_append(const void* q, const void* k_new, const void* v_new,
@@ -1354,5 +1305,23 @@ extern "C" int attn_prefill_hd512_append(const void* q, const void* k_new, const
                                 q_start_pos, kv_lens, batch, total_q, max_q_len, num_q_heads,
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
                                 softmax_scale, sinks, out, out_dtype, lse, false, 0, 0, nullptr,
-                                0, false, 0, 0, k_new, v_new, stream);
+                                0, false, 0, 0, k_new, v_new, false, stream);
+}
+
+extern "C" int attn_prefill_hd512_e4m3_mma(const void* q, const void* k_pages,
+                                           const void* v_pages, float k_scale, float v_scale,
+                                           const int32_t* page_table,
+                                           const int32_t* cu_seqlens_q,
+                                           const int32_t* q_start_pos, const int32_t* kv_lens,
+                                           int batch, int total_q, int max_q_len,
+                                           int num_q_heads, int num_kv_heads, int head_dim,
+                                           int page_size, int num_pages, int max_pages_per_seq,
+                                           float softmax_scale, const float* sinks, void* out,
+                                           int out_dtype, float* lse, hipStream_t stream) {
+    return attn::prefill_launch(q, k_pages, v_pages, true, k_scale, v_scale, page_table,
+                                cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
+                                num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                                max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse,
+                                false, 0, 0, nullptr, 0, false, 0, 0, nullptr, nullptr, true,
+                                stream);
 }

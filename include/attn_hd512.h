@@ -161,6 +161,38 @@ int attn_prefill_hd512_ex(const void* q, const void* k_pages, const void* v_page
                           hipStream_t stream);
 
 /*
+ * Chunked causal prefill over an FP8-E4M3 KV cache with both products on the
+ * gfx950 block-scaled FP8 matrix core (the FP8-MMA form of vLLM
+ * flash-attention PR 199, "Summary": FP8 KV and FP8 QK/PV MMA).  Arguments,
+ * semantics and results as attn_prefill_hd512_ex with kv_dtype
+ * ATTN_FP8_E4M3, up to the rounding of the two operands that are not E4M3
+ * already:
+ *
+ *   Q            each 32 consecutive head dims of a row are scaled by a power
+ *                of two (from their largest magnitude) and split into two
+ *                E4M3 terms, a high part and a residual x 32 (second review,
+ *                commit 4 and finding F1), about 8 significant bits; any
+ *                finite bf16 Q is in range (finding F2's |q| <= 448 limit of
+ *                a fixed scale does not apply).
+ *   P            the softmax weights of each 32-key block of a row are scaled
+ *                by a power of two from the block's largest weight and split
+ *                the same way; weights below about 2^-21 of that maximum lose
+ *                relative precision (finding F1).
+ *
+ * Products accumulate in fp32 (O over the whole key range).  head_dim 512
+ * only; ATTN_ERR_UNSUPPORTED otherwise.  Other errors as for
+ * attn_prefill_hd512_e4m3.
+ */
+int attn_prefill_hd512_e4m3_mma(const void* q, const void* k_pages, const void* v_pages,
+                                float k_scale, float v_scale, const int32_t* page_table,
+                                const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
+                                const int32_t* kv_lens, int batch, int total_q, int max_q_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                                int num_pages, int max_pages_per_seq, float softmax_scale,
+                                const float* sinks, void* out, int out_dtype, float* lse,
+                                hipStream_t stream);
+
+/*
  * Chunked causal prefill of a sliding-window (local) layer over a bf16 pool,
  * at head_dim 256 (the local layers' heads; A custom attention kernel for
  * Gemma 4 on the RTX PRO 6000, "The deployment": local layers attend to the

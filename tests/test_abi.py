@@ -271,3 +271,22 @@ def test_probe_validation(L):
     assert L.attn_hbm_read_probe(None, 1024, FAKE, None) == 1
     assert L.attn_hbm_read_probe(FAKE, 1000, FAKE, None) == 2
     assert L.attn_hbm_probe_sink_words(1 << 20) >= 1
+
+
+def test_prefill_fp8_mma_validation(L):
+    def pm(**over):
+        a = dict(q=FAKE, ks=1.0, vs=1.0, batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=512,
+                 page=64, out_dtype=1)
+        a.update(over)
+        return L.attn_prefill_hd512_e4m3_mma(
+            a["q"], FAKE, FAKE, a["ks"], a["vs"], FAKE, FAKE, FAKE, FAKE, a["batch"],
+            a["total_q"], a["max_q_len"], a["hq"], a["hkv"], a["d"], a["page"], 4, 4, 0.04,
+            None, FAKE, a["out_dtype"], None, None)
+    assert pm(q=None) == 1
+    assert pm(ks=0.0) == 2
+    assert pm(vs=-1.0) == 2
+    assert pm(d=256) == 3
+    assert pm(page=16) == 3
+    assert pm(hq=6, hkv=4) == 2
+    assert pm(out_dtype=2) == 3
+    assert pm(total_q=0, max_q_len=0) == 0
