@@ -39,9 +39,10 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 # SHA-256 is checked at run time and traffic is reported as null otherwise.
 TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
+                "attention_hd512_gqa_amd/csrc/prefill_common.h",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "bc6c041faba515c8917d8205823ce85193d1d43bd5705a2e600e356b6f8297c0",
-    "fetch_bytes": 2005256880,
+    "sha256": "956a6767d30bf9c349714153c72beceb4921fdc5f42aa339d9849c784e6d1620",
+    "fetch_bytes": 2006652945,
     "write_bytes": 268435456,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
@@ -214,14 +215,21 @@ def main():
         c8 = W.chunk_prefill_8k_at_8k(device="cuda", kv_dtype="fp8_e4m3")
         l8 = c8.launches[0]
 
-        def fp8_step():
+        def fp8_step(mma):
             A.prefill(l8.q, c8.k_pool, c8.v_pool, c8.page_table, l8.cu_seqlens_q, l8.q_start,
                       l8.kv_len, out, total_q=l8.total_q, max_q_len=l8.max_q_len,
                       softmax_scale=c8.softmax_scale, kv_dtype="fp8_e4m3", k_scale=c8.k_scale,
-                      v_scale=c8.v_scale, stream=stream)
-        ms8 = timed(fp8_step, args.steps, args.warmup)
+                      v_scale=c8.v_scale, fp8_mma=mma, stream=stream)
+        ms8 = timed(lambda: fp8_step(False), args.steps, args.warmup)
         extra["chunk_prefill_8192_at_8192_fp8"] = {"ms_per_launch": ms8,
                                                    "tflops": flops / (ms8 * 1e-3) / 1e12}
+        # the same bytes with both products on the block-scaled FP8 MFMA
+        ms8m = timed(lambda: fp8_step(True), args.steps, args.warmup)
+        extra["chunk_prefill_8192_at_8192_fp8_mma"] = {
+            "ms_per_launch": ms8m, "tflops": flops / (ms8m * 1e-3) / 1e12,
+            "frac_of_fp8_dense_peak": flops / (ms8m * 1e-3) / 5.0e15}
+        log(f"FP8 pool: widened {ms8:.3f} ms, FP8 MFMA {ms8m:.3f} ms "
+            f"({flops / (ms8m * 1e-3) / 1e12:.1f} TFLOP/s)")
         del c8
         torch.cuda.empty_cache()
         # a short chunk over a long prefix: single pass against split-K

@@ -40,13 +40,14 @@ def sentinel_intact(t: torch.Tensor) -> bool:
     return bool((t.view(torch.int16) == SENTINEL_BF16).all())
 
 
-def run_prefill(A, case, li: int = 0, out_dtype: str = None, pad_rows: int = 0):
+def run_prefill(A, case, li: int = 0, out_dtype: str = None, pad_rows: int = 0,
+                fp8_mma: bool = False):
     lc = case.launches[li]
     out = out_tensor(lc.total_q, case.num_q_heads, out_dtype or case.out_dtype, pad_rows)
     A.prefill(lc.q, case.k_pool, case.v_pool, case.page_table, lc.cu_seqlens_q, lc.q_start,
               lc.kv_len, out, total_q=lc.total_q, max_q_len=lc.max_q_len,
               softmax_scale=case.softmax_scale, kv_dtype=case.kv_dtype,
-              k_scale=case.k_scale, v_scale=case.v_scale)
+              k_scale=case.k_scale, v_scale=case.v_scale, fp8_mma=fp8_mma)
     torch.cuda.synchronize()
     return out
 

@@ -45,27 +45,30 @@ def _compare(got, ref, what):
     check_parity(got[torch.as_tensor(keep, device=got.device)], ref[keep], what)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
-def test_prefill_nan_key_poisons_exactly_its_attenders(A, kv_dtype):
+PREFILL_PATHS = [("bf16", False), ("fp8_e4m3", False), ("fp8_e4m3", True)]
+
+
+@pytest.mark.parametrize("kv_dtype,mma", PREFILL_PATHS, ids=["bf16", "fp8", "fp8_mma"])
+def test_prefill_nan_key_poisons_exactly_its_attenders(A, kv_dtype, mma):
     case = W.build_case("nan_pf", seqs=[(100, 200, 300), (50, 0, 50)], hq=16, hkv=2, seed=83,
                         out_dtype="fp32", device="cuda", kv_dtype=kv_dtype)
     # key 250 of sequence 0, KV head 1: chunk rows at positions >= 250 of
     # heads 8..15 see it; positions 200..249 and sequence 1 do not
     _plant_nan(case, 0, 250, 1, "k", kv_dtype)
-    out = run_prefill(A, case)
+    out = run_prefill(A, case, fp8_mma=mma)
     lc = case.launches[0]
     ref = oracle.attend_all(case.to("cpu"))
-    _compare(out[:lc.total_q], ref, f"prefill NaN k {kv_dtype}")
+    _compare(out[:lc.total_q], ref, f"prefill NaN k {kv_dtype} mma={mma}")
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
-def test_prefill_nan_value_stays_in_its_tile(A, kv_dtype):
+@pytest.mark.parametrize("kv_dtype,mma", PREFILL_PATHS, ids=["bf16", "fp8", "fp8_mma"])
+def test_prefill_nan_value_stays_in_its_tile(A, kv_dtype, mma):
     hq, hkv = 16, 2
     case = W.build_case("nan_pf_v", seqs=[(100, 150, 250), (50, 0, 50)], hq=hq, hkv=hkv,
                         seed=83, out_dtype="fp32", device="cuda", kv_dtype=kv_dtype)
     j = 230                                   # tile 3: keys 192..255
     _plant_nan(case, 0, j, 1, "v", kv_dtype)
-    out = run_prefill(A, case)
+    out = run_prefill(A, case, fp8_mma=mma)
     lc = case.launches[0]
     ref = oracle.attend_all(case.to("cpu"))
     got = out[:lc.total_q].float().cpu().numpy()
@@ -83,7 +86,7 @@ def test_prefill_nan_value_stays_in_its_tile(A, kv_dtype):
     keep = ~nan_got
     keep[~clean] = False
     check_parity(out[:lc.total_q][torch.as_tensor(keep, device="cuda")], ref[keep],
-                 f"prefill NaN v {kv_dtype}, clean rows")
+                 f"prefill NaN v {kv_dtype} mma={mma}, clean rows")
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])

@@ -7,7 +7,8 @@ heads, the pool and output dtypes, and one entry point: the plain or _ex
 prefill (random sinks, log-sum-exp), the split-K prefill (random range
 length or the default plan), the prefill with the KV append fused (bf16
 pool; also bitwise against append_kv + prefill), or the sliding-window
-prefill (head dim 256 or 512, random window, unbounded or ring cache).
+prefill (head dim 256 or 512, random window, unbounded or ring cache); 24
+more draw the FP8-MMA prefill with random sinks and log-sum-exp.
 Decode cases draw 1-8 sequences of 1-6000 keys, 1 to 16 / g tokens each,
 the range length (or the default plan), both pools, sinks and the
 log-sum-exp.  Every element of every written row is held to the parity
@@ -193,3 +194,47 @@ def test_random_decode_shape(A, i):
     ref, ref_lse = oracle.attend_all_lse(case.to("cpu"), sinks=sinks)
     check_parity(out[:B * q_len], ref, what)
     _check_lse(lse, ref_lse, what)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_fp8_mma_shape(A, i):
+    # the FP8-MMA prefill (attn_prefill_hd512_e4m3_mma) over the same kind of
+    # ragged batches, with random sinks and log-sum-exp
+    g_rng = np.random.default_rng(9000 + i)
+    batch = int(g_rng.integers(1, 5))
+    seqs = []
+    for _ in range(batch):
+        ql = int(g_rng.integers(1, 151))
+        st = int(g_rng.integers(0, 2001)) if g_rng.random() < 0.8 else 0
+        seqs.append((ql, st, st + ql))
+    g = int(g_rng.choice([1, 2, 3, 4, 8, 16]))
+    hkv = int(g_rng.choice([1, 2, 4]))
+    while g * hkv > 32:
+        hkv //= 2
+    hq = g * hkv
+    out_dtype = str(g_rng.choice(["fp32", "bf16"]))
+    with_extras = bool(g_rng.random() < 0.5)
+    what = f"fp8 mma case {i}: {seqs} {hq}/{hkv} out={out_dtype} extras={with_extras}"
+    print(f"[case] {what}", flush=True)
+    case = W.build_case(f"rmma{i}", seqs=seqs, hq=hq, hkv=hkv, seed=9500 + i,
+                        out_dtype=out_dtype, device="cuda", kv_dtype="fp8_e4m3", q_pad_rows=2,
+                        extra_pages=2, table_pad=2)
+    lc = case.launches[0]
+    out = out_tensor(lc.total_q, hq, out_dtype, 2)
+    sinks = np.random.default_rng(i).uniform(-2.0, 6.0, hq).astype(np.float32) \
+        if with_extras else None
+    lse = torch.full((lc.total_q, hq), float("nan"), device="cuda") if with_extras else None
+    A.prefill(lc.q, case.k_pool, case.v_pool, case.page_table, lc.cu_seqlens_q, lc.q_start,
+              lc.kv_len, out, total_q=lc.total_q, max_q_len=lc.max_q_len,
+              softmax_scale=case.softmax_scale, kv_dtype="fp8_e4m3", k_scale=case.k_scale,
+              v_scale=case.v_scale, fp8_mma=True, lse=lse,
+              sinks=None if sinks is None else torch.as_tensor(sinks, device="cuda"))
+    torch.cuda.synchronize()
+    assert sentinel_intact(out[lc.total_q:]), f"{what}: rows past total_q were written"
+    cpu = case.to("cpu")
+    if with_extras:
+        ref, ref_lse = oracle.attend_all_lse(cpu, sinks=sinks)
+        _check_lse(lse, ref_lse, what)
+    else:
+        ref = oracle.attend_all(cpu)
+    check_parity(out[:lc.total_q], ref, what)
