@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_hd512_splitk.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I,
                                                 I, I, I, I, I, F, P, P, SZ, P, I, P, P]
         L.attn_prefill_hd512_splitk.restype = I
+        L.attn_prefill_hd512_splitk_e4m3_mma.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I,
+                                                         I, I, I, I, I, I, I, F, P, P, SZ, P, I,
+                                                         P, P]
+        L.attn_prefill_hd512_splitk_e4m3_mma.restype = I
         L.attn_decode_splitk_ex_workspace_size.argtypes = [I, I, I, I, I, I]
         L.attn_decode_splitk_ex_workspace_size.restype = SZ
         L.attn_decode_splitk_ex.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, I,
@@ -224,11 +228,12 @@ def prefill_splitk(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_le
                    workspace, *, total_q: int, max_q_len: int, max_kv_len: int,
                    softmax_scale: float, keys_per_split: int = 0, kv_dtype: str = "bf16",
                    k_scale: float = 1.0, v_scale: float = 1.0, sinks=None, lse=None,
-                   stream=None) -> None:
+                   fp8_mma: bool = False, stream=None) -> None:
     """Chunked causal prefill with the key range split across workgroups
     (attn_prefill_hd512_splitk): split kernel then merge kernel, for short
-    chunks over long prefixes.  `workspace` may be None when
-    prefill_splitk_workspace_size(...) is 0."""
+    chunks over long prefixes.  fp8_mma (FP8 pool only) runs each range on
+    the block-scaled FP8 matrix core (attn_prefill_hd512_splitk_e4m3_mma).
+    `workspace` may be None when prefill_splitk_workspace_size(...) is 0."""
     num_pages, hkv, page, d = k_pages.shape
     hq = q.shape[1]
     batch = kv_lens.shape[0]
@@ -239,9 +244,13 @@ def prefill_splitk(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_le
         ws, ws_bytes = None, 0
     else:
         ws, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
-    code = lib().attn_prefill_hd512_splitk(
-        _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
-        _dev(v_pages, "v_pages", kvt), _KV_CODES[kv_dtype], float(k_scale), float(v_scale),
+    if fp8_mma and kv_dtype != "fp8_e4m3":
+        raise AttnError("fp8_mma needs kv_dtype 'fp8_e4m3'")
+    fn = lib().attn_prefill_hd512_splitk_e4m3_mma if fp8_mma else lib().attn_prefill_hd512_splitk
+    head = (_dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
+            _dev(v_pages, "v_pages", kvt)) + (() if fp8_mma else (_KV_CODES[kv_dtype],))
+    code = fn(
+        *head, float(k_scale), float(v_scale),
         _dev(page_table, "page_table", torch.int32),
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(q_start, "q_start", torch.int32),
         _dev(kv_lens, "kv_lens", torch.int32), int(batch), int(total_q), int(max_q_len),
@@ -250,7 +259,7 @@ def prefill_splitk(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_le
         _opt(sinks, "sinks", torch.float32, hq), ws, ws_bytes,
         _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
         _opt(lse, "lse", torch.float32, int(total_q) * hq), _stream(stream))
-    _check(code, "attn_prefill_hd512_splitk")
+    _check(code, "attn_prefill_hd512_splitk_e4m3_mma" if fp8_mma else "attn_prefill_hd512_splitk")
 
 
 def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_kv_len: int,

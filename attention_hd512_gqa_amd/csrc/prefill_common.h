@@ -68,11 +68,12 @@ struct PrefillArgs {
     const char* v_new;
 };
 
-// The FP8-MFMA prefill (single pass over each workgroup's key range) over
-// `grid` workgroups of 256 threads, with the work-unit numbering of the other
-// prefill kernel; enqueues only (launch errors surface through
-// hipGetLastError).
-void launch_prefill_fp8mma(const PrefillArgs& a, bool out_fp32, unsigned grid,
+// The FP8-MFMA prefill over `grid` workgroups of 256 threads, with the
+// work-unit numbering of the other prefill kernel: one pass per workgroup
+// writing out (and lse), or with `split` one key range per workgroup writing
+// the split-K partials (a.part_o, a.part_ml) for prefill_merge_kernel.
+// Enqueues only (launch errors surface through hipGetLastError).
+void launch_prefill_fp8mma(const PrefillArgs& a, bool out_fp32, bool split, unsigned grid,
                            hipStream_t stream);
 
 }  // namespace attn

@@ -170,7 +170,7 @@ __device__ __forceinline__ void softmax_pair(const f32x16& s, float scale_log2, 
     asm volatile("" : "+v"(psum));
 }
 
-template <bool OUT_FP32>
+template <bool OUT_FP32, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_fp8mma_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem8];
@@ -182,10 +182,13 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     // ---- work unit (as in prefill_hd512_kernel): heaviest query tiles first,
-    // KV head fastest
+    // KV head fastest; split-K ranges outermost
     const int per_rank = a.batch * a.hkv;
-    const int rank = blockIdx.x / per_rank;
-    const int rem = blockIdx.x - rank * per_rank;
+    const int per_split = a.wgs_per_seq * per_rank;
+    const int split = SPLIT ? blockIdx.x / per_split : 0;
+    const int in_split = blockIdx.x - split * per_split;
+    const int rank = in_split / per_rank;
+    const int rem = in_split - rank * per_rank;
     const int kvh = rem % a.hkv;
     const int b = rem / a.hkv;
     const int wg_in_seq = a.wgs_per_seq - 1 - rank;
@@ -203,7 +206,12 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     const int qs = max(a.q_start[b], 0);
     const int n_max = min(qs + t_last + 1, L);
     const int n_min = min(qs + t0 + 1, L);
-    const int ntiles = n_max > 0 ? (n_max + kPage - 1) / kPage : 0;
+    const int ntiles_all = n_max > 0 ? (n_max + kPage - 1) / kPage : 0;
+    // this workgroup's key tiles [kt_lo, kt_lo + ntiles): all of them, or one
+    // split's range (below, tile j means absolute tile kt_lo + j)
+    const int kt_lo = SPLIT ? split * a.split_tiles : 0;
+    const int ntiles = SPLIT ? min(ntiles_all, kt_lo + a.split_tiles) - kt_lo : ntiles_all;
+    if (SPLIT && ntiles <= 0) return;   // no row of this unit needs the split
 
     const int n = lane & 31;
     const int h = lane >> 5;
@@ -313,11 +321,11 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
 
     const int* ptab = a.page_table + (size_t)b * a.max_pages;
     const int staged = min(ntiles, kPagesInLds);
-    for (int i = threadIdx.x; i < staged; i += kThreads) sPage[i] = ptab[i];
+    for (int i = threadIdx.x; i < staged; i += kThreads) sPage[i] = ptab[kt_lo + i];
     __syncthreads();
     auto page_of = [&](int tile) -> int {
         return tile < kPagesInLds ? __builtin_amdgcn_readfirstlane(sPage[tile])
-                                  : load_uniform(ptab, tile);
+                                  : load_uniform(ptab, kt_lo + tile);
     };
     const int lane_off8 = (h << 9) | (((lane & 31) ^ h) << 4);
     const uint32_t lds_u = (uint32_t)(uintptr_t)lds;
@@ -326,7 +334,7 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     auto tdma = [&](bool is_k, int tile, int buf) -> TileDma {
         const bool in = tile < ntiles;
         const int page = in ? page_of(tile) : 0;
-        const int nv = in ? min(L - tile * kPage, kPage) : 0;
+        const int nv = in ? min(L - (kt_lo + tile) * kPage, kPage) : 0;
         return tile_dma(is_k ? a.k_pages : a.v_pages, page, a.num_pages, a.hkv, kvh, nv,
                         lds_u + (is_k ? 0 : kVRegion) + buf * kTile8, wave);
     };
@@ -382,19 +390,24 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
         const int vflip = vbuf * kBufBit;
 #pragma unroll
         for (int w = 0; w < 4; ++w) vx[w] ^= vflip;
-        i32x8 vcur = vread(0);
+        // two operand buffers; each is refilled (two dim blocks ahead) right
+        // after its last MFMA, so a read has two steps (four MFMAs) to land
+        i32x8 vb0 = vread(0), vb1 = vread(1);
         static_for<16>([&](auto DB) {
             constexpr int db = decltype(DB)::value;
-            const i32x8 vop = vcur;
-            if constexpr (db + 1 < 16) vcur = vread(db + 1);
+            const i32x8 vop = (db & 1) ? vb1 : vb0;
             o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, plo, o[db], 0, 0, 0, sa,
                                                                     1, psc);
             o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, phi, o[db], 0, 0, 0, sa,
                                                                     0, psc);
-            // keeps each step's operand read and MFMAs in their step (without
+            // keeps each step's MFMAs and operand read in their step (without
             // it the compiler may hoist all 16 reads above MFMAs sunk to the
             // epilogue and run out of registers)
             asm volatile("" : "+a"(o[db]) :: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (db + 2 < 16) {
+                if constexpr (db & 1) vb1 = vread(db + 2); else vb0 = vread(db + 2);
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
 #pragma unroll
@@ -424,7 +437,7 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
         int e0 = 0;      // block 0's exponent of the tile being built
         float ps0 = 0.f; // its lane sum of p'
         for (int j = 0; j < ntiles; ++j) {
-            const int key0 = j * kPage;
+            const int key0 = (kt_lo + j) * kPage;
             // ---- block 1's softmax of tile j - 1 (completing P(j - 1)) under
             // Q.K^T of block 0 of tile j; K(j + 1) refill
             mfma_vgpr_drain(s1);
@@ -453,8 +466,10 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
             if (key0 + kPage > n_min) mask_block<false>(s0, key0 + 4 * h, n_row, 0);
             float neg_m0 = neg_m;
             if (j == 0 && restarts == 0) {
-                // reference maximum: the row's maximum over the first 32 keys
-                // (key 0 is visible to every row, so it is finite)
+                // reference maximum: the row's maximum over the range's first
+                // 32 keys (without split-K key 0 is visible to every row; a
+                // split can start past a row's causal limit, and that row
+                // then takes 0: every p = 0, an empty partial)
                 float m0 = s0[0];
 #pragma unroll
                 for (int i = 1; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
@@ -474,7 +489,7 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
         // ---- the last tile: block 1's softmax and P.V
         {
             mfma_vgpr_drain(s1);
-            const int key0 = ntiles * kPage;
+            const int key0 = (kt_lo + ntiles) * kPage;
             if (key0 > n_min) mask_block<false>(s1, key0 - kPage + 32 + 4 * h, n_row, 0);
             const float neg_m = -m_ref;
             const int e1 = block_exponent(s1, a.scale_log2, neg_m);
@@ -520,6 +535,27 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     // 32 db + 8 (i / 4) + 4 h + i % 4 of its row, O in the true scale of p
     float l_tot = l_run + __shfl_xor(l_run, 32);
     const float vs = a.v_scale;
+    if constexpr (SPLIT) {
+        // split-K partial: O * v_scale, m (log2 units) and l; a row that saw
+        // no key of the split gives (0, -inf, 0) and adds nothing in the merge
+        if (valid) {
+            const size_t slot = ((size_t)split * a.total_q + (q0 + t)) * a.hq + head;
+            float* dst = a.part_o + slot * kHeadDim;
+#pragma unroll
+            for (int db = 0; db < 16; ++db) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *(f32x4*)(dst + 32 * db + 8 * q4 + 4 * h) =
+                        f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2],
+                              o[db][4 * q4 + 3]} * vs;
+            }
+            if (h == 0) {
+                a.part_ml[2 * slot] = l_tot > 0.f ? m_ref : -__builtin_inff();
+                a.part_ml[2 * slot + 1] = l_tot;
+            }
+        }
+        return;
+    }
     const float sink2 = a.sinks ? a.sinks[head] * 1.4426950408889634f : -__builtin_inff();
     float lse2 = -__builtin_inff();
     if (ntiles == 0) {
@@ -587,12 +623,17 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
 
 }  // namespace
 
-void launch_prefill_fp8mma(const PrefillArgs& a, bool out_fp32, unsigned grid,
+void launch_prefill_fp8mma(const PrefillArgs& a, bool out_fp32, bool split, unsigned grid,
                            hipStream_t stream) {
-    if (out_fp32)
-        hipLaunchKernelGGL(prefill_fp8mma_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+    if (split)
+        hipLaunchKernelGGL((prefill_fp8mma_kernel<false, true>), dim3(grid), dim3(kThreads), 0,
+                           stream, a);
+    else if (out_fp32)
+        hipLaunchKernelGGL((prefill_fp8mma_kernel<true, false>), dim3(grid), dim3(kThreads), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL(prefill_fp8mma_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((prefill_fp8mma_kernel<false, false>), dim3(grid), dim3(kThreads), 0,
+                           stream, a);
 }
 
 }  // namespace attn

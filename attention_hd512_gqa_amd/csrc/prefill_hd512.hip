@@ -1072,7 +1072,7 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     // (given both new-row buffers or neither), at head dim 512 with no window;
     // the FP8-MFMA form is FP8, single-pass, at head dim 512
     const bool append = k_new || v_new;
-    if (fp8_mma && (!fp8 || splitk || swa || append)) return ATTN_ERR_UNSUPPORTED;
+    if (fp8_mma && (!fp8 || swa || append)) return ATTN_ERR_UNSUPPORTED;
     if (swa && (fp8 || splitk)) return ATTN_ERR_UNSUPPORTED;
     if (append && (!k_new || !v_new)) return ATTN_ERR_NULL;
     if (append && (fp8 || splitk || swa)) return ATTN_ERR_UNSUPPORTED;
@@ -1147,7 +1147,9 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
             const long long grid = base * sp.nsplit;
             const long long mgrid = (long long)total_q * num_q_heads;
             if (grid > 0x7fffffffLL || mgrid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-            if (fp8)
+            if (fp8_mma)
+                launch_prefill_fp8mma(a, false, true, (unsigned)grid, stream);
+            else if (fp8)
                 hipLaunchKernelGGL((prefill_hd512_kernel<false, true, true>), dim3((unsigned)grid),
                                    dim3(kThreads), 0, stream, a);
             else
@@ -1168,7 +1170,7 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     const dim3 gd((unsigned)grid);
     const bool f32 = out_dtype == ATTN_FP32;
     if (fp8_mma) {
-        launch_prefill_fp8mma(a, f32, (unsigned)grid, stream);
+        launch_prefill_fp8mma(a, f32, false, (unsigned)grid, stream);
     } else if (append) {
         if (f32)
             hipLaunchKernelGGL((prefill_hd512_kernel<true, false, false, kHeadDim, false, true>),
@@ -1324,4 +1326,20 @@ extern "C" int attn_prefill_hd512_e4m3_mma(const void* q, const void* k_pages,
                                 max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse,
                                 false, 0, 0, nullptr, 0, false, 0, 0, nullptr, nullptr, true,
                                 stream);
+}
+
+extern "C" int attn_prefill_hd512_splitk_e4m3_mma(
+    const void* q, const void* k_pages, const void* v_pages, float k_scale, float v_scale,
+    const int32_t* page_table, const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
+    const int32_t* kv_lens, int batch, int total_q, int max_q_len, int num_q_heads,
+    int num_kv_heads, int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+    int max_kv_len, int keys_per_split, float softmax_scale, const float* sinks,
+    void* workspace, size_t workspace_bytes, void* out, int out_dtype, float* lse,
+    hipStream_t stream) {
+    return attn::prefill_launch(q, k_pages, v_pages, true, k_scale, v_scale, page_table,
+                                cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
+                                num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                                max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, true,
+                                max_kv_len, keys_per_split, workspace, workspace_bytes, false, 0,
+                                0, nullptr, nullptr, true, stream);
 }

@@ -232,8 +232,9 @@ def main():
             f"({flops / (ms8m * 1e-3) / 1e12:.1f} TFLOP/s)")
         del c8
         torch.cuda.empty_cache()
-        # a short chunk over a long prefix: single pass against split-K
-        for kv_dtype in ("bf16", "fp8_e4m3"):
+        # a short chunk over a long prefix: single pass against split-K (the
+        # E4M3 pool on both FP8 kernels)
+        for kv_dtype, mma in (("bf16", False), ("fp8_e4m3", False), ("fp8_e4m3", True)):
             cp = W.prefix_prefill_512_at_32k(device="cuda", kv_dtype=kv_dtype)
             lp = cp.launches[0]
             op = torch.empty((lp.total_q, cp.num_q_heads, W.HEAD_DIM), dtype=torch.bfloat16,
@@ -248,17 +249,18 @@ def main():
                 A.prefill(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q, l.q_start,
                           l.kv_len, o, total_q=l.total_q, max_q_len=l.max_q_len,
                           softmax_scale=c.softmax_scale, kv_dtype=c.kv_dtype,
-                          k_scale=c.k_scale, v_scale=c.v_scale, stream=stream)
+                          k_scale=c.k_scale, v_scale=c.v_scale, fp8_mma=mma, stream=stream)
 
             def split(c=cp, l=lp, o=op, ws=wsp):
                 A.prefill_splitk(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q,
                                  l.q_start, l.kv_len, o, ws, total_q=l.total_q,
                                  max_q_len=l.max_q_len, max_kv_len=l.max_kv_len,
                                  softmax_scale=c.softmax_scale, kv_dtype=c.kv_dtype,
-                                 k_scale=c.k_scale, v_scale=c.v_scale, stream=stream)
+                                 k_scale=c.k_scale, v_scale=c.v_scale, fp8_mma=mma,
+                                 stream=stream)
             ms_1 = timed(single, 10, 3)
             ms_s = timed(split, 10, 3)
-            extra[cp.name] = {"single_pass_ms": ms_1,
+            extra[cp.name + ("_mma" if mma else "")] = {"single_pass_ms": ms_1,
                               "single_pass_tflops": fp / (ms_1 * 1e-3) / 1e12,
                               "splitk_ms": ms_s, "splitk_tflops": fp / (ms_s * 1e-3) / 1e12,
                               "splitk_workspace_bytes": nb}

@@ -275,6 +275,24 @@ int attn_prefill_hd512_splitk(const void* q, const void* k_pages, const void* v_
                               hipStream_t stream);
 
 /*
+ * attn_prefill_hd512_splitk over an FP8-E4M3 pool with both products on the
+ * block-scaled FP8 matrix core: each key range runs the kernel of
+ * attn_prefill_hd512_e4m3_mma (same operand rounding), the merge is the same.
+ * Arguments as attn_prefill_hd512_splitk without kv_dtype (the pools are
+ * E4M3); workspace size from attn_prefill_hd512_splitk_workspace_size.
+ */
+int attn_prefill_hd512_splitk_e4m3_mma(const void* q, const void* k_pages, const void* v_pages,
+                                       float k_scale, float v_scale, const int32_t* page_table,
+                                       const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
+                                       const int32_t* kv_lens, int batch, int total_q,
+                                       int max_q_len, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int page_size, int num_pages,
+                                       int max_pages_per_seq, int max_kv_len, int keys_per_split,
+                                       float softmax_scale, const float* sinks, void* workspace,
+                                       size_t workspace_bytes, void* out, int out_dtype,
+                                       float* lse, hipStream_t stream);
+
+/*
  * Bytes of device workspace attn_decode_splitk needs for these sizes: fp32
  * partial outputs plus (m, l) for up to 4 partials per split, per query head
  * and sequence (valid for either KV dtype).  keys_per_split = 0 selects the

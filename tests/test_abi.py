@@ -290,3 +290,19 @@ def test_prefill_fp8_mma_validation(L):
     assert pm(hq=6, hkv=4) == 2
     assert pm(out_dtype=2) == 3
     assert pm(total_q=0, max_q_len=0) == 0
+
+
+def test_prefill_splitk_fp8_mma_validation(L):
+    def ps(**over):
+        a = dict(ks=1.0, batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=512, page=64,
+                 mkv=64, kps=64, ws=None, wsb=0)
+        a.update(over)
+        return L.attn_prefill_hd512_splitk_e4m3_mma(
+            FAKE, FAKE, FAKE, a["ks"], 1.0, FAKE, FAKE, FAKE, FAKE, a["batch"], a["total_q"],
+            a["max_q_len"], a["hq"], a["hkv"], a["d"], a["page"], 4, 4, a["mkv"], a["kps"], 0.04,
+            None, a["ws"], a["wsb"], FAKE, 1, None, None)
+    assert ps(ks=0.0) == 2
+    assert ps(kps=100) == 2          # not a multiple of 64
+    assert ps(mkv=0) == 2
+    assert ps(d=256) == 3
+    assert ps(total_q=0, max_q_len=0) == 0

@@ -32,8 +32,16 @@ def A():
     return library()
 
 
+# "fp8_mma": the E4M3 pool through the FP8-MMA kernels
+MODES = ["bf16", "fp8_e4m3", "fp8_mma"]
+
+
+def _pool(mode):
+    return ("fp8_e4m3" if mode.startswith("fp8") else "bf16"), mode == "fp8_mma"
+
+
 def run_splitk(A, case, kps, out_dtype=None, sinks=None, with_lse=False, pad_rows=3,
-               li=0):
+               li=0, fp8_mma=False):
     lc = case.launches[li]
     hq = case.num_q_heads
     out = out_tensor(lc.total_q, hq, out_dtype or case.out_dtype, pad_rows)
@@ -47,7 +55,7 @@ def run_splitk(A, case, kps, out_dtype=None, sinks=None, with_lse=False, pad_row
                      softmax_scale=case.softmax_scale, keys_per_split=kps,
                      kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale,
                      sinks=None if sinks is None else torch.as_tensor(sinks, device="cuda"),
-                     lse=lse)
+                     lse=lse, fp8_mma=fp8_mma)
     torch.cuda.synchronize()
     return out, lse, nbytes
 
@@ -72,21 +80,22 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0][0]}-{s[1]}x{s[2]}-k{s[3]}")
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("with_sink", [False, True])
-def test_splitk_small(A, shape, kv_dtype, with_sink):
+def test_splitk_small(A, shape, mode, with_sink):
+    kv_dtype, mma = _pool(mode)
     seqs, hq, hkv, kps = shape
     case = W.build_case("splitk", seqs=seqs, hq=hq, hkv=hkv, seed=41, out_dtype="fp32",
                         device="cuda", kv_dtype=kv_dtype, q_pad_rows=3, extra_pages=2,
                         table_pad=2)
     sinks = (np.random.default_rng(9).uniform(-2.0, 6.0, hq).astype(np.float32)
              if with_sink else None)
-    out, lse, nbytes = run_splitk(A, case, kps, sinks=sinks, with_lse=True)
+    out, lse, nbytes = run_splitk(A, case, kps, sinks=sinks, with_lse=True, fp8_mma=mma)
     assert nbytes > 0, "the fixture is meant to split"
     lc = case.launches[0]
     assert sentinel_intact(out[lc.total_q:]), "rows past total_q were written"
     ref, ref_lse = oracle.attend_all_lse(case.to("cpu"), sinks=sinks)
-    what = f"splitk {seqs} {hq}/{hkv} kps={kps} {kv_dtype} sink={with_sink}"
+    what = f"splitk {seqs} {hq}/{hkv} kps={kps} {mode} sink={with_sink}"
     check_parity(out[:lc.total_q], ref, what)
     _lse_check(lse, ref_lse, what)
 
@@ -136,11 +145,12 @@ def test_splitk_q0_v1_is_exactly_one(A):
     assert bool((out[:lc.total_q] == 1.0).all())
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
-def test_prefix_prefill_512_at_32k_sampled(A, kv_dtype):
+@pytest.mark.parametrize("mode", MODES)
+def test_prefix_prefill_512_at_32k_sampled(A, mode):
+    kv_dtype, mma = _pool(mode)
     case = W.prefix_prefill_512_at_32k(device="cuda", kv_dtype=kv_dtype)
     lc = case.launches[0]
-    out, _, nbytes = run_splitk(A, case, 0, pad_rows=16)
+    out, _, nbytes = run_splitk(A, case, 0, pad_rows=16, fp8_mma=mma)
     assert nbytes > 0
     assert sentinel_intact(out[lc.total_q:])
     g = np.random.default_rng(6)
@@ -149,7 +159,7 @@ def test_prefix_prefill_512_at_32k_sampled(A, kv_dtype):
     rows, toks = sample_rows(lc, case.num_q_heads, tokens)
     ref = oracle.attend_rows(case.to("cpu"), rows).reshape(len(toks), case.num_q_heads, -1)
     check_parity(out[torch.as_tensor(toks, device="cuda")], ref,
-                 f"prefix_prefill_512_at_32k {kv_dtype} sampled")
+                 f"prefix_prefill_512_at_32k {mode} sampled")
 
 
 def _plant_hot_key(case, b, j, kv_dtype):
@@ -166,38 +176,41 @@ def _plant_hot_key(case, b, j, kv_dtype):
         case.k_pool[page, :, j % 64, :] = torch.where(u > 0, 0x7E, 0xFE).to(torch.uint8)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("path", ["single", "splitk"])
-def test_reference_restart_on_hot_key(A, kv_dtype, path):
+def test_reference_restart_on_hot_key(A, mode, path):
+    kv_dtype, mma = _pool(mode)
     case = W.build_case("hot", seqs=[(70, 900, 970), (50, 0, 50)], hq=16, hkv=2, seed=59,
                         out_dtype="fp32", device="cuda", kv_dtype=kv_dtype, q_pad_rows=2)
     _plant_hot_key(case, 0, 700, kv_dtype)    # in the 11th key tile, past the first 32 keys
     _plant_hot_key(case, 1, 40, kv_dtype)     # in the first tile, second half
     lc = case.launches[0]
     if path == "single":
-        out = run_prefill(A, case, pad_rows=2)
+        out = run_prefill(A, case, pad_rows=2, fp8_mma=mma)
     else:
-        out, _, nbytes = run_splitk(A, case, 128, pad_rows=2)
+        out, _, nbytes = run_splitk(A, case, 128, pad_rows=2, fp8_mma=mma)
         assert nbytes > 0
     ref = oracle.attend_all(case.to("cpu"))
     assert np.isfinite(ref).all()
-    check_parity(out[:lc.total_q], ref, f"hot key {kv_dtype} {path}")
+    check_parity(out[:lc.total_q], ref, f"hot key {mode} {path}")
 
 
+@pytest.mark.parametrize("mode", ["bf16", "fp8_mma"])
 @pytest.mark.parametrize("path", ["single", "splitk"])
-def test_context_past_the_staged_page_ids(A, path):
+def test_context_past_the_staged_page_ids(A, path, mode):
     # 300000 keys = 4688 key tiles: past the 4096 page ids a workgroup stages
     # in LDS, so the tail tiles take the page-table path in the loop
+    kv_dtype, mma = _pool(mode)
     case = W.build_case("long300k", seqs=[(64, 299936, 300000)], hq=8, hkv=1, seed=73,
-                        out_dtype="fp32", device="cuda", q_pad_rows=2)
+                        out_dtype="fp32", device="cuda", q_pad_rows=2, kv_dtype=kv_dtype)
     lc = case.launches[0]
     if path == "single":
-        out = run_prefill(A, case, pad_rows=2)
+        out = run_prefill(A, case, pad_rows=2, fp8_mma=mma)
     else:
-        out, _, nbytes = run_splitk(A, case, 0, pad_rows=2)
+        out, _, nbytes = run_splitk(A, case, 0, pad_rows=2, fp8_mma=mma)
         assert nbytes > 0
     assert sentinel_intact(out[lc.total_q:])
     tokens = [0, 1, 31, 62, 63]
     rows, toks = sample_rows(lc, case.num_q_heads, tokens)
     ref = oracle.attend_rows(case.to("cpu"), rows).reshape(len(toks), case.num_q_heads, -1)
-    check_parity(out[torch.as_tensor(toks, device="cuda")], ref, f"300000 keys {path}")
+    check_parity(out[torch.as_tensor(toks, device="cuda")], ref, f"300000 keys {path} {mode}")
