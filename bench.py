@@ -41,8 +41,8 @@ TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/prefill_common.h",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "956a6767d30bf9c349714153c72beceb4921fdc5f42aa339d9849c784e6d1620",
-    "fetch_bytes": 2006652945,
+    "sha256": "9bd85a236b3bbe427400f44d95a0e291284f25f014031530311280f04e623fa8",
+    "fetch_bytes": 2008291693,
     "write_bytes": 268435456,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
