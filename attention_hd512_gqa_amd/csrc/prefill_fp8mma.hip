@@ -151,23 +151,37 @@ __device__ __forceinline__ int block_exponent(const f32x16& s, float scale_log2,
 }
 
 // Softmax of elements i, i + 1 (i even) of a block with exponent offset c
-// (= 7 - e - m_ref): p' = 2^(s scale_log2 + c) in [0, 256), the lane's sum
-// of p' and the two E4M3 terms into dword DW of the P operands.  The empty
-// asm pins the work to the MFMA step it is issued with.
-template <int I, int DW>
-__device__ __forceinline__ void softmax_pair(const f32x16& s, float scale_log2, float c, float& psum,
-                                             i32x8& phi, i32x8& plo) {
+// (= 7 - e - m_ref), in two halves that go into the two gaps of a k-step's
+// dependent MFMA pair (issued after the first MFMA and after the second, so
+// that neither gap's VALU work outlasts the MFMA it hides under):
+// softmax_exp gives p' = 2^(s scale_log2 + c) in [0, 256) and the lane's sum
+// of p'; softmax_split writes the two E4M3 terms into dword DW of the P
+// operands.  The empty asms pin the work to its step.
+template <int I>
+__device__ __forceinline__ void softmax_exp(const f32x16& s, float scale_log2, float c, float& psum,
+                                            float& pa, float& pb) {
     float sa = s[I], sb = s[I + 1];
     asm volatile("" : "+v"(sa), "+v"(sb));
-    const float pa = fast_exp2(__builtin_fmaf(sa, scale_log2, c));
-    const float pb = fast_exp2(__builtin_fmaf(sb, scale_log2, c));
+    pa = fast_exp2(__builtin_fmaf(sa, scale_log2, c));
+    pb = fast_exp2(__builtin_fmaf(sb, scale_log2, c));
     psum += pa;
     psum += pb;
+    asm volatile("" : "+v"(psum), "+v"(pa), "+v"(pb));
+}
+template <int I, int DW>
+__device__ __forceinline__ void softmax_split(float pa, float pb, i32x8& phi, i32x8& plo) {
     int hi = phi[DW], lo = plo[DW];
     split_pair<((I >> 1) & 1) != 0>(pa, pb, hi, lo);
     phi[DW] = hi;
     plo[DW] = lo;
-    asm volatile("" : "+v"(psum));
+    asm volatile("" : "+v"(hi), "+v"(lo));
+}
+template <int I, int DW>
+__device__ __forceinline__ void softmax_pair(const f32x16& s, float scale_log2, float c, float& psum,
+                                             i32x8& phi, i32x8& plo) {
+    float pa, pb;
+    softmax_exp<I>(s, scale_log2, c, psum, pa, pb);
+    softmax_split<I, DW>(pa, pb, phi, plo);
 }
 
 template <bool OUT_FP32, bool SPLIT>
@@ -363,11 +377,15 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     // that every count is the same; the last P.V waits for all.
     // Q.K^T of block kb of the tile in the current K buffer into acc, one
     // refill row pair after each k-step's first MFMA and softmax pair i of
-    // block sp (of the other block) after its second
-    auto qk_phase = [&](auto KB, f32x16& acc, const TileDma& d, const f32x16& sp, float c,
+    // block sp (of the other block) over both of its MFMAs.  `prologue`
+    // (the other block's masking and exponent; it returns the softmax offset
+    // c) runs after the first MFMA is issued, so that it overlaps the matrix
+    // pipe instead of delaying the chain.
+    auto qk_phase = [&](auto KB, f32x16& acc, const TileDma& d, const f32x16& sp, auto prologue,
                         float& psum, auto DWB) {
         constexpr int kb = decltype(KB)::value;
         constexpr int dwb = decltype(DWB)::value;
+        float c = 0.f;
         // one k-step's operand read ahead: two 64-cycle MFMAs cover its latency
         i32x8 knext = kread(kb, 0);
         static_for<8>([&](auto KS) {
@@ -379,9 +397,12 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
             else
                 mfma8_vgpr<2 * (ks & 1) + 1>(acc, cur, qlo[ks], sa, qsc[ks >> 1]);
             tile_rows<ks>(d, lane_off8);
+            if constexpr (ks == 0) c = prologue();
+            float pa, pb;
+            softmax_exp<2 * ks>(sp, a.scale_log2, c, psum, pa, pb);
             __builtin_amdgcn_sched_barrier(0);
             mfma8_vgpr<2 * (ks & 1)>(acc, cur, qhi[ks], sa, qsc[ks >> 1]);
-            softmax_pair<2 * ks, dwb + ks / 2>(sp, a.scale_log2, c, psum, phi, plo);
+            softmax_split<2 * ks, dwb + ks / 2>(pa, pb, phi, plo);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -440,16 +461,19 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
             const int key0 = (kt_lo + j) * kPage;
             // ---- block 1's softmax of tile j - 1 (completing P(j - 1)) under
             // Q.K^T of block 0 of tile j; K(j + 1) refill
-            mfma_vgpr_drain(s1);
-            if (j > 0 && key0 > n_min) mask_block<false>(s1, key0 - kPage + 32 + 4 * h, n_row, 0);
             const float neg_m = -m_ref;
             const TileDma dk = tdma(true, j + 1, (j + 1) & 1);
             wait_vmcnt<8>();
             lds_barrier();
-            const int e1 = block_exponent(s1, a.scale_log2, neg_m);
+            int e1 = 0;
             float ps1 = 0.f;
-            qk_phase(std::integral_constant<int, 0>{}, s0, dk, s1, neg_m + (float)(7 - e1), ps1,
-                     std::integral_constant<int, 4>{});
+            qk_phase(std::integral_constant<int, 0>{}, s0, dk, s1, [&]() {
+                mfma_vgpr_drain(s1);
+                if (j > 0 && key0 > n_min)
+                    mask_block<false>(s1, key0 - kPage + 32 + 4 * h, n_row, 0);
+                e1 = block_exponent(s1, a.scale_log2, neg_m);
+                return neg_m + (float)(7 - e1);
+            }, ps1, std::integral_constant<int, 4>{});
             // ---- P.V of tile j - 1
             if (j > 0) {
                 const int own = h ? e1 : e0;
@@ -462,26 +486,27 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
                 pv_phase((j - 1) & 1, (kE8Hi + own) | ((kE8Lo + own) << 8));
             }
             // ---- block 0's softmax of tile j under Q.K^T of block 1; V(j) refill
-            mfma_vgpr_drain(s0);
-            if (key0 + kPage > n_min) mask_block<false>(s0, key0 + 4 * h, n_row, 0);
-            float neg_m0 = neg_m;
-            if (j == 0 && restarts == 0) {
-                // reference maximum: the row's maximum over the range's first
-                // 32 keys (without split-K key 0 is visible to every row; a
-                // split can start past a row's causal limit, and that row
-                // then takes 0: every p = 0, an empty partial)
-                float m0 = s0[0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
-                m0 = pair_max(m0) * a.scale_log2;
-                m0 = m0 == -__builtin_inff() ? 0.f : m0;
-                m_ref = m0;
-                neg_m0 = -m0;
-            }
-            e0 = block_exponent(s0, a.scale_log2, neg_m0);
             ps0 = 0.f;
-            qk_phase(std::integral_constant<int, 1>{}, s1, tdma(false, j, j & 1), s0,
-                     neg_m0 + (float)(7 - e0), ps0, std::integral_constant<int, 0>{});
+            qk_phase(std::integral_constant<int, 1>{}, s1, tdma(false, j, j & 1), s0, [&]() {
+                mfma_vgpr_drain(s0);
+                if (key0 + kPage > n_min) mask_block<false>(s0, key0 + 4 * h, n_row, 0);
+                float neg_m0 = neg_m;
+                if (j == 0 && restarts == 0) {
+                    // reference maximum: the row's maximum over the range's first
+                    // 32 keys (without split-K key 0 is visible to every row; a
+                    // split can start past a row's causal limit, and that row
+                    // then takes 0: every p = 0, an empty partial)
+                    float m0 = s0[0];
+#pragma unroll
+                    for (int i = 1; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
+                    m0 = pair_max(m0) * a.scale_log2;
+                    m0 = m0 == -__builtin_inff() ? 0.f : m0;
+                    m_ref = m0;
+                    neg_m0 = -m0;
+                }
+                e0 = block_exponent(s0, a.scale_log2, neg_m0);
+                return neg_m0 + (float)(7 - e0);
+            }, ps0, std::integral_constant<int, 0>{});
             // the next tile reads the other K buffer
 #pragma unroll
             for (int i = 0; i < 4; ++i) kx[i] ^= kBufBit;
