@@ -350,12 +350,15 @@ struct VReader8 {
 // k-steps of head_dim.  When OVERLAP, the 16 softmax elements of the previous
 // block's scores `sp` are spread evenly over the MFMAs (one after every other
 // at D = 512, one after each at 256); the half-tile refill `dma` issues one
-// row load after every fourth MFMA.
-template <bool OVERLAP, bool FP8, int D>
+// row load after every fourth MFMA.  `pre` (the previous block's masking and
+// reference, which the softmax needs but the chain does not) runs after the
+// first MFMA is issued, so that it overlaps the matrix pipe.
+template <bool OVERLAP, bool FP8, int D, typename Pre>
 __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(Kv<FP8, D>::kSteps)],
                                          const ATTN_LDS char* sK, const int (&koff)[8],
                                          const f32x16& sp, const SoftmaxCtx& c, float& psum, bf16x8& pf0, bf16x8& pf1,
-                                         const HalfDma& dma, int lane_off, int lane, int wave) {
+                                         const HalfDma& dma, int lane_off, int lane, int wave,
+                                         Pre&& pre) {
     // bf16 at 512: step ks reads chunk 2 ks + h of key row 32 kb + n; with
     // ks = 8 u + v the byte offset is koff[v] + 256 u + 32 KiB kb.  bf16 at
     // 256: chunk (2 ks + h) ^ swzN(n) = (2 ks) ^ (h ^ swzN(n)): koff[0] ^ (32 ks)
@@ -397,6 +400,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(
         if constexpr (ks % kDmaEvery == 0) {
             if (dma.on) half_dma_row<FP8, D, ks / kDmaEvery>(dma, lane_off, lane, wave);
         }
+        if constexpr (ks == 0) pre();
         if constexpr (OVERLAP && (ks % kSmEvery == kSmEvery - 1)) {
             constexpr int i = ks / kSmEvery;
             softmax_elem(c, sp[i], i, psum, pend, i - 1 < 8 ? pf0 : pf1);
@@ -738,35 +742,38 @@ void prefill_hd512_kernel(PrefillArgs a) {
             wait_vmcnt<2 * kD>();
             lds_barrier();
             qk_block<false, FP8, D>(s0, 0, qf, sK, koff, s0, c0, psum, pf[0], pf[1], dv1,
-                                    lane_off, lane, wave);
-            mfma_vgpr_drain(s0);
+                                    lane_off, lane, wave, [] {});
             page_cur = page_n;
             page_nx = t2 >= ntiles ? page_n
                     : (t2_staged ? __builtin_amdgcn_readfirstlane(page_nn_raw)
                                  : load_uniform(ptab, ring > 0 ? t2 % ring : t2));
-            if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
-            if constexpr (WINDOW) lazy_reference(s0, a.scale_log2, m_ref, c0);
-            if (!WINDOW && kt == kt_lo && restarts == 0) {
-                // reference maximum: the row's maximum over the range's first 32
-                // keys (a restarted pass keeps the raised one).  Without split-K key 0 is visible to every row, so it is
-                // finite; a split can start past a row's causal limit, and that
-                // row then takes 0 (every p = 0, an empty partial).
-                float m0 = -__builtin_inff();
-#pragma unroll
-                for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
-                m0 = fmaxf(m0, __shfl_xor(m0, 32)) * a.scale_log2;
-                m0 = m0 == -__builtin_inff() ? 0.f : m0;
-                m_ref = m0;
-                c0.neg_m_ref = -m0;
-            }
 
-            // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill
+            // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill.
+            // Block 0's masking and reference run after QK1's first MFMA.
             const HalfDma dk0 = refill(true, page_n, valid_n, kt + 1, 0, true);
             hold_before_wait<APPEND>();
             wait_vmcnt<2 * kD>();
             lds_barrier();
             qk_block<true, FP8, D>(s1, 1, qf, sK, koff, s0, c0, psum, pf[0], pf[1], dk0,
-                                   lane_off, lane, wave);
+                                   lane_off, lane, wave, [&] {
+                mfma_vgpr_drain(s0);
+                if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
+                if constexpr (WINDOW) lazy_reference(s0, a.scale_log2, m_ref, c0);
+                if (!WINDOW && kt == kt_lo && restarts == 0) {
+                    // reference maximum: the row's maximum over the range's first
+                    // 32 keys (a restarted pass keeps the raised one).  Without
+                    // split-K key 0 is visible to every row, so it is finite; a
+                    // split can start past a row's causal limit, and that row then
+                    // takes 0 (every p = 0, an empty partial).
+                    float m0 = -__builtin_inff();
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
+                    m0 = fmaxf(m0, __shfl_xor(m0, 32)) * a.scale_log2;
+                    m0 = m0 == -__builtin_inff() ? 0.f : m0;
+                    m_ref = m0;
+                    c0.neg_m_ref = -m0;
+                }
+            });
             mfma_vgpr_drain(s1);
             if (mask) mask_block<WINDOW>(s1, key0 + 32 + 4 * h, n_row, lo_row);
             if constexpr (WINDOW) lazy_reference(s1, a.scale_log2, m_ref, c0);
