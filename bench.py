@@ -41,8 +41,8 @@ TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/prefill_common.h",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "9bd85a236b3bbe427400f44d95a0e291284f25f014031530311280f04e623fa8",
-    "fetch_bytes": 2008291693,
+    "sha256": "b9f33b246b82b5c9a16c79e5b4bd21ac6b6a92fea88f11700c0ea0412d7f5135",
+    "fetch_bytes": 1995909501,
     "write_bytes": 268435456,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
