@@ -26,11 +26,14 @@
 // Work unit, softmax bookkeeping (fixed per-row reference maximum, bounded
 // restart), masking and output are those of prefill_hd512_kernel.  The tile
 // pipeline differs, because one 32x32x64 MFMA of P.V spans the whole 64-key
-// tile: per tile, phase 1 runs Q.K^T of both 32-key blocks (32 MFMAs) with
-// block 0's softmax under block 1's MFMAs, and phase 2 runs P.V of the
-// previous tile (32 MFMAs) with block 1's softmax of this tile.  E4M3 tiles
-// are 32 KB, so K and V are double-buffered (128 KB): each tile's refill is
-// issued a whole tile ahead of its use.
+// tile: per tile j the wave runs Q.K^T of block 0 (16 MFMAs) under block 1's
+// softmax of tile j - 1, which completes P(j - 1); then P.V of tile j - 1
+// (32 MFMAs); then Q.K^T of block 1 under block 0's softmax of tile j.  Only
+// one P operand pair is ever live, which keeps the kernel inside 256 VGPRs
+// beside the 256 O accumulators.  E4M3 tiles are 32 KB, so K and V are
+// double-buffered (128 KB of LDS) and each refill is issued a phase or more
+// ahead of the barrier that waits for it.  A split-K form (one key range per
+// workgroup, partials merged by prefill_merge_kernel) shares the code.
 #include "device_common.h"
 #include "prefill_common.h"
 
