@@ -559,94 +559,11 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
         l_run = 0.f;
     }
 
-    // ---- epilogue (as prefill_hd512_kernel): lane holds dims
-    // 32 db + 8 (i / 4) + 4 h + i % 4 of its row, O in the true scale of p
-    float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float vs = a.v_scale;
-    if constexpr (SPLIT) {
-        // split-K partial: O * v_scale, m (log2 units) and l; a row that saw
-        // no key of the split gives (0, -inf, 0) and adds nothing in the merge
-        if (valid) {
-            const size_t slot = ((size_t)split * a.total_q + (q0 + t)) * a.hq + head;
-            float* dst = a.part_o + slot * kHeadDim;
-#pragma unroll
-            for (int db = 0; db < 16; ++db) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    *(f32x4*)(dst + 32 * db + 8 * q4 + 4 * h) =
-                        f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2],
-                              o[db][4 * q4 + 3]} * vs;
-            }
-            if (h == 0) {
-                a.part_ml[2 * slot] = l_tot > 0.f ? m_ref : -__builtin_inff();
-                a.part_ml[2 * slot + 1] = l_tot;
-            }
-        }
-        return;
-    }
-    const float sink2 = a.sinks ? a.sinks[head] * 1.4426950408889634f : -__builtin_inff();
-    float lse2 = -__builtin_inff();
-    if (ntiles == 0) {
-        l_tot = 1.f;
-        lse2 = sink2;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) o[db] = f32x16{};
-    } else if (l_tot == 0.f) {
-        l_tot = 1.f;
-        lse2 = sink2;
-    } else {
-        const float a2 = m_ref + __builtin_log2f(l_tot);
-        const float top = fmaxf(a2, sink2);
-        lse2 = top + __builtin_log2f(fast_exp2(a2 - top) + fast_exp2(sink2 - top));
-        l_tot += fast_exp2(sink2 - m_ref);
-    }
-    if (a.lse && valid && h == 0)
-        a.lse[(size_t)(q0 + t) * a.hq + head] = lse2 * 0.6931471805599453f;
-    if constexpr (!OUT_FP32) {
-        // bf16 rows through the (now idle) tile buffers, stored whole, as in
-        // prefill_hd512_kernel
-        constexpr int kOutRowB = kHeadDim * 2;
-        static_assert(kWaves * 32 * kOutRowB <= kTileArea, "staging fits the tile buffers");
-        __syncthreads();
-        ATTN_LDS char* stage = lds + wave * 32 * kOutRowB;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 v = f32x4{o[db][4 * q4] / l_tot, o[db][4 * q4 + 1] / l_tot,
-                                      o[db][4 * q4 + 2] / l_tot, o[db][4 * q4 + 3] / l_tot} * vs;
-                const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                const int c = 4 * db + q4;
-                *(ATTN_LDS bf16x4*)(stage + n * kOutRowB + ((c ^ (n & 15)) << 4) + 8 * h) = w;
-            }
-        }
-        constexpr int kChunks = kOutRowB / 16;
-        constexpr int kRowsPerStore = 64 / kChunks;
-        const int cl = lane % kChunks;
-#pragma unroll 4
-        for (int i = 0; i < 32 / kRowsPerStore; ++i) {
-            const int rr = i * kRowsPerStore + lane / kChunks;
-            const int pr = wave * 32 + rr;
-            const int trr = pr / a.g;
-            const bf16x8 x = *(const ATTN_LDS bf16x8*)(stage + rr * kOutRowB + ((cl ^ (rr & 15)) << 4));
-            if (trr < a.tok_per_wg && t0 + trr <= t_last) {
-                const size_t ob =
-                    ((size_t)(q0 + t0 + trr) * a.hq + kvh * a.g + (pr - trr * a.g)) * kHeadDim;
-                *(bf16x8*)((__bf16*)a.out + ob + 8 * cl) = x;
-            }
-        }
-    } else if (valid) {
-        const size_t obase = ((size_t)(q0 + t) * a.hq + head) * kHeadDim;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 v = f32x4{o[db][4 * q4] / l_tot, o[db][4 * q4 + 1] / l_tot,
-                                      o[db][4 * q4 + 2] / l_tot, o[db][4 * q4 + 3] / l_tot} * vs;
-                *(f32x4*)((float*)a.out + obase + 32 * db + 8 * q4 + 4 * h) = v;
-            }
-        }
-    }
+    // ---- epilogue (shared with prefill_hd512_kernel): O in the true scale of p
+    static_assert(kWaves * 32 * kHeadDim * 2 <= kTileArea, "staging fits the tile buffers");
+    prefill_epilogue<OUT_FP32, SPLIT, kHeadDim, !OUT_FP32, true>(
+        a, o, l_run, m_ref, ntiles > 0,
+        RowSlot{q0, q0 + t, head, t0, t_last, kvh, split, valid}, lds, lane, wave);
 }
 
 }  // namespace

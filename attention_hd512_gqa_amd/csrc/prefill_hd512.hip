@@ -829,118 +829,12 @@ void prefill_hd512_kernel(PrefillArgs a) {
     }
     wait_vmcnt<0>();   // the empty refills past the last tile
 
-    // ---- epilogue: lane holds d = 32 db + 8 (i/4) + 4 h + (i%4) of its row.
-    float l_tot = l_run + __shfl_xor(l_run, 32);
-    if constexpr (SPLIT) {
-        // split-K partial: O * v_scale, m (log2 units) and l; a row that saw
-        // no key of the split gives (0, -inf, 0) and adds nothing in the merge
-        if (valid) {
-            const size_t slot = ((size_t)split * a.total_q + (q0 + t)) * a.hq + head;
-            float* dst = a.part_o + slot * D;
-            const float vs = a.v_scale;
-#pragma unroll
-            for (int db = 0; db < kDB; ++db) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int d0 = 32 * db + 8 * q4 + 4 * h;
-                    *(f32x4*)(dst + d0) = f32x4{o[db][4 * q4], o[db][4 * q4 + 1],
-                                                o[db][4 * q4 + 2], o[db][4 * q4 + 3]} * vs;
-                }
-            }
-            if (h == 0) {
-                a.part_ml[2 * slot] = l_tot > 0.f ? m_ref : -__builtin_inff();
-                a.part_ml[2 * slot + 1] = l_tot;
-            }
-        }
-        return;
-    }
-    // o = O / l with an IEEE division (not O * (1/l)), as the definition reads:
-    // with V = 1 it returns exactly 1.
-    const float vs = a.v_scale;   // 1 for a bf16 pool
-    // A sink (vLLM flash-attention PR 199, second review, finding F4) adds
-    // 2^(sink - m_ref) to the denominator in the units of l (log2 units,
-    // relative to the row's reference maximum); 0 without one, so that the
-    // division below is then exactly O / l.
-    const float sink2 = a.sinks ? a.sinks[head] * 1.4426950408889634f : -__builtin_inff();
-    float lse2 = -__builtin_inff();   // log2-sum-exp of the row
-    if (ntiles <= kt_lo) {  // no tile with a visible key (empty cache): the output is 0
-        l_tot = 1.f;
-        lse2 = sink2;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) o[db] = f32x16{};
-    } else if (l_tot == 0.f) {  // this row saw no key (its band is past the cache end)
-        l_tot = 1.f;            // O is 0
-        lse2 = sink2;
-    } else {
-        const float a2 = m_ref + __builtin_log2f(l_tot);
-        const float top = fmaxf(a2, sink2);
-        lse2 = top + __builtin_log2f(fast_exp2(a2 - top) + fast_exp2(sink2 - top));
-        l_tot += fast_exp2(sink2 - m_ref);
-    }
-    if (a.lse && valid && h == 0)
-        a.lse[(size_t)(q0 + t) * a.hq + head] = lse2 * 0.6931471805599453f;
-    // bf16 output through LDS: a lane holds 4-dim pieces of its row spread
-    // over the row, so storing them directly puts 16-byte pieces of 32 rows
-    // in every store instruction.  Each wave instead writes its 32 rows into
-    // its own part of the (then free) tile buffers and stores them back one
-    // whole row per instruction.  16-byte chunk c of a staged row r sits at
-    // chunk c ^ (r & 15), so the 16 rows one write instruction covers fall in
-    // distinct bank groups.
-    constexpr int kOutRowB = D * 2;
-    constexpr bool kStageOut = !OUT_FP32 && 2 * kTileB >= kWaves * 32 * kOutRowB;
-    if constexpr (kStageOut) {
-        wait_vmcnt<0>();     // every wave's refills have landed ...
-        __syncthreads();     // ... and no wave reads the tiles any more
-        ATTN_LDS char* stage = (ATTN_LDS char*)smem + wave * 32 * kOutRowB;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                f32x4 v = {o[db][4 * q4] / l_tot, o[db][4 * q4 + 1] / l_tot,
-                           o[db][4 * q4 + 2] / l_tot, o[db][4 * q4 + 3] / l_tot};
-                if constexpr (FP8) v *= vs;
-                const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                const int c = 4 * db + q4;   // dims 32 db + 8 q4 .. + 7; this lane's half: 4 h
-                *(ATTN_LDS bf16x4*)(stage + n * kOutRowB + ((c ^ (n & 15)) << 4) + 8 * h) = w;
-            }
-        }
-        // lane l moves chunk l % (kOutRowB / 16) of staged row
-        // 64 i / (kOutRowB / 16) + l / (kOutRowB / 16)
-        constexpr int kChunks = kOutRowB / 16;
-        constexpr int kRowsPerStore = 64 / kChunks;
-        const int cl = lane % kChunks;
-#pragma unroll 4
-        for (int i = 0; i < 32 / kRowsPerStore; ++i) {
-            const int rr = i * kRowsPerStore + lane / kChunks;   // staged row
-            const int pr = wave * 32 + rr;                       // packed row of the workgroup
-            const int trr = pr / a.g;
-            const bf16x8 x = *(const ATTN_LDS bf16x8*)(stage + rr * kOutRowB + ((cl ^ (rr & 15)) << 4));
-            if (trr < a.tok_per_wg && t0 + trr <= t_last) {
-                const size_t ob = ((size_t)(q0 + t0 + trr) * a.hq + kvh * a.g + (pr - trr * a.g)) * D;
-                *(bf16x8*)((__bf16*)a.out + ob + 8 * cl) = x;
-            }
-        }
-        return;
-    }
-    if (valid) {
-        const size_t obase = ((size_t)(q0 + t) * a.hq + head) * D;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d0 = 32 * db + 8 * q4 + 4 * h;
-                f32x4 v = {o[db][4 * q4] / l_tot, o[db][4 * q4 + 1] / l_tot,
-                           o[db][4 * q4 + 2] / l_tot, o[db][4 * q4 + 3] / l_tot};
-                if constexpr (FP8) v *= vs;
-                if constexpr (OUT_FP32) {
-                    *(f32x4*)((float*)a.out + obase + d0) = v;
-                } else {
-                    bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                    *(bf16x4*)((__bf16*)a.out + obase + d0) = w;
-                }
-            }
-        }
-    }
+    // ---- epilogue: outputs (or split-K partials) of the workgroup's rows
+    constexpr bool kStageOut = !OUT_FP32 && 2 * kTileB >= kWaves * 32 * D * 2;
+    prefill_epilogue<OUT_FP32, SPLIT, D, kStageOut, FP8>(
+        a, o, l_run, m_ref, ntiles > kt_lo,
+        RowSlot{q0, q0 + t, head, t0, t_last, kvh, split, valid}, (ATTN_LDS char*)smem, lane,
+        wave);
 }
 
 
