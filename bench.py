@@ -41,8 +41,8 @@ TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/prefill_common.h",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "b9f33b246b82b5c9a16c79e5b4bd21ac6b6a92fea88f11700c0ea0412d7f5135",
-    "fetch_bytes": 1995909501,
+    "sha256": "d45d61984ea3eb328bf13f8da26a4e6e01fa266ef78bfd0c3796d19649938d62",
+    "fetch_bytes": 1994714519,
     "write_bytes": 268435456,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
