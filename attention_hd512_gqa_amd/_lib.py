@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.attn_hbm_read_probe.restype = I
         L.attn_hbm_probe_sink_words.argtypes = [SZ]
         L.attn_hbm_probe_sink_words.restype = SZ
+        L.attn_clock_stamps.argtypes = [P, I, P]
+        L.attn_clock_stamps.restype = I
         L.attn_status_string.argtypes = [I]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -331,3 +333,12 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
 
 def hbm_probe_sink_words(nbytes: int) -> int:
     return int(lib().attn_hbm_probe_sink_words(int(nbytes)))
+
+
+def clock_stamps(stamps: torch.Tensor, stream=None) -> None:
+    """Enqueue one clock-stamp workgroup per row of `stamps` (int64 [n, 3]):
+    XCD id, shader-clock cycle counter, 100 MHz counter (measurement helper)."""
+    if stamps.dtype != torch.int64 or stamps.dim() != 2 or stamps.shape[1] != 3:
+        raise AttnError("stamps must be an int64 tensor of shape [n, 3]")
+    code = lib().attn_clock_stamps(_dev(stamps, "stamps"), int(stamps.shape[0]), _stream(stream))
+    _check(code, "attn_clock_stamps")

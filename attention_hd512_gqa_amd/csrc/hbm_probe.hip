@@ -1,7 +1,14 @@
+// Measurement helpers.
+//
 // Same-process HBM read roofline: stream a buffer once with 16-byte loads.
 // The buffer should be well beyond the 256 MB Infinity Cache so the rate is
 // the HBM rate.  Each workgroup folds what it read into one word of `sink`
 // so the loads cannot be dropped.
+//
+// Clock stamps: each workgroup's first lane records its XCD and two
+// counters, s_memtime (counts shader-clock cycles, so its rate follows the
+// clock) and s_memrealtime (a constant 100 MHz).  Two stamp launches around
+// a timed region give each XCD's mean shader clock over it.
 #include "device_common.h"
 #include "attn_host.h"
 
@@ -29,8 +36,31 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_kernel(const u32x4* bu
     if (threadIdx.x == 0) sink[blockIdx.x] = w;
 }
 
+// One 64-lane workgroup per slot: lane 0 writes {XCD id, s_memtime,
+// s_memrealtime} (three 64-bit words) to slot blockIdx.x.
+__global__ __launch_bounds__(64) void clock_stamp_kernel(unsigned long long* out) {
+    // HW_REG_XCC_ID (hardware register 20), bits 0..3: the XCD this wave runs on
+    const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);
+    const unsigned long long t = __builtin_amdgcn_s_memtime();
+    const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        out[3 * blockIdx.x] = xcc;
+        out[3 * blockIdx.x + 1] = t;
+        out[3 * blockIdx.x + 2] = rt;
+    }
+}
+
 }  // namespace
 }  // namespace attn
+
+extern "C" int attn_clock_stamps(void* stamps, int slots, hipStream_t stream) {
+    using namespace attn;
+    if (!stamps) return ATTN_ERR_NULL;
+    if (slots < 1 || slots > 65536) return ATTN_ERR_SHAPE;
+    hipLaunchKernelGGL(clock_stamp_kernel, dim3((unsigned)slots), dim3(64), 0, stream,
+                       (unsigned long long*)stamps);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
 
 extern "C" size_t attn_hbm_probe_sink_words(size_t bytes) {
     return (bytes + attn::kBytesPerWg - 1) / attn::kBytesPerWg;

@@ -1,8 +1,9 @@
 // Pieces shared by the prefill kernels' translation units: the bf16 /
 // widened-FP8 kernel (prefill_hd512.hip) and the block-scaled FP8 MFMA kernel
 // (prefill_fp8mma.hip).  Both take one workgroup of 4 waves per 128 packed
-// query rows and keep the same online-softmax bookkeeping (a fixed per-row
-// reference maximum with a bounded restart).  The host validates every
+// query rows and keep the same online-softmax bookkeeping (a per-row
+// reference maximum that is raised, with O and l rescaled, only for the key
+// blocks that would overflow against it).  The host validates every
 // argument in prefill_launch before a launch.
 #pragma once
 
@@ -14,18 +15,10 @@ namespace attn {
 constexpr int kRowsPerWg = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-// Largest allowed excess (log2 units) of a row's scores over its reference
-// maximum: p <= 2^32 and l <= 2^32 * keys stay far inside fp32 and bf16.
-constexpr float kRescaleMargin = 32.f;
-constexpr float kOverSum = 4294967296.f;   // 2^kRescaleMargin
-constexpr float kBlindRaise = 123.f;       // log2(FLT_MAX / 32), rounded down
 // Page ids of the first kPagesInLds tiles are staged in LDS at the start of
 // the workgroup (reading them from the scalar cache inside the loop stalls
 // the wave: scalar loads share the LDS wait counter and return out of order).
 constexpr int kPagesInLds = 4096;
-// Restarts per workgroup are capped so that non-finite inputs (a caller error)
-// cannot loop forever; each genuine restart raises a row's reference by > 32.
-constexpr int kMaxRestarts = 8;
 
 // Masks one block's raw scores in place: element i is key
 // key_base + 8(i/4) + (i%4) (key_base includes 4h); keys >= n_row get -inf,
@@ -38,6 +31,42 @@ __device__ __forceinline__ void mask_block(f32x16& s, int key_base, int n_row, i
         const bool vis = WINDOW ? (key < n_row && key >= lo_row) : key < n_row;
         s[i] = vis ? s[i] : -__builtin_inff();
     }
+}
+
+// x *= s for every element of an accumulator held in AGPRs, one element at a
+// time through one VGPR (VALU cannot read AGPRs): written as asm so that the
+// accumulators stay in AGPRs instead of being copied out whole.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float s) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float x = acc[i];
+        float t;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n\t"
+            "v_mul_f32 %1, %1, %2\n\t"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(x), "=&v"(t)
+            : "v"(s));
+        acc[i] = x;
+    }
+}
+
+// Wait states around scale_acc, tied to every accumulator so that no MFMA
+// moves across them: an MFMA's result must be written before v_accvgpr_read
+// reads it, and an accumulator written by v_accvgpr_write before an MFMA
+// reads it as its C operand.
+template <int NDB>
+__device__ __forceinline__ void acc_fence(f32x16 (&o)[NDB]) {
+    static_assert(NDB == 16 || NDB == 8, "accumulator blocks");
+    if constexpr (NDB == 16)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                       "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+                       "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                       "+a"(o[6]), "+a"(o[7]));
 }
 
 struct PrefillArgs {

@@ -23,8 +23,9 @@
 // k_scale folds into the softmax scale and v_scale multiplies O at the end, as
 // in the widened FP8 path.
 //
-// Work unit, softmax bookkeeping (fixed per-row reference maximum, bounded
-// restart), masking and output are those of prefill_hd512_kernel.  The tile
+// Work unit, softmax bookkeeping (a per-row reference maximum, raised by
+// whole log2 units only for blocks that would overflow against it), masking
+// and output are those of prefill_hd512_kernel.  The tile
 // pipeline differs, because one 32x32x64 MFMA of P.V spans the whole 64-key
 // tile: per tile j the wave runs Q.K^T of block 0 (16 MFMAs) under block 1's
 // softmax of tile j - 1, which completes P(j - 1); then P.V of tile j - 1
@@ -43,12 +44,13 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRow8 = 512;                  // one E4M3 row of 512 dims
 constexpr int kTile8 = kPage * kRow8;       // 32 KB
 constexpr int kVRegion = 2 * kTile8;        // V buffers follow the two K buffers
 constexpr int kTileArea = 4 * kTile8;       // K0 K1 V0 V1
-constexpr int kSmem8 = kTileArea + kPagesInLds * 4 + kWaves * 4;
+constexpr int kSmem8 = kTileArea + kPagesInLds * 4;
 constexpr int kBufBit = kTile8;             // offset bit that selects buffer 1
 static_assert(kBufBit == 1 << 15, "buffers 32 KB apart");
 // E8M0 encodings: 2^(e - 7) for a high term, 2^(e - 12) for a residual that
@@ -142,49 +144,92 @@ __device__ __forceinline__ void split_pair(float xa, float xb, int& hi, int& lo)
                                          __builtin_fmaf(xb, 32.f, -h32[1]), lo, WORD);
 }
 
-// floor of the row's block maximum in log2 units relative to the reference
-// (clamped, so that masked rows and NaN give a finite, encodable exponent)
+// floor of the row's block maximum in log2 units relative to the reference.
+// Clamped below at -100 (masked rows and NaN give a finite exponent; weights
+// under 2^-100 of the reference vanish either way) and above only where the
+// int conversion needs it: a block far above the reference gets its true
+// exponent, so its weights p' stay in [0, 256), and rebase_blocks brings the
+// exponent back into the E8M0 range before the block's P.V.
 __device__ __forceinline__ int block_exponent(const f32x16& s, float scale_log2, float neg_m_ref) {
     float m = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) m = fmaxf(m, s[i]);
     m = pair_max(m);
     const float xl = __builtin_fmaf(m, scale_log2, neg_m_ref);
-    return (int)__builtin_floorf(fminf(fmaxf(xl, -100.f), 120.f));
+    return (int)__builtin_floorf(fminf(fmaxf(xl, -100.f), 1073741824.f));
+}
+
+// Largest block exponent a P.V takes: the block's scale 2^(e - 7) stays
+// encodable, and O and l (at most 2^(e + 1) per key and value) far inside fp32.
+constexpr int kMaxBlockExp = 32;
+
+// True when a row of the wave has a block of the tile whose P.V is next
+// above kMaxBlockExp.
+__device__ __forceinline__ bool blocks_over(int e0, int e1) {
+    return __builtin_amdgcn_ballot_w64(e0 > kMaxBlockExp || e1 > kMaxBlockExp) != 0;
+}
+
+// The reference raise of the online softmax (Flash-Decoding for MQA in CUDA,
+// "One KV head breaks the textbook": one rescale per tile, not per key), run
+// only when a block would pass kMaxBlockExp: every row of the wave raises
+// m_ref by k = max(e0, e1, 0) whole log2 units, multiplies O and l_run by
+// 2^-k (exact), and lowers both block exponents by k.  The blocks' weights
+// p' are relative to their own exponents, so they do not change.  A block
+// left more than 100 log2 units below the new reference takes exponent -100,
+// as block_exponent does, which keeps its E8M0 scale encodable (its weights
+// are then below 2^-92 of the row's largest, in O and in l alike).
+__device__ __forceinline__ void rebase_blocks(f32x16 (&o)[16], float& m_ref, float& l_run,
+                                              int& e0, int& e1) {
+    const int k = max(max(e0, e1), 0);
+    const float f = __builtin_amdgcn_ldexpf(1.f, -k);
+    acc_fence(o);
+#pragma unroll
+    for (int db = 0; db < 16; ++db) scale_acc(o[db], f);
+    acc_fence(o);
+    l_run *= f;
+    m_ref += (float)k;
+    e0 = max(e0 - k, -100);
+    e1 = max(e1 - k, -100);
 }
 
 // Softmax of elements i, i + 1 (i even) of a block with exponent offset c
 // (= 7 - e - m_ref), in two halves that go into the two gaps of a k-step's
 // dependent MFMA pair (issued after the first MFMA and after the second, so
 // that neither gap's VALU work outlasts the MFMA it hides under):
-// softmax_exp gives p' = 2^(s scale_log2 + c) in [0, 256) and the lane's sum
-// of p'; softmax_split writes the two E4M3 terms into dword DW of the P
-// operands.  The empty asms pin the work to its step.
+// softmax_exp gives p' = 2^(s scale_log2 + c) in [0, 256); softmax_split
+// writes the two E4M3 terms into dword DW of the P operands and adds the
+// pair's represented weights hi + lo / 32 (exact in f16: at most 9
+// significant bits) to the lane's block sum, so that l sums the same
+// weights P.V multiplies: a row with one dominant key gets that key's value
+// up to the output rounding.  The empty asms pin the work to its step.
 template <int I>
-__device__ __forceinline__ void softmax_exp(const f32x16& s, float scale_log2, float c, float& psum,
-                                            float& pa, float& pb) {
+__device__ __forceinline__ void softmax_exp(const f32x16& s, float scale_log2, float c, float& pa,
+                                            float& pb) {
     float sa = s[I], sb = s[I + 1];
     asm volatile("" : "+v"(sa), "+v"(sb));
     pa = fast_exp2(__builtin_fmaf(sa, scale_log2, c));
     pb = fast_exp2(__builtin_fmaf(sb, scale_log2, c));
-    psum += pa;
-    psum += pb;
-    asm volatile("" : "+v"(psum), "+v"(pa), "+v"(pb));
+    asm volatile("" : "+v"(pa), "+v"(pb));
 }
 template <int I, int DW>
-__device__ __forceinline__ void softmax_split(float pa, float pb, i32x8& phi, i32x8& plo) {
+__device__ __forceinline__ void softmax_split(float pa, float pb, i32x8& phi, i32x8& plo,
+                                              float& psum) {
+    constexpr bool kWord = ((I >> 1) & 1) != 0;
     int hi = phi[DW], lo = plo[DW];
-    split_pair<((I >> 1) & 1) != 0>(pa, pb, hi, lo);
+    split_pair<kWord>(pa, pb, hi, lo);
     phi[DW] = hi;
     plo[DW] = lo;
-    asm volatile("" : "+v"(hi), "+v"(lo));
+    const f16x2 rep = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.f, kWord) +
+                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 0.03125f, kWord);
+    psum = __builtin_amdgcn_fdot2(rep, f16x2{(_Float16)1.f, (_Float16)1.f}, psum, false);
+    asm volatile("" : "+v"(hi), "+v"(lo), "+v"(psum));
 }
 template <int I, int DW>
 __device__ __forceinline__ void softmax_pair(const f32x16& s, float scale_log2, float c, float& psum,
                                              i32x8& phi, i32x8& plo) {
     float pa, pb;
-    softmax_exp<I>(s, scale_log2, c, psum, pa, pb);
-    softmax_split<I, DW>(pa, pb, phi, plo);
+    softmax_exp<I>(s, scale_log2, c, pa, pb);
+    softmax_split<I, DW>(pa, pb, phi, plo, psum);
 }
 
 template <bool OUT_FP32, bool SPLIT>
@@ -193,7 +238,6 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem8];
     ATTN_LDS char* const lds = (ATTN_LDS char*)smem;
     ATTN_LDS int* const sPage = (ATTN_LDS int*)(lds + kTileArea);
-    ATTN_LDS int* const sFlag = sPage + kPagesInLds;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -361,9 +405,7 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     f32x16 s0, s1;                 // scores of blocks 0 and 1 (raw, then masked)
     i32x8 phi = {}, plo = {};      // P operands: bytes 0-15 block 0, 16-31 block 1
     float m_ref = -__builtin_inff();
-    float l_peak = 0.f;
     float l_run = 0.f;
-    int restarts = 0;
 
     // Per tile j the wave runs, in order: Q.K^T of block 0 of tile j under
     // block 1's softmax of tile j - 1 (which completes P(j - 1)); P.V of tile
@@ -402,10 +444,10 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
             tile_rows<ks>(d, lane_off8);
             if constexpr (ks == 0) c = prologue();
             float pa, pb;
-            softmax_exp<2 * ks>(sp, a.scale_log2, c, psum, pa, pb);
+            softmax_exp<2 * ks>(sp, a.scale_log2, c, pa, pb);
             __builtin_amdgcn_sched_barrier(0);
             mfma8_vgpr<2 * (ks & 1)>(acc, cur, qhi[ks], sa, qsc[ks >> 1]);
-            softmax_split<2 * ks, dwb + ks / 2>(pa, pb, phi, plo);
+            softmax_split<2 * ks, dwb + ks / 2>(pa, pb, phi, plo, psum);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -451,8 +493,7 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     // refill (8 loads) before the newest.  Refills past the last tile are
     // issued too (empty: they land zeros in buffers nothing reads again), so
     // that every count is the same; the last P.V waits for all.
-    for (;;) {   // one pass over the key range; a restart begins a new pass
-        if (ntiles == 0) break;
+    if (ntiles > 0) {
 #pragma unroll
         for (int db = 0; db < 16; ++db) o[db] = f32x16{};
         tile_rows_all(tdma(true, 0, 0), lane_off8, std::make_integer_sequence<int, 8>{});
@@ -469,7 +510,7 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
             wait_vmcnt<8>();
             lds_barrier();
             int e1 = 0;
-            float ps1 = 0.f;
+            float ps1 = 0.f;   // block sums of the represented weights, in units of p'
             qk_phase(std::integral_constant<int, 0>{}, s0, dk, s1, [&]() {
                 mfma_vgpr_drain(s1);
                 if (j > 0 && key0 > n_min)
@@ -479,11 +520,9 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
             }, ps1, std::integral_constant<int, 4>{});
             // ---- P.V of tile j - 1
             if (j > 0) {
+                if (__builtin_expect(blocks_over(e0, e1), 0)) rebase_blocks(o, m_ref, l_run, e0, e1);
                 const int own = h ? e1 : e0;
-                const float psum = __builtin_amdgcn_ldexpf(ps0, e0 - 7) +
-                                   __builtin_amdgcn_ldexpf(ps1, e1 - 7);
-                l_run += psum;
-                l_peak = fmaxf(l_peak, psum);
+                l_run += __builtin_amdgcn_ldexpf(ps0, e0 - 7) + __builtin_amdgcn_ldexpf(ps1, e1 - 7);
                 wait_vmcnt<8>();
                 lds_barrier();
                 pv_phase((j - 1) & 1, (kE8Hi + own) | ((kE8Lo + own) << 8));
@@ -493,8 +532,8 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
             qk_phase(std::integral_constant<int, 1>{}, s1, tdma(false, j, j & 1), s0, [&]() {
                 mfma_vgpr_drain(s0);
                 if (key0 + kPage > n_min) mask_block<false>(s0, key0 + 4 * h, n_row, 0);
-                float neg_m0 = neg_m;
-                if (j == 0 && restarts == 0) {
+                float neg_m0 = -m_ref;   // after any raise above
+                if (j == 0) {
                     // reference maximum: the row's maximum over the range's first
                     // 32 keys (without split-K key 0 is visible to every row; a
                     // split can start past a row's causal limit, and that row
@@ -520,43 +559,20 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
             const int key0 = (kt_lo + ntiles) * kPage;
             if (key0 > n_min) mask_block<false>(s1, key0 - kPage + 32 + 4 * h, n_row, 0);
             const float neg_m = -m_ref;
-            const int e1 = block_exponent(s1, a.scale_log2, neg_m);
+            int e1 = block_exponent(s1, a.scale_log2, neg_m);
             const float c1 = neg_m + (float)(7 - e1);
             float ps1 = 0.f;
             static_for<8>([&](auto I) {
                 constexpr int i = 2 * decltype(I)::value;
                 softmax_pair<i, 4 + i / 4>(s1, a.scale_log2, c1, ps1, phi, plo);
             });
+            if (__builtin_expect(blocks_over(e0, e1), 0)) rebase_blocks(o, m_ref, l_run, e0, e1);
             const int own = h ? e1 : e0;
-            const float psum = __builtin_amdgcn_ldexpf(ps0, e0 - 7) +
-                               __builtin_amdgcn_ldexpf(ps1, e1 - 7);
-            l_run += psum;
-            l_peak = fmaxf(l_peak, psum);
+            l_run += __builtin_amdgcn_ldexpf(ps0, e0 - 7) + __builtin_amdgcn_ldexpf(ps1, e1 - 7);
             wait_vmcnt<0>();
             lds_barrier();
             pv_phase((ntiles - 1) & 1, (kE8Hi + own) | ((kE8Lo + own) << 8));
         }
-        // back to K buffer 0 for a restarted pass
-        if (ntiles & 1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kx[i] ^= kBufBit;
-        }
-        // Restart vote, once per pass, as in prefill_hd512_kernel: a lane
-        // whose tile sum of p passed 2^margin, or whose sums were not finite.
-        const bool over = __any(!(l_peak <= kOverSum) || !(l_run <= 3.0e38f));
-        if (lane == 0) sFlag[wave] = over ? 1 : 0;
-        lds_barrier();
-        const bool restart =
-            restarts < kMaxRestarts && (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0;
-        if (!restart) break;
-        ++restarts;
-        lds_barrier();   // every wave has read the flags before they are rewritten
-        {
-            const float lp = fmaxf(l_peak, __shfl_xor(l_peak, 32));
-            m_ref += !(lp <= 3.0e38f) ? kBlindRaise : (lp > 1.f ? __builtin_log2f(lp) : 0.f);
-        }
-        l_peak = 0.f;
-        l_run = 0.f;
     }
 
     // ---- epilogue (shared with prefill_hd512_kernel): O in the true scale of p

@@ -220,32 +220,118 @@ struct SoftmaxCtx {
     float neg_m_ref;  // -m_ref
 };
 
+// Sum of a packed bf16 pair, added to acc in fp32 (one v_dot2 with 1, 1).
+__device__ __forceinline__ float add_pair(const bf16x8& v, int pair, float acc) {
+    const bf16x2 x = {v[2 * pair], v[2 * pair + 1]};
+    return __builtin_amdgcn_fdot2_f32_bf16(x, bf16x2{(__bf16)1.f, (__bf16)1.f}, acc, false);
+}
+
 // One softmax element: p = 2^(s * scale - m_ref) (0 for masked keys).  The
-// lane's running sum and the P^T operand take p one element later (the
-// previous element's p, `pend`, is added and packed here), so that no
-// instruction reads an exp2 result right after it is written (that read
-// costs a wait state); softmax_flush finishes the block's last element.  No
-// running maximum is kept: the sum bounds every p of the tile, which is all
-// the reference check needs.
+// P^T operand takes p one element later (the previous element's p, `pend`,
+// is packed here), so that no instruction reads an exp2 result right after
+// it is written (that read costs a wait state); softmax_flush finishes the
+// block's last element.  The lane's running sum adds each completed pair as
+// packed, i.e. the same bf16 values P.V multiplies (one v_dot2 per pair), so
+// that numerator and denominator carry the same rounded weights: a row with
+// one dominant key gets that key's value exactly.  LO (the range's first
+// tile) also packs the residual p - bf16(p) as a second bf16 term and adds
+// it to the sum, so that P.V sees p to about 16 significant bits: rows whose
+// few keys all lie in that tile would otherwise carry bf16's relative error
+// on each weight.  No running maximum is kept: the block's sum bounds every
+// p of the block, which is all the overflow check needs.
 // The empty asms pin the element to the MFMA step it is issued with (inputs
 // taken and running values produced inside the step): without them, IR
 // passes gather the softmax arithmetic into one cluster after the MFMA chain
 // and the matrix core idles while it runs.
+template <bool LO = false>
 __device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float s, int i, float& psum,
-                                             float& pend, bf16x8& pf_prev) {
+                                             float& pend, bf16x8& pf_prev, bf16x8& lo_prev) {
     asm volatile("" : "+v"(s));
     const float p = fast_exp2(__builtin_fmaf(s, c.scale_log2, c.neg_m_ref));
     if (i > 0) {
-        psum += pend;
-        pf_prev[(i - 1) & 7] = (__bf16)pend;
+        const int e = (i - 1) & 7;
+        const __bf16 hi = (__bf16)pend;
+        pf_prev[e] = hi;
+        if constexpr (LO) lo_prev[e] = (__bf16)(pend - (float)hi);
+        // a completed pair is packed and summed here, in its step (the
+        // overflow check after the block would otherwise let the packing
+        // sink below it)
+        if (e & 1) {
+            psum = add_pair(pf_prev, e >> 1, psum);
+            if constexpr (LO) psum = add_pair(lo_prev, e >> 1, psum);
+            asm volatile("" : "+v"(pf_prev));
+            if constexpr (LO) asm volatile("" : "+v"(lo_prev));
+        }
     }
     pend = p;
     asm volatile("" : "+v"(psum));
 }
 
-__device__ __forceinline__ void softmax_flush(float& psum, float pend, bf16x8& pf1) {
-    psum += pend;
-    pf1[7] = (__bf16)pend;
+template <bool LO = false>
+__device__ __forceinline__ void softmax_flush(float& psum, float pend, bf16x8& pf1, bf16x8& lo1) {
+    const __bf16 hi = (__bf16)pend;
+    pf1[7] = hi;
+    if constexpr (LO) lo1[7] = (__bf16)(pend - (float)hi);
+    psum = add_pair(pf1, 3, psum);
+    if constexpr (LO) psum = add_pair(lo1, 3, psum);
+    asm volatile("" : "+v"(pf1));
+    if constexpr (LO) asm volatile("" : "+v"(lo1));
+}
+
+// Largest allowed block sum of p before the reference is raised: every p of
+// the block is then at most 2^32, far inside fp32 and bf16, and so are O and l.
+constexpr float kBlockSumCap = 4294967296.f;   // 2^32
+
+// The overflow guard of the online softmax.  The reference m_ref is a row's
+// maximum over its first 32 keys; later keys usually stay near it, so p =
+// 2^(x - m_ref) needs no per-tile rescale.  When a block's sum of p passes
+// kBlockSumCap on some lane (or is not finite), the wave calls this before
+// the block's P.V: every row of the wave takes the exact maximum of its
+// block, raises its reference by the whole number of log2 units k >= 0 that
+// brings it to at least that maximum, multiplies what it has accumulated (O
+// when o_live, l_run, and the sum of the tile's earlier block) by 2^-k,
+// which is exact, and recomputes the block's P against the new reference.
+// A row whose maximum did not rise keeps k = 0 and its values bit for bit.
+// This is the online softmax's rescale, run only for the blocks that need
+// it (Flash-Decoding for MQA in CUDA, "One KV head breaks the textbook":
+// one rescale per tile, not per key), so any finite score range is handled.
+template <bool LO, int NDB>
+__device__ __forceinline__ void raise_reference(f32x16 (&o)[NDB], bool o_live, const f32x16& s,
+                                                float& m_ref, SoftmaxCtx& c, float& l_run,
+                                                float& psum_prev, float& psum, bf16x8& p0,
+                                                bf16x8& p1, bf16x8& lo0, bf16x8& lo1) {
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c.scale_log2;
+    // a row with no visible key yet (window) has m_ref = -inf and p = 0
+    float k = m_ref == -__builtin_inff() ? 0.f : __builtin_ceilf(mx - m_ref);
+    // NaN and -inf give 0; the cap only keeps the int conversion defined
+    // (any k past 150 already makes f = 0)
+    k = k > 0.f ? (k < 1073741824.f ? k : 1073741824.f) : 0.f;
+    const float f = __builtin_amdgcn_ldexpf(1.f, -(int)k);
+    if (o_live) {
+        acc_fence(o);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) scale_acc(o[db], f);
+        acc_fence(o);
+    }
+    l_run *= f;
+    psum_prev *= f;
+    m_ref += k;
+    c.neg_m_ref = m_ref == -__builtin_inff() ? 0.f : -m_ref;
+    psum = 0.f;
+    float pend = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) softmax_elem<LO>(c, s[i], i, psum, pend, i - 1 < 8 ? p0 : p1,
+                                                  i - 1 < 8 ? lo0 : lo1);
+    softmax_flush<LO>(psum, pend, p1, lo1);
+}
+
+// True when some lane of the wave must raise its reference before the
+// block's P.V (a sum past the cap, or not finite).
+__device__ __forceinline__ bool block_over(float psum) {
+    return __builtin_amdgcn_ballot_w64(!(psum <= kBlockSumCap)) != 0;
 }
 
 
@@ -353,10 +439,11 @@ struct VReader8 {
 // row load after every fourth MFMA.  `pre` (the previous block's masking and
 // reference, which the softmax needs but the chain does not) runs after the
 // first MFMA is issued, so that it overlaps the matrix pipe.
-template <bool OVERLAP, bool FP8, int D, typename Pre>
+template <bool OVERLAP, bool FP8, int D, bool LO = false, typename Pre>
 __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(Kv<FP8, D>::kSteps)],
                                          const ATTN_LDS char* sK, const int (&koff)[8],
-                                         const f32x16& sp, const SoftmaxCtx& c, float& psum, bf16x8& pf0, bf16x8& pf1,
+                                         const f32x16& sp, const SoftmaxCtx& c, float& psum,
+                                         bf16x8& pf0, bf16x8& pf1, bf16x8& lo0, bf16x8& lo1,
                                          const HalfDma& dma, int lane_off, int lane, int wave,
                                          Pre&& pre) {
     // bf16 at 512: step ks reads chunk 2 ks + h of key row 32 kb + n; with
@@ -403,25 +490,31 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(
         if constexpr (ks == 0) pre();
         if constexpr (OVERLAP && (ks % kSmEvery == kSmEvery - 1)) {
             constexpr int i = ks / kSmEvery;
-            softmax_elem(c, sp[i], i, psum, pend, i - 1 < 8 ? pf0 : pf1);
+            softmax_elem<LO>(c, sp[i], i, psum, pend, i - 1 < 8 ? pf0 : pf1,
+                             i - 1 < 8 ? lo0 : lo1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
-    if constexpr (OVERLAP) softmax_flush(psum, pend, pf1);
+    if constexpr (OVERLAP) softmax_flush<LO>(psum, pend, pf1, lo1);
 }
 
 // P.V of one 32-key block (k-steps c = 2 kb, 2 kb + 1 of the tile, all D / 32
 // dim blocks).  FIRST: the tile's first k-step starts O from zero (inline
-// c = 0), so O is only ever written by MFMAs.  When OVERLAP, the 16 softmax
+// c = 0), so O is only ever written by MFMAs.  LO: P carries a second bf16
+// term (p0lo, p1lo; the range's first tile), multiplied into O by a second
+// MFMA on the same V operand; LO_NEXT: the overlapped softmax of the next
+// block produces its second term too.  When OVERLAP, the 16 softmax
 // elements of the next block's scores `sn` are spread evenly over the MFMAs;
 // the half-tile refill `dma` issues one row load after every fourth MFMA.
-template <bool FIRST, bool OVERLAP, bool FP8, int D, typename VR>
+template <bool FIRST, bool OVERLAP, bool FP8, int D, bool LO = false, bool LO_NEXT = false,
+          typename VR>
 __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], int kb,
                                          const bf16x8& p0, const bf16x8& p1,
+                                         const bf16x8& p0lo, const bf16x8& p1lo,
                                          const ATTN_LDS char* sV, const VR& vr, const f32x16& sn,
                                          const SoftmaxCtx& c, float& psum,
-                                         bf16x8& pn0, bf16x8& pn1, const HalfDma& dma,
-                                         int lane_off, int lane, int wave) {
+                                         bf16x8& pn0, bf16x8& pn1, bf16x8& ln0, bf16x8& ln1,
+                                         const HalfDma& dma, int lane_off, int lane, int wave) {
     constexpr int kDB = Kv<FP8, D>::kDimBlocks;
     constexpr int kMfma = 2 * kDB;
     constexpr int kDmaEvery = kMfma / Kv<FP8, D>::kDmaPerHalf;
@@ -441,16 +534,18 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
             o[db] = mfma32x32x16(cur, p0, f32x16{});
         else
             o[db] = mfma32x32x16(cur, st < kDB ? p0 : p1, o[db]);
+        if constexpr (LO) o[db] = mfma32x32x16(cur, st < kDB ? p0lo : p1lo, o[db]);
         if constexpr (st % kDmaEvery == 0) {
             if (dma.on) half_dma_row<FP8, D, st / kDmaEvery>(dma, lane_off, lane, wave);
         }
         if constexpr (OVERLAP && (st % kSmEvery == kSmEvery - 1)) {
             constexpr int i = st / kSmEvery;
-            softmax_elem(c, sn[i], i, psum, pend, i - 1 < 8 ? pn0 : pn1);
+            softmax_elem<LO_NEXT>(c, sn[i], i, psum, pend, i - 1 < 8 ? pn0 : pn1,
+                                  i - 1 < 8 ? ln0 : ln1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
-    if constexpr (OVERLAP) softmax_flush(psum, pend, pn1);
+    if constexpr (OVERLAP) softmax_flush<LO_NEXT>(psum, pend, pn1, ln1);
 }
 
 template <bool OUT_FP32, bool FP8, bool SPLIT, int D = kHeadDim, bool WINDOW = false,
@@ -465,7 +560,6 @@ void prefill_hd512_kernel(PrefillArgs a) {
     constexpr int kSteps = Kv<FP8, D>::kSteps;
     constexpr int kDB = Kv<FP8, D>::kDimBlocks;
     __shared__ __attribute__((aligned(1024))) char smem[2 * kTileB];
-    __shared__ int sFlag[kWaves];
     __shared__ int sPage[kPagesInLds];
     ATTN_LDS char* sK = (ATTN_LDS char*)smem;
     ATTN_LDS char* sV = sK + kTileB;
@@ -557,21 +651,16 @@ void prefill_hd512_kernel(PrefillArgs a) {
     const VRd vr(lane);
 
     f32x16 o[kDB];  // written first by the range's first P.V
-    // Online softmax with a fixed per-row reference maximum: p = 2^(x - m_ref)
-    // where m_ref is the row's maximum over its first 32 keys.  O and l carry
-    // the same factor 2^(m_true - m_ref), which cancels in O / l.  A row whose
-    // scores climb more than kRescaleMargin above m_ref pushes a lane's tile
-    // sum of p past 2^kRescaleMargin, and at the end of the pass the
-    // workgroup then restarts its key loop with every row's reference raised
-    // by log2 of its largest tile sum (which bounds every p seen from above
-    // and exceeds the largest p by at most 32x): the rescale of O is replaced
-    // by a recompute that typical inputs never trigger.  This keeps the 256 O accumulators (AGPRs,
-    // which VALU cannot address) out of all VALU code in the loop, and the
-    // per-element work to one exp2, one add and a conversion.
+    // Online softmax against a per-row reference maximum: p = 2^(x - m_ref),
+    // m_ref starting as the row's maximum over its first 32 keys.  O and l
+    // carry the factor 2^(m_true - m_ref), which cancels in O / l.  The
+    // reference only moves when a block's sum of p passes kBlockSumCap
+    // (raise_reference, before that block's P.V), so the 256 O accumulators
+    // (AGPRs, which VALU cannot address) stay out of the loop's VALU code,
+    // and the per-element work is one fma, one exp2, one add and a
+    // conversion.
     float m_ref = -__builtin_inff();
-    float l_peak = 0.f;   // largest tile sum of p of this lane in the pass
     float l_run = 0.f;
-    int restarts = 0;
 
     const int* ptab = a.page_table + (size_t)b * a.max_pages;
     const int lane16 = lane * 16;
@@ -635,7 +724,6 @@ void prefill_hd512_kernel(PrefillArgs a) {
         return tile - kt_lo < kPagesInLds ? __builtin_amdgcn_readfirstlane(sPage[tile - kt_lo])
                                           : load_uniform(ptab, ring > 0 ? tile % ring : tile);
     };
-    auto flags_set = [&]() -> bool { return (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0; };
 
     // Fused append: a group of 8 refill rows starting at position p comes
     // from the new-row buffer when qs <= p and p + 8 <= hi, i.e. when
@@ -700,132 +788,119 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // successor refills are issued too, over an empty key range (a resource
     // with no records lands zeros, fetching nothing) into halves nothing reads
     // again, so that every refill site is unconditional and every count the
-    // same; the pass's end waits for them.
-    for (;;) {   // one pass over the key range; a restart begins a new pass
-        int page_cur = ntiles > kt_lo ? page_of(kt_lo) : 0;   // page of tile kt
-        int page_nx = kt_lo + 1 < ntiles ? page_of(kt_lo + 1) : page_cur;   // of tile kt + 1
-        if (ntiles > kt_lo) {
-            const int page0 = page_cur;
-            const int v0 = min(L - kt_lo * kPage, kPage);
-            half_dma_all<FP8, D>(refill(true, page0, v0, kt_lo, 0, true), lane_off, lane, wave);
-            half_dma_all<FP8, D>(refill(true, page0, v0, kt_lo, 1, true), lane_off, lane, wave);
-            half_dma_all<FP8, D>(refill(false, page0, v0, kt_lo, 0, true), lane_off, lane, wave);
-        }
-        bool restart = false;
-        for (int kt = kt_lo; kt < ntiles; ++kt) {
-            const bool more = kt + 1 < ntiles;
-            const int key0 = kt * kPage;
-            const int valid = min(L - key0, kPage);
-            const int valid_n = more ? min(L - key0 - kPage, kPage) : 0;
-            const int page = page_cur;
-            const int page_n = page_nx;
-            // page id of tile kt + 2: the LDS read is issued here and its value
-            // taken after QK0, so that its latency hides under QK0's MFMAs (the
-            // index is clamped into the staged range; past it the id comes from
-            // the table after QK0)
-            const int t2 = kt + 2;
-            const bool t2_staged = t2 - kt_lo < kPagesInLds;
-            const int page_nn_raw = sPage[min(t2 - kt_lo, kPagesInLds - 1)];
-            // the tile crosses a row's causal limit (or a row's window start)
-            const bool mask = key0 + kPage > n_min || (WINDOW && key0 < lo_last);
-            SoftmaxCtx c0{a.scale_log2, WINDOW && m_ref == -__builtin_inff() ? 0.f : -m_ref};
-            float psum = 0.f;
-            bf16x8 pf[4];
-            f32x16 s0, s1;
+    // same; the loop's end waits for them.
+    int page_cur = ntiles > kt_lo ? page_of(kt_lo) : 0;              // page of tile kt
+    int page_nx = kt_lo + 1 < ntiles ? page_of(kt_lo + 1) : page_cur;  // of tile kt + 1
+    if (ntiles > kt_lo) {
+        const int page0 = page_cur;
+        const int v0 = min(L - kt_lo * kPage, kPage);
+        half_dma_all<FP8, D>(refill(true, page0, v0, kt_lo, 0, true), lane_off, lane, wave);
+        half_dma_all<FP8, D>(refill(true, page0, v0, kt_lo, 1, true), lane_off, lane, wave);
+        half_dma_all<FP8, D>(refill(false, page0, v0, kt_lo, 0, true), lane_off, lane, wave);
+    }
+    // One 64-key tile.  kFirst (the range's first tile, peeled off the loop):
+    // P carries its second bf16 term, the reference maximum is taken, and
+    // P.V starts O from zero.
+    auto tile = [&](auto first_tag, int kt) {
+        constexpr bool kFirst = decltype(first_tag)::value;
+        const bool more = kt + 1 < ntiles;
+        const int key0 = kt * kPage;
+        const int valid = min(L - key0, kPage);
+        const int valid_n = more ? min(L - key0 - kPage, kPage) : 0;
+        const int page = page_cur;
+        const int page_n = page_nx;
+        // page id of tile kt + 2: the LDS read is issued here and its value
+        // taken after QK0, so that its latency hides under QK0's MFMAs (the
+        // index is clamped into the staged range; past it the id comes from
+        // the table after QK0)
+        const int t2 = kt + 2;
+        const bool t2_staged = t2 - kt_lo < kPagesInLds;
+        const int page_nn_raw = sPage[min(t2 - kt_lo, kPagesInLds - 1)];
+        // the tile crosses a row's causal limit (or a row's window start)
+        const bool mask = key0 + kPage > n_min || (WINDOW && key0 < lo_last);
+        SoftmaxCtx c0{a.scale_log2, WINDOW && m_ref == -__builtin_inff() ? 0.f : -m_ref};
+        float psum0 = 0.f, psum1 = 0.f;   // the lane's sums of p of blocks 0 and 1
+        bf16x8 pf[4];
+        bf16x8 pl[4];                     // second terms (kFirst only)
+        f32x16 s0, s1;
 
-            // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill
-            // (each refill is named before the wait that precedes its block, so
-            // that the address work overlaps the wait rather than delaying the
-            // block's first MFMA)
-            const HalfDma dv1 = refill(false, page, valid, kt, 1, true);
-            hold_before_wait<APPEND>();
-            wait_vmcnt<2 * kD>();
-            lds_barrier();
-            qk_block<false, FP8, D>(s0, 0, qf, sK, koff, s0, c0, psum, pf[0], pf[1], dv1,
-                                    lane_off, lane, wave, [] {});
-            page_cur = page_n;
-            page_nx = t2 >= ntiles ? page_n
-                    : (t2_staged ? __builtin_amdgcn_readfirstlane(page_nn_raw)
-                                 : load_uniform(ptab, ring > 0 ? t2 % ring : t2));
-
-            // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill.
-            // Block 0's masking and reference run after QK1's first MFMA.
-            const HalfDma dk0 = refill(true, page_n, valid_n, kt + 1, 0, true);
-            hold_before_wait<APPEND>();
-            wait_vmcnt<2 * kD>();
-            lds_barrier();
-            qk_block<true, FP8, D>(s1, 1, qf, sK, koff, s0, c0, psum, pf[0], pf[1], dk0,
-                                   lane_off, lane, wave, [&] {
-                mfma_vgpr_drain(s0);
-                if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
-                if constexpr (WINDOW) lazy_reference(s0, a.scale_log2, m_ref, c0);
-                if (!WINDOW && kt == kt_lo && restarts == 0) {
-                    // reference maximum: the row's maximum over the range's first
-                    // 32 keys (a restarted pass keeps the raised one).  Without
-                    // split-K key 0 is visible to every row, so it is finite; a
-                    // split can start past a row's causal limit, and that row then
-                    // takes 0 (every p = 0, an empty partial).
-                    float m0 = -__builtin_inff();
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
-                    m0 = fmaxf(m0, __shfl_xor(m0, 32)) * a.scale_log2;
-                    m0 = m0 == -__builtin_inff() ? 0.f : m0;
-                    m_ref = m0;
-                    c0.neg_m_ref = -m0;
-                }
-            });
-            mfma_vgpr_drain(s1);
-            if (mask) mask_block<WINDOW>(s1, key0 + 32 + 4 * h, n_row, lo_row);
-            if constexpr (WINDOW) lazy_reference(s1, a.scale_log2, m_ref, c0);
-
-            // ---- PV0 with block 1's softmax; K rows 32..63 of tile kt+1 refill
-            const HalfDma dk1 = refill(true, page_n, valid_n, kt + 1, 1, true);
-            hold_before_wait<APPEND>();
-            wait_vmcnt<2 * kD>();
-            lds_barrier();
-            const SoftmaxCtx& c1 = c0;
-            if (kt == kt_lo)
-                pv_block<true, true, FP8, D>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
-            else
-                pv_block<false, true, FP8, D>(o, 0, pf[0], pf[1], sV, vr, s1, c1, psum, pf[2], pf[3], dk1, lane_off, lane, wave);
-
-            // ---- PV1; V rows 0..31 of tile kt+1 refill
-            const HalfDma dv0 = refill(false, page_n, valid_n, kt + 1, 0, true);
-            hold_before_wait<APPEND>();
-            wait_vmcnt<2 * kD>();
-            lds_barrier();
-            pv_block<false, false, FP8, D>(o, 1, pf[2], pf[3], sV, vr, s1, c1, psum, pf[2], pf[3],
-                                           dv0, lane_off, lane, wave);
-            l_run += psum;
-            l_peak = fmaxf(l_peak, psum);
-        }
-        // Restart vote, once per pass: a lane whose sum of p passed 2^margin
-        // in some tile (l_peak), or whose sums were not finite (l_run; NaN
-        // does not reach l_peak through fmaxf).  A pass that overshot may
-        // have overflowed O, which the restart recomputes from the start, so
-        // no per-tile vote is needed; typical inputs never restart.  The vote
-        // runs on every lane, outside the lane-0 store.
-        if (ntiles > kt_lo) {
-            const bool over = __any(!(l_peak <= kOverSum) || !(l_run <= 3.0e38f));
-            if (lane == 0) sFlag[wave] = over ? 1 : 0;
-            lds_barrier();   // every wave's flag is visible
-            restart = restarts < kMaxRestarts && flags_set();
-        }
-        if (!restart) break;
-        // start over with every row's reference raised to its maximum so far
-        ++restarts;
-        wait_vmcnt<0>();     // refills still landing in sK / sV
+        // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill
+        // (each refill is named before the wait that precedes its block, so
+        // that the address work overlaps the wait rather than delaying the
+        // block's first MFMA)
+        const HalfDma dv1 = refill(false, page, valid, kt, 1, true);
+        hold_before_wait<APPEND>();
+        wait_vmcnt<2 * kD>();
         lds_barrier();
-        // by log2 of the row's largest tile sum (>= its largest p); a sum that
-        // overflowed says only that some p passed 2^123, so the reference rises
-        // by that much and the pass may restart again.  Rows that saw no key,
-        // or none above the reference, keep it: the reference only rises.
-        {
-            const float lp = fmaxf(l_peak, __shfl_xor(l_peak, 32));
-            m_ref += !(lp <= 3.0e38f) ? kBlindRaise : (lp > 1.f ? __builtin_log2f(lp) : 0.f);
+        qk_block<false, FP8, D>(s0, 0, qf, sK, koff, s0, c0, psum0, pf[0], pf[1], pl[0], pl[1],
+                                dv1, lane_off, lane, wave, [] {});
+        page_cur = page_n;
+        page_nx = t2 >= ntiles ? page_n
+                : (t2_staged ? __builtin_amdgcn_readfirstlane(page_nn_raw)
+                             : load_uniform(ptab, ring > 0 ? t2 % ring : t2));
+
+        // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill.
+        // Block 0's masking and reference run after QK1's first MFMA.
+        const HalfDma dk0 = refill(true, page_n, valid_n, kt + 1, 0, true);
+        hold_before_wait<APPEND>();
+        wait_vmcnt<2 * kD>();
+        lds_barrier();
+        qk_block<true, FP8, D, kFirst>(s1, 1, qf, sK, koff, s0, c0, psum0, pf[0], pf[1], pl[0],
+                                       pl[1], dk0, lane_off, lane, wave, [&] {
+            mfma_vgpr_drain(s0);
+            if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
+            if constexpr (WINDOW) lazy_reference(s0, a.scale_log2, m_ref, c0);
+            if constexpr (!WINDOW && kFirst) {
+                // reference maximum: the row's maximum over the range's first
+                // 32 keys.  Without split-K key 0 is visible to every row, so
+                // it is finite; a split can start past a row's causal limit,
+                // and that row then takes 0 (every p = 0, an empty partial).
+                float m0 = -__builtin_inff();
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
+                m0 = fmaxf(m0, __shfl_xor(m0, 32)) * a.scale_log2;
+                m0 = m0 == -__builtin_inff() ? 0.f : m0;
+                m_ref = m0;
+                c0.neg_m_ref = -m0;
+            }
+        });
+        // block 0's P must be representable before its P.V (O is still
+        // unwritten in the first tile)
+        if (__builtin_expect(block_over(psum0), 0)) {
+            float none = 0.f;
+            raise_reference<kFirst>(o, !kFirst, s0, m_ref, c0, l_run, none, psum0, pf[0], pf[1],
+                                    pl[0], pl[1]);
         }
-        l_peak = 0.f;
-        l_run = 0.f;         // O restarts too: tile 0's P.V overwrites it
+        mfma_vgpr_drain(s1);
+        if (mask) mask_block<WINDOW>(s1, key0 + 32 + 4 * h, n_row, lo_row);
+        if constexpr (WINDOW) lazy_reference(s1, a.scale_log2, m_ref, c0);
+
+        // ---- PV0 with block 1's softmax; K rows 32..63 of tile kt+1 refill
+        const HalfDma dk1 = refill(true, page_n, valid_n, kt + 1, 1, true);
+        hold_before_wait<APPEND>();
+        wait_vmcnt<2 * kD>();
+        lds_barrier();
+        pv_block<kFirst, true, FP8, D, kFirst, kFirst>(o, 0, pf[0], pf[1], pl[0], pl[1], sV, vr,
+                                                       s1, c0, psum1, pf[2], pf[3], pl[2], pl[3],
+                                                       dk1, lane_off, lane, wave);
+        // block 1's P likewise; O now holds block 0 of this tile as well
+        if (__builtin_expect(block_over(psum1), 0))
+            raise_reference<kFirst>(o, true, s1, m_ref, c0, l_run, psum0, psum1, pf[2], pf[3],
+                                    pl[2], pl[3]);
+
+        // ---- PV1; V rows 0..31 of tile kt+1 refill
+        const HalfDma dv0 = refill(false, page_n, valid_n, kt + 1, 0, true);
+        hold_before_wait<APPEND>();
+        wait_vmcnt<2 * kD>();
+        lds_barrier();
+        pv_block<false, false, FP8, D, kFirst, false>(o, 1, pf[2], pf[3], pl[2], pl[3], sV, vr,
+                                                      s1, c0, psum1, pf[2], pf[3], pl[2], pl[3],
+                                                      dv0, lane_off, lane, wave);
+        l_run += psum0 + psum1;
+    };
+    if (ntiles > kt_lo) {
+        tile(std::true_type{}, kt_lo);
+        for (int kt = kt_lo + 1; kt < ntiles; ++kt) tile(std::false_type{}, kt);
     }
     wait_vmcnt<0>();   // the empty refills past the last tile
 

@@ -12,6 +12,8 @@ from __future__ import annotations
 
 from typing import Callable, Dict
 
+import torch
+
 from .gen import PagedCase, build_case, decode_lengths
 
 
@@ -57,6 +59,35 @@ def long_mqa_32k(device="cpu", seed=4, q_zero=False, v_one=False, kv_dtype="bf16
     return build_case(name, seqs=None, chunks=chunks, hq=16, hkv=1, seed=seed,
                       out_dtype="fp32", device=device, row_scale=(0.5, 2.0),
                       q_zero=q_zero, v_one=v_one, kv_dtype=kv_dtype)
+
+
+def chunk_prefill_8k_at_8k_late_keys(device="cpu", seed=3, kv_dtype="bf16") -> PagedCase:
+    """The 8192-row chunk at 8192..16383 with late dominant keys.
+
+    Every query row gets 1.5 u added (u = a fixed +-1 vector over the head
+    dims, re-rounded to bf16), and three keys of every KV head are set to
+    beta u with beta = 1.125, 2.25 and 4.5 at positions 4000, 8191 and 12288:
+    about 38, 76 and 152 nats (scale 1/sqrt(512)) above a typical score, so
+    each lies more than 32 log2 units above what the row saw before it --
+    first above the row's first 32 keys (the softmax reference starts
+    there), then above the previous late key.  Rows at 12288 and later see
+    all three.  In an FP8-E4M3 pool the late keys are the E4M3 codes of
+    beta u / k_scale.
+    """
+    case = chunk_prefill_8k_at_8k(device=device, seed=seed, kv_dtype=kv_dtype)
+    case.name = "chunk_prefill_8192_at_8192_late_keys" + _fp8_suffix(kv_dtype)
+    lc = case.launches[0]
+    u = torch.where(torch.arange(case.head_dim, device=device) % 3 == 0, -1.0, 1.0)
+    lc.q[:lc.total_q] = (lc.q[:lc.total_q].float() + 1.5 * u).to(torch.bfloat16)
+    for j, beta in ((4000, 1.125), (8191, 2.25), (12288, 4.5)):
+        page = int(case.page_table[0, j // 64])
+        row = beta * u
+        if kv_dtype == "bf16":
+            case.k_pool[page, :, j % 64, :] = row.to(torch.bfloat16)
+        else:
+            code = (row / case.k_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+            case.k_pool[page, :, j % 64, :] = code
+    return case
 
 
 def prefix_prefill_512_at_32k(device="cpu", seed=6, kv_dtype="bf16") -> PagedCase:
@@ -112,6 +143,7 @@ WORKLOADS: Dict[str, Callable[..., PagedCase]] = {
     "tiny_prefill_mqa_256": tiny_prefill_mqa,
     "chunk_prefill_2048": chunk_prefill_2k,
     "chunk_prefill_8192_at_8192": chunk_prefill_8k_at_8k,
+    "chunk_prefill_8192_at_8192_late_keys": chunk_prefill_8k_at_8k_late_keys,
     "long_mqa_32k_8x4096": long_mqa_32k,
     "prefix_prefill_512_at_32k": prefix_prefill_512_at_32k,
     "decode_b64_splitk": decode_b64,

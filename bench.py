@@ -60,6 +60,30 @@ def recorded_traffic():
     return TRAFFIC_RECORD["fetch_bytes"] + TRAFFIC_RECORD["write_bytes"], digest
 
 
+def clock_summary(stamps):
+    """Mean shader clock of each XCD between two clock-stamp launches.
+
+    stamps[0] and stamps[1] hold, per workgroup, (XCD id, shader-cycle
+    counter, 100 MHz counter).  For each XCD the earliest stamp of each
+    launch is taken; cycles over ticks, times 100 MHz, is its mean clock.
+    """
+    per = {}
+    for x in sorted(set(int(v) for v in stamps[0][:, 0]) & set(int(v) for v in stamps[1][:, 0])):
+        a = stamps[0][stamps[0][:, 0] == x]
+        b = stamps[1][stamps[1][:, 0] == x]
+        a = a[a[:, 2].argmin()]
+        b = b[b[:, 2].argmin()]
+        ticks = int(b[2]) - int(a[2])
+        if ticks > 0:
+            per[x] = (int(b[1]) - int(a[1])) / ticks * 100.0
+    if not per:
+        return None
+    vals = list(per.values())
+    return {"mean_mhz": sum(vals) / len(vals), "min_mhz": min(vals), "max_mhz": max(vals),
+            "xcds": len(vals),
+            "how": "s_memtime cycles / s_memrealtime 100 MHz ticks per XCD across the timed steps"}
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -159,17 +183,30 @@ def main():
 
     for _ in range(args.warmup):
         prefill_step()
+    # the K timed steps, cut into up to 7 windows by events on the launch
+    # stream (the median window is reported beside the K-step mean), with
+    # clock stamps just outside the timed region
+    n_win = max(1, min(7, args.steps))
+    bounds = [round(i * args.steps / n_win) for i in range(n_win + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_win + 1)]
+    stamps = torch.zeros((2, 256, 3), dtype=torch.int64, device="cuda")
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        prefill_step()
-    e1.record(stream)
+    A.clock_stamps(stamps[0], stream=stream)
+    ev[0].record(stream)
+    for w in range(n_win):
+        for _ in range(bounds[w + 1] - bounds[w]):
+            prefill_step()
+        ev[w + 1].record(stream)
+    A.clock_stamps(stamps[1], stream=stream)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
     tflops = flops / (ms_step * 1e-3) / 1e12
-    log(f"prefill chunk 8192@8192: {ms_step:.3f} ms/launch, {tflops:.1f} TFLOP/s")
+    win_ms = sorted(ev[w].elapsed_time(ev[w + 1]) / (bounds[w + 1] - bounds[w])
+                    for w in range(n_win))
+    clock = clock_summary(stamps.cpu().numpy())
+    log(f"prefill chunk 8192@8192: {ms_step:.3f} ms/launch, {tflops:.1f} TFLOP/s; windows "
+        f"{win_ms[0]:.3f}/{win_ms[len(win_ms) // 2]:.3f}/{win_ms[-1]:.3f} ms (min/median/max); "
+        f"mean shader clock {clock['mean_mhz'] if clock else float('nan'):.0f} MHz")
     assert torch.isfinite(out.float()).all()
 
     extra = {}
@@ -445,6 +482,11 @@ def main():
                    "kv_len": lc.kv_lens[0], "q_heads": case.num_q_heads,
                    "kv_heads": case.num_kv_heads, "head_dim": W.HEAD_DIM,
                    "page_size": W.PAGE_SIZE, "out_dtype": "bf16", "flop_per_launch": flops},
+        "windows": {"n": n_win, "median_ms": win_ms[len(win_ms) // 2], "min_ms": win_ms[0],
+                    "max_ms": win_ms[-1],
+                    "median_tflops": flops / (win_ms[len(win_ms) // 2] * 1e-3) / 1e12,
+                    "how": "the K timed steps cut into windows by events; ms per launch"},
+        "clock": clock,
         "gemm_roofline": {"tflops": gemm, "before": gemm_before, "after": gemm_after,
                           "frac": (tflops / gemm) if gemm else None,
                           "how": "torch.matmul bf16 8192^3 and 16384^3, best"},

@@ -430,6 +430,16 @@ int attn_prefill_hd512_append(const void* q, const void* k_new, const void* v_ne
 int attn_hbm_read_probe(const void* buf, size_t bytes, void* sink, hipStream_t stream);
 size_t attn_hbm_probe_sink_words(size_t bytes);
 
+/*
+ * Measurement helper: launches `slots` one-wave workgroups (1 <= slots <=
+ * 65536) on `stream`; workgroup i writes three uint64 words to stamps[3 i ..]:
+ * the id of the XCD it ran on (0..7), the shader-clock cycle counter
+ * (s_memtime) and the constant 100 MHz counter (s_memrealtime), as read on
+ * that XCD.  Two launches around a timed region give each XCD's mean shader
+ * clock over it: delta(cycles) / delta(100 MHz ticks) * 100 MHz.
+ */
+int attn_clock_stamps(void* stamps, int slots, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

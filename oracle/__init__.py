@@ -71,6 +71,17 @@ def lib():
     return _lib
 
 
+def default_threads() -> int:
+    """OpenMP threads of an oracle call: the CPUs this process may run on,
+    at most 16 (a one-GPU share of the host; the row results do not depend
+    on the count)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _cpu(t: torch.Tensor) -> torch.Tensor:
     assert t.device.type == "cpu", "oracle inputs must be host tensors"
     return t.contiguous()
@@ -108,7 +119,7 @@ def attend_rows(case, rows: Sequence[int], launch_idx: int = 0,
     D = args[16]
     r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     out = np.zeros((len(r), D), dtype=np.float32)
-    nthreads = threads if threads is not None else (os.cpu_count() or 1)
+    nthreads = threads if threads is not None else default_threads()
     window, ring_slots = _window_args(case)
     if window or ring_slots:
         rc = lib().oracle_attn_rows_full(*args, window, ring_slots, None, r.ctypes.data,
@@ -136,7 +147,7 @@ def attend_rows_lse(case, rows: Sequence[int], launch_idx: int = 0,
     if sinks is not None:
         snk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32))
         assert snk.shape == (case.num_q_heads,)
-    nthreads = threads if threads is not None else (os.cpu_count() or 1)
+    nthreads = threads if threads is not None else default_threads()
     window, ring_slots = _window_args(case)
     rc = lib().oracle_attn_rows_full(*args, window, ring_slots,
                                      snk.ctypes.data if snk is not None else None,

@@ -271,6 +271,9 @@ def test_probe_validation(L):
     assert L.attn_hbm_read_probe(None, 1024, FAKE, None) == 1
     assert L.attn_hbm_read_probe(FAKE, 1000, FAKE, None) == 2
     assert L.attn_hbm_probe_sink_words(1 << 20) >= 1
+    assert L.attn_clock_stamps(None, 8, None) == 1
+    assert L.attn_clock_stamps(FAKE, 0, None) == 2
+    assert L.attn_clock_stamps(FAKE, 65537, None) == 2
 
 
 def test_prefill_fp8_mma_validation(L):

@@ -72,6 +72,17 @@ def test_decode_deterministic(A):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_decode_b64_deterministic_ten_calls(A, kv_dtype):
+    # the batch-64 workload, ten calls with the library's default split: the
+    # same bits every time (the merge order and every partial are fixed)
+    case = W.decode_b64(device="cuda", kv_dtype=kv_dtype)
+    a = run_decode(A, case, poison_ws=False)
+    for i in range(9):
+        b = run_decode(A, case, poison_ws=False)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"call {i + 2} differs"
+
+
 def test_decode_workspace_too_small(A):
     case = _decode_case([300], 8, 4)
     lc = case.launches[0]

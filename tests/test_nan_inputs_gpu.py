@@ -2,9 +2,9 @@
 
 A NaN key row makes exactly the rows that attend to it NaN, in the oracle
 (the materialised softmax) and in the kernels alike: masked scores are
-replaced by -inf before the softmax.  A NaN score drives the prefill's
-reference-maximum restart (the pass's sums are not finite), which is
-bounded, so these calls must also return.  A NaN value row makes every row
+replaced by -inf before the softmax.  A NaN score makes its block's sum of
+p non-finite, which sends the prefill through its reference raise once for
+that block (no loop), so these calls must also return.  A NaN value row makes every row
 that attends to it NaN, and may also poison rows of a workgroup that loads
 its 64-key tile without attending to it (masked keys enter P.V with p = 0,
 and 0 x NaN = NaN); rows whose workgroup never loads that tile, and other

@@ -13,7 +13,9 @@ import torch
 
 import attn_workloads as W
 import oracle
-from _gpu_helpers import check_parity, library, run_prefill, sample_rows, sentinel_intact
+from _gpu_helpers import (check_parity, check_parity_any, library, one_token_per_block,
+                          oracle_rows_cached, run_prefill, sample_rows, sentinel_intact,
+                          tokens_per_workgroup)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,37 +52,50 @@ def test_small_shapes_fp8(A, shape, out_dtype):
     seqs, hq, hkv = shape
     case = W.build_case("small_fp8", seqs=seqs, hq=hq, hkv=hkv, seed=19, out_dtype=out_dtype,
                         device="cuda", q_pad_rows=3, extra_pages=2, table_pad=2, kv_dtype=FP8)
-    _full_check(A, case)
+    lc = case.launches[0]
+    ref = oracle.attend_all(case.to("cpu"))
+
+    def run(dt):
+        out = run_prefill(A, case, out_dtype=dt, pad_rows=5)
+        assert sentinel_intact(out[lc.total_q:]), "rows past total_q were written"
+        return out[:lc.total_q]
+    # the one-key shape outputs dequantised V rows (|o| up to ~3.5), whose
+    # own bf16 rounding breaks the mean-abs bound: check_parity_any gates its
+    # fp32 output and requires the bf16 output to be that value rounded
+    check_parity_any(run, ref, f"fp8 {seqs} {hq}/{hkv} out={out_dtype}", out_dtype)
 
 
 def test_chunk_prefill_2048_fp8(A):
     _full_check(A, W.chunk_prefill_2k(device="cuda", kv_dtype=FP8))
 
 
-def test_chunk_prefill_8192_at_8192_fp8_sampled(A):
+def test_chunk_prefill_8192_at_8192_fp8_every_workgroup(A):
+    # one query token from every 16-token workgroup block, all 32 heads, plus
+    # the first and last token (the oracle rows are shared with the FP8-MMA test)
     case = W.chunk_prefill_8k_at_8k(device="cuda", kv_dtype=FP8)
     lc = case.launches[0]
     out = run_prefill(A, case, pad_rows=64)
     assert sentinel_intact(out[lc.total_q:])
-    g = np.random.default_rng(5)
-    tokens = list(range(0, 16)) + list(range(lc.total_q - 16, lc.total_q)) + \
-        g.integers(0, lc.total_q, 32).tolist()
+    tokens = one_token_per_block(lc.total_q, tokens_per_workgroup(32, 4), seed=5)
     rows, toks = sample_rows(lc, case.num_q_heads, tokens)
-    ref = oracle.attend_rows(case.to("cpu"), rows).reshape(len(toks), case.num_q_heads, -1)
-    check_parity(out[torch.as_tensor(toks, device="cuda")], ref, "chunk_8192_at_8192_fp8 sampled")
+    ref = oracle_rows_cached(case.name, case.to("cpu"), rows).reshape(len(toks),
+                                                                      case.num_q_heads, -1)
+    check_parity(out[torch.as_tensor(toks, device="cuda")], ref,
+                 f"chunk_8192_at_8192_fp8 every workgroup ({len(toks)} tokens)")
 
 
-def test_long_mqa_32k_last_chunk_fp8_sampled(A):
+@pytest.mark.parametrize("li", range(8))
+def test_long_mqa_32k_chunk_fp8_every_workgroup(A, li):
     case = W.long_mqa_32k(device="cuda", kv_dtype=FP8)
-    li = len(case.launches) - 1
     lc = case.launches[li]
-    out = run_prefill(A, case, li=li)
-    g = np.random.default_rng(6)
-    tokens = [0, 1, 2, lc.total_q - 1] + g.integers(0, lc.total_q, 12).tolist()
+    out = run_prefill(A, case, li=li, pad_rows=3)
+    assert sentinel_intact(out[lc.total_q:])
+    tokens = one_token_per_block(lc.total_q, tokens_per_workgroup(16, 1), seed=6 + li)
     rows, toks = sample_rows(lc, case.num_q_heads, tokens)
-    ref = oracle.attend_rows(case.to("cpu"), rows, launch_idx=li).reshape(
+    ref = oracle_rows_cached(case.name, case.to("cpu"), rows, launch_idx=li).reshape(
         len(toks), case.num_q_heads, -1)
-    check_parity(out[torch.as_tensor(toks, device="cuda")], ref, "long_mqa_32k last chunk fp8")
+    check_parity(out[torch.as_tensor(toks, device="cuda")], ref,
+                 f"long_mqa_32k fp8 chunk {li} every workgroup ({len(toks)} tokens)")
 
 
 def test_fp8_q0_v1_matches_dequantised_one(A):

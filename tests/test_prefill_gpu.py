@@ -13,7 +13,10 @@ import torch
 
 import attn_workloads as W
 import oracle
-from _gpu_helpers import (check_parity, library, run_prefill, sample_rows, sentinel_intact)
+from _gpu_helpers import (check_parity, check_parity_any, check_parity_floor_case,
+                          floor_breaks_gate, library, one_token_per_block,
+                          oracle_rows_cached, run_prefill, sample_rows, sentinel_intact,
+                          tokens_per_workgroup)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +52,14 @@ def test_small_shapes(A, shape, out_dtype):
     seqs, hq, hkv = shape
     case = W.build_case("small", seqs=seqs, hq=hq, hkv=hkv, seed=17, out_dtype=out_dtype,
                         device="cuda", q_pad_rows=3, extra_pages=2, table_pad=2)
-    _full_check(A, case)
+    lc = case.launches[0]
+    ref = oracle.attend_all(case.to("cpu"))
+
+    def run(dt):
+        out = run_prefill(A, case, out_dtype=dt, pad_rows=5)
+        assert sentinel_intact(out[lc.total_q:]), "rows past total_q were written"
+        return out[:lc.total_q]
+    check_parity_any(run, ref, f"small {seqs} {hq}/{hkv} out={out_dtype}", out_dtype)
 
 
 def test_tiny_prefill_mqa_256(A):
@@ -63,30 +73,62 @@ def test_chunk_prefill_2048(A, out_dtype):
     _full_check(A, case, out_dtype=out_dtype)
 
 
-def test_chunk_prefill_8192_at_8192_sampled(A):
+def test_chunk_prefill_8192_at_8192_every_workgroup(A):
+    # one query token from every workgroup's 16-token block (all 32 heads, so
+    # every (token block, KV head) workgroup of the 8192-row chunk), plus the
+    # first and last token
     case = W.chunk_prefill_8k_at_8k(device="cuda")
     lc = case.launches[0]
     out = run_prefill(A, case, pad_rows=64)
     assert sentinel_intact(out[lc.total_q:])
-    g = np.random.default_rng(3)
-    tokens = list(range(0, 16)) + list(range(lc.total_q - 16, lc.total_q)) + \
-        g.integers(0, lc.total_q, 32).tolist()
+    tokens = one_token_per_block(lc.total_q, tokens_per_workgroup(32, 4), seed=3)
     rows, toks = sample_rows(lc, case.num_q_heads, tokens)
-    ref = oracle.attend_rows(case.to("cpu"), rows).reshape(len(toks), case.num_q_heads, -1)
-    check_parity(out[torch.as_tensor(toks, device="cuda")], ref, "chunk_8192_at_8192 sampled")
+    ref = oracle_rows_cached(case.name, case.to("cpu"), rows).reshape(len(toks),
+                                                                      case.num_q_heads, -1)
+    check_parity(out[torch.as_tensor(toks, device="cuda")], ref,
+                 f"chunk_8192_at_8192 every workgroup ({len(toks)} tokens)")
 
 
-def test_long_mqa_32k_chunks_sampled(A):
+@pytest.mark.parametrize("kv_dtype,fp8_mma", [("bf16", False), ("fp8_e4m3", False),
+                                              ("fp8_e4m3", True)])
+def test_chunk_prefill_8192_at_8192_late_keys_every_workgroup(A, kv_dtype, fp8_mma):
+    # every row sees two or three keys far above what it saw before them
+    # (38, 76 and 151 nats), so every workgroup raises its rows' softmax
+    # reference two or three times; one token of every workgroup checked
+    # (the rows are dominated by one key, so their outputs are that key's
+    # value: over an E4M3 pool the dequantised values' own bf16 rounding can
+    # break the gate, and the floor-case check then gates the fp32 output)
+    case = W.chunk_prefill_8k_at_8k_late_keys(device="cuda", kv_dtype=kv_dtype)
+    lc = case.launches[0]
+    out = run_prefill(A, case, pad_rows=64, fp8_mma=fp8_mma)
+    assert sentinel_intact(out[lc.total_q:])
+    tokens = one_token_per_block(lc.total_q, tokens_per_workgroup(32, 4), seed=8)
+    rows, toks = sample_rows(lc, case.num_q_heads, tokens)
+    ref = oracle_rows_cached(case.name, case.to("cpu"), rows).reshape(len(toks),
+                                                                      case.num_q_heads, -1)
+    sel = torch.as_tensor(toks, device="cuda")
+    what = f"{case.name} mma={fp8_mma} every workgroup ({len(toks)} tokens)"
+    if floor_breaks_gate(ref):
+        out32 = run_prefill(A, case, out_dtype="fp32", fp8_mma=fp8_mma)
+        check_parity_floor_case(out[sel], out32[sel], ref, what)
+    else:
+        check_parity(out[sel], ref, what)
+
+
+@pytest.mark.parametrize("li", range(8))
+def test_long_mqa_32k_chunk_every_workgroup(A, li):
+    # chunk li of the 32K prompt: one token from every 8-token workgroup block
+    # (g = 16), all 16 heads, plus the chunk's first and last token
     case = W.long_mqa_32k(device="cuda")
-    host = case.to("cpu")
-    g = np.random.default_rng(4)
-    for li, lc in enumerate(case.launches):
-        out = run_prefill(A, case, li=li, pad_rows=3)
-        assert sentinel_intact(out[lc.total_q:])
-        tokens = [0, 1, 2, lc.total_q - 1] + g.integers(0, lc.total_q, 12).tolist()
-        rows, toks = sample_rows(lc, case.num_q_heads, tokens)
-        ref = oracle.attend_rows(host, rows, launch_idx=li).reshape(len(toks), case.num_q_heads, -1)
-        check_parity(out[torch.as_tensor(toks, device="cuda")], ref, f"long_mqa chunk {li}")
+    lc = case.launches[li]
+    out = run_prefill(A, case, li=li, pad_rows=3)
+    assert sentinel_intact(out[lc.total_q:])
+    tokens = one_token_per_block(lc.total_q, tokens_per_workgroup(16, 1), seed=4 + li)
+    rows, toks = sample_rows(lc, case.num_q_heads, tokens)
+    ref = oracle_rows_cached(case.name, case.to("cpu"), rows, launch_idx=li).reshape(
+        len(toks), case.num_q_heads, -1)
+    check_parity(out[torch.as_tensor(toks, device="cuda")], ref,
+                 f"long_mqa chunk {li} every workgroup ({len(toks)} tokens)")
 
 
 def test_long_mqa_32k_q0_v1_is_exactly_one(A):
@@ -96,11 +138,17 @@ def test_long_mqa_32k_q0_v1_is_exactly_one(A):
         assert bool((out[:lc.total_q] == 1.0).all()), f"chunk {li}: output differs from 1"
 
 
-def test_deterministic_bitwise(A):
-    case = W.chunk_prefill_2k(device="cuda")
-    a = run_prefill(A, case)
-    b = run_prefill(A, case)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+@pytest.mark.parametrize("kv_dtype,fp8_mma", [("bf16", False), ("fp8_e4m3", False),
+                                              ("fp8_e4m3", True)])
+def test_deterministic_bitwise(A, kv_dtype, fp8_mma):
+    # ten launches of the 2048-row chunk give identical bits: the per-row
+    # accumulation order is fixed, so a difference between runs would point
+    # at an LDS hand-off that depends on timing
+    case = W.chunk_prefill_2k(device="cuda", kv_dtype=kv_dtype)
+    a = run_prefill(A, case, fp8_mma=fp8_mma)
+    for i in range(9):
+        b = run_prefill(A, case, fp8_mma=fp8_mma)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"launch {i + 2} differs"
 
 
 def test_empty_launch_and_bad_arguments(A):

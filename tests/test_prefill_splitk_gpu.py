@@ -8,10 +8,11 @@ dtypes, sinks and the log-sum-exp.  The prefix-prefill workload (512 rows over
 32768 keys) is compared on sampled rows.  The workspace is poisoned with NaN
 so that a partial the merge reads but the split kernel never wrote shows up.
 
-The reference-maximum restart of the key loop (a score far above the row's
-first 32) is exercised here too, on the single-pass and split-K kernels: a
-planted key whose score is about 2^200 above the others would overflow fp32
-without it.
+The raise of the softmax reference (a score far above the row's first 32)
+is exercised here too, on the single-pass and split-K kernels: a planted key
+whose score is about 2^200 above the others would overflow fp32 without it,
+and keys tens of thousands of log2 units apart need it to rise without
+bound.
 """
 import numpy as np
 import pytest
@@ -178,7 +179,7 @@ def _plant_hot_key(case, b, j, kv_dtype):
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("path", ["single", "splitk"])
-def test_reference_restart_on_hot_key(A, mode, path):
+def test_reference_raise_on_hot_key(A, mode, path):
     kv_dtype, mma = _pool(mode)
     case = W.build_case("hot", seqs=[(70, 900, 970), (50, 0, 50)], hq=16, hkv=2, seed=59,
                         out_dtype="fp32", device="cuda", kv_dtype=kv_dtype, q_pad_rows=2)
@@ -193,6 +194,40 @@ def test_reference_restart_on_hot_key(A, mode, path):
     ref = oracle.attend_all(case.to("cpu"))
     assert np.isfinite(ref).all()
     check_parity(out[:lc.total_q], ref, f"hot key {mode} {path}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("path", ["single", "splitk"])
+def test_reference_rises_past_any_range(A, mode, path):
+    # Three keys per sequence, each tens of thousands of log2 units above
+    # everything before it: the softmax reference must rise by far more than
+    # any fixed number of bounded raises would allow.  Every q row is q_mag u
+    # (u a +-1 vector); bf16 pools get keys beta u with beta = 16, 64, 256,
+    # E4M3 pools the codes of 28 u, 112 u and 448 u (exact E4M3 values).  The
+    # rows are then each dominated by one key, whose value is the output.
+    kv_dtype, mma = _pool(mode)
+    case = W.build_case("far", seqs=[(70, 900, 970), (50, 0, 50)], hq=16, hkv=2, seed=61,
+                        out_dtype="fp32", device="cuda", kv_dtype=kv_dtype, q_pad_rows=2)
+    lc = case.launches[0]
+    u = torch.where(torch.arange(512, device="cuda") % 3 == 0, -1.0, 1.0)
+    q_mag = 8.0 if kv_dtype == "bf16" else 1024.0
+    lc.q[:lc.total_q] = (q_mag * u).to(torch.bfloat16)
+    levels = (16.0, 64.0, 256.0) if kv_dtype == "bf16" else (28.0, 112.0, 448.0)
+    for b, keys in ((0, (300, 600, 950)), (1, (5, 20, 40))):
+        for j, lev in zip(keys, levels):
+            page = int(case.page_table[b, j // 64])
+            if kv_dtype == "bf16":
+                case.k_pool[page, :, j % 64, :] = (lev * u).to(torch.bfloat16)
+            else:
+                case.k_pool[page, :, j % 64, :] = (lev * u).to(torch.float8_e4m3fn).view(torch.uint8)
+    if path == "single":
+        out = run_prefill(A, case, pad_rows=2, fp8_mma=mma)
+    else:
+        out, _, nbytes = run_splitk(A, case, 128, pad_rows=2, fp8_mma=mma)
+        assert nbytes > 0
+    ref = oracle.attend_all(case.to("cpu"))
+    assert np.isfinite(ref).all()
+    check_parity(out[:lc.total_q], ref, f"far keys {mode} {path}")
 
 
 @pytest.mark.parametrize("mode", ["bf16", "fp8_mma"])
