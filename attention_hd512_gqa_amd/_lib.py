@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_splitk_ex.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, I,
                                             F, P, P, SZ, P, I, P, P]
         L.attn_decode_splitk_ex.restype = I
+        L.attn_decode_splitk_ex_noalloc.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I,
+                                                    I, I, I, F, P, P, I, P, P]
+        L.attn_decode_splitk_ex_noalloc.restype = I
         L.attn_append_kv.argtypes = [P, P, I, F, F, P, P, P, I, I, I, I, I, I, I, P, P, P]
         L.attn_append_kv.restype = I
         L.attn_decode_splitk_workspace_size.argtypes = [I, I, I, I, I]
@@ -303,6 +306,32 @@ def decode(q, k_pages, v_pages, page_table, kv_lens, out, workspace, *, max_kv_l
             int(page_table.shape[1]), int(max_kv_len), int(keys_per_split), float(softmax_scale),
             *ws, _stream(stream))
         _check(code, "attn_decode_splitk")
+
+
+def decode_noalloc(q, k_pages, v_pages, page_table, kv_lens, out, *, max_kv_len: int,
+                   softmax_scale: float, kv_dtype: str = "bf16", k_scale: float = 1.0,
+                   v_scale: float = 1.0, keys_per_split: int = 0, q_len: int = 1, sinks=None,
+                   lse=None, stream=None) -> None:
+    """decode() without a workspace argument (attn_decode_splitk_ex_noalloc):
+    the partials go to the library's static device scratch (64 MiB), so the
+    call allocates nothing.  Calls that overlap on one GPU share that scratch
+    and race."""
+    num_pages, hkv, page, d = k_pages.shape
+    hq = q.shape[1]
+    batch = kv_lens.shape[0]
+    if q.shape[0] != batch * q_len:
+        raise AttnError(f"q has {q.shape[0]} rows, expected batch * q_len = {batch * q_len}")
+    kvt = torch.bfloat16 if kv_dtype == "bf16" else torch.uint8
+    code = lib().attn_decode_splitk_ex_noalloc(
+        _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
+        _dev(v_pages, "v_pages", kvt), _KV_CODES[kv_dtype], float(k_scale), float(v_scale),
+        _dev(page_table, "page_table", torch.int32), _dev(kv_lens, "kv_lens", torch.int32),
+        int(batch), int(q_len), int(hq), int(hkv), int(d), int(page), int(num_pages),
+        int(page_table.shape[1]), int(max_kv_len), int(keys_per_split), float(softmax_scale),
+        _opt(sinks, "sinks", torch.float32, hq),
+        _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
+        _opt(lse, "lse", torch.float32, int(batch) * int(q_len) * hq), _stream(stream))
+    _check(code, "attn_decode_splitk_ex_noalloc")
 
 
 def append_kv(k_new, v_new, page_table, cu_seqlens, q_start, k_pages, v_pages, *,

@@ -39,6 +39,8 @@
 #include "device_common.h"
 #include "attn_host.h"
 
+#include <mutex>
+
 namespace attn {
 
 namespace {
@@ -556,6 +558,51 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, void* o
             den > 0.f ? (mu + __builtin_log2f(den)) * 0.6931471805599453f : -__builtin_inff();
 }
 
+// Scratch of attn_decode_splitk_ex_noalloc: the partials live in this
+// device array instead of a caller workspace.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is kept in scratch_dev.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxScratchDevices] = {};
+
+}  // namespace
+}  // namespace attn
+
+static __device__ __align__(256) char scratch[attn::kScratchBytes];
+
+namespace attn {
+namespace {
+
+// The scratch address on the device `stream` belongs to (the current device
+// for the null stream).
+int scratch_for_stream(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (stream) {
+        hipDevice_t d;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return ATTN_ERR_HIP;
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return ATTN_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices) return ATTN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_HIP;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return ATTN_ERR_HIP;
+        if (e != hipSuccess || !p) return ATTN_ERR_HIP;
+        scratch_dev[dev] = p;
+    }
+    *out = scratch_dev[dev];
+    return ATTN_OK;
+}
+
 int default_keys_per_split(int batch, int hkv, int max_kv_len) {
     const long long total = (long long)batch * hkv * max_kv_len;
     long long s = (total + kDefaultTargetWgs - 1) / kDefaultTargetWgs;
@@ -589,16 +636,20 @@ extern "C" size_t attn_decode_splitk_workspace_size(int batch, int num_q_heads, 
                                                 keys_per_split);
 }
 
-extern "C" int attn_decode_splitk_ex(const void* q, const void* k_pages, const void* v_pages,
-                                     int kv_dtype, float k_scale, float v_scale,
-                                     const int32_t* page_table, const int32_t* kv_lens,
-                                     int batch, int q_len, int num_q_heads, int num_kv_heads,
-                                     int head_dim, int page_size, int num_pages,
-                                     int max_pages_per_seq, int max_kv_len, int keys_per_split,
-                                     float softmax_scale, const float* sinks, void* workspace,
-                                     size_t workspace_bytes, void* out, int out_dtype,
-                                     float* lse, hipStream_t stream) {
-    using namespace attn;
+namespace attn {
+namespace {
+
+// Validation and launch shared by the caller-workspace entry point and the
+// one that allocates nothing.  workspace == nullptr asks for the library's
+// static scratch (attn_decode_splitk_ex_noalloc).
+int decode_launch(const void* q, const void* k_pages, const void* v_pages, int kv_dtype,
+                  float k_scale, float v_scale, const int32_t* page_table,
+                  const int32_t* kv_lens, int batch, int q_len, int num_q_heads,
+                  int num_kv_heads, int head_dim, int page_size, int num_pages,
+                  int max_pages_per_seq, int max_kv_len, int keys_per_split,
+                  float softmax_scale, const float* sinks, void* workspace,
+                  size_t workspace_bytes, bool noalloc, void* out, int out_dtype, float* lse,
+                  hipStream_t stream) {
     if (!q || !k_pages || !v_pages || !page_table || !kv_lens || !out) return ATTN_ERR_NULL;
     if (batch < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_pages < 1 ||
         max_pages_per_seq < 1 || max_kv_len < 1 || keys_per_split < 0 ||
@@ -612,13 +663,25 @@ extern "C" int attn_decode_splitk_ex(const void* q, const void* k_pages, const v
     if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
     if (out_dtype != ATTN_BF16 && out_dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
     if (kv_dtype == ATTN_FP8_E4M3 && (!(k_scale > 0.f) || !(v_scale > 0.f))) return ATTN_ERR_SHAPE;
-    const size_t need = attn_decode_splitk_ex_workspace_size(batch, q_len, num_q_heads,
-                                                             num_kv_heads, max_kv_len,
-                                                             keys_per_split);
-    if (!workspace || workspace_bytes < need || need == 0) return ATTN_ERR_WORKSPACE;
-
+    const bool fp8 = kv_dtype == ATTN_FP8_E4M3;
     const int kps = keys_per_split ? keys_per_split
                                    : default_keys_per_split(batch, num_kv_heads, max_kv_len);
+    const int sub = fp8 ? kFp8Waves : 1;
+    const int max_splits = (max_kv_len + kps - 1) / kps;
+    // partial slots the launch writes and reads: (O, m, l) per split, partial
+    // of the split and (token, query head)
+    const size_t slots = (size_t)batch * q_len * num_q_heads * max_splits * sub;
+    if (noalloc) {
+        if (slots * (kHeadDim + 2) * sizeof(float) > kScratchBytes) return ATTN_ERR_WORKSPACE;
+        const int rc = scratch_for_stream(stream, &workspace);
+        if (rc != ATTN_OK) return rc;
+    } else {
+        const size_t need = attn_decode_splitk_ex_workspace_size(batch, q_len, num_q_heads,
+                                                                 num_kv_heads, max_kv_len,
+                                                                 keys_per_split);
+        if (!workspace || workspace_bytes < need || need == 0) return ATTN_ERR_WORKSPACE;
+    }
+
     DecodeArgs a;
     a.q = (const __bf16*)q;
     a.k_pages = (const char*)k_pages;
@@ -633,13 +696,11 @@ extern "C" int attn_decode_splitk_ex(const void* q, const void* k_pages, const v
     a.cols = q_len * g;
     a.max_pages = max_pages_per_seq;
     a.num_pages = num_pages;
-    a.max_splits = (max_kv_len + kps - 1) / kps;
+    a.max_splits = max_splits;
     a.tiles_per_split = kps / kPage;
-    const size_t slots = (size_t)batch * q_len * num_q_heads * a.max_splits * kMaxSub;
     a.part_o = (float*)workspace;
     a.part_ml = (float*)workspace + slots * kHeadDim;
-    const bool fp8 = kv_dtype == ATTN_FP8_E4M3;
-    a.sub = fp8 ? kFp8Waves : 1;
+    a.sub = sub;
     a.scale_log2 = softmax_scale * 1.4426950408889634f * (fp8 ? k_scale : 1.f);
     a.v_scale = fp8 ? v_scale : 1.f;
     a.sinks = sinks;
@@ -661,6 +722,42 @@ extern "C" int attn_decode_splitk_ex(const void* q, const void* k_pages, const v
         hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((unsigned)mgrid), dim3(128), 0,
                            stream, a, out);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" int attn_decode_splitk_ex(const void* q, const void* k_pages, const void* v_pages,
+                                     int kv_dtype, float k_scale, float v_scale,
+                                     const int32_t* page_table, const int32_t* kv_lens,
+                                     int batch, int q_len, int num_q_heads, int num_kv_heads,
+                                     int head_dim, int page_size, int num_pages,
+                                     int max_pages_per_seq, int max_kv_len, int keys_per_split,
+                                     float softmax_scale, const float* sinks, void* workspace,
+                                     size_t workspace_bytes, void* out, int out_dtype,
+                                     float* lse, hipStream_t stream) {
+    return attn::decode_launch(q, k_pages, v_pages, kv_dtype, k_scale, v_scale, page_table,
+                               kv_lens, batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                               page_size, num_pages, max_pages_per_seq, max_kv_len,
+                               keys_per_split, softmax_scale, sinks, workspace, workspace_bytes,
+                               false, out, out_dtype, lse, stream);
+}
+
+extern "C" int attn_decode_splitk_ex_noalloc(const void* q, const void* k_pages,
+                                             const void* v_pages, int kv_dtype, float k_scale,
+                                             float v_scale, const int32_t* page_table,
+                                             const int32_t* kv_lens, int batch, int q_len,
+                                             int num_q_heads, int num_kv_heads, int head_dim,
+                                             int page_size, int num_pages,
+                                             int max_pages_per_seq, int max_kv_len,
+                                             int keys_per_split, float softmax_scale,
+                                             const float* sinks, void* out, int out_dtype,
+                                             float* lse, hipStream_t stream) {
+    return attn::decode_launch(q, k_pages, v_pages, kv_dtype, k_scale, v_scale, page_table,
+                               kv_lens, batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                               page_size, num_pages, max_pages_per_seq, max_kv_len,
+                               keys_per_split, softmax_scale, sinks, nullptr, 0, true, out,
+                               out_dtype, lse, stream);
 }
 
 extern "C" int attn_decode_splitk(const void* q, const void* k_pages, const void* v_pages,

@@ -365,6 +365,33 @@ int attn_decode_splitk_ex(const void* q, const void* k_pages, const void* v_page
                           hipStream_t stream);
 
 /*
+ * attn_decode_splitk_ex for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Arguments and results as attn_decode_splitk_ex, without the
+ * workspace: the split kernel's partials go to a static device array of the
+ * library (64 MiB per GPU, held until the process ends), whose address is
+ * looked up once per device on the first call that runs on it (the device
+ * of `stream`; the current device for the null stream).  The call allocates
+ * nothing and enqueues the same two kernels.
+ *
+ * ATTN_ERR_WORKSPACE when the plan's partials, batch * q_len * num_q_heads *
+ * ceil(max_kv_len / keys_per_split) * 2056 bytes (keys_per_split after the
+ * default is applied), exceed 64 MiB; ATTN_ERR_HIP when the address lookup
+ * fails.  The scratch needs no clearing (every partial the merge reads is
+ * written by the same call), but it is one array per GPU shared by every
+ * call: calls that overlap on one GPU (concurrent streams, or threads) race
+ * and give undefined results.
+ */
+int attn_decode_splitk_ex_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                                  int kv_dtype, float k_scale, float v_scale,
+                                  const int32_t* page_table, const int32_t* kv_lens, int batch,
+                                  int q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int page_size, int num_pages, int max_pages_per_seq,
+                                  int max_kv_len, int keys_per_split, float softmax_scale,
+                                  const float* sinks, void* out, int out_dtype, float* lse,
+                                  hipStream_t stream);
+
+/*
  * Paged KV append: writes a chunk's new key and value rows into their cache
  * slots (the pool paged at the attention key block: pegainfer issue 1051,
  * "Proposed Plan").

@@ -267,6 +267,18 @@ def test_workspace_size(L):
     assert L.attn_decode_splitk_ex_workspace_size(64, 0, 8, 4, 28672, 1024) == 0
 
 
+def test_decode_noalloc_validation(L):
+    def call(q=FAKE, batch=64, q_len=1, hq=8, hkv=4, max_kv=28672, kps=0, kv=0, d=512):
+        return L.attn_decode_splitk_ex_noalloc(q, FAKE, FAKE, kv, 1.0, 1.0, FAKE, FAKE, batch,
+                                               q_len, hq, hkv, d, 64, 16384, 448, max_kv, kps,
+                                               0.04, None, FAKE, 0, None, None)
+    assert call(q=None) == 1
+    assert call(d=256) == 3
+    # partials past the 64 MiB scratch: refused before any device call
+    assert call(batch=4096, max_kv=28672, kps=64) == 4
+    assert call(q_len=3, hq=8, hkv=4, batch=4096, kps=1024) == 4
+
+
 def test_probe_validation(L):
     assert L.attn_hbm_read_probe(None, 1024, FAKE, None) == 1
     assert L.attn_hbm_read_probe(FAKE, 1000, FAKE, None) == 2
