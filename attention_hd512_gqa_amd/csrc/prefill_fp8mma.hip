@@ -520,11 +520,13 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
             }, ps1, std::integral_constant<int, 4>{});
             // ---- P.V of tile j - 1
             if (j > 0) {
-                if (__builtin_expect(blocks_over(e0, e1), 0)) rebase_blocks(o, m_ref, l_run, e0, e1);
-                const int own = h ? e1 : e0;
-                l_run += __builtin_amdgcn_ldexpf(ps0, e0 - 7) + __builtin_amdgcn_ldexpf(ps1, e1 - 7);
+                // the vote is taken before the wait and acted on after it
+                const bool over = blocks_over(e0, e1);
                 wait_vmcnt<8>();
                 lds_barrier();
+                if (__builtin_expect(over, 0)) rebase_blocks(o, m_ref, l_run, e0, e1);
+                const int own = h ? e1 : e0;
+                l_run += __builtin_amdgcn_ldexpf(ps0, e0 - 7) + __builtin_amdgcn_ldexpf(ps1, e1 - 7);
                 pv_phase((j - 1) & 1, (kE8Hi + own) | ((kE8Lo + own) << 8));
             }
             // ---- block 0's softmax of tile j under Q.K^T of block 1; V(j) refill
@@ -566,11 +568,12 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
                 constexpr int i = 2 * decltype(I)::value;
                 softmax_pair<i, 4 + i / 4>(s1, a.scale_log2, c1, ps1, phi, plo);
             });
-            if (__builtin_expect(blocks_over(e0, e1), 0)) rebase_blocks(o, m_ref, l_run, e0, e1);
-            const int own = h ? e1 : e0;
-            l_run += __builtin_amdgcn_ldexpf(ps0, e0 - 7) + __builtin_amdgcn_ldexpf(ps1, e1 - 7);
+            const bool over = blocks_over(e0, e1);
             wait_vmcnt<0>();
             lds_barrier();
+            if (__builtin_expect(over, 0)) rebase_blocks(o, m_ref, l_run, e0, e1);
+            const int own = h ? e1 : e0;
+            l_run += __builtin_amdgcn_ldexpf(ps0, e0 - 7) + __builtin_amdgcn_ldexpf(ps1, e1 - 7);
             pv_phase((ntiles - 1) & 1, (kE8Hi + own) | ((kE8Lo + own) << 8));
         }
     }

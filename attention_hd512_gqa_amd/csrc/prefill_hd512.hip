@@ -220,62 +220,77 @@ struct SoftmaxCtx {
     float neg_m_ref;  // -m_ref
 };
 
-// Sum of a packed bf16 pair, added to acc in fp32 (one v_dot2 with 1, 1).
+// One softmax element: p = 2^(s * scale - m_ref) (0 for masked keys).  The
+// P^T operand takes p one element later (the previous element's p, `pend`,
+// is packed here), so that no instruction reads an exp2 result right after
+// it is written (that read costs a wait state); softmax_flush finishes the
+// block's last element.  The lane's running sum adds the packed bf16 pairs,
+// i.e. the same rounded weights P.V multiplies (one v_dot2 per pair), so
+// that numerator and denominator agree: a row with one dominant key gets
+// that key's value exactly.  Each pair is summed one pair after it is
+// packed, so that the v_dot2 never waits for the conversion before it.
+// LO (the range's first tile) also packs the residual p - bf16(p) as a
+// second bf16 term and sums it the same way, so that P.V sees p to about 16
+// significant bits: rows whose few keys all lie in that tile would
+// otherwise carry bf16's relative error on each weight.  No running maximum
+// is kept: the block's sum bounds every p of the block, which is all the
+// overflow check needs.  Elements 0-7 go to p0 (lo0), 8-15 to p1 (lo1).
+// The empty asms pin the element to the MFMA step it is issued with (inputs
+// taken and running values produced inside the step): without them, IR
+// passes gather the softmax arithmetic into one cluster after the MFMA chain
+// and the matrix core idles while it runs.  The input side is pinned through
+// `sc`, the wave-uniform scale that the caller threads through its elements
+// as a chain of SGPR values (an asm that "modifies" it costs nothing), so
+// that the score itself is only read: a score still needed afterwards (the
+// overflow path recomputes P from the block's scores) is not copied.
+// add_pair: the sum of a packed bf16 pair, added to acc in fp32 (one v_dot2
+// with 1, 1).
 __device__ __forceinline__ float add_pair(const bf16x8& v, int pair, float acc) {
     const bf16x2 x = {v[2 * pair], v[2 * pair + 1]};
     return __builtin_amdgcn_fdot2_f32_bf16(x, bf16x2{(__bf16)1.f, (__bf16)1.f}, acc, false);
 }
 
-// One softmax element: p = 2^(s * scale - m_ref) (0 for masked keys).  The
-// P^T operand takes p one element later (the previous element's p, `pend`,
-// is packed here), so that no instruction reads an exp2 result right after
-// it is written (that read costs a wait state); softmax_flush finishes the
-// block's last element.  The lane's running sum adds each completed pair as
-// packed, i.e. the same bf16 values P.V multiplies (one v_dot2 per pair), so
-// that numerator and denominator carry the same rounded weights: a row with
-// one dominant key gets that key's value exactly.  LO (the range's first
-// tile) also packs the residual p - bf16(p) as a second bf16 term and adds
-// it to the sum, so that P.V sees p to about 16 significant bits: rows whose
-// few keys all lie in that tile would otherwise carry bf16's relative error
-// on each weight.  No running maximum is kept: the block's sum bounds every
-// p of the block, which is all the overflow check needs.
-// The empty asms pin the element to the MFMA step it is issued with (inputs
-// taken and running values produced inside the step): without them, IR
-// passes gather the softmax arithmetic into one cluster after the MFMA chain
-// and the matrix core idles while it runs.
 template <bool LO = false>
-__device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float s, int i, float& psum,
-                                             float& pend, bf16x8& pf_prev, bf16x8& lo_prev) {
-    asm volatile("" : "+v"(s));
-    const float p = fast_exp2(__builtin_fmaf(s, c.scale_log2, c.neg_m_ref));
+__device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float& sc, float s, int i,
+                                             float& psum, float& pend, bf16x8& p0, bf16x8& p1,
+                                             bf16x8& lo0, bf16x8& lo1) {
+    asm volatile("" : "+s"(sc));
+    const float p = fast_exp2(__builtin_fmaf(s, sc, c.neg_m_ref));
     if (i > 0) {
-        const int e = (i - 1) & 7;
+        const int e = i - 1;                     // the element packed now
+        bf16x8& pv = e < 8 ? p0 : p1;
+        bf16x8& lv = e < 8 ? lo0 : lo1;
         const __bf16 hi = (__bf16)pend;
-        pf_prev[e] = hi;
-        if constexpr (LO) lo_prev[e] = (__bf16)(pend - (float)hi);
-        // a completed pair is packed and summed here, in its step (the
-        // overflow check after the block would otherwise let the packing
-        // sink below it)
+        pv[e & 7] = hi;
+        if constexpr (LO) lv[e & 7] = (__bf16)(pend - (float)hi);
         if (e & 1) {
-            psum = add_pair(pf_prev, e >> 1, psum);
-            if constexpr (LO) psum = add_pair(lo_prev, e >> 1, psum);
-            asm volatile("" : "+v"(pf_prev));
-            if constexpr (LO) asm volatile("" : "+v"(lo_prev));
+            // pair e / 2 is complete: pin its packing here, and sum the one
+            // completed a pair ago
+            asm volatile("" : "+v"(pv));
+            if constexpr (LO) asm volatile("" : "+v"(lv));
+            const int g = (e >> 1) - 1;
+            if (g >= 0) {
+                psum = add_pair(g < 4 ? p0 : p1, g & 3, psum);
+                if constexpr (LO) psum = add_pair(g < 4 ? lo0 : lo1, g & 3, psum);
+            }
         }
     }
     pend = p;
     asm volatile("" : "+v"(psum));
 }
 
+// The block's last element (15), and the sums of its last two pairs.
 template <bool LO = false>
-__device__ __forceinline__ void softmax_flush(float& psum, float pend, bf16x8& pf1, bf16x8& lo1) {
+__device__ __forceinline__ void softmax_flush(float& psum, float pend, bf16x8& p1, bf16x8& lo1) {
     const __bf16 hi = (__bf16)pend;
-    pf1[7] = hi;
+    p1[7] = hi;
     if constexpr (LO) lo1[7] = (__bf16)(pend - (float)hi);
-    psum = add_pair(pf1, 3, psum);
-    if constexpr (LO) psum = add_pair(lo1, 3, psum);
-    asm volatile("" : "+v"(pf1));
+    asm volatile("" : "+v"(p1));
     if constexpr (LO) asm volatile("" : "+v"(lo1));
+    psum = add_pair(p1, 2, psum);
+    if constexpr (LO) psum = add_pair(lo1, 2, psum);
+    psum = add_pair(p1, 3, psum);
+    if constexpr (LO) psum = add_pair(lo1, 3, psum);
 }
 
 // Largest allowed block sum of p before the reference is raised: every p of
@@ -322,9 +337,9 @@ __device__ __forceinline__ void raise_reference(f32x16 (&o)[NDB], bool o_live, c
     c.neg_m_ref = m_ref == -__builtin_inff() ? 0.f : -m_ref;
     psum = 0.f;
     float pend = 0.f;
+    float sc = c.scale_log2;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) softmax_elem<LO>(c, s[i], i, psum, pend, i - 1 < 8 ? p0 : p1,
-                                                  i - 1 < 8 ? lo0 : lo1);
+    for (int i = 0; i < 16; ++i) softmax_elem<LO>(c, sc, s[i], i, psum, pend, p0, p1, lo0, lo1);
     softmax_flush<LO>(psum, pend, p1, lo1);
 }
 
@@ -467,6 +482,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(
     constexpr int kSmEvery = kSteps / 16;
     Raw kbuf[kPrefetchOf<FP8>];
     float pend = 0.f;   // p of the previous softmax element
+    float sc = c.scale_log2;
 #pragma unroll
     for (int j = 0; j < kPrefetchOf<FP8>; ++j) kbuf[j] = kread(j);
     static_for<kSteps>([&](auto KS) {
@@ -490,8 +506,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(
         if constexpr (ks == 0) pre();
         if constexpr (OVERLAP && (ks % kSmEvery == kSmEvery - 1)) {
             constexpr int i = ks / kSmEvery;
-            softmax_elem<LO>(c, sp[i], i, psum, pend, i - 1 < 8 ? pf0 : pf1,
-                             i - 1 < 8 ? lo0 : lo1);
+            softmax_elem<LO>(c, sc, sp[i], i, psum, pend, pf0, pf1, lo0, lo1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -523,6 +538,7 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
     auto vread = [&](int st) -> Raw { return vr.read(sV, 2 * kb + st / kDB, st % kDB); };
     Raw vbuf[kPrefetchOf<FP8>];
     float pend = 0.f;   // p of the previous softmax element
+    float sc = c.scale_log2;
 #pragma unroll
     for (int j = 0; j < kPrefetchOf<FP8>; ++j) vbuf[j] = vread(j);
     static_for<kMfma>([&](auto ST) {
@@ -540,8 +556,7 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
         }
         if constexpr (OVERLAP && (st % kSmEvery == kSmEvery - 1)) {
             constexpr int i = st / kSmEvery;
-            softmax_elem<LO_NEXT>(c, sn[i], i, psum, pend, i - 1 < 8 ? pn0 : pn1,
-                                  i - 1 < 8 ? ln0 : ln1);
+            softmax_elem<LO_NEXT>(c, sc, sn[i], i, psum, pend, pn0, pn1, ln0, ln1);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -865,12 +880,9 @@ void prefill_hd512_kernel(PrefillArgs a) {
             }
         });
         // block 0's P must be representable before its P.V (O is still
-        // unwritten in the first tile)
-        if (__builtin_expect(block_over(psum0), 0)) {
-            float none = 0.f;
-            raise_reference<kFirst>(o, !kFirst, s0, m_ref, c0, l_run, none, psum0, pf[0], pf[1],
-                                    pl[0], pl[1]);
-        }
+        // unwritten in the first tile): the vote is taken here and acted on
+        // after the barrier, whose wait hides its latency
+        const bool over0 = block_over(psum0);
         mfma_vgpr_drain(s1);
         if (mask) mask_block<WINDOW>(s1, key0 + 32 + 4 * h, n_row, lo_row);
         if constexpr (WINDOW) lazy_reference(s1, a.scale_log2, m_ref, c0);
@@ -880,19 +892,25 @@ void prefill_hd512_kernel(PrefillArgs a) {
         hold_before_wait<APPEND>();
         wait_vmcnt<2 * kD>();
         lds_barrier();
+        if (__builtin_expect(over0, 0)) {
+            float none = 0.f;
+            raise_reference<kFirst>(o, !kFirst, s0, m_ref, c0, l_run, none, psum0, pf[0], pf[1],
+                                    pl[0], pl[1]);
+        }
         pv_block<kFirst, true, FP8, D, kFirst, kFirst>(o, 0, pf[0], pf[1], pl[0], pl[1], sV, vr,
                                                        s1, c0, psum1, pf[2], pf[3], pl[2], pl[3],
                                                        dk1, lane_off, lane, wave);
-        // block 1's P likewise; O now holds block 0 of this tile as well
-        if (__builtin_expect(block_over(psum1), 0))
-            raise_reference<kFirst>(o, true, s1, m_ref, c0, l_run, psum0, psum1, pf[2], pf[3],
-                                    pl[2], pl[3]);
+        // block 1's P likewise (O now holds block 0 of this tile as well)
+        const bool over1 = block_over(psum1);
 
         // ---- PV1; V rows 0..31 of tile kt+1 refill
         const HalfDma dv0 = refill(false, page_n, valid_n, kt + 1, 0, true);
         hold_before_wait<APPEND>();
         wait_vmcnt<2 * kD>();
         lds_barrier();
+        if (__builtin_expect(over1, 0))
+            raise_reference<kFirst>(o, true, s1, m_ref, c0, l_run, psum0, psum1, pf[2], pf[3],
+                                    pl[2], pl[3]);
         pv_block<false, false, FP8, D, kFirst, false>(o, 1, pf[2], pf[3], pl[2], pl[3], sV, vr,
                                                       s1, c0, psum1, pf[2], pf[3], pl[2], pl[3],
                                                       dv0, lane_off, lane, wave);
