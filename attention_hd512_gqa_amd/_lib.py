@@ -50,6 +50,11 @@ def lib() -> ctypes.CDLL:
         L.attn_prefill_hd512_append.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
                                                 I, I, I, F, P, P, I, P, P]
         L.attn_prefill_hd512_append.restype = I
+        L.attn_prefill_hd512_persistent_workspace_size.argtypes = []
+        L.attn_prefill_hd512_persistent_workspace_size.restype = SZ
+        L.attn_prefill_hd512_persistent.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I,
+                                                    I, I, I, I, F, P, P, SZ, P, I, P, P]
+        L.attn_prefill_hd512_persistent.restype = I
         L.attn_prefill_swa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, F,
                                        P, I, P]
         L.attn_prefill_swa.restype = I
@@ -196,6 +201,38 @@ def prefill_append(q, k_new, v_new, k_pages, v_pages, page_table, cu_seqlens_q, 
         _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
         _opt(lse, "lse", torch.float32, int(total_q) * hq), _stream(stream))
     _check(code, "attn_prefill_hd512_append")
+
+
+def prefill_persistent_workspace_size() -> int:
+    return int(lib().attn_prefill_hd512_persistent_workspace_size())
+
+
+def prefill_persistent(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out,
+                       workspace, *, total_q: int, max_q_len: int, softmax_scale: float,
+                       kv_dtype: str = "bf16", k_scale: float = 1.0, v_scale: float = 1.0,
+                       sinks=None, lse=None, stream=None) -> None:
+    """prefill() with persistent heaviest-first scheduling
+    (attn_prefill_hd512_persistent): one workgroup per compute unit taking
+    work units from a counter in `workspace` (a device tensor of at least
+    prefill_persistent_workspace_size() bytes).  Bitwise the same results."""
+    num_pages, hkv, page, d = k_pages.shape
+    hq = q.shape[1]
+    batch = kv_lens.shape[0]
+    if kv_dtype not in _KV_CODES:
+        raise AttnError(f"unsupported kv_dtype {kv_dtype!r}")
+    kvt = torch.bfloat16 if kv_dtype == "bf16" else torch.uint8
+    code = lib().attn_prefill_hd512_persistent(
+        _dev(q, "q", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
+        _dev(v_pages, "v_pages", kvt), _KV_CODES[kv_dtype], float(k_scale), float(v_scale),
+        _dev(page_table, "page_table", torch.int32),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(q_start, "q_start", torch.int32),
+        _dev(kv_lens, "kv_lens", torch.int32), int(batch), int(total_q), int(max_q_len),
+        int(hq), int(hkv), int(d), int(page), int(num_pages), int(page_table.shape[1]),
+        float(softmax_scale), _opt(sinks, "sinks", torch.float32, hq), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(),
+        _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
+        _opt(lse, "lse", torch.float32, int(total_q) * hq), _stream(stream))
+    _check(code, "attn_prefill_hd512_persistent")
 
 
 def prefill_swa(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out, *,

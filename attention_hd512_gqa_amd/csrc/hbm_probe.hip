@@ -5,10 +5,12 @@
 // the HBM rate.  Each workgroup folds what it read into one word of `sink`
 // so the loads cannot be dropped.
 //
-// Clock stamps: each workgroup's first lane records its XCD and two
-// counters, s_memtime (counts shader-clock cycles, so its rate follows the
-// clock) and s_memrealtime (a constant 100 MHz).  Two stamp launches around
-// a timed region give each XCD's mean shader clock over it.
+// Clock stamps: each workgroup's first lane records where it runs (XCD and
+// hardware id) and two counters, s_memtime (counts shader-clock cycles, so
+// its rate follows the clock; not synchronised between compute units) and
+// s_memrealtime (a constant 100 MHz).  Two stamp launches around a timed
+// region give, for every compute unit that holds a stamp of both, its mean
+// shader clock over the region.
 #include "device_common.h"
 #include "attn_host.h"
 
@@ -36,15 +38,18 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_kernel(const u32x4* bu
     if (threadIdx.x == 0) sink[blockIdx.x] = w;
 }
 
-// One 64-lane workgroup per slot: lane 0 writes {XCD id, s_memtime,
-// s_memrealtime} (three 64-bit words) to slot blockIdx.x.
+// One 64-lane workgroup per slot: lane 0 writes {XCD id << 32 | HW_ID,
+// s_memtime, s_memrealtime} (three 64-bit words) to slot blockIdx.x.
 __global__ __launch_bounds__(64) void clock_stamp_kernel(unsigned long long* out) {
-    // HW_REG_XCC_ID (hardware register 20), bits 0..3: the XCD this wave runs on
+    // HW_REG_XCC_ID (hardware register 20), bits 0..3: the XCD this wave runs
+    // on; HW_REG_HW_ID (4): its compute unit (bits 8..11), shader array (12)
+    // and shader engine (13..15), among other fields
     const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);
+    const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
     const unsigned long long t = __builtin_amdgcn_s_memtime();
     const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
     if (threadIdx.x == 0) {
-        out[3 * blockIdx.x] = xcc;
+        out[3 * blockIdx.x] = ((unsigned long long)(xcc & 15) << 32) | hw;
         out[3 * blockIdx.x + 1] = t;
         out[3 * blockIdx.x + 2] = rt;
     }

@@ -95,6 +95,9 @@ struct PrefillArgs {
     // fused append: the chunk's new K and V rows, bf16 [total_q][hkv][512]
     const char* k_new;
     const char* v_new;
+    // persistent launch: the unit counter (workspace) and the unit count
+    int* unit_counter;
+    int total_units;
 };
 
 // The row a prefill workgroup's lane holds, for prefill_epilogue.

@@ -59,6 +59,11 @@ namespace {
 
 constexpr int kRowsPerWaveLoad = kPage / kWaves;  // tile rows each wave moves
 constexpr int kPrefetch = 4;  // LDS operand reads in flight ahead of their MFMA
+constexpr int kXcds = 8;            // XCDs of a gfx950 part (one work queue each)
+constexpr int kCounterStride = 32;  // ints between queue counters (own 128-byte line)
+// Row blocks whose first row sees at most this many keys get P in two bf16
+// terms in their first tile
+constexpr int kLoKeys = 64;
 // FP8 operands are widened in registers; one fewer read in flight keeps the
 // FP8 kernel inside the 256 VGPRs
 template <bool FP8>
@@ -218,6 +223,7 @@ __device__ __forceinline__ bf16x8 operand(const v2i32& x) {
 struct SoftmaxCtx {
     float scale_log2;
     float neg_m_ref;  // -m_ref
+    float lo_f;       // 1 when P's second bf16 term is used, else 0 (zero terms)
 };
 
 // One softmax element: p = 2^(s * scale - m_ref) (0 for masked keys).  The
@@ -262,7 +268,7 @@ __device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float& sc, flo
         bf16x8& lv = e < 8 ? lo0 : lo1;
         const __bf16 hi = (__bf16)pend;
         pv[e & 7] = hi;
-        if constexpr (LO) lv[e & 7] = (__bf16)(pend - (float)hi);
+        if constexpr (LO) lv[e & 7] = (__bf16)((pend - (float)hi) * c.lo_f);
         if (e & 1) {
             // pair e / 2 is complete: pin its packing here, and sum the one
             // completed a pair ago
@@ -281,10 +287,11 @@ __device__ __forceinline__ void softmax_elem(const SoftmaxCtx& c, float& sc, flo
 
 // The block's last element (15), and the sums of its last two pairs.
 template <bool LO = false>
-__device__ __forceinline__ void softmax_flush(float& psum, float pend, bf16x8& p1, bf16x8& lo1) {
+__device__ __forceinline__ void softmax_flush(const SoftmaxCtx& c, float& psum, float pend,
+                                              bf16x8& p1, bf16x8& lo1) {
     const __bf16 hi = (__bf16)pend;
     p1[7] = hi;
-    if constexpr (LO) lo1[7] = (__bf16)(pend - (float)hi);
+    if constexpr (LO) lo1[7] = (__bf16)((pend - (float)hi) * c.lo_f);
     asm volatile("" : "+v"(p1));
     if constexpr (LO) asm volatile("" : "+v"(lo1));
     psum = add_pair(p1, 2, psum);
@@ -340,7 +347,7 @@ __device__ __forceinline__ void raise_reference(f32x16 (&o)[NDB], bool o_live, c
     float sc = c.scale_log2;
 #pragma unroll
     for (int i = 0; i < 16; ++i) softmax_elem<LO>(c, sc, s[i], i, psum, pend, p0, p1, lo0, lo1);
-    softmax_flush<LO>(psum, pend, p1, lo1);
+    softmax_flush<LO>(c, psum, pend, p1, lo1);
 }
 
 // True when some lane of the wave must raise its reference before the
@@ -510,17 +517,18 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(
         }
         __builtin_amdgcn_sched_barrier(0);
     });
-    if constexpr (OVERLAP) softmax_flush<LO>(psum, pend, pf1, lo1);
+    if constexpr (OVERLAP) softmax_flush<LO>(c, psum, pend, pf1, lo1);
 }
 
 // P.V of one 32-key block (k-steps c = 2 kb, 2 kb + 1 of the tile, all D / 32
 // dim blocks).  FIRST: the tile's first k-step starts O from zero (inline
 // c = 0), so O is only ever written by MFMAs.  LO: P carries a second bf16
 // term (p0lo, p1lo; the range's first tile), multiplied into O by a second
-// MFMA on the same V operand; LO_NEXT: the overlapped softmax of the next
-// block produces its second term too.  When OVERLAP, the 16 softmax
-// elements of the next block's scores `sn` are spread evenly over the MFMAs;
-// the half-tile refill `dma` issues one row load after every fourth MFMA.
+// MFMA on the same V operand when lo_on (wave-uniform); LO_NEXT: the
+// overlapped softmax of the next block produces its second term too.  When
+// OVERLAP, the 16 softmax elements of the next block's scores `sn` are
+// spread evenly over the MFMAs; the half-tile refill `dma` issues one row
+// load after every fourth MFMA.
 template <bool FIRST, bool OVERLAP, bool FP8, int D, bool LO = false, bool LO_NEXT = false,
           typename VR>
 __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], int kb,
@@ -529,7 +537,8 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
                                          const ATTN_LDS char* sV, const VR& vr, const f32x16& sn,
                                          const SoftmaxCtx& c, float& psum,
                                          bf16x8& pn0, bf16x8& pn1, bf16x8& ln0, bf16x8& ln1,
-                                         const HalfDma& dma, int lane_off, int lane, int wave) {
+                                         const HalfDma& dma, int lane_off, int lane, int wave,
+                                         bool lo_on = false) {
     constexpr int kDB = Kv<FP8, D>::kDimBlocks;
     constexpr int kMfma = 2 * kDB;
     constexpr int kDmaEvery = kMfma / Kv<FP8, D>::kDmaPerHalf;
@@ -550,7 +559,9 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
             o[db] = mfma32x32x16(cur, p0, f32x16{});
         else
             o[db] = mfma32x32x16(cur, st < kDB ? p0 : p1, o[db]);
-        if constexpr (LO) o[db] = mfma32x32x16(cur, st < kDB ? p0lo : p1lo, o[db]);
+        if constexpr (LO) {
+            if (lo_on) o[db] = mfma32x32x16(cur, st < kDB ? p0lo : p1lo, o[db]);
+        }
         if constexpr (st % kDmaEvery == 0) {
             if (dma.on) half_dma_row<FP8, D, st / kDmaEvery>(dma, lane_off, lane, wave);
         }
@@ -560,16 +571,26 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
         }
         __builtin_amdgcn_sched_barrier(0);
     });
-    if constexpr (OVERLAP) softmax_flush<LO_NEXT>(psum, pend, pn1, ln1);
+    if constexpr (OVERLAP) softmax_flush<LO_NEXT>(c, psum, pend, pn1, ln1);
 }
 
+// PERSIST: the grid is one workgroup per compute unit, and each workgroup
+// takes work units, heaviest first, from counters at a.unit_counter (zeroed
+// by prefill_counter_reset on the same stream); otherwise workgroup i does
+// unit i.  Units are dealt to the XCDs as the one-per-unit launch deals its
+// workgroups (unit u to XCD u % 8, which keeps one KV head's K/V per XCD's
+// L2 when the KV head count divides 8): a workgroup drains the queue of the
+// XCD it runs on (units x, x + 8, ...), then helps with the other queues, so
+// every unit is done whatever the dispatcher's placement.
 template <bool OUT_FP32, bool FP8, bool SPLIT, int D = kHeadDim, bool WINDOW = false,
-          bool APPEND = false>
+          bool APPEND = false, bool PERSIST = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_hd512_kernel(PrefillArgs a) {
     static_assert(!(SPLIT && (WINDOW || D != kHeadDim)), "split-K: head dim 512, no window");
     static_assert(!APPEND || (!FP8 && !SPLIT && !WINDOW && D == kHeadDim),
                   "fused append: bf16 pool, head dim 512, single pass");
+    static_assert(!PERSIST || (!SPLIT && !WINDOW && !APPEND && D == kHeadDim),
+                  "persistent: single pass, head dim 512");
     constexpr int kTileB = Kv<FP8, D>::kTileB;
     constexpr int kD = Kv<FP8, D>::kDmaPerHalf;   // loads per wave per half refill
     constexpr int kSteps = Kv<FP8, D>::kSteps;
@@ -579,16 +600,24 @@ void prefill_hd512_kernel(PrefillArgs a) {
     ATTN_LDS char* sK = (ATTN_LDS char*)smem;
     ATTN_LDS char* sV = sK + kTileB;
 
-    const int lane = threadIdx.x & 63;
+    const int lane0 = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+    // One work unit; a unit with nothing to do returns at once.  at_end()
+    // runs once the unit's key loop is done, before its epilogue.
+    auto run_unit = [&](const int unit, auto&& at_end) {
+    // The lane's offsets are derived from an opaque copy of its index, so
+    // that a persistent workgroup recomputes them per unit instead of
+    // keeping them live across its epilogues and prologues.
+    int lane = lane0;
+    if constexpr (PERSIST) asm volatile("" : "+v"(lane));
     // ---- work unit: heaviest query tiles first; KV head fastest so that
     // consecutive workgroups (spread round-robin over the XCDs) share a KV
     // head per XCD whenever the KV head count divides 8.
     const int per_rank = a.batch * a.hkv;
     const int per_split = a.wgs_per_seq * per_rank;
-    const int split = SPLIT ? blockIdx.x / per_split : 0;
-    const int in_split = blockIdx.x - split * per_split;
+    const int split = SPLIT ? unit / per_split : 0;
+    const int in_split = unit - split * per_split;
     const int rank = in_split / per_rank;
     const int rem = in_split - rank * per_rank;
     const int kvh = rem % a.hkv;
@@ -804,6 +833,8 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // with no records lands zeros, fetching nothing) into halves nothing reads
     // again, so that every refill site is unconditional and every count the
     // same; the loop's end waits for them.
+    // P in two bf16 terms in the first tile (see the tile below)
+    const bool lo_on = n_min - max(kt_lo * kPage, lo_first) <= kLoKeys;
     int page_cur = ntiles > kt_lo ? page_of(kt_lo) : 0;              // page of tile kt
     int page_nx = kt_lo + 1 < ntiles ? page_of(kt_lo + 1) : page_cur;  // of tile kt + 1
     if (ntiles > kt_lo) {
@@ -814,10 +845,14 @@ void prefill_hd512_kernel(PrefillArgs a) {
         half_dma_all<FP8, D>(refill(false, page0, v0, kt_lo, 0, true), lane_off, lane, wave);
     }
     // One 64-key tile.  kFirst (the range's first tile, peeled off the loop):
-    // P carries its second bf16 term, the reference maximum is taken, and
-    // P.V starts O from zero.
+    // the reference maximum is taken, P.V starts O from zero, and P can carry
+    // its second bf16 term, which it does when the block's first row sees at
+    // most kLoKeys keys of the range (lo_on; bf16 P's relative error per
+    // weight only shows in rows with few keys): otherwise the second terms
+    // are zero and their MFMAs are skipped.
     auto tile = [&](auto first_tag, int kt) {
         constexpr bool kFirst = decltype(first_tag)::value;
+        constexpr bool kLo = kFirst;
         const bool more = kt + 1 < ntiles;
         const int key0 = kt * kPage;
         const int valid = min(L - key0, kPage);
@@ -833,10 +868,11 @@ void prefill_hd512_kernel(PrefillArgs a) {
         const int page_nn_raw = sPage[min(t2 - kt_lo, kPagesInLds - 1)];
         // the tile crosses a row's causal limit (or a row's window start)
         const bool mask = key0 + kPage > n_min || (WINDOW && key0 < lo_last);
-        SoftmaxCtx c0{a.scale_log2, WINDOW && m_ref == -__builtin_inff() ? 0.f : -m_ref};
+        SoftmaxCtx c0{a.scale_log2, WINDOW && m_ref == -__builtin_inff() ? 0.f : -m_ref,
+                      lo_on ? 1.f : 0.f};
         float psum0 = 0.f, psum1 = 0.f;   // the lane's sums of p of blocks 0 and 1
         bf16x8 pf[4];
-        bf16x8 pl[4];                     // second terms (kFirst only)
+        bf16x8 pl[4];                     // second terms (kLo only)
         f32x16 s0, s1;
 
         // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill
@@ -860,7 +896,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
         hold_before_wait<APPEND>();
         wait_vmcnt<2 * kD>();
         lds_barrier();
-        qk_block<true, FP8, D, kFirst>(s1, 1, qf, sK, koff, s0, c0, psum0, pf[0], pf[1], pl[0],
+        qk_block<true, FP8, D, kLo>(s1, 1, qf, sK, koff, s0, c0, psum0, pf[0], pf[1], pl[0],
                                        pl[1], dk0, lane_off, lane, wave, [&] {
             mfma_vgpr_drain(s0);
             if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
@@ -894,12 +930,12 @@ void prefill_hd512_kernel(PrefillArgs a) {
         lds_barrier();
         if (__builtin_expect(over0, 0)) {
             float none = 0.f;
-            raise_reference<kFirst>(o, !kFirst, s0, m_ref, c0, l_run, none, psum0, pf[0], pf[1],
+            raise_reference<kLo>(o, !kFirst, s0, m_ref, c0, l_run, none, psum0, pf[0], pf[1],
                                     pl[0], pl[1]);
         }
-        pv_block<kFirst, true, FP8, D, kFirst, kFirst>(o, 0, pf[0], pf[1], pl[0], pl[1], sV, vr,
+        pv_block<kFirst, true, FP8, D, kLo, kLo>(o, 0, pf[0], pf[1], pl[0], pl[1], sV, vr,
                                                        s1, c0, psum1, pf[2], pf[3], pl[2], pl[3],
-                                                       dk1, lane_off, lane, wave);
+                                                       dk1, lane_off, lane, wave, lo_on);
         // block 1's P likewise (O now holds block 0 of this tile as well)
         const bool over1 = block_over(psum1);
 
@@ -909,11 +945,11 @@ void prefill_hd512_kernel(PrefillArgs a) {
         wait_vmcnt<2 * kD>();
         lds_barrier();
         if (__builtin_expect(over1, 0))
-            raise_reference<kFirst>(o, true, s1, m_ref, c0, l_run, psum0, psum1, pf[2], pf[3],
+            raise_reference<kLo>(o, true, s1, m_ref, c0, l_run, psum0, psum1, pf[2], pf[3],
                                     pl[2], pl[3]);
-        pv_block<false, false, FP8, D, kFirst, false>(o, 1, pf[2], pf[3], pl[2], pl[3], sV, vr,
+        pv_block<false, false, FP8, D, kLo, false>(o, 1, pf[2], pf[3], pl[2], pl[3], sV, vr,
                                                       s1, c0, psum1, pf[2], pf[3], pl[2], pl[3],
-                                                      dv0, lane_off, lane, wave);
+                                                      dv0, lane_off, lane, wave, lo_on);
         l_run += psum0 + psum1;
     };
     if (ntiles > kt_lo) {
@@ -922,12 +958,65 @@ void prefill_hd512_kernel(PrefillArgs a) {
     }
     wait_vmcnt<0>();   // the empty refills past the last tile
 
+    at_end();
+
     // ---- epilogue: outputs (or split-K partials) of the workgroup's rows
     constexpr bool kStageOut = !OUT_FP32 && 2 * kTileB >= kWaves * 32 * D * 2;
     prefill_epilogue<OUT_FP32, SPLIT, D, kStageOut, FP8>(
         a, o, l_run, m_ref, ntiles > kt_lo,
         RowSlot{q0, q0 + t, head, t0, t_last, kvh, split, valid}, (ATTN_LDS char*)smem, lane,
         wave);
+    };
+
+    if constexpr (PERSIST) {
+        // HW_REG_XCC_ID (hardware register 20), bits 0..3: this XCD
+        const int xcd = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);
+        // Thread 0 takes the next unit: from this XCD's queue, then from the
+        // others in turn once a queue's counter has passed the last unit;
+        // a.total_units when all are drained.
+        int qi = 0;
+        auto take = [&]() -> int {
+            while (qi < kXcds) {
+                const int queue = (xcd + qi) & (kXcds - 1);
+                const int u =
+                    queue + kXcds * atomicAdd(a.unit_counter + kCounterStride * queue, 1);
+                if (u < a.total_units) return u;
+                ++qi;
+            }
+            return a.total_units;
+        };
+        // The next unit is taken when the current one's key loop is done, so
+        // that the atomic's round trip overlaps the epilogue (taken earlier,
+        // heavy units would no longer pair with light ones).  Every wave
+        // reads the index from LDS after the barrier that ends the unit, and
+        // all leave the loop together.
+        __shared__ int sUnit;
+        if (threadIdx.x == 0) sUnit = take();
+        __syncthreads();
+        for (;;) {
+            const int unit = sUnit;
+            if (unit >= a.total_units) break;
+            bool taken = false;
+            run_unit(unit, [&] {
+                if (threadIdx.x == 0) sUnit = take();   // every wave has read sUnit by now
+                taken = true;
+            });
+            if (!taken && threadIdx.x == 0) sUnit = take();   // a unit with no work
+            // the next unit rewrites the page ids and tile buffers only after
+            // every wave is done with them (the unit's loads have all landed;
+            // its output stores may still be in flight: they only lengthen the
+            // next unit's counted waits, which then cover older operations)
+            __syncthreads();
+        }
+    } else {
+        run_unit(blockIdx.x, [] {});
+    }
+}
+
+// Zeroes the persistent prefill's unit counters (a kernel, not a memset, so
+// that the pair can also be recorded into a graph).
+__global__ void prefill_counter_reset(int* counter) {
+    if (threadIdx.x < kXcds) counter[kCounterStride * threadIdx.x] = 0;
 }
 
 
@@ -1009,6 +1098,8 @@ namespace {
 // partial traffic, the merge and each range's pipeline start; ranges keep
 // at least kMinSplitTiles tiles.  One range means the single-pass kernel.
 constexpr int kCus = 256;               // compute units of a gfx950 part
+// the persistent launch's queue counters, one 128-byte line each
+constexpr size_t kPersistWorkspace = sizeof(int) * kCounterStride * kXcds;
 constexpr int kMinSplitTiles = 8;
 constexpr int kMaxAutoSplits = 64;
 constexpr double kSplitCost = 0.02;
@@ -1061,11 +1152,13 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
                    const float* sinks, void* out, int out_dtype, float* lse,
                    bool splitk, int max_kv_len, int keys_per_split, void* workspace,
                    size_t workspace_bytes, bool swa, int window, int ring_pages,
-                   const void* k_new, const void* v_new, bool fp8_mma, hipStream_t stream) {
+                   const void* k_new, const void* v_new, bool fp8_mma, hipStream_t stream,
+                   bool persist = false) {
     // the sliding-window entry is bf16 and single-pass; so is the fused append
     // (given both new-row buffers or neither), at head dim 512 with no window;
     // the FP8-MFMA form is FP8, single-pass, at head dim 512
     const bool append = k_new || v_new;
+    if (persist && (splitk || swa || append || fp8_mma)) return ATTN_ERR_UNSUPPORTED;
     if (fp8_mma && (!fp8 || swa || append)) return ATTN_ERR_UNSUPPORTED;
     if (swa && (fp8 || splitk)) return ATTN_ERR_UNSUPPORTED;
     if (append && (!k_new || !v_new)) return ATTN_ERR_NULL;
@@ -1124,6 +1217,8 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     a.ring_pages = ring_pages;
     a.k_new = (const char*)k_new;
     a.v_new = (const char*)v_new;
+    a.unit_counter = nullptr;
+    a.total_units = 0;
     // the new-row buffers are addressed by 32-bit buffer offsets
     if (append && (long long)total_q * num_kv_heads * kRowBytes > 0xffffffffLL)
         return ATTN_ERR_SHAPE;
@@ -1163,6 +1258,39 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     const dim3 gd((unsigned)grid);
     const bool f32 = out_dtype == ATTN_FP32;
+    if (persist) {
+        if (!workspace) return ATTN_ERR_NULL;
+        if (workspace_bytes < kPersistWorkspace) return ATTN_ERR_WORKSPACE;
+        // one workgroup per compute unit of the stream's device
+        int dev = -1, cus = 0;
+        if (stream) {
+            hipDevice_t d;
+            if (hipStreamGetDevice(stream, &d) != hipSuccess) return ATTN_ERR_HIP;
+            dev = (int)d;
+        } else if (hipGetDevice(&dev) != hipSuccess) {
+            return ATTN_ERR_HIP;
+        }
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            return ATTN_ERR_HIP;
+        a.unit_counter = (int*)workspace;
+        a.total_units = (int)grid;
+        const dim3 pg((unsigned)(grid < cus ? grid : cus));
+        hipLaunchKernelGGL(prefill_counter_reset, dim3(1), dim3(64), 0, stream, a.unit_counter);
+        if (fp8 && f32)
+            hipLaunchKernelGGL((prefill_hd512_kernel<true, true, false, kHeadDim, false, false, true>),
+                               pg, dim3(kThreads), 0, stream, a);
+        else if (fp8)
+            hipLaunchKernelGGL((prefill_hd512_kernel<false, true, false, kHeadDim, false, false, true>),
+                               pg, dim3(kThreads), 0, stream, a);
+        else if (f32)
+            hipLaunchKernelGGL((prefill_hd512_kernel<true, false, false, kHeadDim, false, false, true>),
+                               pg, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_hd512_kernel<false, false, false, kHeadDim, false, false, true>),
+                               pg, dim3(kThreads), 0, stream, a);
+        return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    }
     if (fp8_mma) {
         launch_prefill_fp8mma(a, f32, false, (unsigned)grid, stream);
     } else if (append) {
@@ -1302,6 +1430,32 @@ extern "C" int attn_prefill_hd512_append(const void* q, const void* k_new, const
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
                                 softmax_scale, sinks, out, out_dtype, lse, false, 0, 0, nullptr,
                                 0, false, 0, 0, k_new, v_new, false, stream);
+}
+
+extern "C" size_t attn_prefill_hd512_persistent_workspace_size(void) {
+    return attn::kPersistWorkspace;
+}
+
+extern "C" int attn_prefill_hd512_persistent(const void* q, const void* k_pages,
+                                             const void* v_pages, int kv_dtype, float k_scale,
+                                             float v_scale, const int32_t* page_table,
+                                             const int32_t* cu_seqlens_q,
+                                             const int32_t* q_start_pos, const int32_t* kv_lens,
+                                             int batch, int total_q, int max_q_len,
+                                             int num_q_heads, int num_kv_heads, int head_dim,
+                                             int page_size, int num_pages, int max_pages_per_seq,
+                                             float softmax_scale, const float* sinks,
+                                             void* workspace, size_t workspace_bytes, void* out,
+                                             int out_dtype, float* lse, hipStream_t stream) {
+    using namespace attn;
+    if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+    const bool fp8 = kv_dtype == ATTN_FP8_E4M3;
+    return prefill_launch(q, k_pages, v_pages, fp8, fp8 ? k_scale : 1.f, fp8 ? v_scale : 1.f,
+                          page_table, cu_seqlens_q, q_start_pos, kv_lens, batch, total_q,
+                          max_q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                          max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse, false, 0,
+                          0, workspace, workspace_bytes, false, 0, 0, nullptr, nullptr, false,
+                          stream, true);
 }
 
 extern "C" int attn_prefill_hd512_e4m3_mma(const void* q, const void* k_pages,

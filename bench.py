@@ -14,6 +14,13 @@ live KV bytes against an HBM read probe taken in the same process; the other
 prefill workloads; and the CPU oracle timed on a bounded sample of the
 headline workload (a baseline, not a target).
 
+The headline is timed as the contract asks: K launches after W warmup
+launches, events on the launch stream, cut into 7 windows (median, min, max
+reported beside the mean) with clock stamps around them.  Every other figure
+is the median of 7 replays of a HIP graph holding 8-100 calls, so that the
+host's launch overhead (about 0.17 ms per call from Python) does not enter
+the shorter launches.
+
 FLOP convention: 4 * head_dim per visible (query, key) pair and head.
 """
 from __future__ import annotations
@@ -61,27 +68,36 @@ def recorded_traffic():
 
 
 def clock_summary(stamps):
-    """Mean shader clock of each XCD between two clock-stamp launches.
+    """Mean shader clock over the region between two clock-stamp launches.
 
-    stamps[0] and stamps[1] hold, per workgroup, (XCD id, shader-cycle
-    counter, 100 MHz counter).  For each XCD the earliest stamp of each
-    launch is taken; cycles over ticks, times 100 MHz, is its mean clock.
+    stamps[0] and stamps[1] hold, per workgroup, (where: XCD << 32 | HW_ID,
+    shader-cycle counter, 100 MHz counter).  The cycle counter is not
+    synchronised between compute units, so stamps are paired by compute unit
+    (XCD, shader engine, shader array, CU): cycles over ticks, times 100 MHz,
+    is that unit's mean clock; the median, min and max over the units that
+    hold a stamp of both launches are reported.
     """
-    per = {}
-    for x in sorted(set(int(v) for v in stamps[0][:, 0]) & set(int(v) for v in stamps[1][:, 0])):
-        a = stamps[0][stamps[0][:, 0] == x]
-        b = stamps[1][stamps[1][:, 0] == x]
-        a = a[a[:, 2].argmin()]
-        b = b[b[:, 2].argmin()]
-        ticks = int(b[2]) - int(a[2])
-        if ticks > 0:
-            per[x] = (int(b[1]) - int(a[1])) / ticks * 100.0
-    if not per:
+    def where(w):
+        w = int(w)
+        return (w >> 32, (w >> 8) & 0xFF)   # XCD; CU | SH << 4 | SE << 5
+    first = {}
+    for row in stamps[0]:
+        first.setdefault(where(row[0]), row)
+    clocks = []
+    for row in stamps[1]:
+        k = where(row[0])
+        if k in first:
+            a = first.pop(k)
+            ticks = int(row[2]) - int(a[2])
+            if ticks > 0:
+                clocks.append((int(row[1]) - int(a[1])) / ticks * 100.0)
+    if not clocks:
         return None
-    vals = list(per.values())
-    return {"mean_mhz": sum(vals) / len(vals), "min_mhz": min(vals), "max_mhz": max(vals),
-            "xcds": len(vals),
-            "how": "s_memtime cycles / s_memrealtime 100 MHz ticks per XCD across the timed steps"}
+    clocks.sort()
+    return {"median_mhz": clocks[len(clocks) // 2], "min_mhz": clocks[0], "max_mhz": clocks[-1],
+            "compute_units": len(clocks),
+            "how": "s_memtime cycles / s_memrealtime 100 MHz ticks per compute unit across "
+                   "the timed steps"}
 
 
 def log(msg: str) -> None:
@@ -133,6 +149,33 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
+
+    def graph_time(fn, calls=20, windows=7):
+        """ms per call of fn: `calls` calls captured in one HIP graph (so the
+        host's launch overhead is not measured), replayed `windows` times;
+        median, min and max over the windows.  fn launches on torch's current
+        stream, which is the capture stream while the graph is recorded."""
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(windows):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / calls)
+        del g
+        ts.sort()
+        return {"ms": ts[len(ts) // 2], "ms_min": ts[0], "ms_max": ts[-1],
+                "how": f"median of {windows} replays of a graph of {calls} calls"}
 
     # ---- same-process bf16 GEMM roofline ---------------------------------
     def gemm_rate():
@@ -206,67 +249,95 @@ def main():
     clock = clock_summary(stamps.cpu().numpy())
     log(f"prefill chunk 8192@8192: {ms_step:.3f} ms/launch, {tflops:.1f} TFLOP/s; windows "
         f"{win_ms[0]:.3f}/{win_ms[len(win_ms) // 2]:.3f}/{win_ms[-1]:.3f} ms (min/median/max); "
-        f"mean shader clock {clock['mean_mhz'] if clock else float('nan'):.0f} MHz")
+        f"shader clock {clock['median_mhz'] if clock else float('nan'):.0f} MHz (median over CUs)")
     assert torch.isfinite(out.float()).all()
 
     extra = {}
     if not args.no_extra:
+        def rate(flop, t):
+            return dict(t, tflops=flop / (t["ms"] * 1e-3) / 1e12)
+
+        def pf(c, l, o, **kw):
+            # a prefill launch on torch's current stream (graph capture)
+            return lambda: A.prefill(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q,
+                                     l.q_start, l.kv_len, o, total_q=l.total_q,
+                                     max_q_len=l.max_q_len, softmax_scale=c.softmax_scale,
+                                     kv_dtype=c.kv_dtype, k_scale=c.k_scale, v_scale=c.v_scale,
+                                     **kw)
+        wsp = torch.empty(A.prefill_persistent_workspace_size() // 4, dtype=torch.int32,
+                          device="cuda")
+
+        def pers(c, l, o):
+            return lambda: A.prefill_persistent(l.q, c.k_pool, c.v_pool, c.page_table,
+                                                l.cu_seqlens_q, l.q_start, l.kv_len, o, wsp,
+                                                total_q=l.total_q, max_q_len=l.max_q_len,
+                                                softmax_scale=c.softmax_scale,
+                                                kv_dtype=c.kv_dtype, k_scale=c.k_scale,
+                                                v_scale=c.v_scale)
+        # the headline chunk, graph-timed too, next to the timing above
+        extra["chunk_prefill_8192_at_8192_graph"] = rate(flops, graph_time(pf(case, lc, out), 8))
+        extra["chunk_prefill_8192_at_8192_persistent"] = rate(
+            flops, graph_time(pers(case, lc, out), 8))
+        # 2048 rows at offset 0: one-workgroup-per-unit and persistent launches
         c2 = W.chunk_prefill_2k(device="cuda")
         l2 = c2.launches[0]
         o2 = torch.empty((l2.total_q, c2.num_q_heads, W.HEAD_DIM), dtype=torch.bfloat16,
                          device="cuda")
-        ms2 = timed(lambda: prefill_step(c2, l2, o2), 20, 5)
         f2 = W.prefill_flops(l2.q_lens, l2.q_starts, l2.kv_lens, c2.num_q_heads)
-        extra["chunk_prefill_2048"] = {"ms_per_launch": ms2, "tflops": f2 / (ms2 * 1e-3) / 1e12}
+        extra["chunk_prefill_2048"] = rate(f2, graph_time(pf(c2, l2, o2)))
+        extra["chunk_prefill_2048_persistent"] = rate(f2, graph_time(pers(c2, l2, o2)))
         del c2, o2
+        # the 32K long-MQA prompt as eight chunks: each chunk, and the prompt
         c4 = W.long_mqa_32k(device="cuda")
         o4 = torch.empty((4096, c4.num_q_heads, W.HEAD_DIM), dtype=torch.float32, device="cuda")
-
-        def long_prompt():
-            for l4 in c4.launches:
-                prefill_step(c4, l4, o4)
-        ms4 = timed(long_prompt, 3, 1)
-        f4 = sum(W.prefill_flops(l.q_lens, l.q_starts, l.kv_lens, c4.num_q_heads)
-                 for l in c4.launches)
-        per_chunk = []
+        per_chunk, per_chunk_p, total, total_p, f4 = [], [], 0.0, 0.0, 0
         for l4 in c4.launches:
-            msc = timed(lambda l4=l4: prefill_step(c4, l4, o4), 10, 2)
             fc = W.prefill_flops(l4.q_lens, l4.q_starts, l4.kv_lens, c4.num_q_heads)
-            per_chunk.append({"ms": msc, "tflops": fc / (msc * 1e-3) / 1e12})
-        extra["long_mqa_32k_8x4096"] = {"ms_per_prompt": ms4, "tflops": f4 / (ms4 * 1e-3) / 1e12,
+            t = rate(fc, graph_time(pf(c4, l4, o4), 8))
+            tp = rate(fc, graph_time(pers(c4, l4, o4), 8))
+            per_chunk.append({"ms": t["ms"], "tflops": t["tflops"]})
+            per_chunk_p.append({"ms": tp["ms"], "tflops": tp["tflops"]})
+            total += t["ms"]
+            total_p += tp["ms"]
+            f4 += fc
+        extra["long_mqa_32k_8x4096"] = {"ms_per_prompt": total,
+                                        "tflops": f4 / (total * 1e-3) / 1e12,
                                         "per_chunk": per_chunk}
+        extra["long_mqa_32k_8x4096_persistent"] = {"ms_per_prompt": total_p,
+                                                   "tflops": f4 / (total_p * 1e-3) / 1e12,
+                                                   "per_chunk": per_chunk_p}
         del c4, o4
-        # the tiny MQA prefill (256 rows, one workgroup per 16 tokens): launch-bound
+        # the tiny MQA prefill (256 rows, one workgroup per 16 tokens)
         c1 = W.tiny_prefill_mqa(device="cuda")
         l1 = c1.launches[0]
         o1 = torch.empty((l1.total_q, c1.num_q_heads, W.HEAD_DIM), dtype=torch.float32,
                          device="cuda")
-        ms1 = timed(lambda: prefill_step(c1, l1, o1), 100, 20)
         f1 = W.prefill_flops(l1.q_lens, l1.q_starts, l1.kv_lens, c1.num_q_heads)
-        extra["tiny_prefill_mqa_256"] = {"us_per_launch": ms1 * 1e3,
-                                         "tflops": f1 / (ms1 * 1e-3) / 1e12,
-                                         "note": "launch-bound (16 workgroups)"}
+        t1 = rate(f1, graph_time(pf(c1, l1, o1), 100))
+        extra["tiny_prefill_mqa_256"] = dict(t1, us_per_launch=t1["ms"] * 1e3,
+                                             note="16 workgroups on 256 compute units")
         del c1, o1
+        torch.cuda.empty_cache()
+        # late dominant keys: every workgroup raises its rows' softmax
+        # reference two or three times (the cost of the overflow path)
+        for kv_dtype, mma in (("bf16", False), ("fp8_e4m3", True)):
+            cl = W.chunk_prefill_8k_at_8k_late_keys(device="cuda", kv_dtype=kv_dtype)
+            ll = cl.launches[0]
+            extra[cl.name + ("_mma" if mma else "")] = rate(
+                flops, graph_time(pf(cl, ll, out, fp8_mma=mma), 8))
+            del cl
         torch.cuda.empty_cache()
         # the headline chunk over an FP8-E4M3 cache (same values, per-tensor scales)
         c8 = W.chunk_prefill_8k_at_8k(device="cuda", kv_dtype="fp8_e4m3")
         l8 = c8.launches[0]
-
-        def fp8_step(mma):
-            A.prefill(l8.q, c8.k_pool, c8.v_pool, c8.page_table, l8.cu_seqlens_q, l8.q_start,
-                      l8.kv_len, out, total_q=l8.total_q, max_q_len=l8.max_q_len,
-                      softmax_scale=c8.softmax_scale, kv_dtype="fp8_e4m3", k_scale=c8.k_scale,
-                      v_scale=c8.v_scale, fp8_mma=mma, stream=stream)
-        ms8 = timed(lambda: fp8_step(False), args.steps, args.warmup)
-        extra["chunk_prefill_8192_at_8192_fp8"] = {"ms_per_launch": ms8,
-                                                   "tflops": flops / (ms8 * 1e-3) / 1e12}
+        t8 = rate(flops, graph_time(pf(c8, l8, out), 8))
+        extra["chunk_prefill_8192_at_8192_fp8"] = t8
         # the same bytes with both products on the block-scaled FP8 MFMA
-        ms8m = timed(lambda: fp8_step(True), args.steps, args.warmup)
-        extra["chunk_prefill_8192_at_8192_fp8_mma"] = {
-            "ms_per_launch": ms8m, "tflops": flops / (ms8m * 1e-3) / 1e12,
-            "frac_of_fp8_dense_peak": flops / (ms8m * 1e-3) / 5.0e15}
-        log(f"FP8 pool: widened {ms8:.3f} ms, FP8 MFMA {ms8m:.3f} ms "
-            f"({flops / (ms8m * 1e-3) / 1e12:.1f} TFLOP/s)")
+        t8m = rate(flops, graph_time(pf(c8, l8, out, fp8_mma=True), 8))
+        t8m["frac_of_fp8_dense_peak"] = t8m["tflops"] / 5000.0
+        extra["chunk_prefill_8192_at_8192_fp8_mma"] = t8m
+        log(f"FP8 pool: widened {t8['ms']:.3f} ms, FP8 MFMA {t8m['ms']:.3f} ms "
+            f"({t8m['tflops']:.1f} TFLOP/s)")
         del c8
         torch.cuda.empty_cache()
         # a short chunk over a long prefix: single pass against split-K (the
@@ -280,28 +351,21 @@ def main():
             nb = A.prefill_splitk_workspace_size(lp.batch, lp.max_q_len, lp.total_q,
                                                  cp.num_q_heads, cp.num_kv_heads,
                                                  lp.max_kv_len, 0)
-            wsp = torch.empty((max(nb, 4) // 4,), dtype=torch.float32, device="cuda")
+            ws = torch.empty((max(nb, 4) // 4,), dtype=torch.float32, device="cuda")
 
-            def single(c=cp, l=lp, o=op):
-                A.prefill(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q, l.q_start,
-                          l.kv_len, o, total_q=l.total_q, max_q_len=l.max_q_len,
-                          softmax_scale=c.softmax_scale, kv_dtype=c.kv_dtype,
-                          k_scale=c.k_scale, v_scale=c.v_scale, fp8_mma=mma, stream=stream)
-
-            def split(c=cp, l=lp, o=op, ws=wsp):
+            def split(c=cp, l=lp, o=op, w=ws):
                 A.prefill_splitk(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q,
-                                 l.q_start, l.kv_len, o, ws, total_q=l.total_q,
+                                 l.q_start, l.kv_len, o, w, total_q=l.total_q,
                                  max_q_len=l.max_q_len, max_kv_len=l.max_kv_len,
                                  softmax_scale=c.softmax_scale, kv_dtype=c.kv_dtype,
-                                 k_scale=c.k_scale, v_scale=c.v_scale, fp8_mma=mma,
-                                 stream=stream)
-            ms_1 = timed(single, 10, 3)
-            ms_s = timed(split, 10, 3)
-            extra[cp.name + ("_mma" if mma else "")] = {"single_pass_ms": ms_1,
-                              "single_pass_tflops": fp / (ms_1 * 1e-3) / 1e12,
-                              "splitk_ms": ms_s, "splitk_tflops": fp / (ms_s * 1e-3) / 1e12,
-                              "splitk_workspace_bytes": nb}
-            del cp, op, wsp
+                                 k_scale=c.k_scale, v_scale=c.v_scale, fp8_mma=mma)
+            t_1 = graph_time(pf(cp, lp, op, fp8_mma=mma))
+            t_s = graph_time(split)
+            extra[cp.name + ("_mma" if mma else "")] = {
+                "single_pass_ms": t_1["ms"], "single_pass_tflops": fp / (t_1["ms"] * 1e-3) / 1e12,
+                "splitk_ms": t_s["ms"], "splitk_tflops": fp / (t_s["ms"] * 1e-3) / 1e12,
+                "splitk_workspace_bytes": nb, "how": t_s["how"]}
+            del cp, op, ws
             torch.cuda.empty_cache()
         # sliding-window (local) layers: head dim 256, window 1024, ring caches
         cs = W.swa_prefill_hd256_8k_at_8k(device="cuda")
@@ -309,33 +373,23 @@ def main():
         os_ = torch.empty((ls.total_q, cs.num_q_heads, cs.head_dim), dtype=torch.bfloat16,
                           device="cuda")
 
-        def swa_prefill(c=cs, l=ls, o=os_):
-            A.prefill_swa(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q, l.q_start,
-                          l.kv_len, o, total_q=l.total_q, max_q_len=l.max_q_len,
-                          softmax_scale=c.softmax_scale, window=c.window,
-                          ring_pages=c.ring_pages, stream=stream)
-        ms_w = timed(swa_prefill, 20, 5)
+        def swa(c, l, o):
+            return lambda: A.prefill_swa(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q,
+                                         l.q_start, l.kv_len, o, total_q=l.total_q,
+                                         max_q_len=l.max_q_len, softmax_scale=c.softmax_scale,
+                                         window=c.window, ring_pages=c.ring_pages)
         f_w = W.prefill_flops(ls.q_lens, ls.q_starts, ls.kv_lens, cs.num_q_heads,
                               head_dim=cs.head_dim, window=cs.window)
-        extra[cs.name] = {"ms_per_launch": ms_w, "tflops": f_w / (ms_w * 1e-3) / 1e12,
-                          "flop_per_launch": f_w}
+        extra[cs.name] = dict(rate(f_w, graph_time(swa(cs, ls, os_))), flop_per_launch=f_w)
         del cs, os_
         cd = W.swa_decode_hd256_b64(device="cuda")
         ld = cd.launches[0]
         od = torch.empty((ld.total_q, cd.num_q_heads, cd.head_dim), dtype=torch.bfloat16,
                          device="cuda")
-
-        def swa_decode(c=cd, l=ld, o=od):
-            A.prefill_swa(l.q, c.k_pool, c.v_pool, c.page_table, l.cu_seqlens_q, l.q_start,
-                          l.kv_len, o, total_q=l.total_q, max_q_len=l.max_q_len,
-                          softmax_scale=c.softmax_scale, window=c.window,
-                          ring_pages=c.ring_pages, stream=stream)
-        for _ in range(10):
-            swa_decode()
-        wins = sorted(timed(swa_decode, 20, 0) for _ in range(7))
+        t_d = graph_time(swa(cd, ld, od), 100)
         nb_d = W.decode_kv_bytes(ld.kv_lens, cd.num_kv_heads, cd.head_dim, 2, cd.window)
-        extra[cd.name] = {"us_per_call": wins[3] * 1e3, "kv_bytes": nb_d,
-                          "GB_per_s": nb_d / (wins[3] * 1e-3) / 1e9}
+        extra[cd.name] = dict(t_d, us_per_call=t_d["ms"] * 1e3, kv_bytes=nb_d,
+                              GB_per_s=nb_d / (t_d["ms"] * 1e-3) / 1e9)
         del cd, od
         torch.cuda.empty_cache()
         log(f"other prefill workloads: {json.dumps(extra)}")
@@ -356,21 +410,20 @@ def main():
             def decode_call():
                 A.decode(qd, dc.k_pool, dc.v_pool, dc.page_table, dl.kv_len, dout, ws,
                          max_kv_len=dl.max_kv_len, softmax_scale=dc.softmax_scale,
-                         kv_dtype=dc.kv_dtype, k_scale=dc.k_scale, v_scale=dc.v_scale,
-                         stream=stream)
-            # median of 7 windows of 20 calls after warmup (windowed timing)
+                         kv_dtype=dc.kv_dtype, k_scale=dc.k_scale, v_scale=dc.v_scale)
+            # median of 7 replays of a graph of 20 calls (P3's 7 windows)
             for _ in range(10):
                 decode_call()
-            wins = sorted(timed(decode_call, 20, 0) for _ in range(7))
-            us = wins[3] * 1e3
+            t = graph_time(decode_call)
+            us = t["ms"] * 1e3
             nbytes = W.decode_kv_bytes(dl.kv_lens, dc.num_kv_heads, W.HEAD_DIM,
                                        1 if kv_dtype == "fp8_e4m3" else 2)
             gbps = nbytes / (us * 1e-6) / 1e9
             decode[kv_dtype] = {
-                "workload": dc.name, "us_per_call": us, "us_min": wins[0] * 1e3,
-                "us_max": wins[-1] * 1e3, "kv_bytes": nbytes, "GB_per_s": gbps,
+                "workload": dc.name, "us_per_call": us, "us_min": t["ms_min"] * 1e3,
+                "us_max": t["ms_max"] * 1e3, "kv_bytes": nbytes, "GB_per_s": gbps,
                 "frac_of_hbm_probe": gbps / hbm_read, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS,
-                "kernels": "split + merge, one stream"}
+                "kernels": "split + merge, one stream", "how": t["how"]}
             log(f"decode {kv_dtype}: {us:.1f} us/call, {gbps:.0f} GB/s "
                 f"({100 * gbps / hbm_read:.1f}% of probe)")
             del dc, dout, ws, qd
@@ -388,9 +441,8 @@ def main():
 
             def append_call():
                 A.append_kv(kn, vn, ac.page_table, al.cu_seqlens_q, al.q_start, kp, vp,
-                            kv_dtype=kv_dtype, k_scale=ac.k_scale, v_scale=ac.v_scale,
-                            stream=stream)
-            ms = timed(append_call, 20, 5)
+                            kv_dtype=kv_dtype, k_scale=ac.k_scale, v_scale=ac.v_scale)
+            ms = graph_time(append_call, 100)["ms"]
             moved = 2 * kn.numel() * 2 + 2 * kn.numel() * (2 if kv_dtype == "bf16" else 1)
             append[kv_dtype] = {"us_per_call": ms * 1e3, "bytes": moved,
                                 "GB_per_s": moved / (ms * 1e-3) / 1e9}
@@ -409,16 +461,15 @@ def main():
                 def fused_call():
                     A.prefill_append(al.q, kn, vn, kp, vp, ac.page_table, al.cu_seqlens_q,
                                      al.q_start, al.kv_len, ao, total_q=al.total_q,
-                                     max_q_len=al.max_q_len, softmax_scale=ac.softmax_scale,
-                                     stream=stream)
+                                     max_q_len=al.max_q_len, softmax_scale=ac.softmax_scale)
 
                 def unfused_call():
                     append_call()
                     A.prefill(al.q, kp, vp, ac.page_table, al.cu_seqlens_q, al.q_start,
                               al.kv_len, ao, total_q=al.total_q, max_q_len=al.max_q_len,
-                              softmax_scale=ac.softmax_scale, stream=stream)
-                ms_f = timed(fused_call, 10, 3)
-                ms_u = timed(unfused_call, 10, 3)
+                              softmax_scale=ac.softmax_scale)
+                ms_f = graph_time(fused_call, 8)["ms"]
+                ms_u = graph_time(unfused_call, 8)["ms"]
                 append["prefill_with_append_bf16"] = {
                     "fused_ms": ms_f, "append_then_prefill_ms": ms_u,
                     "fused_tflops": flops / (ms_f * 1e-3) / 1e12}

@@ -193,6 +193,39 @@ int attn_prefill_hd512_e4m3_mma(const void* q, const void* k_pages, const void* 
                                 hipStream_t stream);
 
 /*
+ * attn_prefill_hd512_ex with persistent, heaviest-first scheduling (A custom
+ * attention kernel for Gemma 4 on the RTX PRO 6000, "The kernel in three
+ * steps", step 3): one workgroup per compute unit of the stream's device,
+ * each taking work units (128 packed query rows of one KV head) from a
+ * counter in `workspace`, heaviest units first, until none is left.  Every
+ * unit computes exactly what the one-workgroup-per-unit launch of
+ * attn_prefill_hd512_ex computes, so the results are bitwise the same.
+ *
+ *   kv_dtype     ATTN_BF16 or ATTN_FP8_E4M3 (widened to bf16, as in
+ *                attn_prefill_hd512_e4m3); other arguments as for
+ *                attn_prefill_hd512_ex.
+ *   workspace    device buffer of at least
+ *                attn_prefill_hd512_persistent_workspace_size() bytes; the
+ *                call resets its counter itself (a one-thread kernel ahead of
+ *                the prefill on `stream`, no memset), so its contents on
+ *                entry are ignored; calls that overlap must not share it.
+ *
+ * ATTN_ERR_NULL for a missing workspace, ATTN_ERR_WORKSPACE when it is too
+ * small, ATTN_ERR_HIP when the device's compute-unit count cannot be read.
+ */
+size_t attn_prefill_hd512_persistent_workspace_size(void);
+
+int attn_prefill_hd512_persistent(const void* q, const void* k_pages, const void* v_pages,
+                                  int kv_dtype, float k_scale, float v_scale,
+                                  const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                  const int32_t* q_start_pos, const int32_t* kv_lens, int batch,
+                                  int total_q, int max_q_len, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int page_size, int num_pages,
+                                  int max_pages_per_seq, float softmax_scale, const float* sinks,
+                                  void* workspace, size_t workspace_bytes, void* out,
+                                  int out_dtype, float* lse, hipStream_t stream);
+
+/*
  * Chunked causal prefill of a sliding-window (local) layer over a bf16 pool,
  * at head_dim 256 (the local layers' heads; A custom attention kernel for
  * Gemma 4 on the RTX PRO 6000, "The deployment": local layers attend to the
@@ -460,10 +493,13 @@ size_t attn_hbm_probe_sink_words(size_t bytes);
 /*
  * Measurement helper: launches `slots` one-wave workgroups (1 <= slots <=
  * 65536) on `stream`; workgroup i writes three uint64 words to stamps[3 i ..]:
- * the id of the XCD it ran on (0..7), the shader-clock cycle counter
- * (s_memtime) and the constant 100 MHz counter (s_memrealtime), as read on
- * that XCD.  Two launches around a timed region give each XCD's mean shader
- * clock over it: delta(cycles) / delta(100 MHz ticks) * 100 MHz.
+ * where it ran (the XCD id, 0..7, in bits 32..35 and the HW_ID hardware
+ * register in bits 0..31: compute unit in bits 8..11, shader array in 12,
+ * shader engine in 13..15), the shader-clock cycle counter (s_memtime, which
+ * is not synchronised between compute units) and the constant 100 MHz
+ * counter (s_memrealtime).  Two launches around a timed region give, for a
+ * compute unit that holds a stamp of both, its mean shader clock over the
+ * region: delta(cycles) / delta(100 MHz ticks) * 100 MHz.
  */
 int attn_clock_stamps(void* stamps, int slots, hipStream_t stream);
 

@@ -279,6 +279,18 @@ def test_decode_noalloc_validation(L):
     assert call(q_len=3, hq=8, hkv=4, batch=4096, kps=1024) == 4
 
 
+def test_prefill_persistent_validation(L):
+    assert L.attn_prefill_hd512_persistent_workspace_size() >= 4
+    def call(ws=FAKE, nbytes=256, kv=0, d=512):
+        return L.attn_prefill_hd512_persistent(FAKE, FAKE, FAKE, kv, 1.0, 1.0, FAKE, FAKE, FAKE,
+                                               FAKE, 1, 4, 4, 8, 1, d, 64, 4, 1, 0.04, None, ws,
+                                               nbytes, FAKE, 1, None, None)
+    assert call(ws=None) == 1
+    assert call(nbytes=2) == 4
+    assert call(kv=7) == 3
+    assert call(d=256) == 3
+
+
 def test_probe_validation(L):
     assert L.attn_hbm_read_probe(None, 1024, FAKE, None) == 1
     assert L.attn_hbm_read_probe(FAKE, 1000, FAKE, None) == 2
