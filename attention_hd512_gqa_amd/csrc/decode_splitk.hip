@@ -55,6 +55,7 @@ constexpr int kMaxSub = 4;          // partials per split workgroup (FP8: one pe
 constexpr int kHalfKeys = 32;       // FP8: keys per wave step
 constexpr int kHalfBytes = kHalfKeys * kHeadDim;   // FP8 rows are 512 bytes
 constexpr float kRefMargin = 10.f;  // FP8: allowed excess of a score over the reference max
+constexpr int kRoutedMaxGroup = 128;  // largest group the prefill takes (128 packed rows)
 
 struct DecodeArgs {
     const __bf16* q;
@@ -603,12 +604,26 @@ int scratch_for_stream(hipStream_t stream, void** out) {
     return ATTN_OK;
 }
 
+// Bytes of the routed path's argument arrays at the head of the workspace
+// (2 batch + 1 ints, rounded up to 256 so the partials stay aligned).
+size_t routed_meta_bytes(int batch) {
+    return ((size_t)(2 * batch + 1) * sizeof(int) + 255) / 256 * 256;
+}
+
 int default_keys_per_split(int batch, int hkv, int max_kv_len) {
     const long long total = (long long)batch * hkv * max_kv_len;
     long long s = (total + kDefaultTargetWgs - 1) / kDefaultTargetWgs;
     s = (s + kPage - 1) / kPage * kPage;
     if (s < 4 * kPage) s = 4 * kPage;
     return (int)s;
+}
+
+// Key ranges of a routed call: the caller's, else the decode default (the
+// prefill's own plan counts compute rounds and keeps one range for decode
+// shapes; here the work is the KV stream, and the ranges balance the
+// sequences' different lengths).
+int routed_keys_per_split(int batch, int hkv, int max_kv_len, int keys_per_split) {
+    return keys_per_split ? keys_per_split : default_keys_per_split(batch, hkv, max_kv_len);
 }
 
 }  // namespace
@@ -622,6 +637,15 @@ extern "C" size_t attn_decode_splitk_ex_workspace_size(int batch, int q_len, int
     if (batch < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_kv_len < 1 ||
         num_q_heads % num_kv_heads || keys_per_split < 0 || keys_per_split % kPage)
         return 0;
+    if ((long long)q_len * (num_q_heads / num_kv_heads) > kDecRows) {
+        // routed to the split-K prefill: row offsets and chunk starts, then
+        // the prefill's partials
+        if ((long long)batch * q_len > 0x7fffffffLL) return 0;
+        return routed_meta_bytes(batch) +
+               attn_prefill_hd512_splitk_workspace_size(
+                   batch, q_len, batch * q_len, num_q_heads, num_kv_heads, max_kv_len,
+                   routed_keys_per_split(batch, num_kv_heads, max_kv_len, keys_per_split));
+    }
     const int kps = keys_per_split ? keys_per_split
                                    : default_keys_per_split(batch, num_kv_heads, max_kv_len);
     const size_t splits = (size_t)(max_kv_len + kps - 1) / kps;
@@ -638,6 +662,65 @@ extern "C" size_t attn_decode_splitk_workspace_size(int batch, int num_q_heads, 
 
 namespace attn {
 namespace {
+
+// Multi-token decode with more (token, head) columns than the decode tile's
+// 16 (e.g. 5 tokens at g = 8: a draft of 4 plus the current token) is the
+// prefill of q_len rows per sequence at positions kv_len - q_len ..
+// kv_len - 1: it runs as the split-K prefill (which reads each K/V tile once
+// for every row of the group), after this kernel has written the prefill's
+// device-side arguments: cu[b] = b q_len (b = 0 .. batch) and
+// qs[b] = kv_len[b] - q_len.
+__global__ __launch_bounds__(256) void decode_route_meta(const int* kv_lens, int batch,
+                                                         int q_len, int* cu, int* qs) {
+    for (int b = threadIdx.x; b <= batch; b += blockDim.x) {
+        cu[b] = b * q_len;
+        if (b < batch) qs[b] = kv_lens[b] - q_len;
+    }
+}
+
+int decode_as_prefill(const void* q, const void* k_pages, const void* v_pages, int kv_dtype,
+                      float k_scale, float v_scale, const int32_t* page_table,
+                      const int32_t* kv_lens, int batch, int q_len, int num_q_heads,
+                      int num_kv_heads, int head_dim, int page_size, int num_pages,
+                      int max_pages_per_seq, int max_kv_len, int keys_per_split,
+                      float softmax_scale, const float* sinks, void* workspace,
+                      size_t workspace_bytes, bool noalloc, void* out, int out_dtype,
+                      float* lse, hipStream_t stream) {
+    // every check the split-K prefill makes runs here, before the kernel
+    // below is launched (the caller has checked pointers, sizes and layout)
+    if ((long long)batch * q_len > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if ((long long)batch * q_len * num_q_heads > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if ((long long)max_pages_per_seq * kPage > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if (num_q_heads / num_kv_heads > kRoutedMaxGroup) return ATTN_ERR_UNSUPPORTED;
+    if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+    if (out_dtype != ATTN_BF16 && out_dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
+    if (kv_dtype == ATTN_FP8_E4M3 && (!(k_scale > 0.f) || !(v_scale > 0.f))) return ATTN_ERR_SHAPE;
+    const int total = batch * q_len;
+    const size_t meta = routed_meta_bytes(batch);
+    keys_per_split = routed_keys_per_split(batch, num_kv_heads, max_kv_len, keys_per_split);
+    const size_t part = attn_prefill_hd512_splitk_workspace_size(
+        batch, q_len, total, num_q_heads, num_kv_heads, max_kv_len, keys_per_split);
+    if (noalloc) {
+        if (meta + part > kScratchBytes) return ATTN_ERR_WORKSPACE;
+        const int rc = scratch_for_stream(stream, &workspace);
+        if (rc != ATTN_OK) return rc;
+        workspace_bytes = kScratchBytes;
+    } else if (!workspace || workspace_bytes < meta + part) {
+        return ATTN_ERR_WORKSPACE;
+    }
+    int* cu = (int*)workspace;
+    int* qs = cu + batch + 1;
+    hipLaunchKernelGGL(decode_route_meta, dim3(1), dim3(256), 0, stream, kv_lens, batch, q_len,
+                       cu, qs);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+    return attn_prefill_hd512_splitk(q, k_pages, v_pages, kv_dtype, k_scale, v_scale, page_table,
+                                     cu, qs, kv_lens, batch, total, q_len, num_q_heads,
+                                     num_kv_heads, head_dim, page_size, num_pages,
+                                     max_pages_per_seq, max_kv_len, keys_per_split,
+                                     softmax_scale, sinks, part ? (char*)workspace + meta : nullptr,
+                                     part ? workspace_bytes - meta : 0, out, out_dtype, lse,
+                                     stream);
+}
 
 // Validation and launch shared by the caller-workspace entry point and the
 // one that allocates nothing.  workspace == nullptr asks for the library's
@@ -659,7 +742,12 @@ int decode_launch(const void* q, const void* k_pages, const void* v_pages, int k
     if ((long long)max_kv_len > (long long)max_pages_per_seq * kPage) return ATTN_ERR_SHAPE;
     if (head_dim != kHeadDim || page_size != kPage) return ATTN_ERR_UNSUPPORTED;
     const int g = num_q_heads / num_kv_heads;
-    if ((long long)q_len * g > kDecRows) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)q_len * g > kDecRows)
+        return decode_as_prefill(q, k_pages, v_pages, kv_dtype, k_scale, v_scale, page_table,
+                                 kv_lens, batch, q_len, num_q_heads, num_kv_heads, head_dim,
+                                 page_size, num_pages, max_pages_per_seq, max_kv_len,
+                                 keys_per_split, softmax_scale, sinks, workspace,
+                                 workspace_bytes, noalloc, out, out_dtype, lse, stream);
     if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
     if (out_dtype != ATTN_BF16 && out_dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
     if (kv_dtype == ATTN_FP8_E4M3 && (!(k_scale > 0.f) || !(v_scale > 0.f))) return ATTN_ERR_SHAPE;

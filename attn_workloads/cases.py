@@ -139,6 +139,21 @@ def decode_b64(device="cpu", seed=5, kv_dtype="bf16", batch=64, lo=4096, hi=2867
                       device=device, kv_dtype=kv_dtype)
 
 
+def decode_mtp_b64(device="cpu", seed=9, kv_dtype="bf16", batch=64, q_len=5, lo=4096,
+                   hi=28672) -> PagedCase:
+    """Batch-64 multi-token decode at the 31B model's global-layer shape: the
+    current token plus a 4-token draft (q_len 5) per sequence, 32 q heads over
+    4 KV heads (g = 8, so 40 (token, head) columns per KV head), lengths
+    U{4096..28672} (Gemma-4 deployment with a 4-token draft: A custom
+    attention kernel for Gemma 4 on the RTX PRO 6000, "The deployment").
+    """
+    lens = decode_lengths(batch, lo, hi, seed)
+    seqs = [(q_len, L - q_len, L) for L in lens]
+    name = f"decode_mtp_b{batch}_q{q_len}_g8" + ("_fp8" if kv_dtype != "bf16" else "")
+    return build_case(name, seqs=seqs, hq=32, hkv=4, seed=seed, out_dtype="bf16",
+                      device=device, kv_dtype=kv_dtype)
+
+
 WORKLOADS: Dict[str, Callable[..., PagedCase]] = {
     "tiny_prefill_mqa_256": tiny_prefill_mqa,
     "chunk_prefill_2048": chunk_prefill_2k,
@@ -147,6 +162,7 @@ WORKLOADS: Dict[str, Callable[..., PagedCase]] = {
     "long_mqa_32k_8x4096": long_mqa_32k,
     "prefix_prefill_512_at_32k": prefix_prefill_512_at_32k,
     "decode_b64_splitk": decode_b64,
+    "decode_mtp_b64_q5_g8": decode_mtp_b64,
     "swa_prefill_hd256_8192_at_8192_w1024": swa_prefill_hd256_8k_at_8k,
     "swa_decode_hd256_b64_w1024": swa_decode_hd256_b64,
 }

@@ -429,6 +429,44 @@ def main():
             del dc, dout, ws, qd
             torch.cuda.empty_cache()
 
+    # ---- multi-token decode at g = 8 (routed through the split-K prefill) -----
+    decode_mtp = {}
+    if not args.no_decode:
+        for kv_dtype in ("bf16", "fp8_e4m3"):
+            mc = W.decode_mtp_b64(device="cuda", kv_dtype=kv_dtype)
+            ml = mc.launches[0]
+            q_len = ml.max_q_len
+            mout = torch.empty((ml.total_q, mc.num_q_heads, W.HEAD_DIM), dtype=torch.bfloat16,
+                               device="cuda")
+            mws = torch.empty(A.decode_workspace_size(ml.batch, mc.num_q_heads, mc.num_kv_heads,
+                                                      ml.max_kv_len, q_len=q_len) // 4,
+                              dtype=torch.float32, device="cuda")
+
+            def mtp_call():
+                A.decode(ml.q, mc.k_pool, mc.v_pool, mc.page_table, ml.kv_len, mout, mws,
+                         max_kv_len=ml.max_kv_len, softmax_scale=mc.softmax_scale,
+                         kv_dtype=mc.kv_dtype, k_scale=mc.k_scale, v_scale=mc.v_scale,
+                         q_len=q_len)
+            for _ in range(5):
+                mtp_call()
+            t = graph_time(mtp_call)
+            us = t["ms"] * 1e3
+            nbytes = W.decode_kv_bytes(ml.kv_lens, mc.num_kv_heads, W.HEAD_DIM,
+                                       1 if kv_dtype == "fp8_e4m3" else 2)
+            flops = W.prefill_flops(ml.q_lens, ml.q_starts, ml.kv_lens, mc.num_q_heads)
+            gbps = nbytes / (us * 1e-6) / 1e9
+            decode_mtp[kv_dtype] = {
+                "workload": mc.name, "q_len": q_len, "us_per_call": us,
+                "us_min": t["ms_min"] * 1e3, "us_max": t["ms_max"] * 1e3, "kv_bytes": nbytes,
+                "GB_per_s": gbps, "frac_of_hbm_probe": gbps / hbm_read,
+                "useful_TFLOP_per_s": flops / (us * 1e-6) / 1e12,
+                "kernels": "route args + split-K prefill + merge", "how": t["how"]}
+            log(f"decode q_len={q_len} g=8 {kv_dtype}: {us:.1f} us/call, {gbps:.0f} GB/s "
+                f"({100 * gbps / hbm_read:.1f}% of probe), "
+                f"{flops / (us * 1e-6) / 1e12:.0f} useful TFLOP/s")
+            del mc, ml, mout, mws
+            torch.cuda.empty_cache()
+
     # ---- paged KV append of the headline chunk (HBM-bound data movement) -----
     append = {}
     if not args.no_decode:
@@ -550,6 +588,7 @@ def main():
         "hbm": {"read_probe_GB_per_s": hbm_read, "probe_bytes": hbm_bytes,
                 "d2d_copy_GB_per_s": d2d},
         "decode": decode,
+        "decode_multi_token": decode_mtp,
         "append_kv": append,
         "prefill_other": extra,
         "cpu_baseline": cpu,

@@ -372,17 +372,26 @@ int attn_decode_splitk(const void* q, const void* k_pages, const void* v_pages, 
 /*
  * Split-K decode with every option: q_len query tokens per sequence
  * (multi-token decode, e.g. verifying q_len - 1 draft tokens; vLLM
- * flash-attention PR 199, second review: "MTP decode"), attention sinks and
- * a log-sum-exp output.  Other arguments as for attn_decode_splitk.
+ * flash-attention PR 199, second review: "MTP decode"; A custom attention
+ * kernel for Gemma 4 on the RTX PRO 6000, "The deployment": a 4-token draft
+ * at 32 query heads over 4 KV heads), attention sinks and a log-sum-exp
+ * output.  Other arguments as for attn_decode_splitk.
  *
  *   q            bf16 [batch * q_len][num_q_heads][512]: token t of sequence
  *                b is row b * q_len + t, at position kv_lens[b] - q_len + t,
- *                and sees keys j <= that position.  1 <= q_len and
- *                q_len * (num_q_heads / num_kv_heads) <= 16 (ATTN_ERR_UNSUPPORTED
- *                otherwise); kv_lens[b] >= q_len is a precondition.
+ *                and sees keys j <= that position.  q_len >= 1;
+ *                kv_lens[b] >= q_len is a precondition.
  *   sinks, lse   as for attn_prefill_hd512_ex; lse is [batch * q_len][num_q_heads].
  *   out          [batch * q_len][num_q_heads][512].
  *   workspace    at least attn_decode_splitk_ex_workspace_size(...) bytes.
+ *
+ * Up to 16 (token, query head) columns per KV head (q_len * g <= 16) run on
+ * the decode kernels.  Wider calls (e.g. 5 tokens at g = 8) are the prefill
+ * of q_len rows per sequence at positions kv_lens[b] - q_len ..: they run as
+ * attn_prefill_hd512_splitk on the same pool (keys_per_split then sets that
+ * call's ranges), after a one-workgroup kernel has written its row offsets
+ * and chunk starts to the head of the workspace; the workspace size covers
+ * both.
  */
 size_t attn_decode_splitk_ex_workspace_size(int batch, int q_len, int num_q_heads,
                                             int num_kv_heads, int max_kv_len,

@@ -116,7 +116,7 @@ def test_decode_validation(L):
     assert decode(L, max_kv=257) == 2              # beyond max_pages * 64
     assert decode(L, hq=6) == 2
     assert decode(L, d=128) == 3
-    assert decode(L, hq=64, hkv=2) == 3            # group of 32 > 16
+    assert decode(L, hq=256, hkv=1) == 3           # group of 256 > 128 (routed, refused)
     assert decode(L, kvd=1) == 3                   # fp32 pool
     assert decode(L, out_dtype=2) == 3
     assert decode(L, kvd=2, ks=0.0) == 2           # FP8 needs positive scales
@@ -140,7 +140,11 @@ def decode_ex(L, **over):
 def test_decode_ex_validation(L):
     assert decode_ex(L, q=None) == 1
     assert decode_ex(L, q_len=0) == 2
-    assert decode_ex(L, q_len=9) == 3            # 9 tokens x g=2 columns > 16
+    # 9 tokens x g = 2 columns > 16: the call becomes a split-K prefill, whose
+    # checks (pool dtype, workspace) still run before any launch
+    assert decode_ex(L, q_len=9, kvd=1) == 3
+    assert decode_ex(L, q_len=9, ws_bytes=16) == 4
+    assert decode_ex(L, q_len=9, ws=None) == 4
     assert decode_ex(L, kvd=1) == 3
     assert decode_ex(L, ws_bytes=16) == 4
 
@@ -289,6 +293,19 @@ def test_prefill_persistent_validation(L):
     assert call(nbytes=2) == 4
     assert call(kv=7) == 3
     assert call(d=256) == 3
+
+
+def test_wide_multi_token_decode_workspace(L):
+    # 5 tokens x g = 8: routed through the split-K prefill; its workspace is
+    # the row offsets and chunk starts (2 batch + 1 ints, padded to 256
+    # bytes) plus the prefill's partials for batch x q_len rows over the
+    # decode's default ranges (1792 keys at batch 64, max 28672 keys)
+    routed = L.attn_decode_splitk_ex_workspace_size(64, 5, 32, 4, 28672, 0)
+    part = L.attn_prefill_hd512_splitk_workspace_size(64, 5, 320, 32, 4, 28672, 1792)
+    assert routed == 768 + part and part == 16 * 320 * 32 * 514 * 4
+    assert L.attn_decode_splitk_ex_workspace_size(64, 5, 32, 4, 28672, 4096) == \
+        768 + L.attn_prefill_hd512_splitk_workspace_size(64, 5, 320, 32, 4, 28672, 4096)
+    assert L.attn_decode_splitk_ex_workspace_size(64, 2, 32, 4, 28672, 0) > 0   # g x q_len = 16
 
 
 def test_probe_validation(L):

@@ -1,6 +1,8 @@
 """GPU parity of the extended entry points against the CPU oracle: multi-token
-decode (q_len query tokens per sequence at its last positions), attention
-sinks and the log-sum-exp output, for prefill and decode, bf16 and FP8 pools.
+decode (q_len query tokens per sequence at its last positions; calls with
+more than 16 (token, head) columns per KV head run as split-K prefill),
+attention sinks and the log-sum-exp output, for prefill and decode, bf16 and
+FP8 pools.
 
 Outputs use the usual gate; the log-sum-exp is compared with the oracle's
 (natural log) to an absolute 2e-3.  Decode fixtures put kv_len next to split
@@ -62,6 +64,11 @@ DECODE = [
     ([260, 900, 5], 5, 6, 3, 256),          # g = 2, q_len 5: 10 columns
     ([4096, 4097, 2049], 4, 16, 4, 0),      # g = 4, 16 columns, library default split
     ([777, 1024], 1, 16, 1, 256),            # g = 16, q_len 1
+    # more than 16 columns: routed through the split-K prefill
+    ([257, 1000, 64, 2049], 3, 32, 4, 256),  # g = 8, q_len 3: 24 columns
+    ([5, 300, 4100], 5, 32, 4, 0),           # g = 8, q_len 5, kv_len = q_len, default split
+    ([700, 129], 2, 16, 1, 256),             # g = 16, q_len 2: 32 columns
+    ([100, 33], 17, 4, 4, 256),              # g = 1, q_len 17
 ]
 
 
@@ -89,6 +96,35 @@ def test_multi_token_decode_bf16_out(A):
     ref, ref_lse = oracle.attend_all_lse(case.to("cpu"), sinks=_sinks(8, 5))
     check_parity(out, ref, "decode q_len=4 bf16 out")
     _lse_check(lse, ref_lse, "decode q_len=4 bf16 out")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_multi_token_decode_b64_q5_g8(A, kv_dtype):
+    # the current token plus a 4-token draft at 32/4 heads, batch 64, lengths
+    # U{4096..28672}: 40 columns per KV head, so the call runs as split-K
+    # prefill.  Every sequence is checked: its 5 tokens on the 8 heads of one
+    # KV group (rotating over the groups) and head 0 of the others.
+    case = W.decode_mtp_b64(device="cuda", kv_dtype=kv_dtype)
+    lc = case.launches[0]
+    q_len, hq, g = 5, case.num_q_heads, case.num_q_heads // case.num_kv_heads
+    sinks = _sinks(hq, 11)
+    out_bf, lse = _run_decode(A, case, q_len, sinks, 0, out_dtype="bf16")
+    rows = []
+    for b in range(lc.batch):
+        kvh = b % case.num_kv_heads
+        heads = sorted(set(range(kvh * g, kvh * g + g)) |
+                       {h * g for h in range(case.num_kv_heads)})
+        rows += [(b * q_len + t) * hq + h for t in range(q_len) for h in heads]
+    rows = np.asarray(rows)
+    ref, ref_lse = oracle.attend_rows_lse(case.to("cpu"), rows, sinks=sinks)
+    what = f"decode_mtp_b64_q5_g8 {kv_dtype} ({len(rows)} rows)"
+    got = out_bf.reshape(-1, out_bf.shape[-1])[torch.as_tensor(rows, device="cuda")]
+    check_parity(got, ref, what)
+    _lse_check(lse.reshape(-1)[torch.as_tensor(rows, device="cuda")], ref_lse, what)
+    assert bool(torch.isfinite(out_bf.float()).all()), "unwritten output rows"
+    # the same bits on a second call
+    again, _ = _run_decode(A, case, q_len, sinks, 0, out_dtype="bf16")
+    assert torch.equal(out_bf.view(torch.int16), again.view(torch.int16))
 
 
 PREFILL = [
