@@ -1,41 +1,46 @@
 // Split-K (Flash-Decoding) decode at head_dim 512 over a paged KV cache, for
-// gfx950 (MI355X): one query token per sequence, GQA/MQA.
+// gfx950 (MI355X): q_len query tokens per sequence at its last positions
+// (1 for plain decode; more for verifying drafted tokens), GQA/MQA.
 //
 // A single KV head per sequence would give one workgroup per (sequence, KV
 // head) and leave most CUs idle, so the key range is cut into splits of
 // `keys_per_split` keys, each handled by one workgroup that writes
-// unnormalised partials (O, m, l) for the query heads of the group; a merge
-// kernel then combines the partials with the online-softmax rule (Flash-
-// Decoding for MQA in CUDA, "One KV head breaks the textbook").  Only the live
-// band [0, kv_len) is read (same page, "The starting point").  Every KV byte
-// is read once per call, with the non-temporal cache policy.
+// unnormalised partials (O, m, l) for the (token, query head) columns of the
+// group; a merge kernel then combines the partials with the online-softmax
+// rule (Flash-Decoding for MQA in CUDA, "One KV head breaks the textbook").
+// Only the live band [0, kv_len) is read (same page, "The starting point").
+// Every KV byte is read once per call, with the non-temporal cache policy.
 //
-// The g query heads of a group are the (zero-padded) 16 columns of
-// v_mfma_f32_16x16x32_bf16 products: S^T = K Q^T and O^T += V^T P^T, O in fp32
-// per key block (vLLM flash-attention PR 199, commit 3 of the first review).
-// Decode moves ~2 bytes per flop: HBM bandwidth, not the MFMA rate, bounds
-// it, and the padded MFMA columns cost issue slots that are free at that
-// ratio.
+// The q_len * g columns of a KV head are the (zero-padded) 16-column blocks
+// of v_mfma_f32_16x16x32_bf16 products: S^T = K Q^T and O^T += V^T P^T, O in
+// fp32 per key block (vLLM flash-attention PR 199, commit 3 of the first
+// review).  Decode moves ~2 bytes per flop per column block: HBM bandwidth,
+// not the MFMA rate, bounds it, and the padded MFMA columns cost issue slots
+// that are free at that ratio.
 //
-// bf16 pool, one 64-key tile (= one page of one KV head) at a time per
-// workgroup of 4 waves: K and V tiles are DMA'd to separate 64 KB LDS
-// buffers (swizzled rows); wave w computes the scores of keys 16 w .. 16 w +
-// 15, the scores meet in a small LDS buffer, every wave runs the softmax of
-// all 64 keys and accumulates its own 128 of the 512 output dims.
+// Tile kernel (bf16 pool; FP8 pool with 2 or 3 column blocks): one 64-key tile
+// (= one page of one KV head) at a time per workgroup of 4 waves.  K and V
+// tiles are DMA'd to separate LDS buffers (swizzled rows); wave w computes
+// the scores of keys 16 w .. 16 w + 15 for every column block, the scores
+// meet in a small LDS buffer, every wave runs the softmax of all 64 keys and
+// accumulates its own 128 of the 512 output dims.  Up to 3 blocks (48
+// columns: e.g. 5 tokens at g = 8) keep Q in registers; wider calls run as
+// split-K prefill.
 //
-// FP8-E4M3 pool: a split workgroup is one wave (the kernel takes any number
-// of waves, each on its own 32-key half pages and writing its own partial),
-// so the loop has no workgroup barrier and four independent waves per CU
-// hide each other's start-up.  The wave streams 32-key half pages: K goes
-// from HBM straight into the MFMA operand registers; V is DMA'd as raw E4M3
-// bytes into a per-wave double buffer in LDS and read back transposed
-// (ds_read_b64_tr_b8).  Both are widened exactly to bf16 (every E4M3 value
-// is a bf16 value) just before their MFMA, k_scale is folded into the
-// softmax scale and v_scale into the partial (vLLM flash-attention PR 199,
-// "Summary": FP8 KV with 16-bit MMA).  The wave keeps a reference maximum
-// and rescales O only when a score exceeds it by more than kRefMargin (log2
-// units), so the 128-register O accumulator is rarely touched by the
-// softmax.
+// Half-page kernel (FP8-E4M3 pool, one column block): a split workgroup is
+// one wave (the kernel takes any number of waves, each on its own 32-key
+// half pages and writing its own partial), so the loop has no workgroup
+// barrier and four independent waves per CU hide each other's start-up.
+// Each wave DMAs raw E4M3 half pages of K and V into its own two LDS buffers
+// and reads K back row-wise, V transposed (ds_read_b64_tr_b8).
+//
+// FP8 values are widened exactly to bf16 (every E4M3 value is a bf16 value)
+// just before their MFMA, k_scale is folded into the softmax scale and
+// v_scale into the partial (vLLM flash-attention PR 199, "Summary": FP8 KV
+// with 16-bit MMA).  The half-page kernel keeps a reference maximum and
+// rescales O only when a score exceeds it by more than kRefMargin (log2
+// units), so its 128-register O accumulator is rarely touched by the
+// softmax; the tile kernel rescales per tile.
 #include "device_common.h"
 #include "attn_host.h"
 
@@ -48,7 +53,6 @@ namespace {
 constexpr int kDecRows = 16;        // query heads of one group, zero-padded
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kSxStride = 272;      // bytes per score-exchange row (256 + 16 pad)
 constexpr int kDefaultTargetWgs = 4096;
 constexpr int kFp8Waves = 1;       // waves per FP8 split workgroup, one partial each
 constexpr int kMaxSub = 4;          // partials per split workgroup (FP8: one per wave)
@@ -56,6 +60,8 @@ constexpr int kHalfKeys = 32;       // FP8: keys per wave step
 constexpr int kHalfBytes = kHalfKeys * kHeadDim;   // FP8 rows are 512 bytes
 constexpr float kRefMargin = 10.f;  // FP8: allowed excess of a score over the reference max
 constexpr int kRoutedMaxGroup = 128;  // largest group the prefill takes (128 packed rows)
+constexpr int kMaxColBlocks = 3;    // 16-column blocks of a decode split (Q stays in registers)
+constexpr int kDecCols = kDecRows * kMaxColBlocks;   // wider calls run as split-K prefill
 
 struct DecodeArgs {
     const __bf16* q;
@@ -140,15 +146,15 @@ __device__ __forceinline__ Column column_of(const DecodeArgs& a, const SplitPlan
 // no key yet keeps m = -inf, and its p = 2^(-inf - 0) = 0, alpha = 1.
 __device__ __forceinline__ float finite_or_zero(float m) { return m == -__builtin_inff() ? 0.f : m; }
 
-// Unnormalised partial of head n: O^T element i of block db is dim
+// Unnormalised partial of column c: O^T element i of block db is dim
 // 16 db + 4 kq + i (db over NB blocks, starting at dim d0); l sums over the
 // four k-groups.
 template <int NB>
-__device__ __forceinline__ void write_partial(const DecodeArgs& a, size_t slot, int n, int kq,
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, size_t slot, int c, int kq,
                                               int d0, const f32x4 (&o)[NB], float m, float l) {
     float l_row = l + __shfl_xor(l, 16);
     l_row += __shfl_xor(l_row, 32);
-    if (n < a.cols) {
+    if (c < a.cols) {
         float* dst = a.part_o + slot * kHeadDim + d0 + 4 * kq;
 #pragma unroll
         for (int db = 0; db < NB; ++db) *(f32x4*)(dst + 16 * db) = o[db] * a.v_scale;
@@ -159,49 +165,157 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, size_t slot, 
     }
 }
 
-// ============================== bf16 pool ==================================
+// ====================== tile kernel (bf16 and wide FP8) ======================
 
-// 16 rows per wave, global -> LDS, rows past `valid` arrive as zeros.
-__device__ __forceinline__ void issue_tile_bf16(const char* src, int valid, ATTN_LDS char* buf,
-                                                int wave, int lane16) {
-    rows16_to_lds<true>(buffer_rsrc(src, (uint32_t)valid * kRowBytes), buf, wave, lane16);
+// LDS layout of E4M3 rows: row r (a key) is 512 bytes, its 16-byte chunk c
+// sits at chunk c ^ swz8(r).  swz8 is a bijection on r mod 16, so the 16 rows
+// of one K operand read land on 16 distinct chunk positions (all 64 banks),
+// and so do the rows of each transposed V read (8 consecutive rows from a
+// multiple of 8; in the half-page kernel rows 4 kq .. 4 kq + 3 and 16 + 4 kq
+// .. 16 + 4 kq + 3).
+__host__ __device__ constexpr int swz8(int r) { return (r & 15) ^ (((r >> 4) & 1) << 2); }
+
+// Eight E4M3 bytes (two words, low byte first) widened exactly to bf16.
+__device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
+    const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 }
 
+// x *= f for an f32x4 accumulator held in AGPRs, one element at a time
+// through one VGPR (VALU cannot read AGPRs), as asm so that the accumulators
+// stay in AGPRs (with Q's registers beside them, VGPRs would not hold them).
+__device__ __forceinline__ void scale_acc4(f32x4& acc, float f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float x = acc[i];
+        float t;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n\t"
+            "v_mul_f32 %1, %1, %2\n\t"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(x), "=&v"(t)
+            : "v"(f));
+        acc[i] = x;
+    }
+}
+
+// Wait states around scale_acc4, tied to the 8 accumulators of one column
+// block so that no MFMA moves across them: an MFMA's result is written before
+// v_accvgpr_read reads it, and a v_accvgpr_write before an MFMA reads the
+// register as its C operand (the asm is opaque to the hazard recognizer).
+__device__ __forceinline__ void acc_fence8(f32x4 (&o)[8]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                   "+a"(o[6]), "+a"(o[7]));
+}
+
+// This wave's 16 rows (16 wave .. 16 wave + 15) of a 64-key tile -> LDS, rows
+// past `valid` as zeros.  bf16: 1 KB rows, one per DMA, swizzled by swz.
+// E4M3: 512-byte rows, two per DMA, 16-byte chunk c of row r stored at chunk
+// c ^ swz8(r) (the FP8 half pages' layout below).
+template <bool FP8>
+__device__ __forceinline__ void issue_tile(const char* src, int valid, ATTN_LDS char* buf,
+                                           int wave, int lane) {
+    if constexpr (!FP8) {
+        rows16_to_lds<true>(buffer_rsrc(src, (uint32_t)valid * kRowBytes), buf, wave, lane * 16);
+    } else {
+        const u32x4 rsrc = buffer_rsrc(src, (uint32_t)valid * kHeadDim);
+        const uint32_t lds = (uint32_t)(uintptr_t)buf + (uint32_t)wave * 16 * kHeadDim;
+        const int hl = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 16 * wave + 2 * i + hl;
+            const int voff = r * kHeadDim + (((lane & 31) ^ swz8(r)) << 4);
+            asm volatile(
+                "s_mov_b32 m0, %1\n\t"
+                "s_nop 0\n\t"
+                "buffer_load_dwordx4 %0, %2, 0 offen nt lds"
+                :
+                : "v"(voff), "s"(lds + 2 * i * kHeadDim), "s"(rsrc)
+                : "memory", "m0");
+        }
+    }
+}
+
+// One 64-key tile (= one page of one KV head) at a time per workgroup of 4
+// waves, NC blocks of 16 (token, head) columns.  K and V tiles are DMA'd to
+// separate LDS buffers.  Wave w owns keys 16 w .. 16 w + 15: it computes
+// their scores for every column block (one K operand read serves all NC
+// blocks) and, once the four waves have exchanged their per-column maxima
+// through LDS, their probabilities, which it writes to LDS as bf16.  Every
+// wave then accumulates its own 128 of the 512 output dims over all 64 keys,
+// reading each V operand once for all blocks.  A column's probabilities are
+// taken against a reference maximum that moves only when a tile's maximum
+// exceeds it by more than kTileMargin (log2 units), so the accumulators are
+// rarely rescaled; l sums the bf16 probabilities the PV products use.  FP8:
+// the tiles hold E4M3 bytes, widened exactly to bf16 as each operand is read
+// (k_scale is in the softmax scale, v_scale in the partial).
+constexpr float kTileMargin = 8.f;
+constexpr int kPStride = 2 * kPage + 16;   // bytes per column row of the P buffer
+
+__device__ __forceinline__ float pair_sum(const bf16x8& v, float acc) {
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2 * j], v[2 * j + 1]}, one, acc, false);
+    return acc;
+}
+
+template <bool FP8, int NC>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_split_bf16_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes + kDecRows * kSxStride];
+void decode_split_tile_kernel(DecodeArgs a) {
+    constexpr int kTB = FP8 ? kPage * kHeadDim : kTileBytes;   // one K or V tile
+    constexpr int kLoads = FP8 ? kPage / 8 : kPage / kDecWaves;  // DMAs per wave per tile
+    constexpr int kCols = NC * kDecRows;
+    __shared__ __attribute__((aligned(1024)))
+        char smem[2 * kTB + kCols * kPStride + kCols * kDecWaves * 4];
     SplitPlan p;
     if (!plan_split(a, p)) return;
     ATTN_LDS char* sK = (ATTN_LDS char*)smem;
-    ATTN_LDS char* sV = sK + kTileBytes;
-    ATTN_LDS char* sX = sV + kTileBytes;
+    ATTN_LDS char* sV = sK + kTB;
+    ATTN_LDS char* sP = sV + kTB;                               // [column][64 keys] bf16
+    ATTN_LDS float* sM = (ATTN_LDS float*)(sP + kCols * kPStride);  // [column][wave]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = lane & 15;   // query head of the group (MFMA column)
+    const int n = lane & 15;   // MFMA column within a block
     const int kq = lane >> 4;  // k-group
-    const int lane16 = lane * 16;
 
-    const Column col = column_of(a, p, n);
-    // Q^T operand, k-step ks covers dims 32 ks .. 32 ks + 31; lane holds 32 ks + 8 kq .. + 7
-    bf16x8 qf[16];
-    {
-        const bf16x8* qp = (const bf16x8*)(a.q + col.q_row * kHeadDim) + kq;
+    // Q^T operand of block cb, k-step ks: bf16 dims 32 ks + 8 kq .. + 7; FP8
+    // dims 64 (ks / 2) + 16 kq + 8 (ks % 2) .. + 7, the order in which one
+    // 16-byte K read delivers two k-steps
+    Column col[NC];
+    bf16x8 qf[NC][16];
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+        col[cb] = column_of(a, p, 16 * cb + n);
+        const __bf16* qrow = a.q + col[cb].q_row * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
-            const bf16x8 v = qp[4 * ks];
-            qf[ks] = col.ok ? v : bf16x8{};
+            const int d = FP8 ? 64 * (ks >> 1) + 16 * kq + 8 * (ks & 1) : 32 * ks + 8 * kq;
+            const bf16x8 v = *(const bf16x8*)(qrow + d);
+            qf[cb][ks] = col[cb].ok ? v : bf16x8{};
         }
     }
-    // K operand: row 16 wave + n, chunk 4 ks + kq; with ks = 4 u + v the byte
-    // offset is koff[v] + 256 u.
+    // K operand: key row 16 wave + n.  bf16: chunk 4 ks + kq, with ks = 4 u +
+    // v at byte koff[v] + 256 u.  FP8: read i (chunk 4 i + kq) at
+    // krow + ((4 i + kq) ^ ksw) * 16.
     int koff[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
         koff[v] = (16 * wave + n) * kRowBytes + (((4 * v + kq) ^ swz(n)) << 4);
-    // V^T operand (transposing reads): key row 32 c + 8 kq + (n >> 2) (+4 for
-    // the second read), dims 128 wave + 16 db + 4 (n & 3), i.e. logical chunk
-    // 16 wave + 2 db + (n & 3) / 2 at byte 8 (n & 1).  Rows of different c
-    // share the swizzle (32 c is a multiple of 16).
+    const int krow = (16 * wave + n) * kHeadDim;
+    const int ksw = swz8(16 * wave + n);
+    // V^T operand (transposing reads).  bf16: key row 32 c + 8 kq + (n >> 2)
+    // (+4 for the second read), dims 128 wave + 16 db + 4 (n & 3), i.e. logical
+    // chunk 16 wave + 2 db + (n & 3) / 2 at byte 8 (n & 1); rows of different c
+    // share the swizzle (32 c is a multiple of 16).  FP8: lane pair n = 2 j +
+    // h of group kq addresses key row 32 c + 8 kq + j at byte 8 h of dim chunk
+    // 8 wave + db, and lane n receives dim 16 (8 wave + db) + n of those 8
+    // keys.  Either way the keys are 32 c + 8 kq .. + 7, those of this lane's
+    // P^T operand, in its order.
     int vrow[2], vsw[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -209,114 +323,171 @@ void decode_split_bf16_kernel(DecodeArgs a) {
         vsw[h] = swz(8 * kq + (n >> 2) + 4 * h);
     }
     const int vchunk0 = 16 * wave + ((n & 3) >> 1);
-    f32x4 o[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] = f32x4{};
-    float m_run = -__builtin_inff();
-    float l_run = 0.f;
+    const int vr8 = 8 * kq + (n >> 1);
+    const int vrow8 = vr8 * kHeadDim + 8 * (n & 1);
+    const int vsw8 = swz8(vr8);   // the same for rows 32 c + vr8
 
+    f32x4 o[NC][8];
+    float m_ref[NC], l_run[NC];
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[cb][db] = f32x4{};
+        m_ref[cb] = -__builtin_inff();
+        l_run[cb] = 0.f;
+    }
+
+    constexpr int kPoolTile = FP8 ? kTileBytes / 2 : kTileBytes;
     auto valid_of = [&](int t) { return min(p.k_end - (p.k_begin + t * kPage), kPage); };
     {
         const int pg = split_page(a, p, 0);
-        issue_tile_bf16(tile_base(a.k_pages, a, pg, p.kvh, kTileBytes), valid_of(0), sK, wave, lane16);
-        issue_tile_bf16(tile_base(a.v_pages, a, pg, p.kvh, kTileBytes), valid_of(0), sV, wave, lane16);
+        issue_tile<FP8>(tile_base(a.k_pages, a, pg, p.kvh, kPoolTile), valid_of(0), sK, wave, lane);
+        issue_tile<FP8>(tile_base(a.v_pages, a, pg, p.kvh, kPoolTile), valid_of(0), sV, wave, lane);
     }
     for (int t = 0; t < p.ntiles; ++t) {
         const int key0 = p.k_begin + t * kPage;
         const bool more = t + 1 < p.ntiles;
         const int pg_next = split_page(a, p, t + 1);   // arrives by the next barrier
-        wait_vmcnt<kPage / kDecWaves>();   // K(t) in; V(t) may still be in flight
+        wait_vmcnt<kLoads>();   // K(t) in; V(t) may still be in flight
         lds_barrier();
 
-        // S^T[16 keys of this wave][16 heads] over 512 dims
-        f32x4 s = f32x4{};
+        // S^T[16 keys of this wave][16 columns] per block, over 512 dims
+        f32x4 s[NC];
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            const bf16x8 kv = *(const ATTN_LDS bf16x8*)(sK + koff[ks & 3] + 256 * (ks >> 2));
-            s = mfma16x16x32(kv, qf[ks], s);
+        for (int cb = 0; cb < NC; ++cb) s[cb] = f32x4{};
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 w = *(const ATTN_LDS u32x4*)(sK + krow + (((4 * i + kq) ^ ksw) << 4));
+                const bf16x8 k0 = widen8(w[0], w[1]);
+                const bf16x8 k1 = widen8(w[2], w[3]);
+#pragma unroll
+                for (int cb = 0; cb < NC; ++cb) {
+                    s[cb] = mfma16x16x32(k0, qf[cb][2 * i], s[cb]);
+                    s[cb] = mfma16x16x32(k1, qf[cb][2 * i + 1], s[cb]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks) {
+                const bf16x8 kv = *(const ATTN_LDS bf16x8*)(sK + koff[ks & 3] + 256 * (ks >> 2));
+#pragma unroll
+                for (int cb = 0; cb < NC; ++cb) s[cb] = mfma16x16x32(kv, qf[cb][ks], s[cb]);
+            }
         }
-        // accumulator element i is key 16 wave + 4 kq + i of head n
-        *(ATTN_LDS f32x4*)(sX + n * kSxStride + (16 * wave + 4 * kq) * 4) = s;
-        lds_barrier();  // scores visible; every wave is done with sK
-        if (more)
-            issue_tile_bf16(tile_base(a.k_pages, a, pg_next, p.kvh, kTileBytes), valid_of(t + 1),
-                            sK, wave, lane16);
-
-        // online softmax over the tile; this lane takes keys 32 c + 8 kq + j
-        float x[2][8];
+        // element i: key 16 wave + 4 kq + i of column 16 cb + n, in log2
+        // units; keys a column may not see are -inf (only in the tiles that
+        // reach past k_end - q_len: earlier keys are visible to every column)
+        const bool edge = key0 + kPage > p.k_end - a.q_len;
+        const int mykey = key0 + 16 * wave + 4 * kq;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const f32x4 lo = *(const ATTN_LDS f32x4*)(sX + n * kSxStride + (32 * c + 8 * kq) * 4);
-            const f32x4 hi = *(const ATTN_LDS f32x4*)(sX + n * kSxStride + (32 * c + 8 * kq + 4) * 4);
+        for (int cb = 0; cb < NC; ++cb) {
+            float mt = -__builtin_inff();
 #pragma unroll
-            for (int j = 0; j < 4; ++j) { x[c][j] = lo[j]; x[c][4 + j] = hi[j]; }
-        }
-        float mt = -__builtin_inff();
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int key = key0 + 32 * c + 8 * kq + j;
-                const float v = key < col.k_lim ? x[c][j] * a.scale_log2 : -__builtin_inff();
-                x[c][j] = v;
+            for (int i = 0; i < 4; ++i) {
+                float v = s[cb][i] * a.scale_log2;
+                if (edge && mykey + i >= col[cb].k_lim) v = -__builtin_inff();
+                s[cb][i] = v;
                 mt = fmaxf(mt, v);
             }
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            if (kq == 0) sM[(16 * cb + n) * kDecWaves + wave] = mt;
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        // -inf until the column's first visible key (a later token of a
-        // multi-token decode can see keys an earlier one cannot)
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = finite_or_zero(m_new);
-        const float alpha = fast_exp2(m_run - m_use);
-        bf16x8 pf[2];
-        float psum = 0.f;
+        lds_barrier();  // column maxima visible; every wave is done with sK
+        if (more)
+            issue_tile<FP8>(tile_base(a.k_pages, a, pg_next, p.kvh, kPoolTile), valid_of(t + 1),
+                            sK, wave, lane);
+
+        // the tile's maximum per column moves the reference when it exceeds it
+        // by more than the margin (the first tile with a visible key always
+        // does: alpha = 0 on the zero O); every wave takes the same decision
+        bool up_any = false;
+        float alpha[NC];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int cb = 0; cb < NC; ++cb) {
+            const f32x4 mm = *(const ATTN_LDS f32x4*)(sM + (16 * cb + n) * kDecWaves);
+            const float mt = fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3]));
+            const bool up = mt > m_ref[cb] + kTileMargin;
+            alpha[cb] = up ? fast_exp2(m_ref[cb] - mt) : 1.f;
+            m_ref[cb] = up ? mt : m_ref[cb];
+            up_any |= up;
+        }
+        if (__builtin_amdgcn_ballot_w64(up_any)) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float pv = fast_exp2(x[c][j] - m_use);
-                psum += pv;
-                pf[c][j] = (__bf16)pv;
+            for (int cb = 0; cb < NC; ++cb) {
+                l_run[cb] *= alpha[cb];
+                if constexpr (NC == 1) {
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) o[cb][db] *= alpha[cb];
+                } else {
+                    acc_fence8(o[cb]);
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) scale_acc4(o[cb][db], alpha[cb]);
+                    acc_fence8(o[cb]);
+                }
             }
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        // probabilities of this wave's keys -> the P buffer
 #pragma unroll
-        for (int db = 0; db < 8; ++db) o[db] *= alpha;
+        for (int cb = 0; cb < NC; ++cb) {
+            const float m_use = finite_or_zero(m_ref[cb]);
+            bf16x4 pw;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pw[i] = (__bf16)fast_exp2(s[cb][i] - m_use);
+            *(ATTN_LDS bf16x4*)(sP + (16 * cb + n) * kPStride + (16 * wave + 4 * kq) * 2) = pw;
+        }
 
-        if (more) wait_vmcnt<kPage / kDecWaves>(); else wait_vmcnt<0>();
-        lds_barrier();  // V(t) visible
+        if (more) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
+        lds_barrier();  // P and V(t) visible
 
-        // O^T[128 dims of this wave][16 heads] += V^T P^T
+        // P^T operand: keys 32 c + 8 kq .. + 7 of column 16 cb + n
+        bf16x8 pf[NC][2];
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                pf[cb][c] = *(const ATTN_LDS bf16x8*)(sP + (16 * cb + n) * kPStride +
+                                                      (32 * c + 8 * kq) * 2);
+                l_run[cb] = pair_sum(pf[cb][c], l_run[cb]);
+            }
+        }
+        // O^T[128 dims of this wave][16 columns] += V^T P^T per block
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const int ch = vchunk0 + 2 * db;
-                const ATTN_LDS char* base = sV + 32 * c * kRowBytes;
-                const bf16x4 va = lds_read_tr16(base + vrow[0] + ((ch ^ vsw[0]) << 4));
-                const bf16x4 vb = lds_read_tr16(base + vrow[1] + ((ch ^ vsw[1]) << 4));
-                const bf16x8 vt = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[db] = mfma16x16x32(vt, pf[c], o[db]);
+                bf16x8 vt;
+                if constexpr (FP8) {
+                    const v2i32 t8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (ATTN_LDS v2i32*)(sV + 32 * c * kHeadDim + vrow8 +
+                                          (((8 * wave + db) ^ vsw8) << 4)));
+                    vt = widen8((uint32_t)t8[0], (uint32_t)t8[1]);
+                } else {
+                    const int ch = vchunk0 + 2 * db;
+                    const ATTN_LDS char* base = sV + 32 * c * kRowBytes;
+                    const bf16x4 va = lds_read_tr16(base + vrow[0] + ((ch ^ vsw[0]) << 4));
+                    const bf16x4 vb = lds_read_tr16(base + vrow[1] + ((ch ^ vsw[1]) << 4));
+                    vt = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+#pragma unroll
+                for (int cb = 0; cb < NC; ++cb) o[cb][db] = mfma16x16x32(vt, pf[cb][c], o[cb][db]);
             }
         }
-        lds_barrier();  // every wave is done with sV and sX
+        lds_barrier();  // every wave is done with sV, sP and sM
         if (more)
-            issue_tile_bf16(tile_base(a.v_pages, a, pg_next, p.kvh, kTileBytes), valid_of(t + 1),
-                            sV, wave, lane16);
+            issue_tile<FP8>(tile_base(a.v_pages, a, pg_next, p.kvh, kPoolTile), valid_of(t + 1),
+                            sV, wave, lane);
     }
-    const size_t slot = (((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub * a.cols + n;
-    write_partial<8>(a, slot, n, kq, 128 * wave, o, m_run, l_run);
+    const size_t slot0 = (((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub * a.cols;
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb)
+        write_partial<8>(a, slot0 + 16 * cb + n, 16 * cb + n, kq, 128 * wave, o[cb], m_ref[cb],
+                         l_run[cb]);
 }
 
 // ============================== FP8 pool ===================================
 
-// LDS layout of a wave's V half page: row r (a key) is 512 bytes, its 16-byte
-// chunk c sits at chunk c ^ swz8(r).  swz8 separates the rows of each
-// transposed read (rows 4 kq .. 4 kq + 3 and 16 + 4 kq .. 16 + 4 kq + 3) and
-// of each half of a wave.
-__host__ __device__ constexpr int swz8(int r) { return (r & 15) ^ (((r >> 4) & 1) << 2); }
 
 // K or V half page (32 rows of 512 E4M3 bytes) -> this wave's LDS buffer by
 // DMA, 2 whole rows (8 full 128-byte lines) per instruction: lane l lands at
@@ -352,13 +523,6 @@ __device__ __forceinline__ u32x4 k_read(const ATTN_LDS char* sk, int gm, int i, 
     return *(const ATTN_LDS u32x4*)(sk + row * kHeadDim + (((4 * i + kq) ^ swz8(row)) << 4));
 }
 
-__device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
-    const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-    const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-    const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-    const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-    return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-}
 
 // Per wave step (half page u of this wave; one K and one V half-page buffer
 // in LDS, both filled by whole-row DMA):
@@ -637,7 +801,7 @@ extern "C" size_t attn_decode_splitk_ex_workspace_size(int batch, int q_len, int
     if (batch < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_kv_len < 1 ||
         num_q_heads % num_kv_heads || keys_per_split < 0 || keys_per_split % kPage)
         return 0;
-    if ((long long)q_len * (num_q_heads / num_kv_heads) > kDecRows) {
+    if ((long long)q_len * (num_q_heads / num_kv_heads) > kDecCols) {
         // routed to the split-K prefill: row offsets and chunk starts, then
         // the prefill's partials
         if ((long long)batch * q_len > 0x7fffffffLL) return 0;
@@ -742,7 +906,7 @@ int decode_launch(const void* q, const void* k_pages, const void* v_pages, int k
     if ((long long)max_kv_len > (long long)max_pages_per_seq * kPage) return ATTN_ERR_SHAPE;
     if (head_dim != kHeadDim || page_size != kPage) return ATTN_ERR_UNSUPPORTED;
     const int g = num_q_heads / num_kv_heads;
-    if ((long long)q_len * g > kDecRows)
+    if ((long long)q_len * g > kDecCols)
         return decode_as_prefill(q, k_pages, v_pages, kv_dtype, k_scale, v_scale, page_table,
                                  kv_lens, batch, q_len, num_q_heads, num_kv_heads, head_dim,
                                  page_size, num_pages, max_pages_per_seq, max_kv_len,
@@ -754,7 +918,9 @@ int decode_launch(const void* q, const void* k_pages, const void* v_pages, int k
     const bool fp8 = kv_dtype == ATTN_FP8_E4M3;
     const int kps = keys_per_split ? keys_per_split
                                    : default_keys_per_split(batch, num_kv_heads, max_kv_len);
-    const int sub = fp8 ? kFp8Waves : 1;
+    const int nc = (q_len * g + kDecRows - 1) / kDecRows;   // 16-column blocks
+    // FP8 with one block: the half-page kernel (a partial per wave)
+    const int sub = fp8 && nc == 1 ? kFp8Waves : 1;
     const int max_splits = (max_kv_len + kps - 1) / kps;
     // partial slots the launch writes and reads: (O, m, l) per split, partial
     // of the split and (token, query head)
@@ -796,12 +962,23 @@ int decode_launch(const void* q, const void* k_pages, const void* v_pages, int k
     const long long grid = (long long)batch * num_kv_heads * a.max_splits;
     const long long mgrid = (long long)batch * q_len * num_q_heads;
     if (grid > 0x7fffffffLL || mgrid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-    if (fp8)
-        hipLaunchKernelGGL(decode_split_fp8_kernel<kFp8Waves>, dim3((unsigned)grid),
-                           dim3(64 * kFp8Waves), 0, stream, a);
-    else
-        hipLaunchKernelGGL(decode_split_bf16_kernel, dim3((unsigned)grid), dim3(kDecThreads), 0,
-                           stream, a);
+    const dim3 tg((unsigned)grid), tb(kDecThreads);
+    if (fp8) {
+        if (nc == 1)
+            hipLaunchKernelGGL(decode_split_fp8_kernel<kFp8Waves>, dim3((unsigned)grid),
+                               dim3(64 * kFp8Waves), 0, stream, a);
+        else if (nc == 2)
+            hipLaunchKernelGGL((decode_split_tile_kernel<true, 2>), tg, tb, 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_split_tile_kernel<true, 3>), tg, tb, 0, stream, a);
+    } else {
+        if (nc == 1)
+            hipLaunchKernelGGL((decode_split_tile_kernel<false, 1>), tg, tb, 0, stream, a);
+        else if (nc == 2)
+            hipLaunchKernelGGL((decode_split_tile_kernel<false, 2>), tg, tb, 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_split_tile_kernel<false, 3>), tg, tb, 0, stream, a);
+    }
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
     if (out_dtype == ATTN_FP32)
         hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((unsigned)mgrid), dim3(128), 0, stream,

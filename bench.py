@@ -460,7 +460,8 @@ def main():
                 "us_min": t["ms_min"] * 1e3, "us_max": t["ms_max"] * 1e3, "kv_bytes": nbytes,
                 "GB_per_s": gbps, "frac_of_hbm_probe": gbps / hbm_read,
                 "useful_TFLOP_per_s": flops / (us * 1e-6) / 1e12,
-                "kernels": "route args + split-K prefill + merge", "how": t["how"]}
+                "kernels": "split (tile kernel, 3 column blocks of 16) + merge",
+                "how": t["how"]}
             log(f"decode q_len={q_len} g=8 {kv_dtype}: {us:.1f} us/call, {gbps:.0f} GB/s "
                 f"({100 * gbps / hbm_read:.1f}% of probe), "
                 f"{flops / (us * 1e-6) / 1e12:.0f} useful TFLOP/s")

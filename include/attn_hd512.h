@@ -385,13 +385,14 @@ int attn_decode_splitk(const void* q, const void* k_pages, const void* v_pages, 
  *   out          [batch * q_len][num_q_heads][512].
  *   workspace    at least attn_decode_splitk_ex_workspace_size(...) bytes.
  *
- * Up to 16 (token, query head) columns per KV head (q_len * g <= 16) run on
- * the decode kernels.  Wider calls (e.g. 5 tokens at g = 8) are the prefill
- * of q_len rows per sequence at positions kv_lens[b] - q_len ..: they run as
- * attn_prefill_hd512_splitk on the same pool (keys_per_split then sets that
- * call's ranges), after a one-workgroup kernel has written its row offsets
- * and chunk starts to the head of the workspace; the workspace size covers
- * both.
+ * Up to 48 (token, query head) columns per KV head (q_len * g <= 48, e.g.
+ * 5 tokens at g = 8) run on the decode kernels, in blocks of 16 columns that
+ * share each K and V tile read.  Wider calls are the prefill of q_len rows
+ * per sequence at positions kv_lens[b] - q_len ..: they run as
+ * attn_prefill_hd512_splitk on the same pool (keys_per_split, else the decode
+ * default, sets that call's ranges), after a one-workgroup kernel has
+ * written its row offsets and chunk starts to the head of the workspace; the
+ * workspace size covers both.
  */
 size_t attn_decode_splitk_ex_workspace_size(int batch, int q_len, int num_q_heads,
                                             int num_kv_heads, int max_kv_len,

@@ -140,11 +140,14 @@ def decode_ex(L, **over):
 def test_decode_ex_validation(L):
     assert decode_ex(L, q=None) == 1
     assert decode_ex(L, q_len=0) == 2
-    # 9 tokens x g = 2 columns > 16: the call becomes a split-K prefill, whose
-    # checks (pool dtype, workspace) still run before any launch
+    # 25 tokens x g = 2 = 50 columns > 48: the call becomes a split-K
+    # prefill, whose checks (pool dtype, workspace) still run before any launch
+    assert decode_ex(L, q_len=25, kvd=1) == 3
+    assert decode_ex(L, q_len=25, ws_bytes=16) == 4
+    assert decode_ex(L, q_len=25, ws=None) == 4
+    # 9 tokens x g = 2 = 18 columns: two column blocks of the decode kernel
     assert decode_ex(L, q_len=9, kvd=1) == 3
     assert decode_ex(L, q_len=9, ws_bytes=16) == 4
-    assert decode_ex(L, q_len=9, ws=None) == 4
     assert decode_ex(L, kvd=1) == 3
     assert decode_ex(L, ws_bytes=16) == 4
 
@@ -296,16 +299,19 @@ def test_prefill_persistent_validation(L):
 
 
 def test_wide_multi_token_decode_workspace(L):
-    # 5 tokens x g = 8: routed through the split-K prefill; its workspace is
-    # the row offsets and chunk starts (2 batch + 1 ints, padded to 256
-    # bytes) plus the prefill's partials for batch x q_len rows over the
-    # decode's default ranges (1792 keys at batch 64, max 28672 keys)
-    routed = L.attn_decode_splitk_ex_workspace_size(64, 5, 32, 4, 28672, 0)
-    part = L.attn_prefill_hd512_splitk_workspace_size(64, 5, 320, 32, 4, 28672, 1792)
-    assert routed == 768 + part and part == 16 * 320 * 32 * 514 * 4
-    assert L.attn_decode_splitk_ex_workspace_size(64, 5, 32, 4, 28672, 4096) == \
-        768 + L.attn_prefill_hd512_splitk_workspace_size(64, 5, 320, 32, 4, 28672, 4096)
-    assert L.attn_decode_splitk_ex_workspace_size(64, 2, 32, 4, 28672, 0) > 0   # g x q_len = 16
+    # up to 48 (token, head) columns per KV head the decode kernels run:
+    # (O, m, l) partials per split and column, 4 slots per column reserved
+    # (1792-key ranges at batch 64, max 28672 keys: 16 splits)
+    dec = L.attn_decode_splitk_ex_workspace_size(64, 5, 32, 4, 28672, 0)   # 40 columns
+    assert dec == 64 * 5 * 32 * 16 * 4 * 514 * 4
+    # 7 tokens x g = 8 = 56 columns: routed through the split-K prefill; its
+    # workspace is the row offsets and chunk starts (2 batch + 1 ints, padded
+    # to 256 bytes) plus the prefill's partials for batch x q_len rows
+    routed = L.attn_decode_splitk_ex_workspace_size(64, 7, 32, 4, 28672, 0)
+    part = L.attn_prefill_hd512_splitk_workspace_size(64, 7, 448, 32, 4, 28672, 1792)
+    assert routed == 768 + part and part == 16 * 448 * 32 * 514 * 4
+    assert L.attn_decode_splitk_ex_workspace_size(64, 7, 32, 4, 28672, 4096) == \
+        768 + L.attn_prefill_hd512_splitk_workspace_size(64, 7, 448, 32, 4, 28672, 4096)
 
 
 def test_probe_validation(L):

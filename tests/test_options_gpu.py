@@ -1,6 +1,7 @@
 """GPU parity of the extended entry points against the CPU oracle: multi-token
-decode (q_len query tokens per sequence at its last positions; calls with
-more than 16 (token, head) columns per KV head run as split-K prefill),
+decode (q_len query tokens per sequence at its last positions, up to three
+blocks of 16 (token, head) columns per KV head in the decode kernels; wider
+calls run as split-K prefill),
 attention sinks and the log-sum-exp output, for prefill and decode, bf16 and
 FP8 pools.
 
@@ -64,11 +65,16 @@ DECODE = [
     ([260, 900, 5], 5, 6, 3, 256),          # g = 2, q_len 5: 10 columns
     ([4096, 4097, 2049], 4, 16, 4, 0),      # g = 4, 16 columns, library default split
     ([777, 1024], 1, 16, 1, 256),            # g = 16, q_len 1
-    # more than 16 columns: routed through the split-K prefill
+    # two and three 16-column blocks per split workgroup
     ([257, 1000, 64, 2049], 3, 32, 4, 256),  # g = 8, q_len 3: 24 columns
     ([5, 300, 4100], 5, 32, 4, 0),           # g = 8, q_len 5, kv_len = q_len, default split
     ([700, 129], 2, 16, 1, 256),             # g = 16, q_len 2: 32 columns
     ([100, 33], 17, 4, 4, 256),              # g = 1, q_len 17
+    ([300, 48, 1100], 12, 16, 4, 512),       # g = 4, q_len 12: 48 columns
+    # more than 48 columns: routed through the split-K prefill
+    ([257, 1000, 7, 2049], 7, 32, 4, 256),   # g = 8, q_len 7: 56 columns
+    ([700, 129], 4, 16, 1, 0),               # g = 16, q_len 4: 64 columns
+    ([100, 64], 50, 4, 4, 256),              # g = 1, q_len 50
 ]
 
 
@@ -101,8 +107,8 @@ def test_multi_token_decode_bf16_out(A):
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
 def test_multi_token_decode_b64_q5_g8(A, kv_dtype):
     # the current token plus a 4-token draft at 32/4 heads, batch 64, lengths
-    # U{4096..28672}: 40 columns per KV head, so the call runs as split-K
-    # prefill.  Every sequence is checked: its 5 tokens on the 8 heads of one
+    # U{4096..28672}: 40 columns per KV head (three column blocks of the
+    # decode kernels).  Every sequence is checked: its 5 tokens on the 8 heads of one
     # KV group (rotating over the groups) and head 0 of the others.
     case = W.decode_mtp_b64(device="cuda", kv_dtype=kv_dtype)
     lc = case.launches[0]

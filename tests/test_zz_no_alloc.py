@@ -70,14 +70,16 @@ def test_noalloc_matches_workspace_entry_point_two_calls(A):
     _pair(A, small, q_len=2, sinks=sinks, with_lse=True)
 
 
-def test_noalloc_routed_multi_token_decode(A):
-    # 3 tokens at g = 8 (24 columns per KV head): both entry points run the
-    # call as split-K prefill, the no-alloc one with its row offsets and
-    # partials in the static scratch
-    print("[case] noalloc routed: 4 sequences x 3 tokens, 32/4 heads, bf16", flush=True)
+@pytest.mark.parametrize("q_len", [5, 7])
+def test_noalloc_wide_multi_token_decode(A, q_len):
+    # g = 8: 5 tokens are three column blocks of the decode kernels, 7 tokens
+    # (56 columns) run as split-K prefill, the no-alloc call with its row
+    # offsets and partials in the static scratch
+    print(f"[case] noalloc multi-token: 4 sequences x {q_len} tokens, 32/4 heads, bf16",
+          flush=True)
     lens = [257, 1000, 64, 2049]
-    case = W.build_case("noalloc_routed", seqs=[(3, L - 3, L) for L in lens], hq=32, hkv=4,
-                        seed=13, out_dtype="fp32", device="cuda")
-    got = _pair(A, case, q_len=3, with_lse=True)
+    case = W.build_case("noalloc_wide", seqs=[(q_len, L - q_len, L) for L in lens], hq=32,
+                        hkv=4, seed=13, out_dtype="fp32", device="cuda")
+    got = _pair(A, case, q_len=q_len, with_lse=True)
     ref = oracle.attend_all(case.to("cpu"))
-    check_parity(got, ref, "noalloc routed decode q_len=3 g=8")
+    check_parity(got, ref, f"noalloc decode q_len={q_len} g=8")
