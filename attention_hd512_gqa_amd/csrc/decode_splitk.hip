@@ -241,18 +241,21 @@ __device__ __forceinline__ void issue_tile(const char* src, int valid, ATTN_LDS 
 }
 
 // One 64-key tile (= one page of one KV head) at a time per workgroup of 4
-// waves, NC blocks of 16 (token, head) columns.  K and V tiles are DMA'd to
-// separate LDS buffers.  Wave w owns keys 16 w .. 16 w + 15: it computes
-// their scores for every column block (one K operand read serves all NC
+// waves, NC blocks of 16 (token, head) columns.  Wave w DMAs keys 16 w ..
+// 16 w + 15 of each K and V tile into LDS; it alone reads those K rows, so
+// it refills them as soon as its own reads have returned.  It computes its
+// keys' scores for every column block (one K operand read serves all NC
 // blocks) and, once the four waves have exchanged their per-column maxima
-// through LDS, their probabilities, which it writes to LDS as bf16.  Every
-// wave then accumulates its own 128 of the 512 output dims over all 64 keys,
-// reading each V operand once for all blocks.  A column's probabilities are
-// taken against a reference maximum that moves only when a tile's maximum
-// exceeds it by more than kTileMargin (log2 units), so the accumulators are
-// rarely rescaled; l sums the bf16 probabilities the PV products use.  FP8:
-// the tiles hold E4M3 bytes, widened exactly to bf16 as each operand is read
-// (k_scale is in the softmax scale, v_scale in the partial).
+// through LDS, their probabilities, which it writes to LDS as bf16; after a
+// second barrier it accumulates its own 128 of the 512 output dims over all
+// 64 keys, reading each V operand once for all blocks, and a third barrier
+// frees the V buffer.  A column's probabilities are taken against a
+// reference maximum that moves only when a tile's maximum exceeds it by more
+// than kTileMargin (log2 units), so the accumulators are rarely rescaled; l
+// sums the bf16 probabilities the PV products use.  FP8: the tiles hold E4M3
+// bytes, widened exactly to bf16 as each operand is read (k_scale is in the
+// softmax scale, v_scale in the partial); their 32 KB tiles fit twice over,
+// so tile t + 2 loads while tile t is consumed.
 constexpr float kTileMargin = 8.f;
 constexpr int kPStride = 2 * kPage + 16;   // bytes per column row of the P buffer
 
@@ -270,13 +273,14 @@ void decode_split_tile_kernel(DecodeArgs a) {
     constexpr int kTB = FP8 ? kPage * kHeadDim : kTileBytes;   // one K or V tile
     constexpr int kLoads = FP8 ? kPage / 8 : kPage / kDecWaves;  // DMAs per wave per tile
     constexpr int kCols = NC * kDecRows;
+    constexpr int kDepth = FP8 ? 2 : 1;   // tiles in flight per operand
     __shared__ __attribute__((aligned(1024)))
-        char smem[2 * kTB + kCols * kPStride + kCols * kDecWaves * 4];
+        char smem[2 * kDepth * kTB + kCols * kPStride + kCols * kDecWaves * 4];
     SplitPlan p;
     if (!plan_split(a, p)) return;
-    ATTN_LDS char* sK = (ATTN_LDS char*)smem;
-    ATTN_LDS char* sV = sK + kTB;
-    ATTN_LDS char* sP = sV + kTB;                               // [column][64 keys] bf16
+    ATTN_LDS char* sK0 = (ATTN_LDS char*)smem;                  // K buffers, then V buffers
+    ATTN_LDS char* sV0 = sK0 + kDepth * kTB;
+    ATTN_LDS char* sP = sV0 + kDepth * kTB;                      // [column][64 keys] bf16
     ATTN_LDS float* sM = (ATTN_LDS float*)(sP + kCols * kPStride);  // [column][wave]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -299,9 +303,9 @@ void decode_split_tile_kernel(DecodeArgs a) {
             qf[cb][ks] = col[cb].ok ? v : bf16x8{};
         }
     }
-    // K operand: key row 16 wave + n.  bf16: chunk 4 ks + kq, with ks = 4 u +
-    // v at byte koff[v] + 256 u.  FP8: read i (chunk 4 i + kq) at
-    // krow + ((4 i + kq) ^ ksw) * 16.
+    // K operand: key row 16 wave + n (the tile layouts of issue_tile).  bf16:
+    // chunk 4 ks + kq, with ks = 4 u + v at byte koff[v] + 256 u.  FP8: read i
+    // (chunk 4 i + kq) at krow + ((4 i + kq) ^ ksw) * 16.
     int koff[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
@@ -338,18 +342,28 @@ void decode_split_tile_kernel(DecodeArgs a) {
     }
 
     constexpr int kPoolTile = FP8 ? kTileBytes / 2 : kTileBytes;
-    auto valid_of = [&](int t) { return min(p.k_end - (p.k_begin + t * kPage), kPage); };
-    {
-        const int pg = split_page(a, p, 0);
-        issue_tile<FP8>(tile_base(a.k_pages, a, pg, p.kvh, kPoolTile), valid_of(0), sK, wave, lane);
-        issue_tile<FP8>(tile_base(a.v_pages, a, pg, p.kvh, kPoolTile), valid_of(0), sV, wave, lane);
+    // keys of tile t below k_end (0 past the split: such loads are
+    // zero-length, so with kDepth 2 every step issues the same loads)
+    auto valid_of = [&](int t) { return max(min(p.k_end - (p.k_begin + t * kPage), kPage), 0); };
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+        const int pg = split_page(a, p, d);
+        issue_tile<FP8>(tile_base(a.k_pages, a, pg, p.kvh, kPoolTile), valid_of(d),
+                        sK0 + d * kTB, wave, lane);
+        issue_tile<FP8>(tile_base(a.v_pages, a, pg, p.kvh, kPoolTile), valid_of(d),
+                        sV0 + d * kTB, wave, lane);
     }
     for (int t = 0; t < p.ntiles; ++t) {
         const int key0 = p.k_begin + t * kPage;
         const bool more = t + 1 < p.ntiles;
-        const int pg_next = split_page(a, p, t + 1);   // arrives by the next barrier
-        wait_vmcnt<kLoads>();   // K(t) in; V(t) may still be in flight
-        lds_barrier();
+        const int buf = kDepth == 2 ? (t & 1) : 0;
+        const ATTN_LDS char* sK = sK0 + buf * kTB;
+        const ATTN_LDS char* sV = sV0 + buf * kTB;
+        // the tile this step's refills bring: t + kDepth
+        const int pg_next = split_page(a, p, t + kDepth);
+        // this wave's K(t) rows are in; the loads issued after them (V(t),
+        // and with kDepth 2 also K(t + 1), V(t + 1)) may still be in flight
+        wait_vmcnt<(2 * kDepth - 1) * kLoads>();
 
         // S^T[16 keys of this wave][16 columns] per block, over 512 dims
         f32x4 s[NC];
@@ -375,6 +389,13 @@ void decode_split_tile_kernel(DecodeArgs a) {
                 for (int cb = 0; cb < NC; ++cb) s[cb] = mfma16x16x32(kv, qf[cb][ks], s[cb]);
             }
         }
+        // this wave's K rows are free once its reads have returned
+        wait_lgkmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kDepth == 2 || more)
+            issue_tile<FP8>(tile_base(a.k_pages, a, pg_next, p.kvh, kPoolTile),
+                            valid_of(t + kDepth), sK0 + buf * kTB, wave, lane);
+
         // element i: key 16 wave + 4 kq + i of column 16 cb + n, in log2
         // units; keys a column may not see are -inf (only in the tiles that
         // reach past k_end - q_len: earlier keys are visible to every column)
@@ -394,10 +415,7 @@ void decode_split_tile_kernel(DecodeArgs a) {
             mt = fmaxf(mt, __shfl_xor(mt, 32));
             if (kq == 0) sM[(16 * cb + n) * kDecWaves + wave] = mt;
         }
-        lds_barrier();  // column maxima visible; every wave is done with sK
-        if (more)
-            issue_tile<FP8>(tile_base(a.k_pages, a, pg_next, p.kvh, kPoolTile), valid_of(t + 1),
-                            sK, wave, lane);
+        lds_barrier();  // column maxima visible
 
         // the tile's maximum per column moves the reference when it exceeds it
         // by more than the margin (the first tile with a visible key always
@@ -438,8 +456,15 @@ void decode_split_tile_kernel(DecodeArgs a) {
             *(ATTN_LDS bf16x4*)(sP + (16 * cb + n) * kPStride + (16 * wave + 4 * kq) * 2) = pw;
         }
 
-        if (more) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
-        lds_barrier();  // P and V(t) visible
+        // this wave's V(t) rows are in: after them were issued K(t + 1) with
+        // kDepth 1 (none on the last tile); K(t + 1), V(t + 1) and K(t + 2)
+        // with kDepth 2
+        if constexpr (kDepth == 2) {
+            wait_vmcnt<3 * kLoads>();
+        } else {
+            if (more) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
+        }
+        lds_barrier();  // P and every wave's V(t) rows visible
 
         // P^T operand: keys 32 c + 8 kq .. + 7 of column 16 cb + n
         bf16x8 pf[NC][2];
@@ -474,11 +499,12 @@ void decode_split_tile_kernel(DecodeArgs a) {
                 for (int cb = 0; cb < NC; ++cb) o[cb][db] = mfma16x16x32(vt, pf[cb][c], o[cb][db]);
             }
         }
-        lds_barrier();  // every wave is done with sV, sP and sM
-        if (more)
-            issue_tile<FP8>(tile_base(a.v_pages, a, pg_next, p.kvh, kPoolTile), valid_of(t + 1),
-                            sV, wave, lane);
+        lds_barrier();  // every wave is done with this V buffer
+        if (kDepth == 2 || more)
+            issue_tile<FP8>(tile_base(a.v_pages, a, pg_next, p.kvh, kPoolTile),
+                            valid_of(t + kDepth), sV0 + buf * kTB, wave, lane);
     }
+    if constexpr (kDepth == 2) wait_vmcnt<0>();   // the zero-length loads past the split
     const size_t slot0 = (((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub * a.cols;
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb)
