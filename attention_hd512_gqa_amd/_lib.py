@@ -7,6 +7,7 @@ If the library is not built, every call raises: there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -15,12 +16,15 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn_hd512.so")
+# the same kernels with wave-dependent sleeps around every LDS hand-off
+DELAY_LIB_PATH = os.path.join(_HERE, "libattn_hd512_delay.so")
 
 ATTN_BF16, ATTN_FP32, ATTN_FP8_E4M3 = 0, 1, 2
 _DTYPE_CODES = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_FP32}
 _KV_CODES = {"bf16": ATTN_BF16, "fp8_e4m3": ATTN_FP8_E4M3}
 
 _lib = None
+_delay_lib = None
 
 
 class AttnError(RuntimeError):
@@ -31,67 +35,89 @@ def lib() -> ctypes.CDLL:
     """The loaded library; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise AttnError(f"{LIB_PATH} is missing: build it with "
-                            "`python -m attention_hd512_gqa_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        L.attn_prefill_hd512.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P]
-        L.attn_prefill_hd512.restype = I
-        L.attn_prefill_hd512_e4m3.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I, I, I, I, I,
-                                              I, F, P, I, P]
-        L.attn_prefill_hd512_e4m3.restype = I
-        L.attn_prefill_hd512_ex.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I, I,
-                                            I, I, F, P, P, I, P, P]
-        L.attn_prefill_hd512_ex.restype = I
-        L.attn_prefill_hd512_e4m3_mma.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I, I, I,
-                                                  I, I, I, F, P, P, I, P, P]
-        L.attn_prefill_hd512_e4m3_mma.restype = I
-        L.attn_prefill_hd512_append.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
-                                                I, I, I, F, P, P, I, P, P]
-        L.attn_prefill_hd512_append.restype = I
-        L.attn_prefill_hd512_persistent_workspace_size.argtypes = []
-        L.attn_prefill_hd512_persistent_workspace_size.restype = SZ
-        L.attn_prefill_hd512_persistent.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I,
-                                                    I, I, I, I, F, P, P, SZ, P, I, P, P]
-        L.attn_prefill_hd512_persistent.restype = I
-        L.attn_prefill_swa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, F,
-                                       P, I, P]
-        L.attn_prefill_swa.restype = I
-        L.attn_prefill_hd512_splitk_workspace_size.argtypes = [I, I, I, I, I, I, I]
-        L.attn_prefill_hd512_splitk_workspace_size.restype = SZ
-        L.attn_prefill_hd512_splitk.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I,
-                                                I, I, I, I, I, F, P, P, SZ, P, I, P, P]
-        L.attn_prefill_hd512_splitk.restype = I
-        L.attn_prefill_hd512_splitk_e4m3_mma.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I,
-                                                         I, I, I, I, I, I, I, F, P, P, SZ, P, I,
-                                                         P, P]
-        L.attn_prefill_hd512_splitk_e4m3_mma.restype = I
-        L.attn_decode_splitk_ex_workspace_size.argtypes = [I, I, I, I, I, I]
-        L.attn_decode_splitk_ex_workspace_size.restype = SZ
-        L.attn_decode_splitk_ex.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, I,
-                                            F, P, P, SZ, P, I, P, P]
-        L.attn_decode_splitk_ex.restype = I
-        L.attn_decode_splitk_ex_noalloc.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I,
-                                                    I, I, I, F, P, P, I, P, P]
-        L.attn_decode_splitk_ex_noalloc.restype = I
-        L.attn_append_kv.argtypes = [P, P, I, F, F, P, P, P, I, I, I, I, I, I, I, P, P, P]
-        L.attn_append_kv.restype = I
-        L.attn_decode_splitk_workspace_size.argtypes = [I, I, I, I, I]
-        L.attn_decode_splitk_workspace_size.restype = SZ
-        L.attn_decode_splitk.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, F,
-                                         P, SZ, P, I, P]
-        L.attn_decode_splitk.restype = I
-        L.attn_hbm_read_probe.argtypes = [P, SZ, P, P]
-        L.attn_hbm_read_probe.restype = I
-        L.attn_hbm_probe_sink_words.argtypes = [SZ]
-        L.attn_hbm_probe_sink_words.restype = SZ
-        L.attn_clock_stamps.argtypes = [P, I, P]
-        L.attn_clock_stamps.restype = I
-        L.attn_status_string.argtypes = [I]
-        L.attn_status_string.restype = ctypes.c_char_p
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def delay_injected():
+    """Within the block every call of this module runs on the delay-injected
+    build (libattn_hd512_delay.so), whose kernels sleep for wave-dependent
+    times after every LDS refill load and before every workgroup barrier;
+    the race tests check that it reproduces the normal build's results."""
+    global _lib, _delay_lib
+    if _delay_lib is None:
+        _delay_lib = _load(DELAY_LIB_PATH)
+    saved = lib()
+    _lib = _delay_lib
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _load(path: str) -> ctypes.CDLL:
+    """Opens one build of the library and declares every entry point."""
+    if not os.path.exists(path):
+        raise AttnError(f"{path} is missing: build it with "
+                        "`python -m attention_hd512_gqa_amd.build`")
+    L = ctypes.CDLL(path)
+    P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_prefill_hd512.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P]
+    L.attn_prefill_hd512.restype = I
+    L.attn_prefill_hd512_e4m3.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I, I, I, I, I,
+                                          I, F, P, I, P]
+    L.attn_prefill_hd512_e4m3.restype = I
+    L.attn_prefill_hd512_ex.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I, I,
+                                        I, I, F, P, P, I, P, P]
+    L.attn_prefill_hd512_ex.restype = I
+    L.attn_prefill_hd512_e4m3_mma.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I, I, I,
+                                              I, I, I, F, P, P, I, P, P]
+    L.attn_prefill_hd512_e4m3_mma.restype = I
+    L.attn_prefill_hd512_append.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                            I, I, I, F, P, P, I, P, P]
+    L.attn_prefill_hd512_append.restype = I
+    L.attn_prefill_hd512_persistent_workspace_size.argtypes = []
+    L.attn_prefill_hd512_persistent_workspace_size.restype = SZ
+    L.attn_prefill_hd512_persistent.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I,
+                                                I, I, I, I, F, P, P, SZ, P, I, P, P]
+    L.attn_prefill_hd512_persistent.restype = I
+    L.attn_prefill_swa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, F,
+                                   P, I, P]
+    L.attn_prefill_swa.restype = I
+    L.attn_prefill_hd512_splitk_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    L.attn_prefill_hd512_splitk_workspace_size.restype = SZ
+    L.attn_prefill_hd512_splitk.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I, I,
+                                            I, I, I, I, I, F, P, P, SZ, P, I, P, P]
+    L.attn_prefill_hd512_splitk.restype = I
+    L.attn_prefill_hd512_splitk_e4m3_mma.argtypes = [P, P, P, F, F, P, P, P, P, I, I, I, I,
+                                                     I, I, I, I, I, I, I, F, P, P, SZ, P, I,
+                                                     P, P]
+    L.attn_prefill_hd512_splitk_e4m3_mma.restype = I
+    L.attn_decode_splitk_ex_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.attn_decode_splitk_ex_workspace_size.restype = SZ
+    L.attn_decode_splitk_ex.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, I,
+                                        F, P, P, SZ, P, I, P, P]
+    L.attn_decode_splitk_ex.restype = I
+    L.attn_decode_splitk_ex_noalloc.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I,
+                                                I, I, I, F, P, P, I, P, P]
+    L.attn_decode_splitk_ex_noalloc.restype = I
+    L.attn_append_kv.argtypes = [P, P, I, F, F, P, P, P, I, I, I, I, I, I, I, P, P, P]
+    L.attn_append_kv.restype = I
+    L.attn_decode_splitk_workspace_size.argtypes = [I, I, I, I, I]
+    L.attn_decode_splitk_workspace_size.restype = SZ
+    L.attn_decode_splitk.argtypes = [P, P, P, I, F, F, P, P, I, I, I, I, I, I, I, I, I, F,
+                                     P, SZ, P, I, P]
+    L.attn_decode_splitk.restype = I
+    L.attn_hbm_read_probe.argtypes = [P, SZ, P, P]
+    L.attn_hbm_read_probe.restype = I
+    L.attn_hbm_probe_sink_words.argtypes = [SZ]
+    L.attn_hbm_probe_sink_words.restype = SZ
+    L.attn_clock_stamps.argtypes = [P, I, P]
+    L.attn_clock_stamps.restype = I
+    L.attn_status_string.argtypes = [I]
+    L.attn_status_string.restype = ctypes.c_char_p
+    return L
 
 
 def status_string(code: int) -> str:

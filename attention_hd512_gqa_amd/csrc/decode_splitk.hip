@@ -237,6 +237,7 @@ __device__ __forceinline__ void issue_tile(const char* src, int valid, ATTN_LDS 
                 : "v"(voff), "s"(lds + 2 * i * kHeadDim), "s"(rsrc)
                 : "memory", "m0");
         }
+        race_delay<0>();
     }
 }
 
@@ -537,6 +538,7 @@ __device__ __forceinline__ void dma_half(const char* src, int rows, ATTN_LDS cha
             : "v"(voff), "s"(lds + 2 * i * kHeadDim), "s"(rsrc)
             : "memory", "m0");
     }
+    race_delay<0>();
 }
 
 // K operand of key group gm (keys 16 gm .. 16 gm + 15), read i: key

@@ -49,6 +49,23 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+// Timing perturbation of the delay-injected test build (-DATTN_RACE_DELAY):
+// 0 to 3 naps of about 128 cycles, the count set by the wave, the workgroup
+// and the call site, after every LDS refill load and before every workgroup
+// barrier.  The waves of a workgroup then reach each hand-off in other
+// orders and at other distances than in the normal build, so a missing wait
+// or barrier changes the results; the kernels are deterministic, so the
+// delayed build must reproduce the normal build's bits.  Nothing is emitted
+// in the normal build.
+template <int SITE>
+__device__ __forceinline__ void race_delay() {
+#ifdef ATTN_RACE_DELAY
+    const int k = (__builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) + (int)blockIdx.x +
+                   SITE) & 3;
+    for (int i = 0; i < k; ++i) __builtin_amdgcn_s_sleep(2);
+#endif
+}
+
 // Words of a raw buffer resource over `bytes` bytes at `base` (gfx9: stride 0,
 // 32-bit data format).  Loads at offsets >= bytes return zeros.
 __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
@@ -101,6 +118,7 @@ __device__ __forceinline__ void dma_row(u32x4 rsrc, uint32_t lds_base, uint32_t 
             : "i"(SWZ | REL), "v"(lane_off), "i"(REL), "s"(lds_base), "s"(rsrc), "s"(soff)
             : "memory", "m0", "scc");
     }
+    race_delay<0>();
 }
 
 // Compile-time loop: f(std::integral_constant<int, i>{}) for i = 0 .. N-1, so
@@ -131,6 +149,7 @@ __device__ __forceinline__ void rows16_to_lds(u32x4 rsrc, const ATTN_LDS char* b
 // then s_barrier.  No memory-model fence, hence no implicit wait for the
 // vector-memory loads still in flight (those are waited for explicitly).
 __device__ __forceinline__ void lds_barrier() {
+    race_delay<1>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 

@@ -185,6 +185,7 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillArgs& a, f32x16 (&
     constexpr int kOutRowB = D * 2;
     if constexpr (STAGE) {
         wait_vmcnt<0>();     // every wave's refills have landed ...
+        race_delay<2>();
         __syncthreads();     // ... and no wave reads the tiles any more
         ATTN_LDS char* stage = smem + wave * 32 * kOutRowB;
 #pragma unroll

@@ -383,6 +383,7 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     const int* ptab = a.page_table + (size_t)b * a.max_pages;
     const int staged = min(ntiles, kPagesInLds);
     for (int i = threadIdx.x; i < staged; i += kThreads) sPage[i] = ptab[kt_lo + i];
+    race_delay<2>();
     __syncthreads();
     auto page_of = [&](int tile) -> int {
         return tile < kPagesInLds ? __builtin_amdgcn_readfirstlane(sPage[tile])

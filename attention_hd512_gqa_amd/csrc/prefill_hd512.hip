@@ -148,6 +148,7 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t m0, uint32_t soff, in
         :
         : "v"(voff), "s"(m0), "s"(rsrc), "s"(soff)
         : "memory", "m0");
+    race_delay<0>();
 }
 
 // Row J of a wave's 8 at J * stride bytes past byte soff of the resource (a
@@ -166,6 +167,7 @@ __device__ __forceinline__ void dma_row_strided(u32x4 rsrc, uint32_t lds_base, u
         : "i"(SWZ), "v"(lane_off), "i"(J), "s"(stride), "s"(lds_base), "i"(REL), "s"(rsrc),
           "s"(soff)
         : "memory", "m0", "scc");
+    race_delay<0>();
 }
 
 // Refill load J of this wave's share of a half: 1 KB rows, row 8 wave + J of
@@ -763,6 +765,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
         // older than every refill load, so the loop's counted waits stay safe)
         if (nlo + nhi > 0) wait_vmcnt<0>();
     }
+    race_delay<2>();
     __syncthreads();
     auto page_of = [&](int tile) -> int {
         return tile - kt_lo < kPagesInLds ? __builtin_amdgcn_readfirstlane(sPage[tile - kt_lo])
@@ -992,6 +995,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
         // all leave the loop together.
         __shared__ int sUnit;
         if (threadIdx.x == 0) sUnit = take();
+        race_delay<2>();
         __syncthreads();
         for (;;) {
             const int unit = sUnit;
@@ -1006,6 +1010,7 @@ void prefill_hd512_kernel(PrefillArgs a) {
             // every wave is done with them (the unit's loads have all landed;
             // its output stores may still be in flight: they only lengthen the
             // next unit's counted waits, which then cover older operations)
+            race_delay<2>();
             __syncthreads();
         }
     } else {

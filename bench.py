@@ -453,18 +453,18 @@ def main():
             us = t["ms"] * 1e3
             nbytes = W.decode_kv_bytes(ml.kv_lens, mc.num_kv_heads, W.HEAD_DIM,
                                        1 if kv_dtype == "fp8_e4m3" else 2)
-            flops = W.prefill_flops(ml.q_lens, ml.q_starts, ml.kv_lens, mc.num_q_heads)
+            mflops = W.prefill_flops(ml.q_lens, ml.q_starts, ml.kv_lens, mc.num_q_heads)
             gbps = nbytes / (us * 1e-6) / 1e9
             decode_mtp[kv_dtype] = {
                 "workload": mc.name, "q_len": q_len, "us_per_call": us,
                 "us_min": t["ms_min"] * 1e3, "us_max": t["ms_max"] * 1e3, "kv_bytes": nbytes,
                 "GB_per_s": gbps, "frac_of_hbm_probe": gbps / hbm_read,
-                "useful_TFLOP_per_s": flops / (us * 1e-6) / 1e12,
+                "useful_TFLOP_per_s": mflops / (us * 1e-6) / 1e12,
                 "kernels": "split (tile kernel, 3 column blocks of 16) + merge",
                 "how": t["how"]}
             log(f"decode q_len={q_len} g=8 {kv_dtype}: {us:.1f} us/call, {gbps:.0f} GB/s "
                 f"({100 * gbps / hbm_read:.1f}% of probe), "
-                f"{flops / (us * 1e-6) / 1e12:.0f} useful TFLOP/s")
+                f"{mflops / (us * 1e-6) / 1e12:.0f} useful TFLOP/s")
             del mc, ml, mout, mws
             torch.cuda.empty_cache()
 
