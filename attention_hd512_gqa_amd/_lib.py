@@ -77,6 +77,9 @@ def _load(path: str) -> ctypes.CDLL:
     L.attn_prefill_hd512_append.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
                                             I, I, I, F, P, P, I, P, P]
     L.attn_prefill_hd512_append.restype = I
+    L.attn_prefill_hd512_e4m3_mma_append.argtypes = [P, P, P, P, P, F, F, P, P, P, P, I, I, I,
+                                                     I, I, I, I, I, I, F, P, P, I, P, P]
+    L.attn_prefill_hd512_e4m3_mma_append.restype = I
     L.attn_prefill_hd512_persistent_workspace_size.argtypes = []
     L.attn_prefill_hd512_persistent_workspace_size.restype = SZ
     L.attn_prefill_hd512_persistent.argtypes = [P, P, P, I, F, F, P, P, P, P, I, I, I, I, I,
@@ -207,26 +210,40 @@ def prefill(q, k_pages, v_pages, page_table, cu_seqlens_q, q_start, kv_lens, out
 
 def prefill_append(q, k_new, v_new, k_pages, v_pages, page_table, cu_seqlens_q, q_start,
                    kv_lens, out, *, total_q: int, max_q_len: int, softmax_scale: float,
+                   kv_dtype: str = "bf16", k_scale: float = 1.0, v_scale: float = 1.0,
                    sinks=None, lse=None, stream=None) -> None:
-    """Chunked causal prefill with the chunk's KV append fused in
-    (attn_prefill_hd512_append): the bf16 rows k_new, v_new [total_q, Hkv, 512]
-    are written into their page slots of the bf16 pool and the chunk's own
-    keys are read from them, giving the same result as append_kv followed by
-    prefill."""
+    """Chunked causal prefill with the chunk's KV append: the bf16 rows
+    k_new, v_new [total_q, Hkv, 512] are written into their page slots and
+    the chunk attends to them, giving the same result as append_kv followed
+    by prefill.  bf16 pool: one fused launch (attn_prefill_hd512_append).
+    E4M3 pool (kv_dtype "fp8_e4m3"): the rows are encoded with k_scale and
+    v_scale and the prefill runs on the FP8 matrix core
+    (attn_prefill_hd512_e4m3_mma_append: the append kernel, then the
+    FP8-MMA prefill, on one stream)."""
     num_pages, hkv, page, d = k_pages.shape
     hq = q.shape[1]
     batch = kv_lens.shape[0]
-    code = lib().attn_prefill_hd512_append(
-        _dev(q, "q", torch.bfloat16), _dev(k_new, "k_new", torch.bfloat16),
-        _dev(v_new, "v_new", torch.bfloat16), _dev(k_pages, "k_pages", torch.bfloat16),
-        _dev(v_pages, "v_pages", torch.bfloat16), _dev(page_table, "page_table", torch.int32),
-        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(q_start, "q_start", torch.int32),
-        _dev(kv_lens, "kv_lens", torch.int32), int(batch), int(total_q), int(max_q_len),
-        int(hq), int(hkv), int(d), int(page), int(num_pages), int(page_table.shape[1]),
-        float(softmax_scale), _opt(sinks, "sinks", torch.float32, hq),
-        _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
-        _opt(lse, "lse", torch.float32, int(total_q) * hq), _stream(stream))
-    _check(code, "attn_prefill_hd512_append")
+    if kv_dtype not in _KV_CODES:
+        raise AttnError(f"unsupported kv_dtype {kv_dtype!r}")
+    fp8 = kv_dtype == "fp8_e4m3"
+    kvt = torch.uint8 if fp8 else torch.bfloat16
+    head = (_dev(q, "q", torch.bfloat16), _dev(k_new, "k_new", torch.bfloat16),
+            _dev(v_new, "v_new", torch.bfloat16), _dev(k_pages, "k_pages", kvt),
+            _dev(v_pages, "v_pages", kvt))
+    rest = (_dev(page_table, "page_table", torch.int32),
+            _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32), _dev(q_start, "q_start", torch.int32),
+            _dev(kv_lens, "kv_lens", torch.int32), int(batch), int(total_q), int(max_q_len),
+            int(hq), int(hkv), int(d), int(page), int(num_pages), int(page_table.shape[1]),
+            float(softmax_scale), _opt(sinks, "sinks", torch.float32, hq),
+            _dev(out, "out", (torch.bfloat16, torch.float32)), _DTYPE_CODES[out.dtype],
+            _opt(lse, "lse", torch.float32, int(total_q) * hq), _stream(stream))
+    if fp8:
+        code = lib().attn_prefill_hd512_e4m3_mma_append(*head, float(k_scale), float(v_scale),
+                                                          *rest)
+        _check(code, "attn_prefill_hd512_e4m3_mma_append")
+    else:
+        code = lib().attn_prefill_hd512_append(*head, *rest)
+        _check(code, "attn_prefill_hd512_append")
 
 
 def prefill_persistent_workspace_size() -> int:

@@ -1158,7 +1158,8 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
                    bool splitk, int max_kv_len, int keys_per_split, void* workspace,
                    size_t workspace_bytes, bool swa, int window, int ring_pages,
                    const void* k_new, const void* v_new, bool fp8_mma, hipStream_t stream,
-                   bool persist = false) {
+                   bool persist = false, bool check_only = false) {
+    // check_only: every check runs, nothing is launched
     // the sliding-window entry is bf16 and single-pass; so is the fused append
     // (given both new-row buffers or neither), at head dim 512 with no window;
     // the FP8-MFMA form is FP8, single-pass, at head dim 512
@@ -1241,6 +1242,7 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
             const long long grid = base * sp.nsplit;
             const long long mgrid = (long long)total_q * num_q_heads;
             if (grid > 0x7fffffffLL || mgrid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+            if (check_only) return ATTN_OK;
             if (fp8_mma)
                 launch_prefill_fp8mma(a, false, true, (unsigned)grid, stream);
             else if (fp8)
@@ -1261,6 +1263,7 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
     }
     const long long grid = base;
     if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    if (check_only && !persist) return ATTN_OK;
     const dim3 gd((unsigned)grid);
     const bool f32 = out_dtype == ATTN_FP32;
     if (persist) {
@@ -1278,6 +1281,7 @@ int prefill_launch(const void* q, const void* k_pages, const void* v_pages, bool
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus < 1)
             return ATTN_ERR_HIP;
+        if (check_only) return ATTN_OK;
         a.unit_counter = (int*)workspace;
         a.total_units = (int)grid;
         const dim3 pg((unsigned)(grid < cus ? grid : cus));
@@ -1435,6 +1439,36 @@ extern "C" int attn_prefill_hd512_append(const void* q, const void* k_new, const
                                 num_kv_heads, head_dim, page_size, num_pages, max_pages_per_seq,
                                 softmax_scale, sinks, out, out_dtype, lse, false, 0, 0, nullptr,
                                 0, false, 0, 0, k_new, v_new, false, stream);
+}
+
+extern "C" int attn_prefill_hd512_e4m3_mma_append(
+    const void* q, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+    float k_scale, float v_scale, const int32_t* page_table, const int32_t* cu_seqlens_q,
+    const int32_t* q_start_pos, const int32_t* kv_lens, int batch, int total_q, int max_q_len,
+    int num_q_heads, int num_kv_heads, int head_dim, int page_size, int num_pages,
+    int max_pages_per_seq, float softmax_scale, const float* sinks, void* out, int out_dtype,
+    float* lse, hipStream_t stream) {
+    if (!k_new || !v_new) return ATTN_ERR_NULL;
+    // every check of both steps runs before the first launch (the append's
+    // are a subset of the prefill's), so a call that fails leaves the pool
+    // as it was
+    int rc = attn::prefill_launch(q, k_pages, v_pages, true, k_scale, v_scale, page_table,
+                                  cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
+                                  num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                                  max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse,
+                                  false, 0, 0, nullptr, 0, false, 0, 0, nullptr, nullptr, true,
+                                  stream, false, true);
+    if (rc != ATTN_OK || total_q == 0 || max_q_len == 0) return rc;
+    rc = attn_append_kv(k_new, v_new, ATTN_FP8_E4M3, k_scale, v_scale, page_table, cu_seqlens_q,
+                        q_start_pos, batch, total_q, num_kv_heads, head_dim, page_size, num_pages,
+                        max_pages_per_seq, k_pages, v_pages, stream);
+    if (rc != ATTN_OK) return rc;
+    return attn::prefill_launch(q, k_pages, v_pages, true, k_scale, v_scale, page_table,
+                                cu_seqlens_q, q_start_pos, kv_lens, batch, total_q, max_q_len,
+                                num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                                max_pages_per_seq, softmax_scale, sinks, out, out_dtype, lse,
+                                false, 0, 0, nullptr, 0, false, 0, 0, nullptr, nullptr, true,
+                                stream);
 }
 
 extern "C" size_t attn_prefill_hd512_persistent_workspace_size(void) {

@@ -492,6 +492,36 @@ int attn_prefill_hd512_append(const void* q, const void* k_new, const void* v_ne
                               hipStream_t stream);
 
 /*
+ * The same call for an FP8-E4M3 pool with both products on the FP8 matrix
+ * core: the chunk's new rows are encoded into the pool as attn_append_kv
+ * (ATTN_FP8_E4M3) encodes them, and the chunk attends to them as codes
+ * (pegainfer issue 1051, "Proposed Plan"; vLLM flash-attention PR 199,
+ * "Summary": FP8 paged KV with FP8 MMA).  Arguments as for
+ * attn_prefill_hd512_append, plus k_scale and v_scale as for
+ * attn_prefill_hd512_e4m3_mma; k_pages and v_pages are E4M3 pools.
+ *
+ * Runs as two launches on `stream`, the append kernel and then the FP8-MMA
+ * prefill, so the output and the pool are bitwise those of attn_append_kv
+ * followed by attn_prefill_hd512_e4m3_mma.  (Encoding the chunk's rows
+ * inside the prefill would put the conversion on the refill path of a
+ * kernel whose VALU issue already sets its pace, and reading them back as
+ * codes would wait on other workgroups' writes; on this hardware even the
+ * bf16 fused launch does not beat the two launches.)  Every argument of both
+ * steps is checked before the first launch: a call that returns an error
+ * leaves the pool untouched.  ATTN_ERR_NULL for a missing k_new or v_new.
+ */
+int attn_prefill_hd512_e4m3_mma_append(const void* q, const void* k_new, const void* v_new,
+                                       void* k_pages, void* v_pages, float k_scale,
+                                       float v_scale, const int32_t* page_table,
+                                       const int32_t* cu_seqlens_q, const int32_t* q_start_pos,
+                                       const int32_t* kv_lens, int batch, int total_q,
+                                       int max_q_len, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int page_size, int num_pages,
+                                       int max_pages_per_seq, float softmax_scale,
+                                       const float* sinks, void* out, int out_dtype, float* lse,
+                                       hipStream_t stream);
+
+/*
  * Measurement helper: streams `bytes` (a multiple of 16) of device memory
  * once with 16-byte loads and writes one word per workgroup to `sink`
  * (at least attn_hbm_probe_sink_words(bytes) uint32 values).  Used to take

@@ -210,6 +210,29 @@ def test_prefill_append_validation(L):
     assert pa(total_q=0, max_q_len=0) == 0
 
 
+def test_prefill_e4m3_mma_append_validation(L):
+    # every check of the append and of the prefill runs before the first
+    # launch; only rejected calls and the empty one are made here
+    def pa(**over):
+        a = dict(kn=FAKE, vn=FAKE, ks=1.0, vs=1.0, batch=1, total_q=4, max_q_len=4, hq=8,
+                 hkv=1, d=512, page=64, out_dtype=1)
+        a.update(over)
+        return L.attn_prefill_hd512_e4m3_mma_append(
+            FAKE, a["kn"], a["vn"], FAKE, FAKE, a["ks"], a["vs"], FAKE, FAKE, FAKE, FAKE,
+            a["batch"], a["total_q"], a["max_q_len"], a["hq"], a["hkv"], a["d"], a["page"], 4,
+            4, 0.04, None, FAKE, a["out_dtype"], None, None)
+    assert pa(kn=None) == 1
+    assert pa(vn=None) == 1
+    assert pa(ks=0.0) == 2
+    assert pa(vs=-1.0) == 2
+    assert pa(d=256) == 3
+    assert pa(page=16) == 3
+    assert pa(hq=6, hkv=4) == 2
+    assert pa(out_dtype=2) == 3
+    assert pa(max_q_len=5) == 2            # larger than total_q
+    assert pa(total_q=0, max_q_len=0) == 0
+
+
 def test_prefill_splitk_validation(L):
     def pf(**over):
         a = dict(kvd=0, ks=1.0, vs=1.0, batch=1, total_q=4, max_q_len=4, hq=8, hkv=1, d=512,
