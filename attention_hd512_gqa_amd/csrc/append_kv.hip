@@ -1,7 +1,7 @@
 // Paged KV append for gfx950: writes the key and value rows of a chunk's new
 // tokens into their cache slots, one page of one KV head holding 64
-// consecutive key rows of 512 (the pool "paged at the attention key block,
-// so a key tile is one copy": pegainfer issue 1051, "Proposed Plan").
+// consecutive key rows of 512, so that one page is exactly one key tile of
+// the attention kernels (pegainfer issue 1051, "Proposed Plan").
 //
 // Token i of sequence b sits at position p = q_start_pos[b] + i; its rows go
 // to page page_table[b][p / 64], slot p % 64, for every KV head.  An FP8-E4M3

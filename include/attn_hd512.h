@@ -436,8 +436,8 @@ int attn_decode_splitk_ex_noalloc(const void* q, const void* k_pages, const void
 
 /*
  * Paged KV append: writes a chunk's new key and value rows into their cache
- * slots (the pool paged at the attention key block: pegainfer issue 1051,
- * "Proposed Plan").
+ * slots (one page per key tile of the attention kernels: pegainfer issue
+ * 1051, "Proposed Plan").
  *
  *   k_new, v_new   bf16 [total_q][num_kv_heads][512]; row order as q.
  *   kv_dtype       ATTN_BF16 (rows copied) or ATTN_FP8_E4M3 (each element
@@ -461,8 +461,8 @@ int attn_append_kv(const void* k_new, const void* v_new, int kv_dtype, float k_s
 
 /*
  * Chunked causal prefill with the chunk's paged KV append fused into the same
- * launch, over a bf16 pool at head_dim 512: the pool is paged at the
- * attention key block, so a key tile is one copy (pegainfer issue 1051,
+ * launch, over a bf16 pool at head_dim 512: a page holds exactly one key
+ * tile, so each tile is a single contiguous copy (pegainfer issue 1051,
  * "Proposed Plan"), and the rows a chunk appends are the keys it attends to
  * last.  Arguments as for attn_prefill_hd512_ex with kv_dtype ATTN_BF16,
  * plus:

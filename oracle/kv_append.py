@@ -3,8 +3,8 @@
 Only the tests may import it; the library never does.  Plain numpy written
 from the definition: token i of sequence b sits at position
 p = q_start[b] + i and its key and value rows (every KV head) go to page
-page_table[b][p // page_size], slot p % page_size (the pool "paged at the
-attention key block": pegainfer issue 1051, "Proposed Plan").  Positions
+page_table[b][p // page_size], slot p % page_size (one page per key tile of
+the attention kernels: pegainfer issue 1051, "Proposed Plan").  Positions
 outside the table and page ids outside the pool are skipped.
 
 An FP8-E4M3 pool stores x / scale saturated to +-448 and rounded to the

@@ -25,8 +25,8 @@
  *  - query heads of one KV head are consecutive, so [B,1,Hq*D] and
  *    [B*Hkv, g, D] are one layout (same page and section);
  *  - FP8 keys/values are decoded from the same E4M3 bytes the kernel reads and
- *    scaled per tensor (vLLM flash-attention PR 199, review tables: the error
- *    is taken "on the same e4m3 bytes").
+ *    scaled per tensor (vLLM flash-attention PR 199, review tables: errors
+ *    are measured against a reference that reads the identical E4M3 data).
  *
  * The Flash-Decoding partial and merge (same page, "One KV head breaks the
  * textbook"): a key range [k0, k1) of one row gives the unnormalised
