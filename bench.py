@@ -48,8 +48,8 @@ TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/prefill_common.h",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "172de9ead21e9fc4e9d5372fc15c5745360ed8d6077f2d2626933bd22ce6ada3",
-    "fetch_bytes": 1958925416,
+    "sha256": "482f2ea8564fcba979420681011edabfcbb232b63cd31fc75063d46df6441bc6",
+    "fetch_bytes": 1977008667,
     "write_bytes": 268435456,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
