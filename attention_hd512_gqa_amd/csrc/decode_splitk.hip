@@ -241,6 +241,45 @@ __device__ __forceinline__ void issue_tile(const char* src, int valid, ATTN_LDS 
     }
 }
 
+// S^T += K Q^T on v_mfma_f32_16x16x32_bf16 with the score accumulator in
+// VGPRs and the Q operand in AGPRs (QA) or VGPRs.  With two or three column
+// blocks Q takes 64 registers per block; holding blocks 1.. in AGPRs, read
+// by the MFMA directly, leaves the VGPRs for operand reads in flight.  The
+// asm is opaque to the hazard recognizer, so: FIRST starts the chain from an
+// inline zero accumulator (no VALU write feeds it), NOP puts 5 wait states
+// in front for a K operand a VALU op (the E4M3 widening) has just written,
+// and qk_drain waits out the MFMAs' passes before the scores are read.
+#define ATTN_QK_MFMA(PRE, C) PRE "v_mfma_f32_16x16x32_bf16 %0, %1, %2, " C
+template <bool QA, bool FIRST, bool NOP>
+__device__ __forceinline__ void qk_mfma(f32x4& acc, const bf16x8& k, const bf16x8& q) {
+    // the wait states sit in the same asm as the MFMA, so that nothing is
+    // scheduled between them
+    if constexpr (FIRST && NOP && QA)
+        asm volatile(ATTN_QK_MFMA("s_nop 4\n\t", "0") : "=&v"(acc) : "v"(k), "a"(q));
+    else if constexpr (FIRST && NOP)
+        asm volatile(ATTN_QK_MFMA("s_nop 4\n\t", "0") : "=&v"(acc) : "v"(k), "v"(q));
+    else if constexpr (FIRST && QA)
+        asm volatile(ATTN_QK_MFMA("", "0") : "=&v"(acc) : "v"(k), "a"(q));
+    else if constexpr (FIRST)
+        asm volatile(ATTN_QK_MFMA("", "0") : "=&v"(acc) : "v"(k), "v"(q));
+    else if constexpr (NOP && QA)
+        asm volatile(ATTN_QK_MFMA("s_nop 4\n\t", "%0") : "+v"(acc) : "v"(k), "a"(q));
+    else if constexpr (NOP)
+        asm volatile(ATTN_QK_MFMA("s_nop 4\n\t", "%0") : "+v"(acc) : "v"(k), "v"(q));
+    else if constexpr (QA)
+        asm volatile(ATTN_QK_MFMA("", "%0") : "+v"(acc) : "v"(k), "a"(q));
+    else
+        asm volatile(ATTN_QK_MFMA("", "%0") : "+v"(acc) : "v"(k), "v"(q));
+}
+#undef ATTN_QK_MFMA
+template <int NC>
+__device__ __forceinline__ void qk_drain(f32x4 (&s)[NC]) {
+    if constexpr (NC == 2)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]));
+}
+
 // One 64-key tile (= one page of one KV head) at a time per workgroup of 4
 // waves, NC blocks of 16 (token, head) columns.  Wave w DMAs keys 16 w ..
 // 16 w + 15 of each K and V tile into LDS; it alone reads those K rows, so
@@ -249,14 +288,16 @@ __device__ __forceinline__ void issue_tile(const char* src, int valid, ATTN_LDS 
 // blocks) and, once the four waves have exchanged their per-column maxima
 // through LDS, their probabilities, which it writes to LDS as bf16; after a
 // second barrier it accumulates its own 128 of the 512 output dims over all
-// 64 keys, reading each V operand once for all blocks, and a third barrier
-// frees the V buffer.  A column's probabilities are taken against a
-// reference maximum that moves only when a tile's maximum exceeds it by more
-// than kTileMargin (log2 units), so the accumulators are rarely rescaled; l
-// sums the bf16 probabilities the PV products use.  FP8: the tiles hold E4M3
-// bytes, widened exactly to bf16 as each operand is read (k_scale is in the
-// softmax scale, v_scale in the partial); their 32 KB tiles fit twice over,
-// so tile t + 2 loads while tile t is consumed.
+// 64 keys, reading each V operand once for all blocks.  bf16: a third
+// barrier frees the V buffer for the next tile.  A column's probabilities are
+// taken against a reference maximum that moves only when a tile's maximum
+// exceeds it by more than kTileMargin (log2 units), so the accumulators are
+// rarely rescaled; l sums the bf16 probabilities the PV products use.  FP8:
+// the tiles hold E4M3 bytes, widened exactly to bf16 as each operand is read
+// (k_scale is in the softmax scale, v_scale in the partial); their 32 KB
+// tiles fit twice over, so K(t + 2) loads while tile t is consumed, and V(t +
+// 1) goes out after tile t's first barrier (every wave is then past P.V of
+// tile t - 1, whose buffer it takes): two barriers per tile.
 constexpr float kTileMargin = 8.f;
 constexpr int kPStride = 2 * kPage + 16;   // bytes per column row of the P buffer
 
@@ -362,33 +403,65 @@ void decode_split_tile_kernel(DecodeArgs a) {
         const ATTN_LDS char* sV = sV0 + buf * kTB;
         // the tile this step's refills bring: t + kDepth
         const int pg_next = split_page(a, p, t + kDepth);
-        // this wave's K(t) rows are in; the loads issued after them (V(t),
-        // and with kDepth 2 also K(t + 1), V(t + 1)) may still be in flight
-        wait_vmcnt<(2 * kDepth - 1) * kLoads>();
+        // this wave's K(t) rows are in.  kDepth 1: V(t), issued after them,
+        // may still be in flight.  kDepth 2 (the issue order is K0 V0 K1 V1,
+        // then per step t: K(t + 2), and V(t + 1) from t = 1): of the loads
+        // after K(t), V(t - 1) has landed and at most K(t + 1), V(t) remain
+        // (on the first step also V0 is waited for)
+        wait_vmcnt<(kDepth == 2 ? 2 : 1) * kLoads>();
 
         // S^T[16 keys of this wave][16 columns] per block, over 512 dims
         f32x4 s[NC];
+        if constexpr (NC == 1) {
+            s[0] = f32x4{};
+            if constexpr (FP8) {
 #pragma unroll
-        for (int cb = 0; cb < NC; ++cb) s[cb] = f32x4{};
-        if constexpr (FP8) {
+                for (int i = 0; i < 8; ++i) {
+                    const u32x4 w =
+                        *(const ATTN_LDS u32x4*)(sK + krow + (((4 * i + kq) ^ ksw) << 4));
+                    s[0] = mfma16x16x32(widen8(w[0], w[1]), qf[0][2 * i], s[0]);
+                    s[0] = mfma16x16x32(widen8(w[2], w[3]), qf[0][2 * i + 1], s[0]);
+                }
+            } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const u32x4 w = *(const ATTN_LDS u32x4*)(sK + krow + (((4 * i + kq) ^ ksw) << 4));
-                const bf16x8 k0 = widen8(w[0], w[1]);
-                const bf16x8 k1 = widen8(w[2], w[3]);
-#pragma unroll
-                for (int cb = 0; cb < NC; ++cb) {
-                    s[cb] = mfma16x16x32(k0, qf[cb][2 * i], s[cb]);
-                    s[cb] = mfma16x16x32(k1, qf[cb][2 * i + 1], s[cb]);
+                for (int ks = 0; ks < 16; ++ks) {
+                    const bf16x8 kv =
+                        *(const ATTN_LDS bf16x8*)(sK + koff[ks & 3] + 256 * (ks >> 2));
+                    s[0] = mfma16x16x32(kv, qf[0][ks], s[0]);
                 }
             }
         } else {
+            // block 0's Q in VGPRs, the others' in AGPRs.  The asm MFMAs are
+            // scheduling boundaries, so the K operand reads are prefetched
+            // kAhead k-steps ahead here (E4M3: 8 raw bytes per step, widened
+            // just before its MFMAs)
+            using Raw = typename std::conditional<FP8, unsigned long long, bf16x8>::type;
+            constexpr int kAhead = FP8 ? 4 : 3;
+            auto kread = [&](int ks) -> Raw {
+                if constexpr (FP8)
+                    return *(const ATTN_LDS unsigned long long*)(sK + krow + 8 * (ks & 1) +
+                                                    (((2 * (ks & ~1) + kq) ^ ksw) << 4));
+                else
+                    return *(const ATTN_LDS bf16x8*)(sK + koff[ks & 3] + 256 * (ks >> 2));
+            };
+            Raw kb[kAhead];
 #pragma unroll
-            for (int ks = 0; ks < 16; ++ks) {
-                const bf16x8 kv = *(const ATTN_LDS bf16x8*)(sK + koff[ks & 3] + 256 * (ks >> 2));
-#pragma unroll
-                for (int cb = 0; cb < NC; ++cb) s[cb] = mfma16x16x32(kv, qf[cb][ks], s[cb]);
-            }
+            for (int j = 0; j < kAhead; ++j) kb[j] = kread(j);
+            static_for<16>([&](auto KS) {
+                constexpr int ks = decltype(KS)::value;
+                const Raw raw = kb[ks % kAhead];
+                if constexpr (ks + kAhead < 16) kb[ks % kAhead] = kread(ks + kAhead);
+                bf16x8 kv;
+                if constexpr (FP8)
+                    kv = widen8(unsigned(raw), unsigned(raw >> 32));
+                else
+                    kv = raw;
+                static_for<NC>([&](auto CB) {
+                    constexpr int cb = decltype(CB)::value;
+                    qk_mfma<(cb > 0), (ks == 0), (FP8 && cb == 0)>(s[cb], kv, qf[cb][ks]);
+                });
+            });
+            qk_drain<NC>(s);
         }
         // this wave's K rows are free once its reads have returned
         wait_lgkmcnt0();
@@ -417,6 +490,11 @@ void decode_split_tile_kernel(DecodeArgs a) {
             if (kq == 0) sM[(16 * cb + n) * kDecWaves + wave] = mt;
         }
         lds_barrier();  // column maxima visible
+        // kDepth 2: every wave is past P.V of tile t - 1, so its V buffer
+        // takes tile t + 1 (zero-length past the split)
+        if (kDepth == 2 && t >= 1)
+            issue_tile<FP8>(tile_base(a.v_pages, a, split_page(a, p, t + 1), p.kvh, kPoolTile),
+                            valid_of(t + 1), sV0 + ((t + 1) & 1) * kTB, wave, lane);
 
         // the tile's maximum per column moves the reference when it exceeds it
         // by more than the margin (the first tile with a visible key always
@@ -458,10 +536,10 @@ void decode_split_tile_kernel(DecodeArgs a) {
         }
 
         // this wave's V(t) rows are in: after them were issued K(t + 1) with
-        // kDepth 1 (none on the last tile); K(t + 1), V(t + 1) and K(t + 2)
-        // with kDepth 2
+        // kDepth 1 (none on the last tile); K(t + 2) and V(t + 1) with kDepth 2
+        // (on the first step K1, V1 and K2: V0 is waited for with K1)
         if constexpr (kDepth == 2) {
-            wait_vmcnt<3 * kLoads>();
+            wait_vmcnt<2 * kLoads>();
         } else {
             if (more) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
         }
@@ -500,10 +578,12 @@ void decode_split_tile_kernel(DecodeArgs a) {
                 for (int cb = 0; cb < NC; ++cb) o[cb][db] = mfma16x16x32(vt, pf[cb][c], o[cb][db]);
             }
         }
-        lds_barrier();  // every wave is done with this V buffer
-        if (kDepth == 2 || more)
-            issue_tile<FP8>(tile_base(a.v_pages, a, pg_next, p.kvh, kPoolTile),
-                            valid_of(t + kDepth), sV0 + buf * kTB, wave, lane);
+        if constexpr (kDepth == 1) {
+            lds_barrier();  // every wave is done with the V buffer
+            if (more)
+                issue_tile<FP8>(tile_base(a.v_pages, a, pg_next, p.kvh, kPoolTile),
+                                valid_of(t + 1), sV0, wave, lane);
+        }
     }
     if constexpr (kDepth == 2) wait_vmcnt<0>();   // the zero-length loads past the split
     const size_t slot0 = (((size_t)p.b * a.hkv + p.kvh) * a.max_splits + p.split) * a.sub * a.cols;
