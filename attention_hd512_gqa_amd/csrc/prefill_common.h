@@ -150,8 +150,13 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillArgs& a, f32x16 (&
         }
         return;
     }
-    // o = O / l with an IEEE division (not O * (1/l)), as the definition reads:
-    // with V = 1 it returns exactly 1.
+    // o = O / l, correctly rounded (not O * (1/l)), as the definition reads:
+    // with V = 1 it returns exactly 1.  Every value of the lane shares l, so
+    // one IEEE division gives r = RN(1 / l), and per value q = RN(O r) is
+    // within an ulp of O / l; the remainder O - q l is exact as one fma, and
+    // q + (O - q l) r rounded once is then RN(O / l) (Markstein's correction
+    // step for a correctly rounded reciprocal): three VALU operations per
+    // value instead of a division's ten.
     const float vs = a.v_scale;   // 1 for a bf16 pool
     // A sink (vLLM flash-attention PR 199, second review, finding F4) adds
     // 2^(sink - m_ref) to the denominator in the units of l (log2 units,
@@ -182,6 +187,11 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillArgs& a, f32x16 (&
     // whole row per instruction.  16-byte chunk c of a staged row r sits at
     // chunk c ^ (r & 15), so the 16 rows one write instruction covers fall in
     // distinct bank groups.
+    const float r_l = 1.f / l_tot;
+    auto quot = [&](float x) {
+        const float q = x * r_l;
+        return __builtin_fmaf(__builtin_fmaf(-q, l_tot, x), r_l, q);
+    };
     constexpr int kOutRowB = D * 2;
     if constexpr (STAGE) {
         wait_vmcnt<0>();     // every wave's refills have landed ...
@@ -192,8 +202,8 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillArgs& a, f32x16 (&
         for (int db = 0; db < (D / 32); ++db) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                f32x4 v = {o[db][4 * q4] / l_tot, o[db][4 * q4 + 1] / l_tot,
-                           o[db][4 * q4 + 2] / l_tot, o[db][4 * q4 + 3] / l_tot};
+                f32x4 v = {quot(o[db][4 * q4]), quot(o[db][4 * q4 + 1]),
+                           quot(o[db][4 * q4 + 2]), quot(o[db][4 * q4 + 3])};
                 if constexpr (SCALE_V) v *= vs;
                 const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
                 const int c = 4 * db + q4;   // dims 32 db + 8 q4 .. + 7; this lane's half: 4 h
@@ -225,8 +235,8 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillArgs& a, f32x16 (&
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int d0 = 32 * db + 8 * q4 + 4 * h;
-                f32x4 v = {o[db][4 * q4] / l_tot, o[db][4 * q4 + 1] / l_tot,
-                           o[db][4 * q4 + 2] / l_tot, o[db][4 * q4 + 3] / l_tot};
+                f32x4 v = {quot(o[db][4 * q4]), quot(o[db][4 * q4 + 1]),
+                           quot(o[db][4 * q4 + 2]), quot(o[db][4 * q4 + 3])};
                 if constexpr (SCALE_V) v *= vs;
                 if constexpr (OUT_FP32) {
                     *(f32x4*)((float*)a.out + obase + d0) = v;
