@@ -21,11 +21,11 @@
 // Tile kernel (bf16 pool; FP8 pool with 2 or 3 column blocks): one 64-key tile
 // (= one page of one KV head) at a time per workgroup of 4 waves.  K and V
 // tiles are DMA'd to separate LDS buffers (swizzled rows); wave w computes
-// the scores of keys 16 w .. 16 w + 15 for every column block, the scores
-// meet in a small LDS buffer, every wave runs the softmax of all 64 keys and
-// accumulates its own 128 of the 512 output dims.  Up to 3 blocks (48
-// columns: e.g. 5 tokens at g = 8) keep Q in registers; wider calls run as
-// split-K prefill.
+// the scores and probabilities of keys 16 w .. 16 w + 15 for every column
+// block, the probabilities meet in a small LDS buffer, and every wave
+// accumulates its own 128 of the 512 output dims over all 64 keys.  Up to 3
+// blocks (48 columns: e.g. 5 tokens at g = 8) keep Q in registers; wider
+// calls run as split-K prefill.
 //
 // Half-page kernel (FP8-E4M3 pool, one column block): a split workgroup is
 // one wave (the kernel takes any number of waves, each on its own 32-key
@@ -37,10 +37,9 @@
 // FP8 values are widened exactly to bf16 (every E4M3 value is a bf16 value)
 // just before their MFMA, k_scale is folded into the softmax scale and
 // v_scale into the partial (vLLM flash-attention PR 199, "Summary": FP8 KV
-// with 16-bit MMA).  The half-page kernel keeps a reference maximum and
-// rescales O only when a score exceeds it by more than kRefMargin (log2
-// units), so its 128-register O accumulator is rarely touched by the
-// softmax; the tile kernel rescales per tile.
+// with 16-bit MMA).  Both kernels keep a reference maximum per column and
+// rescale O only when a score exceeds it by more than a margin (log2 units),
+// so the O accumulators are rarely touched by the softmax.
 #include "device_common.h"
 #include "attn_host.h"
 
@@ -285,19 +284,23 @@ __device__ __forceinline__ void qk_drain(f32x4 (&s)[NC]) {
 // 16 w + 15 of each K and V tile into LDS; it alone reads those K rows, so
 // it refills them as soon as its own reads have returned.  It computes its
 // keys' scores for every column block (one K operand read serves all NC
-// blocks) and, once the four waves have exchanged their per-column maxima
-// through LDS, their probabilities, which it writes to LDS as bf16; after a
-// second barrier it accumulates its own 128 of the 512 output dims over all
-// 64 keys, reading each V operand once for all blocks.  bf16: a third
-// barrier frees the V buffer for the next tile.  A column's probabilities are
-// taken against a reference maximum that moves only when a tile's maximum
-// exceeds it by more than kTileMargin (log2 units), so the accumulators are
-// rarely rescaled; l sums the bf16 probabilities the PV products use.  FP8:
-// the tiles hold E4M3 bytes, widened exactly to bf16 as each operand is read
+// blocks) and their probabilities, which it writes to LDS as bf16; after a
+// barrier it accumulates its own 128 of the 512 output dims over all 64
+// keys, reading each V operand once for all blocks.  A column's
+// probabilities are taken against a reference maximum that moves only when
+// a tile's maximum exceeds it by more than kTileMargin (log2 units), so the
+// accumulators are rarely rescaled; l sums the bf16 probabilities the PV
+// products use.  The probabilities are written against the current
+// references at once, with each wave's vote on whether one of its scores
+// passes the margin; only when a vote is cast (every column's first tile,
+// then rarely) do the waves exchange per-column maxima, move references,
+// rescale and write the probabilities again, two barriers more.  bf16: a
+// second barrier per tile frees the V buffer for the next tile.  FP8: the
+// tiles hold E4M3 bytes, widened exactly to bf16 as each operand is read
 // (k_scale is in the softmax scale, v_scale in the partial); their 32 KB
 // tiles fit twice over, so K(t + 2) loads while tile t is consumed, and V(t +
-// 1) goes out after tile t's first barrier (every wave is then past P.V of
-// tile t - 1, whose buffer it takes): two barriers per tile.
+// 1) goes out after tile t's barrier (every wave is then past P.V of tile
+// t - 1, whose buffer it takes): one barrier per tile.
 constexpr float kTileMargin = 8.f;
 constexpr int kPStride = 2 * kPage + 16;   // bytes per column row of the P buffer
 
@@ -316,14 +319,16 @@ void decode_split_tile_kernel(DecodeArgs a) {
     constexpr int kLoads = FP8 ? kPage / 8 : kPage / kDecWaves;  // DMAs per wave per tile
     constexpr int kCols = NC * kDecRows;
     constexpr int kDepth = FP8 ? 2 : 1;   // tiles in flight per operand
+    constexpr int kPBytes = kCols * kPStride;   // one P buffer
     __shared__ __attribute__((aligned(1024)))
-        char smem[2 * kDepth * kTB + kCols * kPStride + kCols * kDecWaves * 4];
+        char smem[2 * kDepth * kTB + 2 * kPBytes + kCols * kDecWaves * 4 + 2 * kDecWaves * 4];
     SplitPlan p;
     if (!plan_split(a, p)) return;
     ATTN_LDS char* sK0 = (ATTN_LDS char*)smem;                  // K buffers, then V buffers
     ATTN_LDS char* sV0 = sK0 + kDepth * kTB;
-    ATTN_LDS char* sP = sV0 + kDepth * kTB;                      // [column][64 keys] bf16
-    ATTN_LDS float* sM = (ATTN_LDS float*)(sP + kCols * kPStride);  // [column][wave]
+    ATTN_LDS char* sP0 = sV0 + kDepth * kTB;                     // 2 x [column][64 keys] bf16
+    ATTN_LDS float* sM = (ATTN_LDS float*)(sP0 + 2 * kPBytes);   // [column][wave]
+    ATTN_LDS int* sVote = (ATTN_LDS int*)(sM + kCols * kDecWaves);  // 2 x [wave]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;   // MFMA column within a block
@@ -472,78 +477,104 @@ void decode_split_tile_kernel(DecodeArgs a) {
 
         // element i: key 16 wave + 4 kq + i of column 16 cb + n, in log2
         // units; keys a column may not see are -inf (only in the tiles that
-        // reach past k_end - q_len: earlier keys are visible to every column)
+        // reach past k_end - q_len: earlier keys are visible to every column).
+        // The wave votes to move the references when one of its scores is
+        // above its column's reference by more than the margin.
         const bool edge = key0 + kPage > p.k_end - a.q_len;
         const int mykey = key0 + 16 * wave + 4 * kq;
+        bool over = false;
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb) {
-            float mt = -__builtin_inff();
+            const float lim = m_ref[cb] + kTileMargin;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float v = s[cb][i] * a.scale_log2;
                 if (edge && mykey + i >= col[cb].k_lim) v = -__builtin_inff();
                 s[cb][i] = v;
-                mt = fmaxf(mt, v);
+                over |= v > lim;
             }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            if (kq == 0) sM[(16 * cb + n) * kDecWaves + wave] = mt;
         }
-        lds_barrier();  // column maxima visible
+        // probabilities of this wave's keys against the references -> P
+        // buffer t % 2 (two buffers: a wave may write tile t + 1's while
+        // another still reads tile t's)
+        ATTN_LDS char* sP = sP0 + (t & 1) * kPBytes;
+        auto write_p = [&] {
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) {
+                const float m_use = finite_or_zero(m_ref[cb]);
+                bf16x4 pw;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pw[i] = (__bf16)fast_exp2(s[cb][i] - m_use);
+                *(ATTN_LDS bf16x4*)(sP + (16 * cb + n) * kPStride + (16 * wave + 4 * kq) * 2) = pw;
+            }
+        };
+        write_p();
+        const bool vote = __builtin_amdgcn_ballot_w64(over) != 0;
+        if (lane == 0) sVote[(t & 1) * kDecWaves + wave] = vote;
+
+        // this wave's V(t) rows are in.  kDepth 1: after them were issued
+        // K(t + 1) (none on the last tile).  kDepth 2 (issue order K0 V0 K1
+        // V1, then per step t: K(t + 2), and V(t + 1) from t = 1): after V(t)
+        // only K(t + 2) from t = 2 on (the first two steps wait for a little
+        // more than they need)
+        if constexpr (kDepth == 2) {
+            wait_vmcnt<kLoads>();
+        } else {
+            if (more) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
+        }
+        lds_barrier();  // P, the votes and every wave's V(t) rows visible
         // kDepth 2: every wave is past P.V of tile t - 1, so its V buffer
         // takes tile t + 1 (zero-length past the split)
         if (kDepth == 2 && t >= 1)
             issue_tile<FP8>(tile_base(a.v_pages, a, split_page(a, p, t + 1), p.kvh, kPoolTile),
                             valid_of(t + 1), sV0 + ((t + 1) & 1) * kTB, wave, lane);
 
-        // the tile's maximum per column moves the reference when it exceeds it
-        // by more than the margin (the first tile with a visible key always
-        // does: alpha = 0 on the zero O); every wave takes the same decision
-        bool up_any = false;
-        float alpha[NC];
-#pragma unroll
-        for (int cb = 0; cb < NC; ++cb) {
-            const f32x4 mm = *(const ATTN_LDS f32x4*)(sM + (16 * cb + n) * kDecWaves);
-            const float mt = fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3]));
-            const bool up = mt > m_ref[cb] + kTileMargin;
-            alpha[cb] = up ? fast_exp2(m_ref[cb] - mt) : 1.f;
-            m_ref[cb] = up ? mt : m_ref[cb];
-            up_any |= up;
-        }
-        if (__builtin_amdgcn_ballot_w64(up_any)) {
+        const u32x4 votes = *(const ATTN_LDS u32x4*)(sVote + (t & 1) * kDecWaves);
+        if (__builtin_expect((votes[0] | votes[1] | votes[2] | votes[3]) != 0, 0)) {
+            // Some score is above its reference by more than the margin (the
+            // first tile with a visible key always is, against m_ref = -inf):
+            // the waves exchange their per-column maxima, a column's reference
+            // moves to its tile maximum when that exceeds it by more than the
+            // margin (alpha = 0 on the zero O the first time), and the waves
+            // write their probabilities again.  Every wave takes the same
+            // decisions, so O, l and P are those of a tile-by-tile exchange.
 #pragma unroll
             for (int cb = 0; cb < NC; ++cb) {
-                l_run[cb] *= alpha[cb];
-                if constexpr (NC == 1) {
+                float mt = fmaxf(fmaxf(s[cb][0], s[cb][1]), fmaxf(s[cb][2], s[cb][3]));
+                mt = fmaxf(mt, __shfl_xor(mt, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                if (kq == 0) sM[(16 * cb + n) * kDecWaves + wave] = mt;
+            }
+            lds_barrier();  // column maxima visible
+            bool up_any = false;
+            float alpha[NC];
 #pragma unroll
-                    for (int db = 0; db < 8; ++db) o[cb][db] *= alpha[cb];
-                } else {
-                    acc_fence8(o[cb]);
+            for (int cb = 0; cb < NC; ++cb) {
+                const f32x4 mm = *(const ATTN_LDS f32x4*)(sM + (16 * cb + n) * kDecWaves);
+                const float mt = fmaxf(fmaxf(mm[0], mm[1]), fmaxf(mm[2], mm[3]));
+                const bool up = mt > m_ref[cb] + kTileMargin;
+                alpha[cb] = up ? fast_exp2(m_ref[cb] - mt) : 1.f;
+                m_ref[cb] = up ? mt : m_ref[cb];
+                up_any |= up;
+            }
+            if (__builtin_amdgcn_ballot_w64(up_any)) {
 #pragma unroll
-                    for (int db = 0; db < 8; ++db) scale_acc4(o[cb][db], alpha[cb]);
-                    acc_fence8(o[cb]);
+                for (int cb = 0; cb < NC; ++cb) {
+                    l_run[cb] *= alpha[cb];
+                    if constexpr (NC == 1) {
+#pragma unroll
+                        for (int db = 0; db < 8; ++db) o[cb][db] *= alpha[cb];
+                    } else {
+                        acc_fence8(o[cb]);
+#pragma unroll
+                        for (int db = 0; db < 8; ++db) scale_acc4(o[cb][db], alpha[cb]);
+                        acc_fence8(o[cb]);
+                    }
                 }
             }
+            write_p();
+            lds_barrier();  // the new P visible
         }
-        // probabilities of this wave's keys -> the P buffer
-#pragma unroll
-        for (int cb = 0; cb < NC; ++cb) {
-            const float m_use = finite_or_zero(m_ref[cb]);
-            bf16x4 pw;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pw[i] = (__bf16)fast_exp2(s[cb][i] - m_use);
-            *(ATTN_LDS bf16x4*)(sP + (16 * cb + n) * kPStride + (16 * wave + 4 * kq) * 2) = pw;
-        }
-
-        // this wave's V(t) rows are in: after them were issued K(t + 1) with
-        // kDepth 1 (none on the last tile); K(t + 2) and V(t + 1) with kDepth 2
-        // (on the first step K1, V1 and K2: V0 is waited for with K1)
-        if constexpr (kDepth == 2) {
-            wait_vmcnt<2 * kLoads>();
-        } else {
-            if (more) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();
-        }
-        lds_barrier();  // P and every wave's V(t) rows visible
 
         // P^T operand: keys 32 c + 8 kq .. + 7 of column 16 cb + n
         bf16x8 pf[NC][2];
