@@ -913,9 +913,15 @@ size_t routed_meta_bytes(int batch) {
     return ((size_t)(2 * batch + 1) * sizeof(int) + 255) / 256 * 256;
 }
 
-int default_keys_per_split(int batch, int hkv, int max_kv_len) {
+// Default split: about kDefaultTargetWgs splits over the largest key ranges.
+// A split with two or three 16-column blocks (a multi-token decode) pays
+// about three times the fixed cost per split of a one-block split (Q of up
+// to 48 columns, their 96 KB of partials, the first tile's reference
+// exchange, the pipeline fill), so its splits are made twice as long.
+int default_keys_per_split(int batch, int hkv, int max_kv_len, int col_blocks) {
     const long long total = (long long)batch * hkv * max_kv_len;
-    long long s = (total + kDefaultTargetWgs - 1) / kDefaultTargetWgs;
+    const int target = col_blocks > 1 ? kDefaultTargetWgs / 2 : kDefaultTargetWgs;
+    long long s = (total + target - 1) / target;
     s = (s + kPage - 1) / kPage * kPage;
     if (s < 4 * kPage) s = 4 * kPage;
     return (int)s;
@@ -926,7 +932,7 @@ int default_keys_per_split(int batch, int hkv, int max_kv_len) {
 // shapes; here the work is the KV stream, and the ranges balance the
 // sequences' different lengths).
 int routed_keys_per_split(int batch, int hkv, int max_kv_len, int keys_per_split) {
-    return keys_per_split ? keys_per_split : default_keys_per_split(batch, hkv, max_kv_len);
+    return keys_per_split ? keys_per_split : default_keys_per_split(batch, hkv, max_kv_len, 1);
 }
 
 }  // namespace
@@ -949,8 +955,9 @@ extern "C" size_t attn_decode_splitk_ex_workspace_size(int batch, int q_len, int
                    batch, q_len, batch * q_len, num_q_heads, num_kv_heads, max_kv_len,
                    routed_keys_per_split(batch, num_kv_heads, max_kv_len, keys_per_split));
     }
+    const int nc = (q_len * (num_q_heads / num_kv_heads) + kDecRows - 1) / kDecRows;
     const int kps = keys_per_split ? keys_per_split
-                                   : default_keys_per_split(batch, num_kv_heads, max_kv_len);
+                                   : default_keys_per_split(batch, num_kv_heads, max_kv_len, nc);
     const size_t splits = (size_t)(max_kv_len + kps - 1) / kps;
     // hkv * (q_len * g) columns = q_len * hq
     const size_t slots = (size_t)batch * q_len * num_q_heads * splits * kMaxSub;
@@ -1055,9 +1062,9 @@ int decode_launch(const void* q, const void* k_pages, const void* v_pages, int k
     if (out_dtype != ATTN_BF16 && out_dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
     if (kv_dtype == ATTN_FP8_E4M3 && (!(k_scale > 0.f) || !(v_scale > 0.f))) return ATTN_ERR_SHAPE;
     const bool fp8 = kv_dtype == ATTN_FP8_E4M3;
-    const int kps = keys_per_split ? keys_per_split
-                                   : default_keys_per_split(batch, num_kv_heads, max_kv_len);
     const int nc = (q_len * g + kDecRows - 1) / kDecRows;   // 16-column blocks
+    const int kps = keys_per_split ? keys_per_split
+                                   : default_keys_per_split(batch, num_kv_heads, max_kv_len, nc);
     // FP8 with one block: the half-page kernel (a partial per wave)
     const int sub = fp8 && nc == 1 ? kFp8Waves : 1;
     const int max_splits = (max_kv_len + kps - 1) / kps;

@@ -329,7 +329,10 @@ int attn_prefill_hd512_splitk_e4m3_mma(const void* q, const void* k_pages, const
  * Bytes of device workspace attn_decode_splitk needs for these sizes: fp32
  * partial outputs plus (m, l) for up to 4 partials per split, per query head
  * and sequence (valid for either KV dtype).  keys_per_split = 0 selects the
- * library default.  Returns 0 for invalid sizes.
+ * library default: batch * num_kv_heads * max_kv_len keys over about 4096
+ * ranges (2048 when a split carries two or three 16-column blocks of a
+ * multi-token decode), rounded up to a multiple of 64 and at least 256.
+ * Returns 0 for invalid sizes.
  */
 size_t attn_decode_splitk_workspace_size(int batch, int num_q_heads, int num_kv_heads,
                                          int max_kv_len, int keys_per_split);

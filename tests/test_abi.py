@@ -323,10 +323,13 @@ def test_prefill_persistent_validation(L):
 
 def test_wide_multi_token_decode_workspace(L):
     # up to 48 (token, head) columns per KV head the decode kernels run:
-    # (O, m, l) partials per split and column, 4 slots per column reserved
-    # (1792-key ranges at batch 64, max 28672 keys: 16 splits)
+    # (O, m, l) partials per split and column, 4 slots per column reserved.
+    # The default ranges: 1792 keys at batch 64, max 28672 keys (16 splits)
+    # for one 16-column block, twice that for two or three (8 splits)
     dec = L.attn_decode_splitk_ex_workspace_size(64, 5, 32, 4, 28672, 0)   # 40 columns
-    assert dec == 64 * 5 * 32 * 16 * 4 * 514 * 4
+    assert dec == 64 * 5 * 32 * 8 * 4 * 514 * 4
+    one = L.attn_decode_splitk_ex_workspace_size(64, 1, 8, 4, 28672, 0)    # 2 columns
+    assert one == 64 * 1 * 8 * 16 * 4 * 514 * 4
     # 7 tokens x g = 8 = 56 columns: routed through the split-K prefill; its
     # workspace is the row offsets and chunk starts (2 batch + 1 ints, padded
     # to 256 bytes) plus the prefill's partials for batch x q_len rows
