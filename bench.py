@@ -48,8 +48,8 @@ TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/prefill_common.h",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "482f2ea8564fcba979420681011edabfcbb232b63cd31fc75063d46df6441bc6",
-    "fetch_bytes": 1977008667,
+    "sha256": "ec445d3a80dd14ecaa8c13f68c50dfabdfce94d9883684a87a3b669534e16713",
+    "fetch_bytes": 1983035157,
     "write_bytes": 268435456,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
