@@ -154,6 +154,47 @@ def decode_mtp_b64(device="cpu", seed=9, kv_dtype="bf16", batch=64, q_len=5, lo=
                       device=device, kv_dtype=kv_dtype)
 
 
+def decode_late_keys(device="cpu", seed=29, kv_dtype="bf16", q_len=1) -> PagedCase:
+    """Decode of q_len tokens per sequence (kv_len 700, 1500, 3000; 32 q heads
+    over 4 KV heads, fp32 out) with late dominant keys, for the split
+    kernels' reference moves.
+
+    As in the 8192-row chunk with late keys: every query row gets 1.5 u
+    added (u = a fixed +-1 vector over the head dims), and some keys of every
+    KV head are set to beta u.  beta = 0.375 puts a key about 18.6 log2 units
+    above a typical score (scores are about N(0, 2.7) log2 units, a tile's
+    maximum about 6.5): 12 above what its split saw before it, more than the
+    decode kernels' margins (8 and 10).  Sequences 0 and 1 have one such key,
+    at positions 100 and 1400 (inside a 256- or 1024-key split, after its
+    first tile): it dominates the output while the keys before it still
+    weigh about 2^-12 each, so O and l must be rescaled when the reference
+    moves, not restarted.  Sequence 2 climbs: beta = 0.375, 0.625, 1 and 2
+    at positions 100, 420, 2800 and 2900 (about 18.6, 31, 50 and 99 log2
+    units).  In an FP8-E4M3 pool the keys are the E4M3 codes of beta u /
+    k_scale (within the E4M3 range at these betas).
+    """
+    lens = (700, 1500, 3000)
+    plant = (((100, 0.375),), ((1400, 0.375),),
+             ((100, 0.375), (420, 0.625), (2800, 1.0), (2900, 2.0)))
+    case = build_case(f"decode_late_keys_q{q_len}" + _fp8_suffix(kv_dtype),
+                      seqs=[(q_len, L - q_len, L) for L in lens], hq=32, hkv=4, seed=seed,
+                      out_dtype="fp32", device=device, kv_dtype=kv_dtype, extra_pages=2,
+                      table_pad=2)
+    lc = case.launches[0]
+    u = torch.where(torch.arange(case.head_dim, device=device) % 3 == 0, -1.0, 1.0)
+    lc.q[:lc.total_q] = (lc.q[:lc.total_q].float() + 1.5 * u).to(torch.bfloat16)
+    for b in range(len(lens)):
+        for j, beta in plant[b]:
+            page = int(case.page_table[b, j // 64])
+            row = beta * u
+            if kv_dtype == "bf16":
+                case.k_pool[page, :, j % 64, :] = row.to(torch.bfloat16)
+            else:
+                code = (row / case.k_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+                case.k_pool[page, :, j % 64, :] = code
+    return case
+
+
 WORKLOADS: Dict[str, Callable[..., PagedCase]] = {
     "tiny_prefill_mqa_256": tiny_prefill_mqa,
     "chunk_prefill_2048": chunk_prefill_2k,

@@ -94,6 +94,22 @@ def test_multi_token_decode(A, fx, kv_dtype, with_sink):
     _lse_check(lse, ref_lse, what)
 
 
+@pytest.mark.parametrize("kps", [256, 1024], ids=["split256", "split1024"])
+@pytest.mark.parametrize("q_len", [1, 3, 5])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_decode_late_dominant_keys(A, kv_dtype, q_len, kps):
+    # a key 12 log2 units above what its split saw before it (two
+    # sequences) and a climb to 99 (the third), inside later tiles of their
+    # splits: the split kernels move their references and rescale O and l
+    # after the first tile; one to three column blocks at g = 8
+    case = W.decode_late_keys(device="cuda", kv_dtype=kv_dtype, q_len=q_len)
+    out, lse = _run_decode(A, case, q_len, None, kps)
+    ref, ref_lse = oracle.attend_all_lse(case.to("cpu"))
+    what = f"decode late keys q_len={q_len} {kv_dtype} split={kps}"
+    check_parity(out, ref, what)
+    _lse_check(lse, ref_lse, what)
+
+
 def test_multi_token_decode_bf16_out(A):
     lens = [300, 1000, 2049]
     case = W.build_case("mtp_bf16", seqs=[(4, L - 4, L) for L in lens], hq=8, hkv=4, seed=31,

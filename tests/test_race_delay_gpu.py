@@ -206,3 +206,28 @@ def test_decode_delayed(A, fx, kv):
     a, b = _both(A, run)
     _same_bits(a, b, what)
     check_parity(b, oracle.attend_all(case.to("cpu")), what + " (delayed)")
+
+
+@pytest.mark.parametrize("q_len", [1, 5])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_decode_late_keys_delayed(A, q_len, kv):
+    # the reference moves after a split's first tile (the per-column maxima
+    # exchanged, O and l rescaled, the probabilities written again)
+    what = f"decode late keys q_len={q_len} {kv}"
+    print(f"[case] delay {what}", flush=True)
+    case = W.decode_late_keys(device="cuda", kv_dtype=kv, q_len=q_len)
+    lc = case.launches[0]
+    rows = lc.batch * q_len
+    nb = A.decode_workspace_size(lc.batch, 32, 4, lc.max_kv_len, 256, q_len=q_len)
+    ws = torch.empty(nb // 4, device="cuda")
+
+    def run():
+        out = out_tensor(rows, 32, "fp32")
+        A.decode(lc.q[:rows], case.k_pool, case.v_pool, case.page_table, lc.kv_len, out, ws,
+                 max_kv_len=lc.max_kv_len, softmax_scale=case.softmax_scale, kv_dtype=kv,
+                 k_scale=case.k_scale, v_scale=case.v_scale, keys_per_split=256, q_len=q_len)
+        return out
+
+    a, b = _both(A, run)
+    _same_bits(a, b, what)
+    check_parity(b, oracle.attend_all(case.to("cpu")), what + " (delayed)")
