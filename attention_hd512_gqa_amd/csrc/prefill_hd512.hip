@@ -36,7 +36,9 @@
 // the K or V buffer; after the phase's barrier that half is refilled for the
 // tile that needs it two phases later, with the wave's 8 row loads spread one
 // per four MFMAs over the next phase (a burst of 1 KB buffer->LDS loads would
-// stall the wave's instruction issue and starve the matrix core).
+// stall the wave's instruction issue and starve the matrix core).  A phase's
+// last MFMAs go out after the next phase's barrier, beside that phase's first
+// operand reads, so that the matrix core has work while they come back.
 //
 // The same kernel, by template parameters, also covers: an FP8-E4M3 pool
 // (512-byte tile rows, bytes widened exactly to bf16 at their MFMA); head dim
@@ -190,13 +192,6 @@ __device__ __forceinline__ void half_dma_row(const HalfDma& d, int lane_off, int
         }
         dma_row<(swz(J) << 4), J * kRowBytes>(d.rsrc, d.lds_base, d.soff, lane_off);
     }
-}
-
-// Keeps the instructions before it (a refill's address work) ahead of the
-// wait and barrier that follow, where they overlap the wait.
-template <bool ON>
-__device__ __forceinline__ void hold_before_wait() {
-    if constexpr (ON) __builtin_amdgcn_sched_barrier(0);
 }
 
 template <bool FP8, int D>
@@ -456,48 +451,90 @@ struct VReader8 {
     }
 };
 
+// LDS operand reads of the two products.  A phase's first kPrefetchOf reads
+// are issued by the phase before it, right after the barrier that opens the
+// phase (see qk_block), into a ring the tile loop owns.
+template <bool FP8>
+using RawOf = typename std::conditional<FP8, v2i32, bf16x8>::type;
+
+// K operand of k-step ks of 32-key block kb.  bf16 at 512: step ks reads
+// chunk 2 ks + h of key row 32 kb + n; with ks = 8 u + v the byte offset is
+// koff[v] + 256 u + 32 KiB kb.  bf16 at 256: chunk (2 ks + h) ^ swzN(n) =
+// (2 ks) ^ (h ^ swzN(n)): koff[0] ^ (32 ks) + 16 KiB kb.  FP8: bytes 16 ks +
+// 8 h of row 32 kb + n, chunk ks at ks ^ n: koff[0] ^ (16 ks) + 16 KiB kb.
+// FP8 operands are read as raw bytes and widened at their MFMA.
+template <bool FP8, int D>
+__device__ __forceinline__ RawOf<FP8> k_operand(const ATTN_LDS char* sK, const int (&koff)[8],
+                                                int kb, int ks) {
+    if constexpr (FP8)
+        return *(const ATTN_LDS v2i32*)(sK + (koff[0] ^ (ks << 4)) + kb * 32 * 512);
+    else if constexpr (Kv<FP8, D>::kNarrow)
+        return *(const ATTN_LDS bf16x8*)(sK + (koff[0] ^ (ks << 5)) + kb * 32 * 512);
+    else
+        return *(const ATTN_LDS bf16x8*)(sK + koff[ks & 7] + 256 * (ks >> 3) +
+                                          kb * 32 * kRowBytes);
+}
+
+// V^T operand of MFMA step st of P.V block kb: k-step 2 kb + st / kDB of the
+// tile, dim block st % kDB.
+template <bool FP8, int D, typename VR>
+__device__ __forceinline__ RawOf<FP8> v_operand(const ATTN_LDS char* sV, const VR& vr, int kb,
+                                                int st) {
+    constexpr int kDB = Kv<FP8, D>::kDimBlocks;
+    return vr.read(sV, 2 * kb + st / kDB, st % kDB);
+}
+
+// MFMAs each phase leaves for after the barrier that opens the next phase.
+// Their operands are already in registers, so they keep the matrix core busy
+// while the barrier releases and the next phase's first operand reads come
+// back from LDS, which would otherwise leave it idle at every phase start.
+// All phases share one operand ring, and held step i reads slot i (the step
+// count minus the held count is a multiple of the ring size), so the next
+// phase's read i refills the slot its held MFMA has just taken: no register
+// holds more than one operand at a time.  Measured on the 8192- and 2048-row
+// chunks, holding the whole ring (4) took 0.7 % and 3 % off the launch time
+// on a bf16 pool; the FP8 pool's kernel (ring of 3, so at most 2 held) ran no
+// faster and holds none.
+template <bool FP8>
+constexpr int kHoldOf = FP8 ? 0 : 4;
+
 // Q.K^T of one 32-key block kb: D / 16 MFMAs (VGPR accumulator) over the
-// k-steps of head_dim.  When OVERLAP, the 16 softmax elements of the previous
-// block's scores `sp` are spread evenly over the MFMAs (one after every other
-// at D = 512, one after each at 256); the half-tile refill `dma` issues one
-// row load after every fourth MFMA.  `pre` (the previous block's masking and
-// reference, which the softmax needs but the chain does not) runs after the
-// first MFMA is issued, so that it overlaps the matrix pipe.
-template <bool OVERLAP, bool FP8, int D, bool LO = false, typename Pre>
+// k-steps of head_dim, operands from the ring `kbuf` (filled here unless PRE:
+// then the previous phase read them).  When OVERLAP, the 16 softmax elements
+// of the previous block's scores `sp` are spread evenly over the MFMAs (one
+// after every other at D = 512, one after each at 256); the half-tile refill
+// `dma` issues one row load after every fourth MFMA.  `pre` (the previous
+// block's masking and reference, which the softmax needs but the chain does
+// not) runs after the first MFMA is issued, so that it overlaps the matrix
+// pipe.  The last HOLD MFMAs (and the softmax elements beside them) are
+// issued after `sync()` (the wait and barrier that open the next phase),
+// interleaved with `fill(i)`, the next phase's first operand reads.  Without
+// a next phase (tail_on false) there is no barrier to wait for, and the
+// reads are still issued (in-bounds LDS reads whose values go unused), so
+// that the ring holds one version of its values at every point.
+template <bool OVERLAP, bool FP8, int D, bool LO, bool PRE, int HOLD, typename Pre, typename Sync,
+          typename Fill>
 __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(Kv<FP8, D>::kSteps)],
                                          const ATTN_LDS char* sK, const int (&koff)[8],
+                                         RawOf<FP8> (&kbuf)[kPrefetchOf<FP8>],
                                          const f32x16& sp, const SoftmaxCtx& c, float& psum,
                                          bf16x8& pf0, bf16x8& pf1, bf16x8& lo0, bf16x8& lo1,
                                          const HalfDma& dma, int lane_off, int lane, int wave,
-                                         Pre&& pre) {
-    // bf16 at 512: step ks reads chunk 2 ks + h of key row 32 kb + n; with
-    // ks = 8 u + v the byte offset is koff[v] + 256 u + 32 KiB kb.  bf16 at
-    // 256: chunk (2 ks + h) ^ swzN(n) = (2 ks) ^ (h ^ swzN(n)): koff[0] ^ (32 ks)
-    // + 16 KiB kb.  FP8: bytes 16 ks + 8 h of row 32 kb + n, chunk ks at
-    // ks ^ n: koff[0] ^ (16 ks) + 16 KiB kb.  FP8 operands are prefetched as
-    // raw bytes and widened at their MFMA.
+                                         Pre&& pre, bool tail_on, Sync&& sync, Fill&& fill) {
     constexpr int kSteps = Kv<FP8, D>::kSteps;
-    using Raw = typename std::conditional<FP8, v2i32, bf16x8>::type;
-    auto kread = [&](int ks) -> Raw {
-        if constexpr (FP8)
-            return *(const ATTN_LDS v2i32*)(sK + (koff[0] ^ (ks << 4)) + kb * 32 * 512);
-        else if constexpr (Kv<FP8, D>::kNarrow)
-            return *(const ATTN_LDS bf16x8*)(sK + (koff[0] ^ (ks << 5)) + kb * 32 * 512);
-        else
-            return *(const ATTN_LDS bf16x8*)(sK + koff[ks & 7] + 256 * (ks >> 3) +
-                                              kb * 32 * kRowBytes);
-    };
+    constexpr int kP = kPrefetchOf<FP8>;
+    static_assert(HOLD >= 0 && HOLD <= kP && HOLD < kSteps, "held MFMAs");
+    // held step i must read ring slot i (see kHoldOf)
+    static_assert(HOLD == 0 || (kSteps - HOLD) % kP == 0, "held steps and ring slots");
     constexpr int kDmaEvery = kSteps / Kv<FP8, D>::kDmaPerHalf;
     constexpr int kSmEvery = kSteps / 16;
-    Raw kbuf[kPrefetchOf<FP8>];
     float pend = 0.f;   // p of the previous softmax element
     float sc = c.scale_log2;
-#pragma unroll
-    for (int j = 0; j < kPrefetchOf<FP8>; ++j) kbuf[j] = kread(j);
-    static_for<kSteps>([&](auto KS) {
+    // MFMA of step ks and the softmax element placed after it
+    auto step = [&](auto KS) {
         constexpr int ks = decltype(KS)::value;
-        const bf16x8 cur = operand(kbuf[ks % kPrefetchOf<FP8>]);
-        if (ks + kPrefetchOf<FP8> < kSteps) kbuf[ks % kPrefetchOf<FP8>] = kread(ks + kPrefetchOf<FP8>);
+        const bf16x8 cur = operand(kbuf[ks % kP]);
+        if (ks + kP < kSteps) kbuf[ks % kP] = k_operand<FP8, D>(sK, koff, kb, ks + kP);
         if constexpr (FP8) {   // cur was just written by the widening VALU ops
             if constexpr (ks == 0)
                 mfma32x32x16_vgpr_first_va(s, cur, qf[0]);
@@ -509,53 +546,72 @@ __device__ __forceinline__ void qk_block(f32x16& s, int kb, const bf16x8 (&qf)[(
             else
                 mfma32x32x16_vgpr(s, cur, qf[ks]);
         }
-        if constexpr (ks % kDmaEvery == 0) {
-            if (dma.on) half_dma_row<FP8, D, ks / kDmaEvery>(dma, lane_off, lane, wave);
-        }
         if constexpr (ks == 0) pre();
         if constexpr (OVERLAP && (ks % kSmEvery == kSmEvery - 1)) {
             constexpr int i = ks / kSmEvery;
             softmax_elem<LO>(c, sc, sp[i], i, psum, pend, pf0, pf1, lo0, lo1);
         }
+    };
+    if constexpr (!PRE) {
+#pragma unroll
+        for (int j = 0; j < kP; ++j) kbuf[j] = k_operand<FP8, D>(sK, koff, kb, j);
+    }
+    static_for<kSteps>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        if constexpr (ks < kSteps - HOLD) step(KS);
+        if constexpr (ks % kDmaEvery == 0) {
+            if (dma.on) half_dma_row<FP8, D, ks / kDmaEvery>(dma, lane_off, lane, wave);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    if (tail_on) sync();
+    static_for<kP>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < HOLD) step(std::integral_constant<int, kSteps - HOLD + i>{});
+        __builtin_amdgcn_sched_barrier(0);
+        fill(I);
         __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (OVERLAP) softmax_flush<LO>(c, psum, pend, pf1, lo1);
 }
 
 // P.V of one 32-key block (k-steps c = 2 kb, 2 kb + 1 of the tile, all D / 32
-// dim blocks).  FIRST: the tile's first k-step starts O from zero (inline
-// c = 0), so O is only ever written by MFMAs.  LO: P carries a second bf16
-// term (p0lo, p1lo; the range's first tile), multiplied into O by a second
-// MFMA on the same V operand when lo_on (wave-uniform); LO_NEXT: the
-// overlapped softmax of the next block produces its second term too.  When
-// OVERLAP, the 16 softmax elements of the next block's scores `sn` are
-// spread evenly over the MFMAs; the half-tile refill `dma` issues one row
-// load after every fourth MFMA.
-template <bool FIRST, bool OVERLAP, bool FP8, int D, bool LO = false, bool LO_NEXT = false,
-          typename VR>
+// dim blocks), operands from the ring `vbuf` (filled here unless PRE).
+// FIRST: the tile's first k-step starts O from zero (inline c = 0), so O is
+// only ever written by MFMAs.  LO: P carries a second bf16 term (p0lo, p1lo;
+// the range's first tile), multiplied into O by a second MFMA on the same V
+// operand when lo_on (wave-uniform); LO_NEXT: the overlapped softmax of the
+// next block produces its second term too.  When OVERLAP, the 16 softmax
+// elements of the next block's scores `sn` are spread evenly over the MFMAs
+// (`pre`, run after the first MFMA, readies them); the half-tile refill
+// `dma` issues one row load after every fourth MFMA.  HOLD, sync, fill and
+// tail_on as in qk_block.
+template <bool FIRST, bool OVERLAP, bool FP8, int D, bool LO, bool LO_NEXT, bool PRE, int HOLD,
+          typename VR, typename Pre, typename Sync, typename Fill>
 __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], int kb,
                                          const bf16x8& p0, const bf16x8& p1,
                                          const bf16x8& p0lo, const bf16x8& p1lo,
-                                         const ATTN_LDS char* sV, const VR& vr, const f32x16& sn,
+                                         const ATTN_LDS char* sV, const VR& vr,
+                                         RawOf<FP8> (&vbuf)[kPrefetchOf<FP8>], const f32x16& sn,
                                          const SoftmaxCtx& c, float& psum,
                                          bf16x8& pn0, bf16x8& pn1, bf16x8& ln0, bf16x8& ln1,
                                          const HalfDma& dma, int lane_off, int lane, int wave,
-                                         bool lo_on = false) {
+                                         bool lo_on, Pre&& pre, bool tail_on, Sync&& sync,
+                                         Fill&& fill) {
     constexpr int kDB = Kv<FP8, D>::kDimBlocks;
     constexpr int kMfma = 2 * kDB;
+    constexpr int kP = kPrefetchOf<FP8>;
+    static_assert(HOLD >= 0 && HOLD <= kP && HOLD <= kDB, "held MFMAs");
+    // held step i must read ring slot i (see kHoldOf)
+    static_assert(HOLD == 0 || (kMfma - HOLD) % kP == 0, "held steps and ring slots");
     constexpr int kDmaEvery = kMfma / Kv<FP8, D>::kDmaPerHalf;
     constexpr int kSmEvery = kMfma / 16;
-    using Raw = typename std::conditional<FP8, v2i32, bf16x8>::type;
-    auto vread = [&](int st) -> Raw { return vr.read(sV, 2 * kb + st / kDB, st % kDB); };
-    Raw vbuf[kPrefetchOf<FP8>];
     float pend = 0.f;   // p of the previous softmax element
     float sc = c.scale_log2;
-#pragma unroll
-    for (int j = 0; j < kPrefetchOf<FP8>; ++j) vbuf[j] = vread(j);
-    static_for<kMfma>([&](auto ST) {
+    auto step = [&](auto ST) {
         constexpr int st = decltype(ST)::value;
-        const bf16x8 cur = operand(vbuf[st % kPrefetchOf<FP8>]);
-        if (st + kPrefetchOf<FP8> < kMfma) vbuf[st % kPrefetchOf<FP8>] = vread(st + kPrefetchOf<FP8>);
+        const bf16x8 cur = operand(vbuf[st % kP]);
+        if (st + kP < kMfma) vbuf[st % kP] = v_operand<FP8, D>(sV, vr, kb, st + kP);
         constexpr int db = st % kDB;
         if constexpr (FIRST && st < kDB)
             o[db] = mfma32x32x16(cur, p0, f32x16{});
@@ -564,13 +620,30 @@ __device__ __forceinline__ void pv_block(f32x16 (&o)[(Kv<FP8, D>::kDimBlocks)], 
         if constexpr (LO) {
             if (lo_on) o[db] = mfma32x32x16(cur, st < kDB ? p0lo : p1lo, o[db]);
         }
-        if constexpr (st % kDmaEvery == 0) {
-            if (dma.on) half_dma_row<FP8, D, st / kDmaEvery>(dma, lane_off, lane, wave);
-        }
+        if constexpr (st == 0) pre();
         if constexpr (OVERLAP && (st % kSmEvery == kSmEvery - 1)) {
             constexpr int i = st / kSmEvery;
             softmax_elem<LO_NEXT>(c, sc, sn[i], i, psum, pend, pn0, pn1, ln0, ln1);
         }
+    };
+    if constexpr (!PRE) {
+#pragma unroll
+        for (int j = 0; j < kP; ++j) vbuf[j] = v_operand<FP8, D>(sV, vr, kb, j);
+    }
+    static_for<kMfma>([&](auto ST) {
+        constexpr int st = decltype(ST)::value;
+        if constexpr (st < kMfma - HOLD) step(ST);
+        if constexpr (st % kDmaEvery == 0) {
+            if (dma.on) half_dma_row<FP8, D, st / kDmaEvery>(dma, lane_off, lane, wave);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    if (tail_on) sync();
+    static_for<kP>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < HOLD) step(std::integral_constant<int, kMfma - HOLD + i>{});
+        __builtin_amdgcn_sched_barrier(0);
+        fill(I);
         __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (OVERLAP) softmax_flush<LO_NEXT>(c, psum, pend, pn1, ln1);
@@ -847,6 +920,15 @@ void prefill_hd512_kernel(PrefillArgs a) {
         half_dma_all<FP8, D>(refill(true, page0, v0, kt_lo, 1, true), lane_off, lane, wave);
         half_dma_all<FP8, D>(refill(false, page0, v0, kt_lo, 0, true), lane_off, lane, wave);
     }
+    // The operand ring `opr` of the phases (each phase's first reads are issued by
+    // the phase before it), and the wait and barrier that open every phase: before each phase the half
+    // it reads was issued two refills (2 kD loads) before the newest.
+    constexpr int kHold = kHoldOf<FP8>;
+    RawOf<FP8> opr[kPrefetchOf<FP8>];
+    auto sync = [&] {
+        wait_vmcnt<2 * kD>();
+        lds_barrier();
+    };
     // One 64-key tile.  kFirst (the range's first tile, peeled off the loop):
     // the reference maximum is taken, P.V starts O from zero, and P can carry
     // its second bf16 term, which it does when the block's first row sees at
@@ -878,16 +960,20 @@ void prefill_hd512_kernel(PrefillArgs a) {
         bf16x8 pl[4];                     // second terms (kLo only)
         f32x16 s0, s1;
 
-        // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill
-        // (each refill is named before the wait that precedes its block, so
-        // that the address work overlaps the wait rather than delaying the
-        // block's first MFMA)
+        // ---- QK0: reads K rows 0..31 of tile kt; V rows 32..63 of kt refill.
+        // Past the range's first tile the barrier that opens QK0 was taken at
+        // the end of the previous tile's PV1, which also read QK0's first
+        // operands into `opr` and issued its own last MFMAs after it.  Every
+        // phase ends the same way: its last kHold MFMAs go out after the next
+        // phase's barrier, beside that phase's first operand reads.  Each
+        // refill is named after the barrier of the phase that issues it,
+        // where those held MFMAs cover the address work.
+        if constexpr (kFirst) sync();
         const HalfDma dv1 = refill(false, page, valid, kt, 1, true);
-        hold_before_wait<APPEND>();
-        wait_vmcnt<2 * kD>();
-        lds_barrier();
-        qk_block<false, FP8, D>(s0, 0, qf, sK, koff, s0, c0, psum0, pf[0], pf[1], pl[0], pl[1],
-                                dv1, lane_off, lane, wave, [] {});
+        qk_block<false, FP8, D, false, !kFirst, kHold>(
+            s0, 0, qf, sK, koff, opr, s0, c0, psum0, pf[0], pf[1], pl[0], pl[1], dv1, lane_off,
+            lane, wave, [] {}, true, sync,
+            [&](auto I) { opr[decltype(I)::value] = k_operand<FP8, D>(sK, koff, 1, I); });
         page_cur = page_n;
         page_nx = t2 >= ntiles ? page_n
                 : (t2_staged ? __builtin_amdgcn_readfirstlane(page_nn_raw)
@@ -896,63 +982,66 @@ void prefill_hd512_kernel(PrefillArgs a) {
         // ---- QK1 with block 0's softmax; K rows 0..31 of tile kt+1 refill.
         // Block 0's masking and reference run after QK1's first MFMA.
         const HalfDma dk0 = refill(true, page_n, valid_n, kt + 1, 0, true);
-        hold_before_wait<APPEND>();
-        wait_vmcnt<2 * kD>();
-        lds_barrier();
-        qk_block<true, FP8, D, kLo>(s1, 1, qf, sK, koff, s0, c0, psum0, pf[0], pf[1], pl[0],
-                                       pl[1], dk0, lane_off, lane, wave, [&] {
-            mfma_vgpr_drain(s0);
-            if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
-            if constexpr (WINDOW) lazy_reference(s0, a.scale_log2, m_ref, c0);
-            if constexpr (!WINDOW && kFirst) {
-                // reference maximum: the row's maximum over the range's first
-                // 32 keys.  Without split-K key 0 is visible to every row, so
-                // it is finite; a split can start past a row's causal limit,
-                // and that row then takes 0 (every p = 0, an empty partial).
-                float m0 = -__builtin_inff();
+        qk_block<true, FP8, D, kLo, true, kHold>(
+            s1, 1, qf, sK, koff, opr, s0, c0, psum0, pf[0], pf[1], pl[0], pl[1], dk0, lane_off,
+            lane, wave,
+            [&] {
+                mfma_vgpr_drain(s0);
+                if (mask) mask_block<WINDOW>(s0, key0 + 4 * h, n_row, lo_row);
+                if constexpr (WINDOW) lazy_reference(s0, a.scale_log2, m_ref, c0);
+                if constexpr (!WINDOW && kFirst) {
+                    // reference maximum: the row's maximum over the range's
+                    // first 32 keys.  Without split-K key 0 is visible to
+                    // every row, so it is finite; a split can start past a
+                    // row's causal limit, and that row then takes 0 (every
+                    // p = 0, an empty partial).
+                    float m0 = -__builtin_inff();
 #pragma unroll
-                for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
-                m0 = fmaxf(m0, __shfl_xor(m0, 32)) * a.scale_log2;
-                m0 = m0 == -__builtin_inff() ? 0.f : m0;
-                m_ref = m0;
-                c0.neg_m_ref = -m0;
-            }
-        });
+                    for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s0[i]);
+                    m0 = fmaxf(m0, __shfl_xor(m0, 32)) * a.scale_log2;
+                    m0 = m0 == -__builtin_inff() ? 0.f : m0;
+                    m_ref = m0;
+                    c0.neg_m_ref = -m0;
+                }
+            },
+            true, sync,
+            [&](auto I) { opr[decltype(I)::value] = v_operand<FP8, D>(sV, vr, 0, I); });
         // block 0's P must be representable before its P.V (O is still
-        // unwritten in the first tile): the vote is taken here and acted on
-        // after the barrier, whose wait hides its latency
+        // unwritten in the first tile)
         const bool over0 = block_over(psum0);
-        mfma_vgpr_drain(s1);
-        if (mask) mask_block<WINDOW>(s1, key0 + 32 + 4 * h, n_row, lo_row);
-        if constexpr (WINDOW) lazy_reference(s1, a.scale_log2, m_ref, c0);
 
-        // ---- PV0 with block 1's softmax; K rows 32..63 of tile kt+1 refill
-        const HalfDma dk1 = refill(true, page_n, valid_n, kt + 1, 1, true);
-        hold_before_wait<APPEND>();
-        wait_vmcnt<2 * kD>();
-        lds_barrier();
+        // ---- PV0 with block 1's softmax; K rows 32..63 of tile kt+1 refill.
+        // Block 1's masking runs after PV0's first MFMA (the last MFMAs of
+        // its Q.K^T went out after the barrier).
         if (__builtin_expect(over0, 0)) {
             float none = 0.f;
             raise_reference<kLo>(o, !kFirst, s0, m_ref, c0, l_run, none, psum0, pf[0], pf[1],
                                     pl[0], pl[1]);
         }
-        pv_block<kFirst, true, FP8, D, kLo, kLo>(o, 0, pf[0], pf[1], pl[0], pl[1], sV, vr,
-                                                       s1, c0, psum1, pf[2], pf[3], pl[2], pl[3],
-                                                       dk1, lane_off, lane, wave, lo_on);
+        const HalfDma dk1 = refill(true, page_n, valid_n, kt + 1, 1, true);
+        pv_block<kFirst, true, FP8, D, kLo, kLo, true, kHold>(
+            o, 0, pf[0], pf[1], pl[0], pl[1], sV, vr, opr, s1, c0, psum1, pf[2], pf[3], pl[2],
+            pl[3], dk1, lane_off, lane, wave, lo_on,
+            [&] {
+                mfma_vgpr_drain(s1);
+                if (mask) mask_block<WINDOW>(s1, key0 + 32 + 4 * h, n_row, lo_row);
+                if constexpr (WINDOW) lazy_reference(s1, a.scale_log2, m_ref, c0);
+            },
+            true, sync,
+            [&](auto I) { opr[decltype(I)::value] = v_operand<FP8, D>(sV, vr, 1, I); });
         // block 1's P likewise (O now holds block 0 of this tile as well)
         const bool over1 = block_over(psum1);
 
-        // ---- PV1; V rows 0..31 of tile kt+1 refill
-        const HalfDma dv0 = refill(false, page_n, valid_n, kt + 1, 0, true);
-        hold_before_wait<APPEND>();
-        wait_vmcnt<2 * kD>();
-        lds_barrier();
+        // ---- PV1; V rows 0..31 of tile kt+1 refill.  Its tail opens the
+        // next tile's QK0 (there is none after the range's last tile).
         if (__builtin_expect(over1, 0))
             raise_reference<kLo>(o, true, s1, m_ref, c0, l_run, psum0, psum1, pf[2], pf[3],
                                     pl[2], pl[3]);
-        pv_block<false, false, FP8, D, kLo, false>(o, 1, pf[2], pf[3], pl[2], pl[3], sV, vr,
-                                                      s1, c0, psum1, pf[2], pf[3], pl[2], pl[3],
-                                                      dv0, lane_off, lane, wave, lo_on);
+        const HalfDma dv0 = refill(false, page_n, valid_n, kt + 1, 0, true);
+        pv_block<false, false, FP8, D, kLo, false, true, kHold>(
+            o, 1, pf[2], pf[3], pl[2], pl[3], sV, vr, opr, s1, c0, psum1, pf[2], pf[3], pl[2],
+            pl[3], dv0, lane_off, lane, wave, lo_on, [] {}, more, sync,
+            [&](auto I) { opr[decltype(I)::value] = k_operand<FP8, D>(sK, koff, 0, I); });
         l_run += psum0 + psum1;
     };
     if (ntiles > kt_lo) {
