@@ -48,8 +48,8 @@ TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/prefill_common.h",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "ec445d3a80dd14ecaa8c13f68c50dfabdfce94d9883684a87a3b669534e16713",
-    "fetch_bytes": 1983035157,
+    "sha256": "07278d38ab6c47796513c589cfe37fd12174ad3aa6ee11d255a01d1b1eada639",
+    "fetch_bytes": 1982881178,
     "write_bytes": 268435456,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
