@@ -905,10 +905,12 @@ void prefill_hd512_kernel(PrefillArgs a) {
     // order V1(j) [during QK0(j)], K0(j+1) [QK1(j)], K1(j+1) [PV0(j)],
     // V0(j+1) [PV1(j)], kD loads each; before each phase the half it reads was
     // issued two refills (2 kD loads) before the newest.  The last tile's
-    // successor refills are issued too, over an empty key range (a resource
-    // with no records lands zeros, fetching nothing) into halves nothing reads
-    // again, so that every refill site is unconditional and every count the
-    // same; the loop's end waits for them.
+    // successor refills are issued too, into halves nothing reads again, so
+    // that every refill site is unconditional and every count the same; the
+    // loop's end waits for them.  They re-read the last tile's own rows (its
+    // page, which is page_n there), already in the L2: loads over an empty
+    // range would fetch nothing, but measured slower than real ones (a copy
+    // whose refills all had no records ran 22 % slower than the kernel).
     // P in two bf16 terms in the first tile (see the tile below)
     const bool lo_on = n_min - max(kt_lo * kPage, lo_first) <= kLoKeys;
     int page_cur = ntiles > kt_lo ? page_of(kt_lo) : 0;              // page of tile kt
@@ -941,7 +943,8 @@ void prefill_hd512_kernel(PrefillArgs a) {
         const bool more = kt + 1 < ntiles;
         const int key0 = kt * kPage;
         const int valid = min(L - key0, kPage);
-        const int valid_n = more ? min(L - key0 - kPage, kPage) : 0;
+        // the last tile's successor refills re-read its own rows (see above)
+        const int valid_n = more ? min(L - key0 - kPage, kPage) : valid;
         const int page = page_cur;
         const int page_n = page_nx;
         // page id of tile kt + 2: the LDS read is issued here and its value
