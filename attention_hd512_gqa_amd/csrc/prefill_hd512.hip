@@ -172,6 +172,37 @@ __device__ __forceinline__ void dma_row_strided(u32x4 rsrc, uint32_t lds_base, u
     race_delay<0>();
 }
 
+// Row J of a wave's 8 (1 KB rows), as dma_row places it, with M0 written only
+// for rows 0 and 4: the buffer instruction's offset field, which the
+// hardware adds to both the source and the LDS address, carries (J % 4) KB,
+// and the XOR that forms the lane's source offset carries the 4 KB of rows
+// 4..7.  The loads of rows 1..3 and 5..7 use the M0 of the row-0 or row-4
+// load before them: every refill of a half starts at row 0, nothing else
+// in these kernels writes M0, and the asm statements keep their order.
+template <int J>
+__device__ __forceinline__ void dma_row_m0(u32x4 rsrc, uint32_t lds_base, uint32_t soff,
+                                           int lane_off) {
+    constexpr int kSwz = (swz(J) << 4) | ((J / 4) * 4096);
+    int voff;
+    if constexpr (J % 4 == 0) {
+        asm volatile(
+            "s_add_u32 m0, %3, %2\n\t"
+            "v_xor_b32 %0, %4, %1\n\t"
+            "buffer_load_dwordx4 %0, %5, %6 offen lds"
+            : "=&v"(voff)
+            : "v"(lane_off), "i"((J / 4) * 4096), "s"(lds_base), "i"(kSwz), "s"(rsrc), "s"(soff)
+            : "memory", "m0", "scc");
+    } else {
+        asm volatile(
+            "v_xor_b32 %0, %2, %1\n\t"
+            "buffer_load_dwordx4 %0, %3, %4 offen offset:%5 lds"
+            : "=&v"(voff)
+            : "v"(lane_off), "i"(kSwz), "s"(rsrc), "s"(soff), "i"((J % 4) * kRowBytes)
+            : "memory");
+    }
+    race_delay<0>();
+}
+
 // Refill load J of this wave's share of a half: 1 KB rows, row 8 wave + J of
 // the half; narrow rows, rows 8 wave + 2 J and + 1 (lanes 0-31 and 32-63),
 // each lane fetching the logical chunk that the swizzle stores at its LDS
@@ -190,7 +221,7 @@ __device__ __forceinline__ void half_dma_row(const HalfDma& d, int lane_off, int
                                                               d.stride, lane_off);
             return;
         }
-        dma_row<(swz(J) << 4), J * kRowBytes>(d.rsrc, d.lds_base, d.soff, lane_off);
+        dma_row_m0<J>(d.rsrc, d.lds_base, d.soff, lane_off);
     }
 }
 
