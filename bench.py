@@ -48,8 +48,8 @@ TRAFFIC_RECORD = {
     "sources": ["attention_hd512_gqa_amd/csrc/prefill_hd512.hip",
                 "attention_hd512_gqa_amd/csrc/prefill_common.h",
                 "attention_hd512_gqa_amd/csrc/device_common.h"],
-    "sha256": "07278d38ab6c47796513c589cfe37fd12174ad3aa6ee11d255a01d1b1eada639",
-    "fetch_bytes": 1982881178,
+    "sha256": "554357e1e25d8eadaf453c310006660510032aed151989912676826fc6366efd",
+    "fetch_bytes": 1988078376,
     "write_bytes": 268435456,
     "profile": "profiles/prefill_hd512_chunk8192_at_8192.md",
 }
