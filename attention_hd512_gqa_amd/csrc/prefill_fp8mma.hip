@@ -580,12 +580,12 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     }
 
     // ---- epilogue (shared with prefill_hd512_kernel): O in the true scale of p.
-    // The row's token and head are derived again from an opaque copy of the
-    // lane index: kept from the prologue they would stay live across the key
+    // The row's token and head are derived again from the lane index, which
+    // is itself recounted here (mbcnt) rather than read from the thread
+    // index: kept from the prologue, either would stay live across the key
     // loop, where every register is taken, and spill.
     static_assert(kWaves * 32 * kHeadDim * 2 <= kTileArea, "staging fits the tile buffers");
-    int lane_e = lane;
-    asm volatile("" : "+v"(lane_e));
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int r_e = wave * 32 + (lane_e & 31);
     const int tr_e = r_e / a.g;
     const bool valid_e = (tr_e < a.tok_per_wg) && (t0 + tr_e <= t_last);
@@ -593,7 +593,7 @@ void prefill_fp8mma_kernel(PrefillArgs a) {
     const int head_e = kvh * a.g + (valid_e ? r_e - tr_e * a.g : 0);
     prefill_epilogue<OUT_FP32, SPLIT, kHeadDim, !OUT_FP32, true>(
         a, o, l_run, m_ref, ntiles > 0,
-        RowSlot{q0, q0 + t_e, head_e, t0, t_last, kvh, split, valid_e}, lds, lane, wave);
+        RowSlot{q0, q0 + t_e, head_e, t0, t_last, kvh, split, valid_e}, lds, lane_e, wave);
 }
 
 }  // namespace
