@@ -211,6 +211,40 @@ __device__ __forceinline__ void acc_fence8(f32x4 (&o)[8]) {
                    "+a"(o[6]), "+a"(o[7]));
 }
 
+// Load I of an E4M3 row-pair refill: rows 2 I and 2 I + 1 of a block (lanes
+// 0-31 and 32-63), 16 bytes per lane, landing at LDS bytes 1024 I + 16 lane
+// past `lds` and fetched from block byte 1024 I + 512 (lane / 32) + 16 c,
+// c = (lane % 32) ^ swz8(row).  For rows 2 I + h (h = lane / 32) of a block
+// that starts at a multiple of 32 rows, swz8 is h OR (2 (I % 8) ^ 4 (I / 8)),
+// so the whole per-lane offset is lane_base XOR a constant; a block starting
+// at 16 mod 32 (the tile kernel's odd waves) takes bit 2 of swz8 into
+// lane_base.  M0 is written for every fourth load: the instruction's offset
+// field, which the hardware adds to both the source and the LDS address,
+// carries (I % 4) KB; it also enters the resource's range check, so rows past
+// the record count still arrive as zeros.  The SALU write of M0 and the load
+// that reads it are one VALU op apart.
+template <int I>
+__device__ __forceinline__ void dma_row_pair(u32x4 rsrc, uint32_t lds, int lane_base) {
+    constexpr int kC = (((2 * (I % 8)) ^ (4 * (I / 8))) << 4) | ((I / 4) * 4096);
+    int voff;
+    if constexpr (I % 4 == 0) {
+        asm volatile(
+            "s_add_u32 m0, %3, %2\n\t"
+            "v_xor_b32 %0, %4, %1\n\t"
+            "buffer_load_dwordx4 %0, %5, 0 offen nt lds"
+            : "=&v"(voff)
+            : "v"(lane_base), "i"((I / 4) * 4096), "s"(lds), "i"(kC), "s"(rsrc)
+            : "memory", "m0", "scc");
+    } else {
+        asm volatile(
+            "v_xor_b32 %0, %2, %1\n\t"
+            "buffer_load_dwordx4 %0, %3, 0 offen offset:%4 nt lds"
+            : "=&v"(voff)
+            : "v"(lane_base), "i"(kC), "s"(rsrc), "i"((I % 4) * 2 * kHeadDim)
+            : "memory");
+    }
+}
+
 // This wave's 16 rows (16 wave .. 16 wave + 15) of a 64-key tile -> LDS, rows
 // past `valid` as zeros.  bf16: 1 KB rows, one per DMA, swizzled by swz.
 // E4M3: 512-byte rows, two per DMA, 16-byte chunk c of row r stored at chunk
@@ -221,21 +255,14 @@ __device__ __forceinline__ void issue_tile(const char* src, int valid, ATTN_LDS 
     if constexpr (!FP8) {
         rows16_to_lds<true>(buffer_rsrc(src, (uint32_t)valid * kRowBytes), buf, wave, lane * 16);
     } else {
+        // rows 16 wave + 2 i + h: the wave's block starts 16 wave rows in
         const u32x4 rsrc = buffer_rsrc(src, (uint32_t)valid * kHeadDim);
-        const uint32_t lds = (uint32_t)(uintptr_t)buf + (uint32_t)wave * 16 * kHeadDim;
+        const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)((uint32_t)(uintptr_t)buf + (uint32_t)wave * 16 * kHeadDim));
         const int hl = lane >> 5;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 16 * wave + 2 * i + hl;
-            const int voff = r * kHeadDim + (((lane & 31) ^ swz8(r)) << 4);
-            asm volatile(
-                "s_mov_b32 m0, %1\n\t"
-                "s_nop 0\n\t"
-                "buffer_load_dwordx4 %0, %2, 0 offen nt lds"
-                :
-                : "v"(voff), "s"(lds + 2 * i * kHeadDim), "s"(rsrc)
-                : "memory", "m0");
-        }
+        const int lane_base = (wave * 16 * kHeadDim) | (hl << 9) |
+                              ((((lane & 31) ^ hl) ^ (4 * (wave & 1))) << 4);
+        static_for<8>([&](auto I) { dma_row_pair<decltype(I)::value>(rsrc, lds, lane_base); });
         race_delay<0>();
     }
 }
@@ -635,20 +662,10 @@ void decode_split_tile_kernel(DecodeArgs a) {
 __device__ __forceinline__ void dma_half(const char* src, int rows, ATTN_LDS char* buf,
                                            int lane) {
     const u32x4 rsrc = buffer_rsrc(src, (uint32_t)rows * kHeadDim);
-    const uint32_t lds = (uint32_t)(uintptr_t)buf;
+    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)buf);
     const int hl = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < kHalfKeys / 2; ++i) {
-        const int r = 2 * i + hl;
-        const int voff = r * kHeadDim + (((lane & 31) ^ swz8(r)) << 4);
-        asm volatile(
-            "s_mov_b32 m0, %1\n\t"
-            "s_nop 0\n\t"
-            "buffer_load_dwordx4 %0, %2, 0 offen nt lds"
-            :
-            : "v"(voff), "s"(lds + 2 * i * kHeadDim), "s"(rsrc)
-            : "memory", "m0");
-    }
+    const int lane_base = (hl << 9) | (((lane & 31) ^ hl) << 4);
+    static_for<kHalfKeys / 2>([&](auto I) { dma_row_pair<decltype(I)::value>(rsrc, lds, lane_base); });
     race_delay<0>();
 }
 
